@@ -1,0 +1,275 @@
+"""fp64 CPU oracle for one GPU's shard of a Megatron-LM tensor-parallel layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this
+module: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it.  It shares no code with the HIP library.
+
+Everything here is the plain definition written out in numpy float64
+(``np.matmul`` is the only library step, plus ``scipy.special.erf``); there is
+no tiling, fusion or reordering.  Sources (the pages these definitions come
+from):
+
+* [JY] "Parallelism on Jiang Yi's Homepage", note "megatron-lm": sections
+  FFN (Y = GeLU(X W1) W2, the column split of W1 and the row split of W2, the
+  f/g table, the SwiGLU split), Attention (per-head outputs, O = [o_1..o_h] W_O).
+* [HC] "Splitting the model: five parallelisms and the traffic they make",
+  section 3.4 "Tensor parallelism", Figures 3.4-3.6 (Z = sum_k Z_k; g
+  all-reduces the partial sums forward, f all-reduces dX backward; heads are
+  assigned to GPUs in contiguous groups).
+* [BM] "tensor-parallelism" (brunomaga.github.io), section "Megatron-LM tensor
+  parallelism" (Megatron_f / Megatron_g, the feed-forward block with its bias
+  added after the reduction, the attention block with its causal mask and
+  1/sqrt(head_dim) scale).
+* [DW] "Chapter 8: Distributed Training", section 8.4.2 NCCL (all-reduce SUM).
+
+Readings taken where the pages are silent or garbled are listed in the
+repository's design notes; the ones that change arithmetic are: the exact
+erf form of GeLU, 1/sqrt(d_h) as the softmax scale ([JY]'s attention equation
+prints d_h without the root), W1 as the Swish'd gate of SwiGLU, the causal
+mask keeping u <= t, and weights laid out [in x out] with Y = X W.
+
+Every function returns float64 arrays.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+try:  # scipy's erf; math.erf is the fallback and the brute-force cross-check
+    from scipy.special import erf as _erf
+except Exception:  # pragma: no cover
+    _erf = np.vectorize(math.erf, otypes=[np.float64])
+
+__all__ = [
+    "gelu", "gelu_prime", "swish", "swish_prime",
+    "mlp_shard_fwd", "mlp_shard_bwd", "mlp_unsharded", "mlp_unsharded_bwd",
+    "swiglu_shard_fwd", "swiglu_shard_bwd", "swiglu_unsharded",
+    "attn_shard_fwd", "attn_unsharded", "attn_core",
+    "shard_reduce", "shard_range",
+]
+
+_SQRT2 = math.sqrt(2.0)
+_INV_SQRT_2PI = 1.0 / math.sqrt(2.0 * math.pi)
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Activations.  GeLU is named on the pages ([JY] FFN; [HC] 3.4; [BM] MLP
+# block) and called as PyTorch's default (erf) form in the code listings.
+# ----------------------------------------------------------------------------
+
+def gelu(x):
+    """GeLU(x) = x * Phi(x), Phi the standard normal CDF (exact erf form)."""
+    x = _f64(x)
+    return x * 0.5 * (1.0 + _erf(x / _SQRT2))
+
+
+def gelu_prime(x):
+    """dGeLU/dx = Phi(x) + x * phi(x), phi the standard normal density."""
+    x = _f64(x)
+    return 0.5 * (1.0 + _erf(x / _SQRT2)) + x * _INV_SQRT_2PI * np.exp(-0.5 * x * x)
+
+
+def _sigmoid(x):
+    x = _f64(x)
+    # exp of a non-positive argument only: no overflow for large |x|
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def swish(x):
+    """Swish(x) = x * sigmoid(x) ([JY] SwiGLU section; ``F.silu`` in its code)."""
+    x = _f64(x)
+    return x * _sigmoid(x)
+
+
+def swish_prime(x):
+    """dSwish/dx = sigmoid(x) * (1 + x * (1 - sigmoid(x)))."""
+    x = _f64(x)
+    s = _sigmoid(x)
+    return s * (1.0 + x * (1.0 - s))
+
+
+# ----------------------------------------------------------------------------
+# GeLU MLP shard.  [JY] FFN: W1 = [W11, W12] split by columns, GeLU applied
+# per slice, W2 split by rows, Y = sum_i GeLU(X W1_i) W2_i.  [HC] Figure 3.4.
+# ----------------------------------------------------------------------------
+
+def mlp_shard_fwd(X, W1_i, W2_i) -> Dict[str, np.ndarray]:
+    """A_i = X W1_i; H_i = GeLU(A_i); Z_i = H_i W2_i (this shard's summand)."""
+    X, W1_i, W2_i = _f64(X), _f64(W1_i), _f64(W2_i)
+    A = X @ W1_i
+    H = gelu(A)
+    Z = H @ W2_i
+    return {"A": A, "H": H, "Z": Z}
+
+
+def mlp_shard_bwd(X, W1_i, W2_i, dY) -> Dict[str, np.ndarray]:
+    """Gradients of this shard given the full upstream gradient dY.
+
+    g is the identity in the backward pass ([JY] f/g table; [BM] Megatron_g),
+    so every shard sees the whole dY.  Chain rule through Z_i = GeLU(X W1_i) W2_i:
+    dH = dY W2_i^T, dA = dH * GeLU'(A), dW2_i = H^T dY, dW1_i = X^T dA,
+    dX_i = dA W1_i^T (the summand that f all-reduces, [HC] 3.4).
+    """
+    X, W1_i, W2_i, dY = _f64(X), _f64(W1_i), _f64(W2_i), _f64(dY)
+    A = X @ W1_i
+    H = gelu(A)
+    dH = dY @ W2_i.T
+    dA = dH * gelu_prime(A)
+    return {"dH": dH, "dA": dA, "dW2": H.T @ dY, "dW1": X.T @ dA, "dX": dA @ W1_i.T}
+
+
+def mlp_unsharded(X, W1, W2) -> np.ndarray:
+    """Y = GeLU(X W1) W2 on one device ([JY] FFN, first equation)."""
+    return gelu(_f64(X) @ _f64(W1)) @ _f64(W2)
+
+
+def mlp_unsharded_bwd(X, W1, W2, dY) -> Dict[str, np.ndarray]:
+    """Unsharded gradients of Y = GeLU(X W1) W2."""
+    return mlp_shard_bwd(X, W1, W2, dY)
+
+
+# ----------------------------------------------------------------------------
+# SwiGLU shard.  [JY] FFN, SwiGLU part: Y = (X W3 (.) Swish(X W1)) W2 with
+# W1, W3 split by columns and W2 by rows; the code computes
+# w2(silu(w1(x)) * w3(x)), so W1 is the Swish'd gate and W3 the multiplier.
+# ----------------------------------------------------------------------------
+
+def swiglu_shard_fwd(X, W1_i, W3_i, W2_i) -> Dict[str, np.ndarray]:
+    """G = X W1_i; U = X W3_i; H = Swish(G) * U; Z_i = H W2_i."""
+    X = _f64(X)
+    G = X @ _f64(W1_i)
+    U = X @ _f64(W3_i)
+    H = swish(G) * U
+    Z = H @ _f64(W2_i)
+    return {"G": G, "U": U, "H": H, "Z": Z}
+
+
+def swiglu_shard_bwd(X, W1_i, W3_i, W2_i, dY) -> Dict[str, np.ndarray]:
+    """dH = dY W2_i^T; dU = dH * Swish(G); dG = dH * U * Swish'(G);
+    dW2 = H^T dY; dW1 = X^T dG; dW3 = X^T dU; dX_i = dG W1_i^T + dU W3_i^T."""
+    X, W1_i, W3_i, W2_i, dY = map(_f64, (X, W1_i, W3_i, W2_i, dY))
+    G = X @ W1_i
+    U = X @ W3_i
+    H = swish(G) * U
+    dH = dY @ W2_i.T
+    dU = dH * swish(G)
+    dG = dH * U * swish_prime(G)
+    return {"dH": dH, "dG": dG, "dU": dU, "dW2": H.T @ dY, "dW1": X.T @ dG,
+            "dW3": X.T @ dU, "dX": dG @ W1_i.T + dU @ W3_i.T}
+
+
+def swiglu_unsharded(X, W1, W3, W2) -> np.ndarray:
+    X = _f64(X)
+    return (swish(X @ _f64(W1)) * (X @ _f64(W3))) @ _f64(W2)
+
+
+# ----------------------------------------------------------------------------
+# Attention head-group shard.  [JY] Attention: o_i = softmax(Q_i K_i^T / s) V_i,
+# O = [o_1..o_h] W_O.  [BM] Megatron_MHA: Q/K/V column-parallel by heads,
+# local causal softmax with masked_fill(tril == 0, -inf), scale head_dim^-0.5,
+# heads concatenated in order, row-parallel output projection.  [HC] Figure
+# 3.5: shard i owns a contiguous group of heads.
+# ----------------------------------------------------------------------------
+
+def attn_core(Q, K, V, causal: bool = True, scale: Optional[float] = None) -> np.ndarray:
+    """softmax(Q K^T * scale, masked) V for one head; Q, K, V are [s x d_h].
+
+    Masked entries (u > t when causal) are -inf before the softmax, so they
+    get weight exactly zero.  The softmax is taken directly over the row.
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    s, dh = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(dh)
+    S = (Q @ K.T) * scale
+    if causal:
+        S = np.where(np.tril(np.ones((s, K.shape[0]), dtype=bool)), S, -np.inf)
+    S = S - S.max(axis=1, keepdims=True)
+    P = np.exp(S)
+    P = P / P.sum(axis=1, keepdims=True)
+    return P @ V
+
+
+def attn_shard_fwd(X, Wq, Wk, Wv, Wo, b: int, s: int, h_local: int, d_head: int,
+                   causal: bool = True, scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """One shard's attention: returns Q, K, V as [b, h_l, s, d_h], the
+    concatenated head outputs O [b*s, h_l*d_h] and the partial Z = O W_O,i.
+
+    Local head j uses columns [j*d_h, (j+1)*d_h) of the shard's W_Q/W_K/W_V
+    and rows [j*d_h, (j+1)*d_h) of its W_O slice.
+    """
+    X = _f64(X).reshape(b, s, -1)
+    hd = h_local * d_head
+    Qf = X @ _f64(Wq)            # [b, s, hd]
+    Kf = X @ _f64(Wk)
+    Vf = X @ _f64(Wv)
+    Q = Qf.reshape(b, s, h_local, d_head).transpose(0, 2, 1, 3)
+    K = Kf.reshape(b, s, h_local, d_head).transpose(0, 2, 1, 3)
+    V = Vf.reshape(b, s, h_local, d_head).transpose(0, 2, 1, 3)
+    O = np.empty((b, s, h_local, d_head))
+    for bi in range(b):
+        for j in range(h_local):
+            O[bi, :, j, :] = attn_core(Q[bi, j], K[bi, j], V[bi, j], causal, scale)
+    O = O.reshape(b * s, hd)
+    Z = O @ _f64(Wo)
+    return {"Q": Q, "K": K, "V": V, "O": O, "Z": Z}
+
+
+def attn_unsharded(X, Wq, Wk, Wv, Wo, b: int, s: int, heads: int, d_head: int,
+                   causal: bool = True) -> Dict[str, np.ndarray]:
+    """All heads on one device: O = [o_1..o_h] W_O ([JY] Attention)."""
+    return attn_shard_fwd(X, Wq, Wk, Wv, Wo, b, s, heads, d_head, causal)
+
+
+# ----------------------------------------------------------------------------
+# Shard-reduce: the sum that g performs in the forward pass and f in the
+# backward pass ([JY] f/g table; [HC] 3.4 Z = sum_k Z_k; [DW] 8.4.2 all_reduce
+# with ReduceOp.SUM).  The row-parallel bias is added once, after the sum
+# ([BM] Megatron_FeedForward: the bias is added after Megatron_g).
+# ----------------------------------------------------------------------------
+
+def shard_reduce(partials: Sequence, bias=None) -> np.ndarray:
+    """out = sum_i P_i (+ bias broadcast over the trailing dimension, once)."""
+    P = [_f64(p) for p in partials]
+    out = np.zeros_like(P[0])
+    for p in P:
+        out = out + p
+    if bias is not None:
+        bias = _f64(bias).reshape(-1)
+        flat = out.reshape(-1)
+        flat += np.resize(bias, flat.shape)   # element e gets bias[e % len]
+        out = flat.reshape(out.shape)
+    return out
+
+
+def shard_range(total: int, n_shards: int, index: int):
+    """Contiguous equal split: shard ``index`` owns [index*k, (index+1)*k),
+    k = total / n_shards.  Indivisible totals are an error, as the pages'
+    listings assert ([JY] Implementation: divisibility asserts on features,
+    heads and vocabulary; [BM] Megatron_MHA raises ValueError)."""
+    if n_shards <= 0 or total <= 0 or not (0 <= index < n_shards):
+        raise ValueError("bad shard arguments")
+    if total % n_shards:
+        raise ValueError(f"{total} is not divisible by {n_shards}")
+    k = total // n_shards
+    return index * k, k
+
+
+def max_rel_err(y, ref) -> float:
+    """||y - ref||_inf / ||ref||_inf over all elements (0 when both are 0)."""
+    y, ref = _f64(y), _f64(ref)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(y - ref))) if ref.size else 0.0
+    if den == 0.0:
+        return num
+    return num / den
+
+
+__all__.append("max_rel_err")

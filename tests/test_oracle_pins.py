@@ -1,0 +1,374 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test ties the oracle to something other than itself: textbook values of
+the normal distribution, closed-form identities, central finite differences,
+brute-force loops on tiny inputs (``math.fsum``/``math.erf``/``math.exp``, not
+numpy), the pages' sharding identities and their printed worked examples.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import tpsynth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- activations
+
+def test_gelu_textbook_values():
+    # Phi(1), Phi(2), phi(1) from standard normal tables (e.g. Abramowitz &
+    # Stegun, Table 26.1): GeLU(x) = x Phi(x); GeLU'(x) = Phi(x) + x phi(x).
+    phi1, Phi1, Phi2 = 0.24197072451914337, 0.8413447460685429, 0.9772498680518208
+    assert O.gelu(1.0) == pytest.approx(Phi1, abs=1e-15)
+    assert O.gelu(2.0) == pytest.approx(2 * Phi2, abs=1e-15)
+    assert O.gelu(-1.0) == pytest.approx(-(1 - Phi1), abs=1e-15)
+    assert O.gelu(0.0) == 0.0
+    assert O.gelu_prime(0.0) == pytest.approx(0.5, abs=1e-15)
+    assert O.gelu_prime(1.0) == pytest.approx(Phi1 + phi1, abs=1e-15)
+    assert O.gelu(10.0) == pytest.approx(10.0, abs=1e-15)
+    assert abs(O.gelu(-10.0)) < 1e-20
+
+
+def test_swish_closed_forms():
+    sig1 = 1.0 / (1.0 + math.exp(-1.0))
+    assert O.swish(1.0) == pytest.approx(sig1, abs=1e-15)
+    assert O.swish(1.0) == pytest.approx(0.7310585786300049, abs=1e-15)
+    assert O.swish_prime(0.0) == pytest.approx(0.5, abs=1e-15)
+    assert O.swish_prime(1.0) == pytest.approx(0.9276705118714869, abs=1e-14)
+    assert O.swish(0.0) == 0.0
+    # no overflow far out on either side
+    assert O.swish(-800.0) == pytest.approx(0.0, abs=1e-300)
+    assert O.swish(800.0) == pytest.approx(800.0)
+
+
+def test_activation_reflection_identities():
+    x = np.random.default_rng(1).standard_normal(1000) * 4
+    # Phi(-x) = 1 - Phi(x)  =>  GeLU(-x) = GeLU(x) - x ; likewise for Swish
+    np.testing.assert_allclose(O.gelu(-x), O.gelu(x) - x, atol=1e-13)
+    np.testing.assert_allclose(O.swish(-x), O.swish(x) - x, atol=1e-13)
+
+
+def test_activation_derivatives_match_finite_differences():
+    x = np.linspace(-6, 6, 241)
+    h = 1e-5
+    fd_g = (O.gelu(x + h) - O.gelu(x - h)) / (2 * h)
+    fd_s = (O.swish(x + h) - O.swish(x - h)) / (2 * h)
+    np.testing.assert_allclose(O.gelu_prime(x), fd_g, atol=1e-9)
+    np.testing.assert_allclose(O.swish_prime(x), fd_s, atol=1e-9)
+
+
+def test_erf_matches_math_erf():
+    x = np.linspace(-5, 5, 101)
+    ref = np.array([0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in x])
+    np.testing.assert_allclose(O.gelu(x), ref, rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------------- brute-force helpers
+
+def _bf_matmul(A, B):
+    A, B = np.asarray(A, float), np.asarray(B, float)
+    n, k = A.shape
+    k2, m = B.shape
+    assert k == k2
+    return np.array([[math.fsum(A[i, t] * B[t, j] for t in range(k)) for j in range(m)]
+                     for i in range(n)])
+
+
+def _bf_gelu(v):
+    return v * 0.5 * (1.0 + math.erf(v / math.sqrt(2.0)))
+
+
+def _bf_swish(v):
+    return v / (1.0 + math.exp(-v))
+
+
+def _tiny(shape, seed, std=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * std
+
+
+# ------------------------------------------------------------------ GeLU MLP
+
+def test_mlp_fwd_brute_force():
+    X, W1, W2 = _tiny((3, 4), 0), _tiny((4, 5), 1), _tiny((5, 4), 2)
+    r = O.mlp_shard_fwd(X, W1, W2)
+    A = _bf_matmul(X, W1)
+    H = np.vectorize(_bf_gelu)(A)
+    Z = _bf_matmul(H, W2)
+    np.testing.assert_allclose(r["A"], A, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(r["H"], H, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(r["Z"], Z, rtol=1e-13, atol=1e-14)
+
+
+def test_mlp_fwd_brute_force_c1_size():
+    wl = tpsynth.WORKLOADS["C1"]
+    inp = tpsynth.mlp_inputs(wl)
+    r = O.mlp_shard_fwd(inp["X"], inp["W1s"][0], inp["W2s"][0])
+    A = _bf_matmul(inp["X"], inp["W1s"][0])
+    np.testing.assert_allclose(r["A"], A, rtol=1e-13, atol=1e-13)
+
+
+def _fd_grad(fun, arr, h=1e-6):
+    g = np.zeros_like(arr)
+    it = np.nditer(arr, flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        old = arr[idx]
+        arr[idx] = old + h
+        fp = fun()
+        arr[idx] = old - h
+        fm = fun()
+        arr[idx] = old
+        g[idx] = (fp - fm) / (2 * h)
+    return g
+
+
+def test_mlp_bwd_matches_finite_differences():
+    X, W1, W2, dY = _tiny((3, 4), 3), _tiny((4, 6), 4, 0.7), _tiny((6, 4), 5, 0.7), _tiny((3, 4), 6)
+    loss = lambda: float(np.sum(dY * O.mlp_shard_fwd(X, W1, W2)["Z"]))
+    g = O.mlp_shard_bwd(X, W1, W2, dY)
+    np.testing.assert_allclose(g["dX"], _fd_grad(loss, X), atol=1e-8)
+    np.testing.assert_allclose(g["dW1"], _fd_grad(loss, W1), atol=1e-8)
+    np.testing.assert_allclose(g["dW2"], _fd_grad(loss, W2), atol=1e-8)
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_mlp_sharding_identity_equal_splits(n):
+    # [JY] FFN: GeLU(X W1) W2 = sum_i GeLU(X W1_i) W2_i for a column split of
+    # W1 and the matching row split of W2; backward: dX = sum_i dX_i ([HC] 3.4).
+    wl = tpsynth.WORKLOADS["C1"]
+    inp = tpsynth.mlp_inputs(wl)
+    X, W1, W2, dY = inp["X"], inp["W1"], inp["W2"], inp["dY"]
+    f = W1.shape[1] // n
+    Y = O.mlp_unsharded(X, W1, W2)
+    full = O.mlp_unsharded_bwd(X, W1, W2, dY)
+    parts = [O.mlp_shard_fwd(X, W1[:, i * f:(i + 1) * f], W2[i * f:(i + 1) * f]) for i in range(n)]
+    grads = [O.mlp_shard_bwd(X, W1[:, i * f:(i + 1) * f], W2[i * f:(i + 1) * f], dY) for i in range(n)]
+    assert O.max_rel_err(O.shard_reduce([p["Z"] for p in parts]), Y) < 1e-12
+    assert O.max_rel_err(O.shard_reduce([g["dX"] for g in grads]), full["dX"]) < 1e-12
+    assert O.max_rel_err(np.concatenate([g["dW1"] for g in grads], axis=1), full["dW1"]) < 1e-12
+    assert O.max_rel_err(np.concatenate([g["dW2"] for g in grads], axis=0), full["dW2"]) < 1e-12
+
+
+def test_mlp_sharding_identity_uneven_split():
+    # [JY] FFN allows any d_1 + d_2 = d_ff.
+    wl = tpsynth.WORKLOADS["C1"]
+    inp = tpsynth.mlp_inputs(wl)
+    X, W1, W2 = inp["X"], inp["W1"], inp["W2"]
+    cuts = [0, 37, 100, 201, 256]
+    Zs = [O.mlp_shard_fwd(X, W1[:, a:b], W2[a:b])["Z"] for a, b in zip(cuts[:-1], cuts[1:])]
+    assert O.max_rel_err(O.shard_reduce(Zs), O.mlp_unsharded(X, W1, W2)) < 1e-12
+
+
+def test_mlp_sharding_identity_c2_shape():
+    # All 8 shards of the GPT-2-medium-shaped workload, on a sample of 128 rows
+    # (rows are independent in this identity).
+    wl = tpsynth.WORKLOADS["C2"]
+    inp = tpsynth.mlp_inputs(wl)
+    X = inp["X"][::64]
+    Zs = [O.mlp_shard_fwd(X, inp["W1s"][i], inp["W2s"][i])["Z"] for i in range(8)]
+    assert O.max_rel_err(O.shard_reduce(Zs), O.mlp_unsharded(X, inp["W1"], inp["W2"])) < 1e-12
+
+
+def test_row_split_before_gelu_is_not_a_sharding():
+    # [JY] FFN and [BM] (quoting the Megatron paper): splitting W1 by rows and
+    # X by columns needs a sum before the GeLU, GeLU(X1A1 + X2A2) != GeLU(X1A1) + GeLU(X2A2).
+    assert O.gelu(1.0) + O.gelu(1.0) == pytest.approx(1.6826894921370859, abs=1e-15)
+    assert abs(O.gelu(2.0) - 2 * O.gelu(1.0)) > 0.27
+    inp = tpsynth.mlp_inputs(tpsynth.WORKLOADS["C1"])
+    X, W1 = inp["X"].astype(float), inp["W1"].astype(float)
+    k = X.shape[1] // 2
+    ref = O.gelu(X @ W1)
+    wrong = O.gelu(X[:, :k] @ W1[:k]) + O.gelu(X[:, k:] @ W1[k:])
+    right = O.gelu(X[:, :k] @ W1[:k] + X[:, k:] @ W1[k:])
+    assert O.max_rel_err(wrong, ref) > 1e-2
+    assert O.max_rel_err(right, ref) < 1e-13
+
+
+# -------------------------------------------------------------------- SwiGLU
+
+def test_swiglu_fwd_brute_force():
+    X, W1, W3, W2 = _tiny((3, 4), 10), _tiny((4, 5), 11), _tiny((4, 5), 12), _tiny((5, 4), 13)
+    r = O.swiglu_shard_fwd(X, W1, W3, W2)
+    G, U = _bf_matmul(X, W1), _bf_matmul(X, W3)
+    H = np.vectorize(_bf_swish)(G) * U
+    np.testing.assert_allclose(r["G"], G, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(r["H"], H, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(r["Z"], _bf_matmul(H, W2), rtol=1e-13, atol=1e-14)
+
+
+def test_swiglu_bwd_matches_finite_differences():
+    X, W1, W3, W2, dY = (_tiny((3, 4), 20), _tiny((4, 5), 21, 0.7), _tiny((4, 5), 22, 0.7),
+                         _tiny((5, 4), 23, 0.7), _tiny((3, 4), 24))
+    loss = lambda: float(np.sum(dY * O.swiglu_shard_fwd(X, W1, W3, W2)["Z"]))
+    g = O.swiglu_shard_bwd(X, W1, W3, W2, dY)
+    for name, arr in (("dX", X), ("dW1", W1), ("dW3", W3), ("dW2", W2)):
+        np.testing.assert_allclose(g[name], _fd_grad(loss, arr), atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("cuts", [[0, 64, 128], [0, 32, 64, 96, 128], [0, 5, 77, 128]])
+def test_swiglu_sharding_identity(cuts):
+    # [JY] FFN, SwiGLU: Y = sum_i (X W3_i (.) Swish(X W1_i)) W2_i.
+    inp = tpsynth.random_swiglu(40, 48, 128, "f32", seed=7, w_std=0.1)
+    X, W1, W3, W2, dY = inp["X"], inp["W1"], inp["W3"], inp["W2"], inp["dY"]
+    Y = O.swiglu_unsharded(X, W1, W3, W2)
+    full = O.swiglu_shard_bwd(X, W1, W3, W2, dY)
+    Zs, dXs = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        Zs.append(O.swiglu_shard_fwd(X, W1[:, a:b], W3[:, a:b], W2[a:b])["Z"])
+        dXs.append(O.swiglu_shard_bwd(X, W1[:, a:b], W3[:, a:b], W2[a:b], dY)["dX"])
+    assert O.max_rel_err(O.shard_reduce(Zs), Y) < 1e-12
+    assert O.max_rel_err(O.shard_reduce(dXs), full["dX"]) < 1e-12
+
+
+# ----------------------------------------------------------------- attention
+
+def _bf_attention_head(Q, K, V, scale, causal=True):
+    s = Q.shape[0]
+    out = np.zeros_like(V)
+    for t in range(s):
+        us = range(t + 1) if causal else range(s)
+        sc = [math.fsum(Q[t, c] * K[u, c] for c in range(Q.shape[1])) * scale for u in us]
+        m = max(sc)
+        w = [math.exp(v - m) for v in sc]
+        z = math.fsum(w)
+        for c in range(V.shape[1]):
+            out[t, c] = math.fsum(w[i] * V[u, c] for i, u in enumerate(us)) / z
+    return out
+
+
+def test_attention_brute_force():
+    b, s, h, dh, d = 1, 5, 2, 4, 6
+    X, Wq, Wk, Wv, Wo = (_tiny((b * s, d), 30), _tiny((d, h * dh), 31), _tiny((d, h * dh), 32),
+                         _tiny((d, h * dh), 33), _tiny((h * dh, d), 34))
+    r = O.attn_shard_fwd(X, Wq, Wk, Wv, Wo, b, s, h, dh)
+    Qf, Kf, Vf = _bf_matmul(X, Wq), _bf_matmul(X, Wk), _bf_matmul(X, Wv)
+    heads = []
+    for j in range(h):
+        sl = slice(j * dh, (j + 1) * dh)
+        heads.append(_bf_attention_head(Qf[:, sl], Kf[:, sl], Vf[:, sl], 1 / math.sqrt(dh)))
+    Ob = np.concatenate(heads, axis=1)
+    np.testing.assert_allclose(r["O"], Ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["Z"], _bf_matmul(Ob, Wo), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["Q"][0, 1], Qf[:, dh:2 * dh], rtol=1e-13, atol=1e-14)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(40)
+    s, dh = 9, 4
+    Q, K, V = rng.standard_normal((s, dh)), rng.standard_normal((s, dh)), rng.standard_normal((s, dh))
+    o = O.attn_core(Q, K, V)
+    np.testing.assert_array_equal(o[0], V[0])                      # row 0 sees key 0 only
+    o0 = O.attn_core(Q, np.zeros_like(K), V)                       # equal scores
+    prefix = np.cumsum(V, axis=0) / np.arange(1, s + 1)[:, None]
+    np.testing.assert_allclose(o0, prefix, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(O.attn_core(Q[:1], K[:1], V[:1]), V[:1], rtol=0, atol=0)
+    c = 1.7                                                        # scaling Q by c
+    np.testing.assert_allclose(O.attn_core(c * Q, K, V), O.attn_core(Q, K, V, scale=c / math.sqrt(dh)),
+                               rtol=1e-13, atol=1e-14)
+    full = O.attn_core(Q, K, V, causal=False)                      # last row unaffected by the mask
+    np.testing.assert_allclose(o[-1], full[-1], rtol=1e-13, atol=1e-14)
+
+
+def test_attention_shards_concatenate_and_sum_to_unsharded():
+    # [JY] Attention: heads may be placed on GPUs one or several at a time;
+    # [HC] Figure 3.5: contiguous groups; the W_O row split leaves partial sums.
+    n, h_l, dh, b, s, d = 4, 2, 8, 2, 12, 24
+    inp = tpsynth.random_attn(b, s, d, h_l, dh, "f32", seed=41, w_std=0.2, n_shards=n)
+    full = O.attn_unsharded(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], b, s, n * h_l, dh)
+    shards = [O.attn_shard_fwd(inp["X"], inp["Wqs"][i], inp["Wks"][i], inp["Wvs"][i], inp["Wos"][i],
+                               b, s, h_l, dh) for i in range(n)]
+    np.testing.assert_allclose(np.concatenate([r["O"] for r in shards], axis=1), full["O"], rtol=1e-13, atol=1e-14)
+    assert O.max_rel_err(O.shard_reduce([r["Z"] for r in shards]), full["Z"]) < 1e-12
+
+
+def test_online_softmax_tiling_equals_direct_softmax():
+    # The GPU kernel streams keys in tiles with a running max and sum; in exact
+    # arithmetic this is the direct softmax.  Written here in fp64, tile 3.
+    rng = np.random.default_rng(42)
+    s, dh, tile = 11, 5, 3
+    Q, K, V = rng.standard_normal((s, dh)), rng.standard_normal((s, dh)), rng.standard_normal((s, dh))
+    scale = 1 / math.sqrt(dh)
+    out = np.zeros((s, dh))
+    for t in range(s):
+        m, l, acc = -np.inf, 0.0, np.zeros(dh)
+        for u0 in range(0, t + 1, tile):
+            u1 = min(u0 + tile, t + 1)
+            sc = (K[u0:u1] @ Q[t]) * scale
+            m_new = max(m, sc.max())
+            corr = math.exp(m - m_new) if m > -np.inf else 0.0
+            p = np.exp(sc - m_new)
+            l = l * corr + p.sum()
+            acc = acc * corr + p @ V[u0:u1]
+            m = m_new
+        out[t] = acc / l
+    np.testing.assert_allclose(out, O.attn_core(Q, K, V), rtol=1e-13, atol=1e-14)
+
+
+# -------------------------------------------------------------- shard-reduce
+
+def _read_golden_allreduce():
+    ranks, ar, rs = {}, None, {}
+    with open(os.path.join(GOLDEN, "allreduce_world4.txt")) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            t = line.split()
+            if t[0] == "rank":
+                ranks[int(t[1])] = [float(v) for v in t[3:]]
+            elif t[0] == "allreduce":
+                ar = [float(v) for v in t[1:]]
+            elif t[0] == "reducescatter":
+                rs[int(t[1][4:])] = float(t[2])
+    return ranks, ar, rs
+
+
+def test_shard_reduce_pages_worked_example():
+    ranks, ar, rs = _read_golden_allreduce()
+    out = O.shard_reduce([ranks[r] for r in range(4)])
+    np.testing.assert_array_equal(out, ar)
+    for c in range(4):                                # reduce-scatter: column c on rank c
+        assert out[c] == rs[c]
+    # all-gather of the reduce-scatter pieces rebuilds the all-reduce
+    np.testing.assert_array_equal(np.array([rs[c] for c in range(4)]), ar)
+
+
+def test_shard_reduce_bias_added_once():
+    rng = np.random.default_rng(50)
+    P = rng.standard_normal((3, 4, 6))
+    bias = rng.standard_normal(6)
+    out = O.shard_reduce(list(P), bias)
+    np.testing.assert_allclose(out - P.sum(axis=0), np.broadcast_to(bias, (4, 6)), atol=1e-14)
+
+
+def test_shard_range_divisibility():
+    assert O.shard_range(4096, 8, 3) == (1536, 512)
+    with pytest.raises(ValueError):
+        O.shard_range(11008, 3, 0)
+    with pytest.raises(ValueError):
+        O.shard_range(16, 4, 4)
+
+
+def test_max_rel_err():
+    assert O.max_rel_err([1.0, -2.0], [1.0, -2.0]) == 0.0
+    assert O.max_rel_err([1.0, -2.2], [1.0, -2.0]) == pytest.approx(0.1)
+
+
+# --------------------------------------------------------------- input recipe
+
+def test_bf16_rounding_ties_to_even():
+    vals = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -(1.0 + 2 ** -8), 3.0e38],
+                    dtype=np.float32)
+    r = tpsynth.round_to_bf16(vals)
+    np.testing.assert_array_equal(r[:4], np.array([1.0, 1.0 + 2 ** -6, 1.0, -1.0], dtype=np.float32))
+    assert np.isfinite(r[4])
+
+
+def test_workload_shapes():
+    W = tpsynth.WORKLOADS
+    assert (W["C2"].M, W["C2"].f_local) == (8192, 512)
+    assert W["C3"].f_local == 2752 and W["C4"].h_local == 8
+    assert (W["C5"].M, W["C5"].d, W["C5"].f_local) == (8192, 8192, 4096)
