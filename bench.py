@@ -1,0 +1,366 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's Megatron-LM tensor-parallel shard on MI355X.
+
+Headline: the large GeLU MLP shard (b 2, s 4096, d 8192, d_ff 32768, TP 8,
+so this GPU's slice is W1 [8192 x 4096] and W2 [4096 x 8192]), forward +
+backward through the C ABI, bf16 operands with fp32 accumulation.  A step is
+tp_mlp_fwd + tp_mlp_bwd on resident synthetic inputs (seed 0).  value is the
+algorithmic FLOP rate: 6 products of 2*M*N*K = 549.76 GFLOP each per step.
+
+Also reported (not the headline): the GPT-2-medium-shaped shard with all 8
+shards and both shard-reduces, the SwiGLU shard and the causal attention
+shard, each timed on its own.  The fp64 oracle is timed on the host's cores on
+a bounded token sample of the headline workload (cpu_baseline), and the same
+sample yields the max relative error of the GPU outputs.
+
+Prints ONE JSON line.  Runs on one GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PAGES_CONTEXT = ("Megatron-LM weak scaling quoted on the 'Parallelism on Jiang Yi's Homepage' "
+                 "megatron-lm note: 76% at 512 GPUs (text; its table gives 74% for TP-8 x DP-64), "
+                 "GPU type not stated; context only, not a target")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- HIP events
+class HipEvents:
+    """hipEvent_t pairs for the library's kernel-timing hook."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.n = n
+        self.start = (ctypes.c_void_p * n)()
+        self.stop = (ctypes.c_void_p * n)()
+        for i in range(n):
+            for arr in (self.start, self.stop):
+                ev = ctypes.c_void_p()
+                rc = self.hip.hipEventCreate(ctypes.byref(ev))
+                if rc != 0:
+                    raise RuntimeError(f"hipEventCreate failed ({rc})")
+                arr[i] = ev
+
+    def elapsed_ms(self, i: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.start[i])
+            self.hip.hipEventDestroy(self.stop[i])
+
+
+def timed(tp, torch, step, steps: int, warmup: int, kernels_per_step: int):
+    """Warm up, then time exactly `steps` steps between two synchronisations;
+    per-kernel durations come from the library's hipEvent hook on the same
+    stream."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents(steps * kernels_per_step + 8)
+    L = tp.lib()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    rc = L.tp_profile_begin(ev.start, ev.stop, ev.n)
+    if rc != 0:
+        raise RuntimeError("tp_profile_begin failed")
+    t0.record()
+    wall0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    n = L.tp_profile_end()
+    per = {}
+    for i in range(n):
+        lab = L.tp_profile_label(i).decode()
+        per.setdefault(lab, []).append(ev.elapsed_ms(i))
+    ev.close()
+    return t0.elapsed_time(t1) / steps, wall, per
+
+
+def gemm_flops(M, N, K):
+    return 2.0 * M * N * K
+
+
+# ------------------------------------------------------------ headline (C5)
+def run_headline(tp, torch, wl, steps, warmup):
+    import tpsynth
+    log(f"generating {wl.name} inputs")
+    inp = tpsynth.mlp_inputs(wl)
+    bf = torch.bfloat16
+    dev = lambda a: torch.from_numpy(a).to(bf).cuda()
+    M, d, f = wl.M, wl.d, wl.f_local
+    X, W1, W2, dY = dev(inp["X"]), dev(inp["W1s"][0]), dev(inp["W2s"][0]), dev(inp["dY"])
+    A = torch.empty((M, f), dtype=bf, device="cuda")
+    H = torch.empty_like(A)
+    Z = torch.empty((M, d), dtype=bf, device="cuda")
+    dX = torch.empty_like(Z)
+    dW1 = torch.empty((d, f), dtype=torch.float32, device="cuda")
+    dW2 = torch.empty((f, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tp.tp_mlp_bwd_workspace_bytes(tp.TP_DT_BF16, M, d, f), dtype=torch.uint8, device="cuda")
+
+    def step():
+        tp.tp_mlp_fwd(X, W1, W2, A, H, Z)
+        tp.tp_mlp_bwd(X, W1, W2, A, H, dY, dX, dW1, dW2, ws)
+
+    log(f"timing {wl.name}: warmup {warmup}, steps {steps}")
+    ms, wall, per = timed(tp, torch, step, steps, warmup, 8)
+    flops = 6 * gemm_flops(M, f, d)
+    outs = {"A": A, "H": H, "Z": Z, "dX": dX, "dW1": dW1, "dW2": dW2}
+    return ms, wall, per, flops, inp, outs
+
+
+def roofline_for(per, M, d, f):
+    """The dominant kernel (largest total time) against the bf16 MFMA peak."""
+    lab, times = max(per.items(), key=lambda kv: sum(kv[1]))
+    avg_ms = sum(times) / len(times)
+    fl = gemm_flops(M, f, d)      # every product of the shard is M x f x d
+    achieved = fl / (avg_ms * 1e-3) / 1e12
+    return {"kernel": lab, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "flop_per_launch": fl, "avg_launch_ms": round(avg_ms, 4), "launches": len(times)}
+
+
+# ------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, inp, outs, torch, rows_n=128, cols_n=8):
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(123)
+    rows = np.sort(rng.choice(wl.M, rows_n, replace=False))
+    X, W1, W2, dY = inp["X"][rows], inp["W1s"][0], inp["W2s"][0], inp["dY"][rows]
+    log(f"cpu_baseline: oracle fwd+bwd on {rows_n} of {wl.M} tokens ({cores} threads)")
+    t = time.perf_counter()
+    fw = O.mlp_shard_fwd(X, W1, W2)
+    bw = O.mlp_shard_bwd(X, W1, W2, dY)
+    secs = time.perf_counter() - t
+    fl = 12.0 * rows_n * wl.d * wl.f_local
+    host = lambda tname: outs[tname].float().cpu().numpy()
+    err = {k: O.max_rel_err(host(k)[rows], fw[k]) for k in ("A", "H", "Z")}
+    err["dX"] = O.max_rel_err(host("dX")[rows], bw["dX"])
+    cols = np.sort(rng.choice(wl.f_local, cols_n, replace=False))
+    sub = O.mlp_shard_bwd(inp["X"], W1[:, cols], W2[cols], inp["dY"])    # the columns as a sub-shard
+    err["dW1"] = O.max_rel_err(host("dW1")[:, cols], sub["dW1"])
+    err["dW2"] = O.max_rel_err(host("dW2")[cols], sub["dW2"])
+    return ({"value": round(fl / secs / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+             "seconds": round(secs, 3),
+             "sample": f"fp64 numpy oracle, shard fwd+bwd for {rows_n} of {wl.M} token rows "
+                       f"({fl / 1e9:.1f} GFLOP), same weights"}, err)
+
+
+# ------------------------------------------------------- other workloads
+def run_c2(tp, torch, steps, warmup):
+    import tpsynth
+    wl = tpsynth.WORKLOADS["C2"]
+    inp = tpsynth.mlp_inputs(wl)
+    bf = torch.bfloat16
+    dev = lambda a: torch.from_numpy(a).to(bf).cuda()
+    M, d, f, n = wl.M, wl.d, wl.f_local, wl.n_shards
+    X, dY = dev(inp["X"]), dev(inp["dY"])
+    W1s = [dev(w) for w in inp["W1s"]]
+    W2s = [dev(w) for w in inp["W2s"]]
+    A = torch.empty((n, M, f), dtype=bf, device="cuda")
+    H = torch.empty_like(A)
+    Zp = torch.empty((n, M, d), dtype=bf, device="cuda")
+    dXp = torch.empty_like(Zp)
+    Z = torch.empty((M, d), dtype=bf, device="cuda")
+    dX = torch.empty_like(Z)
+    dW1 = torch.empty((n, d, f), dtype=torch.float32, device="cuda")
+    dW2 = torch.empty((n, f, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tp.tp_mlp_bwd_workspace_bytes(tp.TP_DT_BF16, M, d, f), dtype=torch.uint8, device="cuda")
+
+    def step():
+        for i in range(n):
+            tp.tp_mlp_fwd(X, W1s[i], W2s[i], A[i], H[i], Zp[i])
+        tp.tp_shard_reduce(Zp, Z, n, M * d)
+        for i in range(n):
+            tp.tp_mlp_bwd(X, W1s[i], W2s[i], A[i], H[i], dY, dXp[i], dW1[i], dW2[i], ws)
+        tp.tp_shard_reduce(dXp, dX, n, M * d)
+
+    ms, _, per = timed(tp, torch, step, steps, warmup, 8 * 10 + 2)
+    flops = n * 6 * gemm_flops(M, f, d)
+    red = per.get("shard_reduce.vec8", [])
+    # the reduce reads 8 partials and writes 1 output: (n + 1) * M * d * 2 bytes
+    rbytes = (n + 1) * M * d * 2
+    red_ms = sum(red) / len(red) if red else None
+    # cold read of the partials: evict the 256 MB Infinity Cache, then time one reduce
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = []
+    ev = HipEvents(1)
+    for _ in range(3):
+        scratch.fill_(1)
+        torch.cuda.synchronize()
+        tp.lib().tp_profile_begin(ev.start, ev.stop, 1)
+        tp.tp_shard_reduce(Zp, Z, n, M * d)
+        tp.lib().tp_profile_end()
+        torch.cuda.synchronize()
+        cold.append(ev.elapsed_ms(0))
+    ev.close()
+    del scratch
+    cold_ms = min(cold)
+    return {"workload": "C2 GPT-2-medium-shaped GeLU MLP, b 8 s 1024 d 1024 d_ff 4096, all 8 TP shards "
+                        "fwd+bwd + Z and dX shard-reduce",
+            "ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+            "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "shard_reduce": {"bytes": rbytes, "warm_ms": round(red_ms, 4) if red_ms else None,
+                             "warm_GBps": round(rbytes / red_ms / 1e6, 1) if red_ms else None,
+                             "cold_ms": round(cold_ms, 4), "cold_GBps": round(rbytes / cold_ms / 1e6, 1),
+                             "peak_GBps": PEAK_HBM_GBS},
+            "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in per.items()}}
+
+
+def run_c3(tp, torch, steps, warmup):
+    import tpsynth
+    wl = tpsynth.WORKLOADS["C3"]
+    inp = tpsynth.swiglu_inputs(wl)
+    bf = torch.bfloat16
+    dev = lambda a: torch.from_numpy(a).to(bf).cuda()
+    M, d, f = wl.M, wl.d, wl.f_local
+    X, W1, W3, W2, dY = (dev(inp[k]) for k in ("X", "W1", "W3", "W2", "dY"))
+    G, U, H = (torch.empty((M, f), dtype=bf, device="cuda") for _ in range(3))
+    Z = torch.empty((M, d), dtype=bf, device="cuda")
+    dX = torch.empty_like(Z)
+    dW1, dW3 = (torch.empty((d, f), dtype=torch.float32, device="cuda") for _ in range(2))
+    dW2 = torch.empty((f, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tp.tp_swiglu_bwd_workspace_bytes(tp.TP_DT_BF16, M, d, f), dtype=torch.uint8, device="cuda")
+
+    def step():
+        tp.tp_swiglu_fwd(X, W1, W3, W2, G, U, H, Z)
+        tp.tp_swiglu_bwd(X, W1, W3, W2, G, U, H, dY, dX, dW1, dW3, dW2, ws)
+
+    ms, _, per = timed(tp, torch, step, steps, warmup, 8)
+    flops = 9 * gemm_flops(M, f, d)
+    return {"workload": "C3 SwiGLU MLP shard, b 4 s 2048 d 4096 d_ff 11008, TP 4 (slice 2752), fwd+bwd",
+            "ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+            "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in per.items()}}
+
+
+def run_c4(tp, torch, steps, warmup):
+    import tpsynth
+    wl = tpsynth.WORKLOADS["C4"]
+    inp = tpsynth.attn_inputs(wl)
+    bf = torch.bfloat16
+    dev = lambda a: torch.from_numpy(a).to(bf).cuda()
+    b, s, d, hl, dh = wl.b, wl.s, wl.d, wl.h_local, wl.d_head
+    X, Wq, Wk, Wv, Wo = (dev(inp[k]) for k in ("X", "Wq", "Wk", "Wv", "Wo"))
+    Q, K, V = (torch.empty((b, hl, s, dh), dtype=bf, device="cuda") for _ in range(3))
+    Ob = torch.empty((b * s, hl * dh), dtype=bf, device="cuda")
+    Z = torch.empty((b * s, d), dtype=bf, device="cuda")
+
+    def step():
+        tp.tp_attn_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, Z, b, s, hl, dh, causal=True)
+
+    ms, _, per = timed(tp, torch, step, steps, warmup, 4)
+    M, N = b * s, hl * dh
+    core = 2 * 2.0 * b * hl * (s * (s + 1) / 2) * dh      # causal pairs only: QK^T and PV
+    flops = 3 * gemm_flops(M, N, d) + core + gemm_flops(M, d, N)
+    core_ms = [v for k, v in per.items() if k.startswith("attn.core")]
+    core_avg = sum(core_ms[0]) / len(core_ms[0]) if core_ms else None
+    return {"workload": "C4 causal self-attention shard, b 4 s 2048 d 4096, 8 of 32 heads of 128, fwd",
+            "ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+            "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "core_tflops": round(core / core_avg / 1e9, 1) if core_avg else None,
+            "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in per.items()}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--extra-steps", type=int, default=5)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's TP shard on one GPU only; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported: run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import megatron_tensor_transformer_fwd_amd as tp
+    import tpsynth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tp.lib()
+    torch.cuda.set_device(0)
+
+    wl = tpsynth.WORKLOADS["C5"]
+    ms, wall, per, flops, inp, outs = run_headline(tp, torch, wl, args.steps, args.warmup)
+    value = flops / ms / 1e9
+    result = {
+        "metric": "shard MLP fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak; max rel err",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs, random-init weights)",
+        "config": {"workload": "C5 large GeLU MLP shard: b 2, s 4096, d 8192, d_ff 32768, TP 8 -> "
+                               "W1 [8192x4096], W2 [4096x8192]; fwd+bwd",
+                   "global_batch": wl.b, "seq_len": wl.s, "d_model": wl.d, "d_ff": wl.d_ff,
+                   "tp_degree": wl.n_shards, "f_local": wl.f_local,
+                   "parallelism": "one TP shard on one GPU"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "flop_per_step": flops,
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline_for(per, wl.M, wl.d, wl.f_local),
+        "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in per.items()},
+        "context": PAGES_CONTEXT,
+    }
+    if not args.no_cpu_baseline:
+        cb, err = cpu_baseline(wl, inp, outs, torch)
+        result["cpu_baseline"] = cb
+        result["max_rel_err"] = {k: float(f"{v:.3e}") for k, v in err.items()}
+        result["max_rel_err_all"] = float(f"{max(err.values()):.3e}")
+        result["tolerance"] = 2e-2
+    del inp, outs
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        wls = {}
+        for name, fn in (("C2", run_c2), ("C3", run_c3), ("C4", run_c4)):
+            log(f"timing {name}")
+            wls[name] = fn(tp, torch, args.extra_steps, 2)
+            torch.cuda.empty_cache()
+        result["workloads"] = wls
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+/*
+ * tp_shard.h — C ABI of libtpshard: one GPU's shard of a Megatron-LM
+ * tensor-parallel transformer layer, hand-written for AMD gfx950 (MI355X).
+ *
+ * The operations follow these pages (cited by title and section):
+ *  [JY] "Parallelism on Jiang Yi's Homepage", note "megatron-lm", sections
+ *       FFN (Y = GeLU(X W1) W2; W1 split by columns, W2 by rows; the f/g
+ *       table; the SwiGLU split) and Attention (heads split across GPUs,
+ *       O = [o_1 .. o_h] W_O).
+ *  [HC] "Splitting the model: five parallelisms and the traffic they make",
+ *       section 3.4 "Tensor parallelism", Figures 3.4-3.6 (Z = sum_k Z_k;
+ *       g all-reduces the partial outputs forward, f all-reduces dX backward).
+ *  [BM] "tensor-parallelism" (brunomaga.github.io), section "Megatron-LM tensor
+ *       parallelism" (Megatron_f/Megatron_g, the feed-forward block with the
+ *       bias added after the reduction, Megatron_MHA with its causal mask and
+ *       1/sqrt(head_dim) scale).
+ *  [DW] "Chapter 8: Distributed Training", section 8.4.2 NCCL (all_reduce SUM).
+ *
+ * Conventions shared by every entry point
+ *  - Matrices are dense, row-major, contiguous: an [R x C] matrix has element
+ *    (r, c) at offset r*C + c.  Weights are [in x out] and products are X W,
+ *    as in [JY] FFN (W1 in R^{d x d_ff}, W2 in R^{d_ff x d}).
+ *  - M = b*s tokens (rows of X).  f is this shard's slice of d_ff.
+ *  - dtype TP_DT_BF16: bf16 operands, activations and partial outputs; every
+ *    product accumulates in fp32; weight gradients are fp32.  TP_DT_F32: all
+ *    fp32.  bf16 results are rounded to nearest, ties to even.
+ *  - Every pointer except `stream` is a device pointer, 16-byte aligned.  The
+ *    caller owns all memory; the library allocates nothing, never
+ *    synchronises and never changes the current device.  The only state it
+ *    keeps between calls is thread-local: the last error text and the
+ *    optional kernel-timing hook (tp_profile_begin).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work and return; faults raised while a kernel runs surface at
+ *    the caller's next synchronisation.
+ *  - Arguments are validated on the host before any HIP call.  Every entry
+ *    point returns TP_OK (0) or a negative status; tp_last_error_detail()
+ *    then holds a thread-local description.  No exception crosses the ABI.
+ *  - Outputs must not overlap any input or each other (except where noted).
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TP_ABI_VERSION 1
+
+typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype_t;
+
+/* status codes */
+#define TP_OK           0
+#define TP_E_NULL      -1   /* a required pointer is NULL                     */
+#define TP_E_DIM       -2   /* a size is <= 0, too large, or not supported    */
+#define TP_E_DIVIS     -3   /* a size is not a multiple of what it must be    */
+#define TP_E_DTYPE     -4   /* unsupported dtype for this entry point         */
+#define TP_E_ALIGN     -5   /* a pointer is not 16-byte aligned               */
+#define TP_E_ALIAS     -6   /* an output overlaps an input or another output  */
+#define TP_E_WORKSPACE -7   /* workspace NULL or smaller than required        */
+#define TP_E_HIP       -8   /* a HIP launch failed (text in the detail)       */
+
+/* ---------------------------------------------------------------------------
+ * tp_shard_range — the contiguous equal split of `total` features, heads or
+ * rows over `n_shards` shards: shard `index` owns [index*k, (index+1)*k) with
+ * k = total / n_shards.  Returns TP_E_DIVIS when total % n_shards != 0 (the
+ * pages' listings assert divisibility: [JY] Implementation; [BM]
+ * Megatron_MHA raises ValueError), TP_E_DIM for non-positive sizes or an
+ * index outside [0, n_shards), TP_E_NULL for NULL outputs.  Host only.
+ * ------------------------------------------------------------------------- */
+int tp_shard_range(int64_t total, int64_t n_shards, int64_t index,
+                   int64_t* start, int64_t* len);
+
+/* ---------------------------------------------------------------------------
+ * tp_mlp_fwd — GeLU MLP shard forward ([JY] FFN; [HC] Figure 3.4):
+ *   A = X W1        (column-parallel product; W1 is this shard's column slice)
+ *   H = GeLU(A)     (exact erf form, applied in the product's epilogue)
+ *   Z = H W2        (row-parallel product; this shard's summand of Y)
+ * X [M x d], W1 [d x f], W2 [f x d], A and H [M x f], Z [M x d].
+ * A may be NULL (pre-activation not kept); H and Z are required.
+ * d and f must be multiples of 8.
+ * ------------------------------------------------------------------------- */
+int tp_mlp_fwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
+               const void* X, const void* W1, const void* W2,
+               void* A, void* H, void* Z);
+
+/* ---------------------------------------------------------------------------
+ * tp_mlp_bwd — GeLU MLP shard backward.  g is the identity backward, so dY
+ * is the full upstream gradient ([JY] f/g table; [BM] Megatron_g):
+ *   dA  = (dY W2^T) * GeLU'(A)     (GeLU' fused into the dgrad epilogue)
+ *   dW2 = H^T dY                   (fp32, [f x d])
+ *   dX  = dA W1^T                  (this shard's summand; f sums them, [HC] 3.4)
+ *   dW1 = X^T dA                   (fp32, [d x f])
+ * A, H are the forward's saved outputs.  dX [M x d] has dtype dt; dW1, dW2
+ * are always fp32.  ws: device workspace of at least
+ * tp_mlp_bwd_workspace_bytes(dt, M, d, f) bytes (holds dA and split-K
+ * partials); it is scratch, contents undefined after the call.
+ * ------------------------------------------------------------------------- */
+int tp_mlp_bwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
+               const void* X, const void* W1, const void* W2,
+               const void* A, const void* H, const void* dY,
+               void* dX, float* dW1, float* dW2, void* ws, size_t ws_bytes);
+size_t tp_mlp_bwd_workspace_bytes(tp_dtype_t dt, int64_t M, int64_t d, int64_t f);
+
+/* ---------------------------------------------------------------------------
+ * tp_swiglu_fwd — SwiGLU MLP shard forward ([JY] FFN, SwiGLU part: W1 and
+ * W3 split by columns, W2 by rows; the listing computes
+ * w2(silu(w1(x)) * w3(x)), so W1 is the Swish'd gate and W3 the up projection):
+ *   G = X W1, U = X W3  (one pass over X, both slices in the same tile)
+ *   H = Swish(G) * U    (Swish(x) = x sigmoid(x), in the epilogue)
+ *   Z = H W2
+ * X [M x d], W1, W3 [d x f], W2 [f x d], G, U, H [M x f], Z [M x d].
+ * G and U may both be NULL (not kept; then no backward is possible).
+ * ------------------------------------------------------------------------- */
+int tp_swiglu_fwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
+                  const void* X, const void* W1, const void* W3, const void* W2,
+                  void* G, void* U, void* H, void* Z);
+
+/* ---------------------------------------------------------------------------
+ * tp_swiglu_bwd — SwiGLU MLP shard backward (chain rule through the forward):
+ *   dH = dY W2^T;  dU = dH * Swish(G);  dG = dH * U * Swish'(G)
+ *   dW2 = H^T dY;  dW1 = X^T dG;  dW3 = X^T dU      (fp32)
+ *   dX  = dG W1^T + dU W3^T                          (this shard's summand)
+ * ws: at least tp_swiglu_bwd_workspace_bytes(dt, M, d, f) bytes.
+ * ------------------------------------------------------------------------- */
+int tp_swiglu_bwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
+                  const void* X, const void* W1, const void* W3, const void* W2,
+                  const void* G, const void* U, const void* H, const void* dY,
+                  void* dX, float* dW1, float* dW3, float* dW2,
+                  void* ws, size_t ws_bytes);
+size_t tp_swiglu_bwd_workspace_bytes(tp_dtype_t dt, int64_t M, int64_t d, int64_t f);
+
+/* ---------------------------------------------------------------------------
+ * tp_attn_shard_fwd — head-group attention shard forward ([JY] Attention;
+ * [BM] Megatron_MHA; [HC] Figure 3.5).  This shard owns h_local heads; local
+ * head j uses columns [j*d_head, (j+1)*d_head) of Wq, Wk, Wv and rows
+ * [j*d_head, (j+1)*d_head) of Wo.  For each batch row bi and head j:
+ *   Q, K, V = X_bi W{q,k,v}[:, j]          written head-major [b, h_local, s, d_head]
+ *   S[t,u]  = scale * Q_t . K_u, and -inf for u > t when causal
+ *   o_j     = softmax_u(S) V              (online softmax, never stored as s x s)
+ *   O       = [o_0 | ... | o_{h_local-1}] [b*s x h_local*d_head]
+ *   Z       = O Wo                         this shard's partial [b*s x d]
+ * X [b*s x d]; Wq, Wk, Wv [d x h_local*d_head]; Wo [h_local*d_head x d].
+ * Q, K, V and O are outputs (kept for inspection or a backward pass).
+ * Supported: dt = TP_DT_BF16, d_head = 64 or 128, d a multiple of 8.
+ * scale <= 0 selects 1/sqrt(d_head).  causal is 0 or 1.
+ * ------------------------------------------------------------------------- */
+int tp_attn_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
+                      int64_t h_local, int64_t d_head, int causal, float scale,
+                      const void* X, const void* Wq, const void* Wk, const void* Wv,
+                      const void* Wo, void* Q, void* K, void* V, void* O, void* Z);
+
+/* ---------------------------------------------------------------------------
+ * tp_shard_reduce — the local stand-in for the g (forward) and f (backward)
+ * all-reduce SUM of [JY] f/g table, [HC] 3.4 and [DW] 8.4.2, over the
+ * partials of n_shards shards resident on this GPU:
+ *   out[e] = sum_{i=0}^{n_shards-1} partials[i*shard_stride + e]
+ *            (+ bias[e % bias_len], added once, after the sum: [BM]
+ *             Megatron_FeedForward adds the row-parallel bias after g)
+ * for e in [0, numel).  Sums in fp32 in shard order 0..n_shards-1 (bitwise
+ * deterministic).  dt_in is the dtype of partials and bias, dt_out of out.
+ * bias may be NULL (bias_len ignored), else bias_len > 0.
+ * shard_stride >= numel (elements).  out may alias partials block 0 exactly
+ * (in-place); any other overlap is TP_E_ALIAS.
+ * ------------------------------------------------------------------------- */
+int tp_shard_reduce(void* stream, tp_dtype_t dt_in, tp_dtype_t dt_out,
+                    int64_t n_shards, int64_t numel,
+                    const void* partials, int64_t shard_stride,
+                    const void* bias, int64_t bias_len, void* out);
+
+/* ---------------------------------------------------------------------------
+ * Kernel-timing hook for measurement tools (no effect on results).
+ * tp_profile_begin arms it on the calling thread: the i-th kernel that later
+ * entry-point calls on this thread launch (i counting from 0, up to
+ * `capacity`) is launched with hipExtLaunchKernelGGL so that it records the
+ * caller's hipEvent_t start_events[i] before it runs and stop_events[i] after
+ * it.  The events are created and owned by the caller and must belong to the
+ * device the kernels run on.  tp_profile_end disarms the hook and returns the
+ * number of kernels that recorded events; tp_profile_label(i) names kernel i
+ * (static text such as "mlp_fwd.xw1_gelu"; "" out of range).  Launches past
+ * `capacity` run untimed.  Returns TP_E_NULL / TP_E_DIM on bad arguments.
+ * ------------------------------------------------------------------------- */
+int tp_profile_begin(void* const* start_events, void* const* stop_events, int capacity);
+int tp_profile_end(void);
+const char* tp_profile_label(int i);
+
+/* Human-readable text for a status code (static storage). */
+const char* tp_strerror(int status);
+/* Thread-local text describing the last failure on this thread ("" if none). */
+const char* tp_last_error_detail(void);
+/* TP_ABI_VERSION of the loaded library. */
+int tp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TP_SHARD_H */

@@ -1,0 +1,175 @@
+"""Python binding of libtpshard (one GPU's shard of a Megatron-LM TP layer).
+
+Argument marshalling only: every function takes torch tensors that live on
+the GPU, reads their sizes and device pointers, and calls the C entry point
+of the same name in libtpshard.so on the current (or given) HIP stream.  All
+arithmetic runs in the library's gfx950 kernels; there is no fallback, and
+importing the binding without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "TPError", "lib", "LIB_PATH", "TP_DT_F32", "TP_DT_BF16",
+    "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_workspace_bytes",
+    "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes",
+    "tp_attn_shard_fwd", "tp_shard_reduce", "tp_shard_range",
+    "tp_abi_version", "EXPORTS",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtpshard.so")
+
+TP_DT_F32 = 0
+TP_DT_BF16 = 1
+
+STATUS = {0: "TP_OK", -1: "TP_E_NULL", -2: "TP_E_DIM", -3: "TP_E_DIVIS", -4: "TP_E_DTYPE",
+          -5: "TP_E_ALIGN", -6: "TP_E_ALIAS", -7: "TP_E_WORKSPACE", -8: "TP_E_HIP"}
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/tp_shard.h
+EXPORTS = {
+    "tp_shard_range": (_i32, [_i64, _i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "tp_mlp_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
+    "tp_mlp_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz]),
+    "tp_mlp_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
+    "tp_swiglu_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "tp_swiglu_bwd": (_i32, [_p, _i32, _i64, _i64, _i64] + [_p] * 8 + [_p] * 4 + [_p, _sz]),
+    "tp_swiglu_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
+    "tp_attn_shard_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _i64, _i32, ctypes.c_float]
+                          + [_p] * 5 + [_p] * 5),
+    "tp_shard_reduce": (_i32, [_p, _i32, _i32, _i64, _i64, _p, _i64, _p, _i64, _p]),
+    "tp_strerror": (ctypes.c_char_p, [_i32]),
+    "tp_last_error_detail": (ctypes.c_char_p, []),
+    "tp_abi_version": (_i32, []),
+    "tp_profile_begin": (_i32, [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32]),
+    "tp_profile_end": (_i32, []),
+    "tp_profile_label": (ctypes.c_char_p, [_i32]),
+}
+
+_LIB = None
+
+
+class TPError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtpshard.so (built in-tree by build.build())."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "megatron_tensor_transformer_fwd_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise TPError(status, lib().tp_last_error_detail().decode())
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return TP_DT_BF16
+    if t.dtype == torch.float32:
+        return TP_DT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def tp_abi_version() -> int:
+    return lib().tp_abi_version()
+
+
+def tp_shard_range(total: int, n_shards: int, index: int):
+    s, n = _i64(), _i64()
+    _check(lib().tp_shard_range(total, n_shards, index, ctypes.byref(s), ctypes.byref(n)))
+    return s.value, n.value
+
+
+def tp_mlp_fwd(X, W1, W2, A, H, Z, stream=None) -> None:
+    """A = X W1, H = GeLU(A), Z = H W2 (see include/tp_shard.h)."""
+    M, d = X.shape
+    f = W1.shape[1]
+    _check(lib().tp_mlp_fwd(_stream(stream), _dt(X), M, d, f, _ptr(X), _ptr(W1), _ptr(W2),
+                            _ptr(A), _ptr(H), _ptr(Z)))
+
+
+def tp_mlp_bwd_workspace_bytes(dtype: int, M: int, d: int, f: int) -> int:
+    return lib().tp_mlp_bwd_workspace_bytes(dtype, M, d, f)
+
+
+def tp_mlp_bwd(X, W1, W2, A, H, dY, dX, dW1, dW2, ws, stream=None) -> None:
+    M, d = X.shape
+    f = W1.shape[1]
+    _check(lib().tp_mlp_bwd(_stream(stream), _dt(X), M, d, f, _ptr(X), _ptr(W1), _ptr(W2), _ptr(A),
+                            _ptr(H), _ptr(dY), _ptr(dX), _ptr(dW1), _ptr(dW2), _ptr(ws),
+                            ws.numel() * ws.element_size()))
+
+
+def tp_swiglu_fwd(X, W1, W3, W2, G, U, H, Z, stream=None) -> None:
+    M, d = X.shape
+    f = W1.shape[1]
+    _check(lib().tp_swiglu_fwd(_stream(stream), _dt(X), M, d, f, _ptr(X), _ptr(W1), _ptr(W3), _ptr(W2),
+                               _ptr(G), _ptr(U), _ptr(H), _ptr(Z)))
+
+
+def tp_swiglu_bwd_workspace_bytes(dtype: int, M: int, d: int, f: int) -> int:
+    return lib().tp_swiglu_bwd_workspace_bytes(dtype, M, d, f)
+
+
+def tp_swiglu_bwd(X, W1, W3, W2, G, U, H, dY, dX, dW1, dW3, dW2, ws, stream=None) -> None:
+    M, d = X.shape
+    f = W1.shape[1]
+    _check(lib().tp_swiglu_bwd(_stream(stream), _dt(X), M, d, f, _ptr(X), _ptr(W1), _ptr(W3), _ptr(W2),
+                               _ptr(G), _ptr(U), _ptr(H), _ptr(dY), _ptr(dX), _ptr(dW1), _ptr(dW3),
+                               _ptr(dW2), _ptr(ws), ws.numel() * ws.element_size()))
+
+
+def tp_attn_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, O, Z, b: int, s: int, h_local: int, d_head: int,
+                      causal: bool = True, scale: float = 0.0, stream=None) -> None:
+    d = X.shape[1]
+    _check(lib().tp_attn_shard_fwd(_stream(stream), _dt(X), b, s, d, h_local, d_head, int(causal),
+                                   float(scale), _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo),
+                                   _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(Z)))
+
+
+def tp_shard_reduce(partials, out, n_shards: int, numel: int, shard_stride: Optional[int] = None,
+                    bias=None, stream=None) -> None:
+    """out[e] = sum_i partials[i*stride + e] (+ bias[e % len(bias)])."""
+    stride = numel if shard_stride is None else shard_stride
+    _check(lib().tp_shard_reduce(_stream(stream), _dt(partials), _dt(out), n_shards, numel, _ptr(partials),
+                                 stride, _ptr(bias), 0 if bias is None else bias.numel(), _ptr(out)))

@@ -1,0 +1,139 @@
+// Host-side tile-shape choice and launch of the GEMM kernels.
+#pragma once
+#include <algorithm>
+#include "gemm.hpp"
+#include "gemm_f32.hpp"
+#include "launch.hpp"
+#include "profile.hpp"
+
+namespace tpk {
+
+// Tile shapes.  L: 256x256 (4 waves of 128x128), the shape for large
+// shards; M: 256x128 (4 waves of 128x64); S: 128x128 (4 waves of 64x64) for
+// narrow outputs such as a TP-8 slice of a 4096-wide feed-forward layer.
+using CfgL = TileCfg<256, 256, 64, 2, 2>;
+using CfgM = TileCfg<256, 128, 64, 2, 2>;
+using CfgS = TileCfg<128, 128, 64, 2, 2>;
+
+enum { CFG_L = 0, CFG_M = 1, CFG_S = 2 };
+
+struct GemmPlan {
+  int cfg;
+  int split;
+};
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int64_t tiles_for(int cfg, int64_t M, int64_t N, bool dual) {
+  const int bm = cfg == CFG_S ? 128 : 256;
+  int bn = cfg == CFG_L ? 256 : 128;
+  if (dual) bn /= 2;
+  return cdiv(M, bm) * cdiv(N, bn);
+}
+
+// Choose the largest tile that still gives every CU (256 of them) at least
+// one tile; products with a small output and a long K (weight gradients of
+// narrow shards) are split along K into a deterministic fp32 workspace.
+inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow_split) {
+  constexpr int64_t CUS = 256;
+  GemmPlan p{CFG_S, 1};
+  if (tiles_for(CFG_L, M, N, dual) >= CUS) p.cfg = CFG_L;
+  else if (tiles_for(CFG_M, M, N, dual) >= CUS) p.cfg = CFG_M;
+  if (allow_split) {
+    const int64_t t = tiles_for(p.cfg, M, N, dual);
+    if (t < CUS / 2) {
+      int64_t s = CUS / t;
+      s = std::min<int64_t>(s, std::max<int64_t>(1, K / 1024));
+      p.split = (int)std::max<int64_t>(1, std::min<int64_t>(s, 16));
+    }
+  }
+  return p;
+}
+
+template <class Cfg, bool A_KM, bool B_KM, bool DUAL, class Epi>
+hipError_t launch_gemm_cfg(hipStream_t st, const char* label, GemmParams p, const Epi& epi, int nz) {
+  constexpr int BNL = DUAL ? Cfg::BN / 2 : Cfg::BN;
+  p.tiles_m = (int)cdiv(p.M, Cfg::BM);
+  p.tiles_n = (int)cdiv(p.N, BNL);
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.split_k, (unsigned)nz);
+  return launch(label, gemm_bf16_kernel<Cfg, A_KM, B_KM, DUAL, Epi>, grid, dim3(Cfg::NT), st, p, epi);
+}
+
+template <bool A_KM, bool B_KM, bool DUAL, class Epi>
+hipError_t launch_gemm(hipStream_t st, const char* label, GemmParams p, const Epi& epi, GemmPlan plan,
+                       int nz = 1) {
+  p.split_k = plan.split;
+  switch (plan.cfg) {
+    case CFG_L: return launch_gemm_cfg<CfgL, A_KM, B_KM, DUAL, Epi>(st, label, p, epi, nz);
+    case CFG_M: return launch_gemm_cfg<CfgM, A_KM, B_KM, DUAL, Epi>(st, label, p, epi, nz);
+    default: return launch_gemm_cfg<CfgS, A_KM, B_KM, DUAL, Epi>(st, label, p, epi, nz);
+  }
+}
+
+// One K segment of a bf16 product.  a_rows_or_k / b: the extent of each
+// operand's slow dimension, used for the readable range.
+inline GemmSeg make_seg(const void* A, int64_t lda, int64_t a_elems,
+                        const void* B, int64_t ldb, int64_t b_elems, int64_t K,
+                        const void* B2 = nullptr) {
+  GemmSeg s;
+  s.A = static_cast<const bf16*>(A);
+  s.B = static_cast<const bf16*>(B);
+  s.B2 = static_cast<const bf16*>(B2);
+  s.lda = lda;
+  s.ldb = ldb;
+  s.a_elems = a_elems;
+  s.b_elems = b_elems;
+  s.K = (int)K;
+  return s;
+}
+
+inline GemmParams make_params(int64_t M, int64_t N, GemmSeg s0) {
+  GemmParams p{};
+  p.M = (int)M;
+  p.N = (int)N;
+  p.nseg = 1;
+  p.seg[0] = s0;
+  p.Bz[0] = p.Bz[1] = p.Bz[2] = nullptr;
+  p.split_k = 1;
+  return p;
+}
+
+// fp32 path
+template <bool A_KM, bool B_KM, bool DUAL, class Epi>
+hipError_t launch_gemm_f32(hipStream_t st, const char* label, GemmParamsF32 p, const Epi& epi) {
+  const dim3 grid((unsigned)cdiv(p.M, 64), (unsigned)p.split_k, (unsigned)cdiv(p.N, 64));
+  return launch(label, gemm_f32_kernel<A_KM, B_KM, DUAL, Epi>, grid, dim3(256), st, p, epi);
+}
+
+inline GemmSegF32 make_seg_f32(const void* A, int64_t lda, int64_t a_rows,
+                               const void* B, int64_t ldb, int64_t b_cols, int64_t K,
+                               const void* B2 = nullptr) {
+  GemmSegF32 s;
+  s.A = static_cast<const float*>(A);
+  s.B = static_cast<const float*>(B);
+  s.B2 = static_cast<const float*>(B2);
+  s.lda = lda;
+  s.ldb = ldb;
+  s.K = K;
+  s.a_rows = a_rows;
+  s.b_cols = b_cols;
+  return s;
+}
+
+inline GemmParamsF32 make_params_f32(int64_t M, int64_t N, GemmSegF32 s0) {
+  GemmParamsF32 p{};
+  p.M = (int)M;
+  p.N = (int)N;
+  p.nseg = 1;
+  p.seg[0] = s0;
+  p.split_k = 1;
+  return p;
+}
+
+#define TPK_TRY(expr)                         \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return e_;          \
+  } while (0)
+
+}  // namespace tpk

@@ -1,0 +1,39 @@
+// Internal launchers behind the C ABI (host side).  Arguments are already
+// validated by tp_shard.cpp; these only choose tile shapes and enqueue.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tpk {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+hipError_t launch_shard_reduce(hipStream_t st, int dt_in, int dt_out, int n, int64_t numel,
+                               const void* P, int64_t stride, const void* bias, int64_t bias_len,
+                               void* out);
+
+hipError_t launch_mlp_fwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t f,
+                          const void* X, const void* W1, const void* W2,
+                          void* A, void* H, void* Z);
+size_t mlp_bwd_ws_bytes(int dt, int64_t M, int64_t d, int64_t f);
+hipError_t launch_mlp_bwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t f,
+                          const void* X, const void* W1, const void* W2,
+                          const void* A, const void* H, const void* dY,
+                          void* dX, float* dW1, float* dW2, void* ws);
+
+hipError_t launch_swiglu_fwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t f,
+                             const void* X, const void* W1, const void* W3, const void* W2,
+                             void* G, void* U, void* H, void* Z);
+size_t swiglu_bwd_ws_bytes(int dt, int64_t M, int64_t d, int64_t f);
+hipError_t launch_swiglu_bwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t f,
+                             const void* X, const void* W1, const void* W3, const void* W2,
+                             const void* G, const void* U, const void* H, const void* dY,
+                             void* dX, float* dW1, float* dW3, float* dW2, void* ws);
+
+hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local,
+                           int64_t d_head, int causal, float scale,
+                           const void* X, const void* Wq, const void* Wk, const void* Wv,
+                           const void* Wo, void* Q, void* K, void* V, void* O, void* Z);
+
+}  // namespace tpk

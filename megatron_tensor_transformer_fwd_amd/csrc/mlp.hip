@@ -1,0 +1,165 @@
+// GeLU MLP shard, forward and backward ([JY] FFN; [HC] 3.4, Figure 3.4).
+//
+// Forward:  A = X W1 (column-parallel, GeLU fused: H = GeLU(A)),
+//           Z = H W2 (row-parallel partial).
+// Backward: dA = (dY W2^T) * GeLU'(A)      NT product, GeLU' fused
+//           dW2 = H^T dY                   TN product (fp32, split-K if narrow)
+//           dX = dA W1^T                   NT product (this shard's summand)
+//           dW1 = X^T dA                   TN product (fp32, split-K if narrow)
+#include "epilogues.hpp"
+#include "gemm_dispatch.hpp"
+
+namespace tpk {
+
+static inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// ------------------------------------------------------------------ bf16
+static hipError_t mlp_fwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t f,
+                               const void* X, const void* W1, const void* W2,
+                               void* A, void* H, void* Z) {
+  {  // A = X W1, H = GeLU(A)
+    GemmParams p = make_params(M, f, make_seg(X, d, M * d, W1, f, d * f, d));
+    EpiGelu<bf16> e{static_cast<bf16*>(A), static_cast<bf16*>(H), f};
+    TPK_TRY((launch_gemm<true, false, false>(st, "mlp_fwd.xw1_gelu", p, e, plan_gemm(M, f, d, false, false))));
+  }
+  {  // Z = H W2
+    GemmParams p = make_params(M, d, make_seg(H, f, M * f, W2, d, f * d, f));
+    EpiStore<bf16> e{static_cast<bf16*>(Z), d, 0};
+    TPK_TRY((launch_gemm<true, false, false>(st, "mlp_fwd.hw2", p, e, plan_gemm(M, d, f, false, false))));
+  }
+  return hipSuccess;
+}
+
+struct MlpBwdPlan {
+  GemmPlan dW2, dW1;
+  size_t dA_bytes, split_bytes;
+};
+
+static MlpBwdPlan mlp_bwd_plan(int dt, int64_t M, int64_t d, int64_t f) {
+  MlpBwdPlan pl;
+  const size_t es = dt == DT_BF16 ? 2 : 4;
+  pl.dA_bytes = align256((size_t)M * f * es);
+  if (dt == DT_BF16) {
+    pl.dW2 = plan_gemm(f, d, M, false, true);
+    pl.dW1 = plan_gemm(d, f, M, false, true);
+  } else {
+    pl.dW2 = pl.dW1 = GemmPlan{CFG_S, 1};
+  }
+  const int smax = std::max(pl.dW2.split, pl.dW1.split);
+  pl.split_bytes = smax > 1 ? align256((size_t)smax * d * f * 4) : 0;
+  return pl;
+}
+
+size_t mlp_bwd_ws_bytes(int dt, int64_t M, int64_t d, int64_t f) {
+  const MlpBwdPlan pl = mlp_bwd_plan(dt, M, d, f);
+  return pl.dA_bytes + pl.split_bytes;
+}
+
+// fp32 weight gradient C[Mo x No] = A^T B over K tokens, through the split-K
+// workspace when the plan splits.
+template <class Launch>
+static hipError_t wgrad_f32_out(hipStream_t st, GemmPlan plan, int64_t Mo, int64_t No,
+                                float* out, float* split_ws, Launch&& run) {
+  if (plan.split > 1) {
+    EpiStore<float> e{split_ws, No, Mo * No};
+    TPK_TRY(run(e, plan));
+    return launch_shard_reduce(st, DT_F32, DT_F32, plan.split, Mo * No, split_ws, Mo * No,
+                               nullptr, 0, out);
+  }
+  EpiStore<float> e{out, No, 0};
+  return run(e, plan);
+}
+
+static hipError_t mlp_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t f,
+                               const void* X, const void* W1, const void* W2,
+                               const void* A, const void* H, const void* dY,
+                               void* dX, float* dW1, float* dW2, void* ws) {
+  const MlpBwdPlan pl = mlp_bwd_plan(DT_BF16, M, d, f);
+  bf16* dA = static_cast<bf16*>(ws);
+  float* split_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.dA_bytes);
+  {  // dA = (dY W2^T) * GeLU'(A);  B(k, n) = W2[n][k]
+    GemmParams p = make_params(M, f, make_seg(dY, d, M * d, W2, d, f * d, d));
+    EpiDGelu<bf16> e{static_cast<const bf16*>(A), dA, f};
+    TPK_TRY((launch_gemm<true, true, false>(st, "mlp_bwd.dyw2t_dgelu", p, e, plan_gemm(M, f, d, false, false))));
+  }
+  {  // dW2 = H^T dY:  A(m, k) = H[k][m], B(k, n) = dY[k][n]
+    GemmParams p = make_params(f, d, make_seg(H, f, M * f, dY, d, M * d, M));
+    TPK_TRY(wgrad_f32_out(st, pl.dW2, f, d, dW2, split_ws, [&](const EpiStore<float>& e, GemmPlan g) {
+      return launch_gemm<false, false, false>(st, "mlp_bwd.htdy", p, e, g);
+    }));
+  }
+  {  // dX = dA W1^T;  B(k, n) = W1[n][k]
+    GemmParams p = make_params(M, d, make_seg(dA, f, M * f, W1, f, d * f, f));
+    EpiStore<bf16> e{static_cast<bf16*>(dX), d, 0};
+    TPK_TRY((launch_gemm<true, true, false>(st, "mlp_bwd.daw1t", p, e, plan_gemm(M, d, f, false, false))));
+  }
+  {  // dW1 = X^T dA:  A(m, k) = X[k][m], B(k, n) = dA[k][n]
+    GemmParams p = make_params(d, f, make_seg(X, d, M * d, dA, f, M * f, M));
+    TPK_TRY(wgrad_f32_out(st, pl.dW1, d, f, dW1, split_ws, [&](const EpiStore<float>& e, GemmPlan g) {
+      return launch_gemm<false, false, false>(st, "mlp_bwd.xtda", p, e, g);
+    }));
+  }
+  return hipSuccess;
+}
+
+// ------------------------------------------------------------------ fp32
+static hipError_t mlp_fwd_f32(hipStream_t st, int64_t M, int64_t d, int64_t f,
+                              const void* X, const void* W1, const void* W2,
+                              void* A, void* H, void* Z) {
+  {
+    GemmParamsF32 p = make_params_f32(M, f, make_seg_f32(X, d, M, W1, f, f, d));
+    EpiGelu<float> e{static_cast<float*>(A), static_cast<float*>(H), f};
+    TPK_TRY((launch_gemm_f32<true, false, false>(st, "mlp_f32.nn", p, e)));
+  }
+  {
+    GemmParamsF32 p = make_params_f32(M, d, make_seg_f32(H, f, M, W2, d, d, f));
+    EpiStore<float> e{static_cast<float*>(Z), d, 0};
+    TPK_TRY((launch_gemm_f32<true, false, false>(st, "mlp_f32.nn", p, e)));
+  }
+  return hipSuccess;
+}
+
+static hipError_t mlp_bwd_f32(hipStream_t st, int64_t M, int64_t d, int64_t f,
+                              const void* X, const void* W1, const void* W2,
+                              const void* A, const void* H, const void* dY,
+                              void* dX, float* dW1, float* dW2, void* ws) {
+  float* dA = static_cast<float*>(ws);
+  {
+    GemmParamsF32 p = make_params_f32(M, f, make_seg_f32(dY, d, M, W2, d, f, d));
+    EpiDGelu<float> e{static_cast<const float*>(A), dA, f};
+    TPK_TRY((launch_gemm_f32<true, true, false>(st, "mlp_f32.nt", p, e)));
+  }
+  {
+    GemmParamsF32 p = make_params_f32(f, d, make_seg_f32(H, f, f, dY, d, d, M));
+    EpiStore<float> e{dW2, d, 0};
+    TPK_TRY((launch_gemm_f32<false, false, false>(st, "mlp_f32.tn", p, e)));
+  }
+  {
+    GemmParamsF32 p = make_params_f32(M, d, make_seg_f32(dA, f, M, W1, f, d, f));
+    EpiStore<float> e{static_cast<float*>(dX), d, 0};
+    TPK_TRY((launch_gemm_f32<true, true, false>(st, "mlp_f32.nt", p, e)));
+  }
+  {
+    GemmParamsF32 p = make_params_f32(d, f, make_seg_f32(X, d, d, dA, f, f, M));
+    EpiStore<float> e{dW1, f, 0};
+    TPK_TRY((launch_gemm_f32<false, false, false>(st, "mlp_f32.tn", p, e)));
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_mlp_fwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t f,
+                          const void* X, const void* W1, const void* W2,
+                          void* A, void* H, void* Z) {
+  return dt == DT_BF16 ? mlp_fwd_bf16(st, M, d, f, X, W1, W2, A, H, Z)
+                       : mlp_fwd_f32(st, M, d, f, X, W1, W2, A, H, Z);
+}
+
+hipError_t launch_mlp_bwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t f,
+                          const void* X, const void* W1, const void* W2,
+                          const void* A, const void* H, const void* dY,
+                          void* dX, float* dW1, float* dW2, void* ws) {
+  return dt == DT_BF16 ? mlp_bwd_bf16(st, M, d, f, X, W1, W2, A, H, dY, dX, dW1, dW2, ws)
+                       : mlp_bwd_f32(st, M, d, f, X, W1, W2, A, H, dY, dX, dW1, dW2, ws);
+}
+
+}  // namespace tpk

@@ -1,0 +1,306 @@
+// C ABI of libtpshard: host-side validation and dispatch.  Every check runs
+// before the first HIP call, so each error path can be exercised on a
+// machine without a GPU.  No exception crosses the ABI.
+#include "../../include/tp_shard.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+#include "profile.hpp"
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return code;
+}
+
+int ok() {
+  g_detail.clear();
+  return TP_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TP_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+size_t esize(int dt) { return dt == TP_DT_BF16 ? 2 : 4; }
+
+bool dtype_ok(int dt) { return dt == TP_DT_F32 || dt == TP_DT_BF16; }
+
+struct Span {
+  const char* name;
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Pointer presence, alignment, and output/input overlap.
+int check_buffers(const std::vector<Span>& ins, const std::vector<Span>& outs,
+                  const std::vector<const char*>& required) {
+  auto find = [&](const char* n) -> const Span* {
+    for (const auto& s : ins)
+      if (std::string(s.name) == n) return &s;
+    for (const auto& s : outs)
+      if (std::string(s.name) == n) return &s;
+    return nullptr;
+  };
+  for (const char* n : required) {
+    const Span* s = find(n);
+    if (!s || !s->p) return fail(TP_E_NULL, "%s is NULL", n);
+  }
+  for (const auto* v : {&ins, &outs})
+    for (const auto& s : *v)
+      if (s.p && (reinterpret_cast<uintptr_t>(s.p) & 15u))
+        return fail(TP_E_ALIGN, "%s (%p) is not 16-byte aligned", s.name, s.p);
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const auto& in : ins)
+      if (overlap(outs[i], in)) return fail(TP_E_ALIAS, "output %s overlaps input %s", outs[i].name, in.name);
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(TP_E_ALIAS, "output %s overlaps output %s", outs[i].name, outs[j].name);
+  }
+  return TP_OK;
+}
+
+int check_dims(std::initializer_list<std::pair<const char*, int64_t>> dims) {
+  for (const auto& d : dims) {
+    if (d.second <= 0) return fail(TP_E_DIM, "%s = %lld must be positive", d.first, (long long)d.second);
+    if (d.second > kMaxDim) return fail(TP_E_DIM, "%s = %lld exceeds 2^30", d.first, (long long)d.second);
+  }
+  return TP_OK;
+}
+
+int check_mult8(std::initializer_list<std::pair<const char*, int64_t>> dims) {
+  for (const auto& d : dims)
+    if (d.second % 8) return fail(TP_E_DIVIS, "%s = %lld must be a multiple of 8", d.first, (long long)d.second);
+  return TP_OK;
+}
+
+#define TP_CHECK(expr)         \
+  do {                         \
+    int rc_ = (expr);          \
+    if (rc_ != TP_OK) return rc_; \
+  } while (0)
+
+int mlp_common(tp_dtype_t dt, int64_t M, int64_t d, int64_t f) {
+  if (!dtype_ok(dt)) return fail(TP_E_DTYPE, "dtype %d is not TP_DT_F32 or TP_DT_BF16", (int)dt);
+  TP_CHECK(check_dims({{"M", M}, {"d", d}, {"f", f}}));
+  TP_CHECK(check_mult8({{"d", d}, {"f", f}}));
+  if ((double)M * (double)std::max(d, f) * 2 > 9.0e15) return fail(TP_E_DIM, "operand too large");
+  return TP_OK;
+}
+
+}  // namespace
+
+namespace tpk {
+ProfileState& profile_state() {
+  static thread_local ProfileState ps;
+  return ps;
+}
+}  // namespace tpk
+
+extern "C" {
+
+int tp_abi_version(void) { return TP_ABI_VERSION; }
+
+int tp_profile_begin(void* const* start_events, void* const* stop_events, int capacity) {
+  if (!start_events || !stop_events) return fail(TP_E_NULL, "event arrays are NULL");
+  if (capacity <= 0) return fail(TP_E_DIM, "capacity must be positive");
+  tpk::ProfileState& ps = tpk::profile_state();
+  ps.start = reinterpret_cast<hipEvent_t const*>(start_events);
+  ps.stop = reinterpret_cast<hipEvent_t const*>(stop_events);
+  ps.capacity = capacity;
+  ps.count = 0;
+  return ok();
+}
+
+int tp_profile_end(void) {
+  tpk::ProfileState& ps = tpk::profile_state();
+  const int n = ps.count < ps.capacity ? ps.count : ps.capacity;
+  ps.start = ps.stop = nullptr;
+  ps.capacity = 0;
+  return n;
+}
+
+const char* tp_profile_label(int i) {
+  const tpk::ProfileState& ps = tpk::profile_state();
+  if (i < 0 || i >= ps.count || i >= tpk::ProfileState::kMaxLabels || !ps.labels[i]) return "";
+  return ps.labels[i];
+}
+
+const char* tp_last_error_detail(void) { return g_detail.c_str(); }
+
+const char* tp_strerror(int status) {
+  switch (status) {
+    case TP_OK: return "ok";
+    case TP_E_NULL: return "required pointer is NULL";
+    case TP_E_DIM: return "size is non-positive, too large or unsupported";
+    case TP_E_DIVIS: return "size is not a multiple of what it must be";
+    case TP_E_DTYPE: return "unsupported dtype";
+    case TP_E_ALIGN: return "pointer is not 16-byte aligned";
+    case TP_E_ALIAS: return "output overlaps an input or another output";
+    case TP_E_WORKSPACE: return "workspace missing or too small";
+    case TP_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int tp_shard_range(int64_t total, int64_t n_shards, int64_t index, int64_t* start, int64_t* len) {
+  if (!start || !len) return fail(TP_E_NULL, "start/len output pointer is NULL");
+  if (total <= 0 || n_shards <= 0) return fail(TP_E_DIM, "total and n_shards must be positive");
+  if (index < 0 || index >= n_shards)
+    return fail(TP_E_DIM, "index %lld outside [0, %lld)", (long long)index, (long long)n_shards);
+  if (total % n_shards)
+    return fail(TP_E_DIVIS, "%lld is not divisible by %lld shards", (long long)total, (long long)n_shards);
+  const int64_t k = total / n_shards;
+  *start = index * k;
+  *len = k;
+  return ok();
+}
+
+int tp_mlp_fwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
+               const void* X, const void* W1, const void* W2, void* A, void* H, void* Z) {
+  TP_CHECK(mlp_common(dt, M, d, f));
+  const size_t e = esize(dt);
+  TP_CHECK(check_buffers({{"X", X, M * d * e}, {"W1", W1, d * f * e}, {"W2", W2, f * d * e}},
+                         {{"A", A, M * f * e}, {"H", H, M * f * e}, {"Z", Z, M * d * e}},
+                         {"X", "W1", "W2", "H", "Z"}));
+  return hip_status(tpk::launch_mlp_fwd(static_cast<hipStream_t>(stream), dt, M, d, f, X, W1, W2, A, H, Z),
+                    "tp_mlp_fwd");
+}
+
+size_t tp_mlp_bwd_workspace_bytes(tp_dtype_t dt, int64_t M, int64_t d, int64_t f) {
+  if (mlp_common(dt, M, d, f) != TP_OK) return 0;
+  return tpk::mlp_bwd_ws_bytes(dt, M, d, f);
+}
+
+int tp_mlp_bwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
+               const void* X, const void* W1, const void* W2, const void* A, const void* H,
+               const void* dY, void* dX, float* dW1, float* dW2, void* ws, size_t ws_bytes) {
+  TP_CHECK(mlp_common(dt, M, d, f));
+  const size_t e = esize(dt);
+  const size_t need = tpk::mlp_bwd_ws_bytes(dt, M, d, f);
+  TP_CHECK(check_buffers(
+      {{"X", X, M * d * e}, {"W1", W1, d * f * e}, {"W2", W2, f * d * e}, {"A", A, M * f * e},
+       {"H", H, M * f * e}, {"dY", dY, M * d * e}},
+      {{"dX", dX, M * d * e}, {"dW1", dW1, d * f * (size_t)4}, {"dW2", dW2, f * d * (size_t)4}, {"ws", ws, need}},
+      {"X", "W1", "W2", "A", "H", "dY", "dX", "dW1", "dW2"}));
+  if (!ws || ws_bytes < need)
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes given, %zu required", ws ? ws_bytes : (size_t)0, need);
+  return hip_status(tpk::launch_mlp_bwd(static_cast<hipStream_t>(stream), dt, M, d, f, X, W1, W2, A, H, dY,
+                                        dX, dW1, dW2, ws),
+                    "tp_mlp_bwd");
+}
+
+int tp_swiglu_fwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
+                  const void* X, const void* W1, const void* W3, const void* W2,
+                  void* G, void* U, void* H, void* Z) {
+  TP_CHECK(mlp_common(dt, M, d, f));
+  if ((G == nullptr) != (U == nullptr)) return fail(TP_E_NULL, "G and U must both be given or both be NULL");
+  const size_t e = esize(dt);
+  TP_CHECK(check_buffers({{"X", X, M * d * e}, {"W1", W1, d * f * e}, {"W3", W3, d * f * e},
+                          {"W2", W2, f * d * e}},
+                         {{"G", G, M * f * e}, {"U", U, M * f * e}, {"H", H, M * f * e}, {"Z", Z, M * d * e}},
+                         {"X", "W1", "W3", "W2", "H", "Z"}));
+  return hip_status(tpk::launch_swiglu_fwd(static_cast<hipStream_t>(stream), dt, M, d, f, X, W1, W3, W2,
+                                           G, U, H, Z),
+                    "tp_swiglu_fwd");
+}
+
+size_t tp_swiglu_bwd_workspace_bytes(tp_dtype_t dt, int64_t M, int64_t d, int64_t f) {
+  if (mlp_common(dt, M, d, f) != TP_OK) return 0;
+  return tpk::swiglu_bwd_ws_bytes(dt, M, d, f);
+}
+
+int tp_swiglu_bwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
+                  const void* X, const void* W1, const void* W3, const void* W2,
+                  const void* G, const void* U, const void* H, const void* dY,
+                  void* dX, float* dW1, float* dW3, float* dW2, void* ws, size_t ws_bytes) {
+  TP_CHECK(mlp_common(dt, M, d, f));
+  const size_t e = esize(dt);
+  const size_t need = tpk::swiglu_bwd_ws_bytes(dt, M, d, f);
+  TP_CHECK(check_buffers(
+      {{"X", X, M * d * e}, {"W1", W1, d * f * e}, {"W3", W3, d * f * e}, {"W2", W2, f * d * e},
+       {"G", G, M * f * e}, {"U", U, M * f * e}, {"H", H, M * f * e}, {"dY", dY, M * d * e}},
+      {{"dX", dX, M * d * e}, {"dW1", dW1, d * f * (size_t)4}, {"dW3", dW3, d * f * (size_t)4}, {"dW2", dW2, f * d * (size_t)4},
+       {"ws", ws, need}},
+      {"X", "W1", "W3", "W2", "G", "U", "H", "dY", "dX", "dW1", "dW3", "dW2"}));
+  if (!ws || ws_bytes < need)
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes given, %zu required", ws ? ws_bytes : (size_t)0, need);
+  return hip_status(tpk::launch_swiglu_bwd(static_cast<hipStream_t>(stream), dt, M, d, f, X, W1, W3, W2,
+                                           G, U, H, dY, dX, dW1, dW3, dW2, ws),
+                    "tp_swiglu_bwd");
+}
+
+int tp_attn_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
+                      int64_t h_local, int64_t d_head, int causal, float scale,
+                      const void* X, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                      void* Q, void* K, void* V, void* O, void* Z) {
+  if (dt != TP_DT_BF16) return fail(TP_E_DTYPE, "attention supports TP_DT_BF16 only");
+  TP_CHECK(check_dims({{"b", b}, {"s", s}, {"d", d}, {"h_local", h_local}, {"d_head", d_head}}));
+  if (d_head != 64 && d_head != 128) return fail(TP_E_DIM, "d_head = %lld; 64 and 128 are supported", (long long)d_head);
+  if (causal != 0 && causal != 1) return fail(TP_E_DIM, "causal must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(TP_E_DIM, "scale is not finite");
+  TP_CHECK(check_mult8({{"d", d}}));
+  const int64_t M = b * s, N = h_local * d_head;
+  TP_CHECK(check_dims({{"b*s", M}, {"h_local*d_head", N}}));
+  const size_t e = 2;
+  TP_CHECK(check_buffers({{"X", X, M * d * e}, {"Wq", Wq, d * N * e}, {"Wk", Wk, d * N * e},
+                          {"Wv", Wv, d * N * e}, {"Wo", Wo, N * d * e}},
+                         {{"Q", Q, M * N * e}, {"K", K, M * N * e}, {"V", V, M * N * e},
+                          {"O", O, M * N * e}, {"Z", Z, M * d * e}},
+                         {"X", "Wq", "Wk", "Wv", "Wo", "Q", "K", "V", "O", "Z"}));
+  return hip_status(tpk::launch_attn_fwd(static_cast<hipStream_t>(stream), b, s, d, h_local, d_head, causal,
+                                         scale, X, Wq, Wk, Wv, Wo, Q, K, V, O, Z),
+                    "tp_attn_shard_fwd");
+}
+
+int tp_shard_reduce(void* stream, tp_dtype_t dt_in, tp_dtype_t dt_out, int64_t n_shards, int64_t numel,
+                    const void* partials, int64_t shard_stride, const void* bias, int64_t bias_len,
+                    void* out) {
+  if (!dtype_ok(dt_in) || !dtype_ok(dt_out)) return fail(TP_E_DTYPE, "dtype is not TP_DT_F32 or TP_DT_BF16");
+  if (n_shards <= 0 || n_shards > 4096) return fail(TP_E_DIM, "n_shards = %lld outside [1, 4096]", (long long)n_shards);
+  if (numel <= 0) return fail(TP_E_DIM, "numel must be positive");
+  if (shard_stride < numel) return fail(TP_E_DIM, "shard_stride %lld < numel %lld", (long long)shard_stride, (long long)numel);
+  if (bias && bias_len <= 0) return fail(TP_E_DIM, "bias_len must be positive when bias is given");
+  const size_t ei = esize(dt_in), eo = esize(dt_out);
+  const size_t in_bytes = ((size_t)(n_shards - 1) * shard_stride + numel) * ei;
+  const bool in_place = out == partials && dt_in == dt_out;
+  const Span sp{"partials", partials, in_place ? 0 : in_bytes};
+  TP_CHECK(check_buffers({sp, {"bias", bias, bias ? bias_len * ei : 0}},
+                         {{"out", out, numel * eo}}, {"partials", "out"}));
+  if (in_place) {  // out is block 0 itself: it must not reach into block 1 or the bias
+    const Span rest{"partials[1:]", static_cast<const char*>(partials) + shard_stride * ei,
+                    n_shards > 1 ? in_bytes - shard_stride * ei : 0};
+    if (overlap({"out", out, numel * eo}, rest)) return fail(TP_E_ALIAS, "output out overlaps input partials");
+  } else if (out == partials) {
+    return fail(TP_E_ALIAS, "in-place shard-reduce needs dt_in == dt_out");
+  }
+  return hip_status(tpk::launch_shard_reduce(static_cast<hipStream_t>(stream), dt_in, dt_out, (int)n_shards,
+                                             numel, partials, shard_stride, bias, bias ? bias_len : 0, out),
+                    "tp_shard_reduce");
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status before
+any HIP call (so none of these calls touches a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import megatron_tensor_transformer_fwd_amd as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_shard.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tp.LIB_PATH), reason="libtpshard.so not built")
+
+OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+BF16, F32 = tp.TP_DT_BF16, tp.TP_DT_F32
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree_and_library_exports_all():
+    names = _declared_functions()
+    assert set(names) == set(tp.EXPORTS), (names, sorted(tp.EXPORTS))
+    L = tp.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strerror():
+    assert tp.tp_abi_version() == 1
+    L = tp.lib()
+    for code in (OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP):
+        assert L.tp_strerror(code) and L.tp_strerror(code) != b"unknown status"
+    assert L.tp_strerror(-99) == b"unknown status"
+
+
+def test_shard_range():
+    assert tp.tp_shard_range(4096, 8, 3) == (1536, 512)
+    assert tp.tp_shard_range(11008, 4, 3) == (8256, 2752)
+    assert tp.tp_shard_range(32, 4, 0) == (0, 8)
+    with pytest.raises(tp.TPError) as e:
+        tp.tp_shard_range(11008, 3, 0)
+    assert e.value.status == E_DIVIS and "divisible" in e.value.detail
+    for args in ((0, 4, 0), (16, 0, 0), (16, 4, 4), (16, 4, -1)):
+        with pytest.raises(tp.TPError) as e:
+            tp.tp_shard_range(*args)
+        assert e.value.status == E_DIM
+    assert tp.lib().tp_shard_range(8, 2, 0, None, None) == E_NULL
+
+
+# Fake, well separated, 16-byte aligned device addresses: validation never
+# dereferences them and every case below fails before any HIP call.
+BASE = 1 << 40
+
+
+def _addrs(n, gap=1 << 32):
+    return [BASE + i * gap for i in range(n)]
+
+
+def _mlp_fwd(**kw):
+    X, W1, W2, A, H, Z = _addrs(6)
+    args = dict(stream=None, dt=BF16, M=64, d=64, f=128, X=X, W1=W1, W2=W2, A=A, H=H, Z=Z)
+    args.update(kw)
+    rc = tp.lib().tp_mlp_fwd(*args.values())
+    return rc, tp.lib().tp_last_error_detail().decode()
+
+
+def test_mlp_fwd_validation():
+    assert _mlp_fwd(X=None)[0] == E_NULL
+    assert _mlp_fwd(H=None)[0] == E_NULL
+    assert _mlp_fwd(M=0)[0] == E_DIM
+    assert _mlp_fwd(d=-8)[0] == E_DIM
+    assert _mlp_fwd(M=(1 << 30) + 1)[0] == E_DIM
+    assert _mlp_fwd(d=60)[0] == E_DIVIS
+    assert _mlp_fwd(f=130)[0] == E_DIVIS
+    assert _mlp_fwd(dt=7)[0] == E_DTYPE
+    assert _mlp_fwd(W1=BASE + (1 << 32) + 8)[0] == E_ALIGN
+    rc, msg = _mlp_fwd(Z=BASE + 16)          # Z on top of X
+    assert rc == E_ALIAS and "Z" in msg and "X" in msg
+    assert _mlp_fwd(H=BASE + 7 * (1 << 32), Z=BASE + 7 * (1 << 32) + 64)[0] == E_ALIAS   # H and Z overlap
+
+
+def _mlp_bwd(**kw):
+    ptrs = _addrs(10)
+    names = ["X", "W1", "W2", "A", "H", "dY", "dX", "dW1", "dW2", "ws"]
+    args = dict(stream=None, dt=BF16, M=64, d=64, f=128)
+    args.update(dict(zip(names, ptrs)))
+    args["ws_bytes"] = 1 << 30
+    args.update(kw)
+    return tp.lib().tp_mlp_bwd(*args.values())
+
+
+def test_mlp_bwd_validation_and_workspace():
+    need = tp.tp_mlp_bwd_workspace_bytes(BF16, 64, 64, 128)
+    assert need >= 64 * 128 * 2
+    assert tp.tp_mlp_bwd_workspace_bytes(F32, 64, 64, 128) >= 64 * 128 * 4
+    assert tp.tp_mlp_bwd_workspace_bytes(BF16, 0, 64, 128) == 0
+    assert tp.tp_mlp_bwd_workspace_bytes(BF16, 64, 60, 128) == 0
+    assert _mlp_bwd(ws_bytes=need - 1) == E_WS
+    assert _mlp_bwd(ws=None) in (E_WS, E_NULL)
+    assert _mlp_bwd(A=None) == E_NULL
+    assert _mlp_bwd(dW1=BASE + 4) == E_ALIGN
+    assert _mlp_bwd(dX=BASE + 5 * (1 << 32)) == E_ALIAS       # dX on top of dY
+    assert _mlp_bwd(f=12) == E_DIVIS
+
+
+def test_mlp_bwd_workspace_grows_with_split_k():
+    # narrow weight-gradient outputs take a split-K workspace of fp32 partials
+    small = tp.tp_mlp_bwd_workspace_bytes(BF16, 8192, 1024, 512)
+    assert small >= 8192 * 512 * 2 + 2 * 1024 * 512 * 4
+
+
+def test_swiglu_validation():
+    L = tp.lib()
+    p = _addrs(8)
+    assert L.tp_swiglu_fwd(None, BF16, 64, 64, 128, *p[:4], p[4], None, p[6], p[7]) == E_NULL   # G without U
+    assert L.tp_swiglu_fwd(None, BF16, 64, 64, 124, *p[:4], p[4], p[5], p[6], p[7]) == E_DIVIS
+    assert L.tp_swiglu_fwd(None, 3, 64, 64, 128, *p[:4], p[4], p[5], p[6], p[7]) == E_DTYPE
+    q = _addrs(17)
+    need = tp.tp_swiglu_bwd_workspace_bytes(BF16, 64, 64, 128)
+    assert need >= 64 * 256 * 2
+    assert L.tp_swiglu_bwd(None, BF16, 64, 64, 128, *q[:12], q[16], need - 16) == E_WS
+    assert L.tp_swiglu_bwd(None, BF16, 64, 64, 128, *q[:4], None, *q[5:12], q[16], need) == E_NULL
+
+
+def _attn(**kw):
+    p = _addrs(10)
+    args = dict(stream=None, dt=BF16, b=2, s=64, d=64, h_local=2, d_head=128, causal=1, scale=0.0)
+    args.update(dict(zip(["X", "Wq", "Wk", "Wv", "Wo", "Q", "K", "V", "O", "Z"], p)))
+    args.update(kw)
+    return tp.lib().tp_attn_shard_fwd(*args.values())
+
+
+def test_attention_validation():
+    assert _attn(dt=F32) == E_DTYPE
+    assert _attn(d_head=96) == E_DIM
+    assert _attn(s=0) == E_DIM
+    assert _attn(causal=2) == E_DIM
+    assert _attn(scale=float("nan")) == E_DIM
+    assert _attn(d=60) == E_DIVIS
+    assert _attn(O=None) == E_NULL
+    assert _attn(Q=BASE + 8) == E_ALIGN
+    assert _attn(Z=BASE) == E_ALIAS
+
+
+def test_shard_reduce_validation():
+    L = tp.lib()
+    P, out, bias = _addrs(3)
+    assert L.tp_shard_reduce(None, BF16, BF16, 0, 16, P, 16, None, 0, out) == E_DIM
+    assert L.tp_shard_reduce(None, BF16, BF16, 4, 0, P, 16, None, 0, out) == E_DIM
+    assert L.tp_shard_reduce(None, BF16, BF16, 4, 16, P, 8, None, 0, out) == E_DIM       # stride < numel
+    assert L.tp_shard_reduce(None, BF16, BF16, 4, 16, P, 16, bias, 0, out) == E_DIM      # bias_len
+    assert L.tp_shard_reduce(None, 5, BF16, 4, 16, P, 16, None, 0, out) == E_DTYPE
+    assert L.tp_shard_reduce(None, BF16, BF16, 4, 16, None, 16, None, 0, out) == E_NULL
+    assert L.tp_shard_reduce(None, BF16, BF16, 4, 16, P + 2, 16, None, 0, out) == E_ALIGN
+    assert L.tp_shard_reduce(None, BF16, BF16, 4, 16, P, 16, None, 0, P + 32) == E_ALIAS  # into block 1
+    assert L.tp_shard_reduce(None, BF16, F32, 4, 16, P, 16, None, 0, P) == E_ALIAS       # in place, dtypes differ
+    assert L.tp_shard_reduce(None, F32, F32, 4, 16, P, 8 + 8, None, 0, P + 16) == E_ALIAS
+    # an exactly in-place reduce with out's extent inside block 0 passes validation:
+    # only the launch (no device here) can then fail, with TP_E_HIP.
+    assert L.tp_last_error_detail() != b""

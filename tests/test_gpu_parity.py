@@ -1,0 +1,339 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: max_rel_err = ||gpu - oracle||_inf / ||oracle||_inf <= 2e-2 for bf16
+inputs with fp32 accumulation and <= 1e-5 for the all-fp32 path, for every
+output tensor.  Inputs are the seeded synthetic ones (tpsynth); the oracle
+sees exactly the bf16-rounded values the GPU sees.  Full-size workloads are
+checked on sampled rows and columns the oracle computes directly (rows of
+the output depend only on rows of X and dY; a subset of the shard's d_ff
+columns is itself a smaller shard).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import tpsynth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import megatron_tensor_transformer_fwd_amd as m
+    m.lib()          # raises if the library is missing: no fallback path exists
+    return m
+
+
+def dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(dtype=torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def empty(shape, dtype):
+    return torch.empty(shape, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+
+
+def check(name, got, ref, dtype):
+    err = O.max_rel_err(host(got) if torch.is_tensor(got) else got, ref)
+    assert np.isfinite(err) and err <= TOL[dtype], f"{name}: max_rel_err {err:.3e} > {TOL[dtype]}"
+    return err
+
+
+def run_mlp_shard(tp, X, W1, W2, dY, dtype):
+    M, d = X.shape
+    f = W1.shape[1]
+    A, H, Z = empty((M, f), dtype), empty((M, f), dtype), empty((M, d), dtype)
+    tp.tp_mlp_fwd(X, W1, W2, A, H, Z)
+    out = {"A": A, "H": H, "Z": Z}
+    if dY is not None:
+        dX = empty((M, d), dtype)
+        dW1 = torch.empty((d, f), dtype=torch.float32, device="cuda")
+        dW2 = torch.empty((f, d), dtype=torch.float32, device="cuda")
+        dt = tp.TP_DT_BF16 if dtype == "bf16" else tp.TP_DT_F32
+        ws = torch.empty(tp.tp_mlp_bwd_workspace_bytes(dt, M, d, f), dtype=torch.uint8, device="cuda")
+        tp.tp_mlp_bwd(X, W1, W2, A, H, dY, dX, dW1, dW2, ws)
+        out.update(dX=dX, dW1=dW1, dW2=dW2)
+    torch.cuda.synchronize()
+    return out
+
+
+# ------------------------------------------------------------- shard-reduce
+
+def test_shard_reduce_pages_worked_example(tp):
+    _say("shard_reduce pages example")
+    # "Chapter 8: Distributed Training", 8.4.2: ranks r = 0..3 hold [0,1,2,3] + r
+    for dtype in ("f32", "bf16"):
+        P = dev(np.stack([np.arange(4) + r for r in range(4)]), dtype)
+        out = empty((4,), dtype)
+        tp.tp_shard_reduce(P, out, 4, 4)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(out), [6, 10, 14, 18])
+
+
+@pytest.mark.parametrize("dtype_in,dtype_out,n,numel,stride,bias_len", [
+    ("bf16", "bf16", 8, 8192 * 1024, None, 0),        # C2: 8 partials of [8192 x 1024]
+    ("bf16", "bf16", 3, 1001, 1008, 7),                # ragged numel, padded stride, bias
+    ("f32", "f32", 2, 32 * 64, None, 64),              # C1 size with a row bias
+    ("bf16", "f32", 5, 4099, 4101, 0),                 # stride breaks 16-byte alignment
+    ("f32", "bf16", 9, 77, None, 0),
+])
+def test_shard_reduce_random(tp, dtype_in, dtype_out, n, numel, stride, bias_len):
+    _say(f"shard_reduce {dtype_in}->{dtype_out} n={n} numel={numel} stride={stride} bias={bias_len}")
+    st = stride or numel
+    inp = tpsynth.reduce_inputs(n, st, dtype_in, seed=3, bias_len=bias_len)
+    P = dev(inp["P"], dtype_in)
+    bias = dev(inp["bias"], dtype_in) if bias_len else None
+    out = empty((numel,), dtype_out)
+    tp.tp_shard_reduce(P, out, n, numel, shard_stride=st, bias=bias)
+    torch.cuda.synchronize()
+    ref = O.shard_reduce([inp["P"][i, :numel] for i in range(n)], inp["bias"])
+    check("out", out, ref, "bf16" if "bf16" in (dtype_in, dtype_out) else "f32")
+    out2 = empty((numel,), dtype_out)
+    tp.tp_shard_reduce(P, out2, n, numel, shard_stride=st, bias=bias)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "shard-reduce is not bitwise deterministic"
+
+
+def test_shard_reduce_in_place(tp):
+    _say("shard_reduce in place")
+    inp = tpsynth.reduce_inputs(4, 4096, "bf16", seed=4)
+    P = dev(inp["P"], "bf16")
+    tp.tp_shard_reduce(P, P[0], 4, 4096)
+    torch.cuda.synchronize()
+    check("out", P[0], O.shard_reduce(list(inp["P"])), "bf16")
+
+
+# ---------------------------------------------------------------- GeLU MLP
+
+def test_mlp_c1_fp32_two_shards(tp):
+    _say("mlp C1 fp32, both shards, Z and dX reduces")
+    wl = tpsynth.WORKLOADS["C1"]
+    inp = tpsynth.mlp_inputs(wl)
+    X, dY = dev(inp["X"], "f32"), dev(inp["dY"], "f32")
+    Zs, dXs = [], []
+    for i in range(wl.n_shards):
+        W1, W2 = inp["W1s"][i], inp["W2s"][i]
+        out = run_mlp_shard(tp, X, dev(W1, "f32"), dev(W2, "f32"), dY, "f32")
+        ref = O.mlp_shard_fwd(inp["X"], W1, W2)
+        refb = O.mlp_shard_bwd(inp["X"], W1, W2, inp["dY"])
+        for k in ("A", "H", "Z"):
+            check(f"{k}_{i}", out[k], ref[k], "f32")
+        for k in ("dX", "dW1", "dW2"):
+            check(f"{k}_{i}", out[k], refb[k], "f32")
+        Zs.append(out["Z"])
+        dXs.append(out["dX"])
+    M, d = inp["X"].shape
+    Zp, dXp = torch.stack(Zs), torch.stack(dXs)
+    Z, dX = empty((M, d), "f32"), empty((M, d), "f32")
+    tp.tp_shard_reduce(Zp, Z, wl.n_shards, M * d)
+    tp.tp_shard_reduce(dXp, dX, wl.n_shards, M * d)
+    torch.cuda.synchronize()
+    check("Y", Z, O.mlp_unsharded(inp["X"], inp["W1"], inp["W2"]), "f32")
+    check("dX", dX, O.mlp_unsharded_bwd(inp["X"], inp["W1"], inp["W2"], inp["dY"])["dX"], "f32")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,d,f", [(300, 136, 200), (1, 8, 8), (520, 264, 392), (64, 64, 128)])
+def test_mlp_ragged_shapes(tp, dtype, M, d, f):
+    _say(f"mlp ragged {dtype} M={M} d={d} f={f}")
+    inp = tpsynth.random_mlp(M, d, f, dtype, seed=M + d + f, w_std=0.05)
+    out = run_mlp_shard(tp, dev(inp["X"], dtype), dev(inp["W1"], dtype), dev(inp["W2"], dtype),
+                        dev(inp["dY"], dtype), dtype)
+    ref = O.mlp_shard_fwd(inp["X"], inp["W1"], inp["W2"])
+    refb = O.mlp_shard_bwd(inp["X"], inp["W1"], inp["W2"], inp["dY"])
+    for k in ("A", "H", "Z"):
+        check(k, out[k], ref[k], dtype)
+    for k in ("dX", "dW1", "dW2"):
+        check(k, out[k], refb[k], dtype)
+
+
+def test_mlp_c2_all_shards_and_reduces(tp):
+    _say("mlp C2 bf16, 8 shards + Z/dX shard-reduce")
+    wl = tpsynth.WORKLOADS["C2"]
+    inp = tpsynth.mlp_inputs(wl)
+    M, d = inp["X"].shape
+    X, dY = dev(inp["X"], "bf16"), dev(inp["dY"], "bf16")
+    Zp = empty((wl.n_shards, M, d), "bf16")
+    dXp = empty((wl.n_shards, M, d), "bf16")
+    for i in range(wl.n_shards):
+        out = run_mlp_shard(tp, X, dev(inp["W1s"][i], "bf16"), dev(inp["W2s"][i], "bf16"), dY, "bf16")
+        Zp[i].copy_(out["Z"])
+        dXp[i].copy_(out["dX"])
+        if i in (0, wl.n_shards - 1):   # every output tensor of two shards, in full
+            ref = O.mlp_shard_fwd(inp["X"], inp["W1s"][i], inp["W2s"][i])
+            refb = O.mlp_shard_bwd(inp["X"], inp["W1s"][i], inp["W2s"][i], inp["dY"])
+            for k in ("A", "H", "Z"):
+                check(f"{k}_{i}", out[k], ref[k], "bf16")
+            for k in ("dX", "dW1", "dW2"):
+                check(f"{k}_{i}", out[k], refb[k], "bf16")
+    Z, dX = empty((M, d), "bf16"), empty((M, d), "bf16")
+    tp.tp_shard_reduce(Zp, Z, wl.n_shards, M * d)
+    tp.tp_shard_reduce(dXp, dX, wl.n_shards, M * d)
+    torch.cuda.synchronize()
+    check("Y", Z, O.mlp_unsharded(inp["X"], inp["W1"], inp["W2"]), "bf16")
+    check("dX", dX, O.mlp_unsharded_bwd(inp["X"], inp["W1"], inp["W2"], inp["dY"])["dX"], "bf16")
+
+
+def test_mlp_bwd_bitwise_deterministic(tp):
+    _say("mlp C2-shard backward twice, bitwise")
+    wl = tpsynth.WORKLOADS["C2"]
+    inp = tpsynth.mlp_inputs(wl)
+    args = (dev(inp["X"], "bf16"), dev(inp["W1s"][3], "bf16"), dev(inp["W2s"][3], "bf16"), dev(inp["dY"], "bf16"))
+    a = run_mlp_shard(tp, *args, "bf16")
+    b = run_mlp_shard(tp, *args, "bf16")
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def _sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.choice(n, size=k, replace=False))
+    idx[0], idx[-1] = 0, n - 1      # the first and last row/column always
+    return np.unique(idx)
+
+
+def test_mlp_c5_full_size_sampled(tp):
+    _say("mlp C5 bf16 full size, sampled rows/cols")
+    wl = tpsynth.WORKLOADS["C5"]
+    inp = tpsynth.mlp_inputs(wl)
+    Xh, W1h, W2h, dYh = inp["X"], inp["W1s"][0], inp["W2s"][0], inp["dY"]
+    out = run_mlp_shard(tp, dev(Xh, "bf16"), dev(W1h, "bf16"), dev(W2h, "bf16"), dev(dYh, "bf16"), "bf16")
+    rows = _sample(wl.M, 48, 11)
+    cols = _sample(wl.f_local, 16, 12)
+    ref = O.mlp_shard_fwd(Xh[rows], W1h, W2h)
+    for k in ("A", "H", "Z"):
+        check(k, host(out[k])[rows], ref[k], "bf16")
+    check("dX", host(out["dX"])[rows], O.mlp_shard_bwd(Xh[rows], W1h, W2h, dYh[rows])["dX"], "bf16")
+    sub = O.mlp_shard_bwd(Xh, W1h[:, cols], W2h[cols], dYh)      # the columns `cols` as a sub-shard
+    check("dW1", host(out["dW1"])[:, cols], sub["dW1"], "bf16")
+    check("dW2", host(out["dW2"])[cols], sub["dW2"], "bf16")
+
+
+# ------------------------------------------------------------------ SwiGLU
+
+def run_swiglu(tp, inp, dtype):
+    X, W1, W3, W2, dY = (dev(inp[k], dtype) for k in ("X", "W1", "W3", "W2", "dY"))
+    M, d = X.shape
+    f = W1.shape[1]
+    G, U, H = empty((M, f), dtype), empty((M, f), dtype), empty((M, f), dtype)
+    Z = empty((M, d), dtype)
+    tp.tp_swiglu_fwd(X, W1, W3, W2, G, U, H, Z)
+    dX = empty((M, d), dtype)
+    dW1, dW3 = (torch.empty((d, f), dtype=torch.float32, device="cuda") for _ in range(2))
+    dW2 = torch.empty((f, d), dtype=torch.float32, device="cuda")
+    dt = tp.TP_DT_BF16 if dtype == "bf16" else tp.TP_DT_F32
+    ws = torch.empty(tp.tp_swiglu_bwd_workspace_bytes(dt, M, d, f), dtype=torch.uint8, device="cuda")
+    tp.tp_swiglu_bwd(X, W1, W3, W2, G, U, H, dY, dX, dW1, dW3, dW2, ws)
+    torch.cuda.synchronize()
+    return dict(G=G, U=U, H=H, Z=Z, dX=dX, dW1=dW1, dW3=dW3, dW2=dW2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,d,f", [(300, 136, 200), (257, 64, 2752 // 8), (8, 8, 8)])
+def test_swiglu_ragged_shapes(tp, dtype, M, d, f):
+    _say(f"swiglu ragged {dtype} M={M} d={d} f={f}")
+    inp = tpsynth.random_swiglu(M, d, f, dtype, seed=M * 3 + f, w_std=0.05)
+    out = run_swiglu(tp, inp, dtype)
+    ref = O.swiglu_shard_fwd(inp["X"], inp["W1"], inp["W3"], inp["W2"])
+    refb = O.swiglu_shard_bwd(inp["X"], inp["W1"], inp["W3"], inp["W2"], inp["dY"])
+    for k in ("G", "U", "H", "Z"):
+        check(k, out[k], ref[k], dtype)
+    for k in ("dX", "dW1", "dW3", "dW2"):
+        check(k, out[k], refb[k], dtype)
+
+
+def test_swiglu_c3_full_size_sampled(tp):
+    _say("swiglu C3 bf16 full size, sampled rows/cols")
+    wl = tpsynth.WORKLOADS["C3"]
+    inp = tpsynth.swiglu_inputs(wl)
+    out = run_swiglu(tp, inp, "bf16")
+    X, W1, W3, W2, dY = (inp[k] for k in ("X", "W1", "W3", "W2", "dY"))
+    rows = _sample(wl.M, 48, 21)
+    cols = np.unique(np.concatenate([_sample(wl.f_local, 14, 22), [2687, 2688, 2751]]))  # ragged last tile
+    ref = O.swiglu_shard_fwd(X[rows], W1, W3, W2)
+    for k in ("G", "U", "H", "Z"):
+        check(k, host(out[k])[rows], ref[k], "bf16")
+    check("dX", host(out["dX"])[rows], O.swiglu_shard_bwd(X[rows], W1, W3, W2, dY[rows])["dX"], "bf16")
+    sub = O.swiglu_shard_bwd(X, W1[:, cols], W3[:, cols], W2[cols], dY)
+    check("dW1", host(out["dW1"])[:, cols], sub["dW1"], "bf16")
+    check("dW3", host(out["dW3"])[:, cols], sub["dW3"], "bf16")
+    check("dW2", host(out["dW2"])[cols], sub["dW2"], "bf16")
+
+
+# --------------------------------------------------------------- attention
+
+def run_attn(tp, inp, b, s, h_l, dh, causal=True):
+    X, Wq, Wk, Wv, Wo = (dev(inp[k], "bf16") for k in ("X", "Wq", "Wk", "Wv", "Wo"))
+    d = X.shape[1]
+    Q, K, V = (empty((b, h_l, s, dh), "bf16") for _ in range(3))
+    Ob, Z = empty((b * s, h_l * dh), "bf16"), empty((b * s, d), "bf16")
+    tp.tp_attn_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, Z, b, s, h_l, dh, causal=causal)
+    torch.cuda.synchronize()
+    return dict(Q=Q, K=K, V=V, O=Ob, Z=Z)
+
+
+@pytest.mark.parametrize("b,s,d,h_l,dh,causal", [
+    (2, 200, 64, 2, 128, True),      # ragged sequence (not a multiple of the 128-query tile)
+    (1, 64, 136, 3, 64, True),
+    (2, 130, 64, 1, 128, False),
+    (1, 1, 32, 2, 128, True),        # one token: o = v
+    (3, 257, 96, 2, 64, True),
+])
+def test_attention_small_shapes(tp, b, s, d, h_l, dh, causal):
+    _say(f"attention b={b} s={s} d={d} h_l={h_l} dh={dh} causal={causal}")
+    inp = tpsynth.random_attn(b, s, d, h_l, dh, "bf16", seed=b * s + dh, w_std=0.1)
+    out = run_attn(tp, inp, b, s, h_l, dh, causal)
+    ref = O.attn_shard_fwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], b, s, h_l, dh, causal)
+    for k in ("Q", "K", "V", "O", "Z"):
+        check(k, out[k], ref[k], "bf16")
+
+
+def test_attention_shards_sum_to_unsharded(tp):
+    _say("attention 4 shards summed == unsharded")
+    n, b, s, d, h_l, dh = 4, 1, 96, 64, 1, 64
+    inp = tpsynth.random_attn(b, s, d, h_l, dh, "bf16", seed=5, w_std=0.1, n_shards=n)
+    X = inp["X"]
+    Zp = empty((n, b * s, d), "bf16")
+    for i in range(n):
+        sh = {"X": X, "Wq": inp["Wqs"][i], "Wk": inp["Wks"][i], "Wv": inp["Wvs"][i], "Wo": inp["Wos"][i]}
+        Zp[i].copy_(run_attn(tp, sh, b, s, h_l, dh)["Z"])
+    Z = empty((b * s, d), "bf16")
+    tp.tp_shard_reduce(Zp, Z, n, b * s * d)
+    torch.cuda.synchronize()
+    full = O.attn_unsharded(X, inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], b, s, n * h_l, dh)
+    check("Z", Z, full["Z"], "bf16")
+
+
+def test_attention_c4_full_size_sampled(tp):
+    _say("attention C4 bf16 full size, sampled heads and queries")
+    wl = tpsynth.WORKLOADS["C4"]
+    inp = tpsynth.attn_inputs(wl)
+    b, s, h_l, dh = wl.b, wl.s, wl.h_local, wl.d_head
+    out = run_attn(tp, inp, b, s, h_l, dh)
+    bi = b - 1                                  # one batch row, all heads, all positions
+    Xb = inp["X"][bi * s:(bi + 1) * s]
+    ref = O.attn_shard_fwd(Xb, inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], 1, s, h_l, dh)
+    for k in ("Q", "K", "V"):
+        check(k, host(out[k])[bi], ref[k][0], "bf16")
+    check("O", host(out["O"])[bi * s:(bi + 1) * s], ref["O"], "bf16")
+    check("Z", host(out["Z"])[bi * s:(bi + 1) * s], ref["Z"], "bf16")
+    rows = _sample(s, 32, 31)                  # batch 0: sampled query rows
+    ref0 = O.attn_shard_fwd(inp["X"][:s], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], 1, s, h_l, dh)
+    check("O[b0]", host(out["O"])[rows], ref0["O"][rows], "bf16")
