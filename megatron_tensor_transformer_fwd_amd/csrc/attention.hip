@@ -22,6 +22,7 @@
 // tiles are dispatched first.
 #include "epilogues.hpp"
 #include "gemm_dispatch.hpp"
+#include "stage_regs.hpp"
 
 namespace tpk {
 

@@ -2,27 +2,33 @@
 // with a fused epilogue.
 //
 // Design (CDNA4-first):
-//  * Workgroup tile BM x BN x BK, WM x WN wavefronts of 64 lanes; every wave
-//    owns a (BM/WM) x (BN/WN) sub-tile computed with v_mfma_f32_32x32x16_bf16.
-//  * Both operands are staged through LDS as rows of BK contiguous k values
-//    (pitch BK+8 bf16, which keeps 16-lane groups of 16-byte reads and
-//    writes on distinct banks), double-buffered: the global loads of tile
-//    t+1 are in flight while the MFMAs of tile t run, and one barrier per
-//    k-tile separates the two buffers.
-//  * An operand whose k index is contiguous in memory (K-major) is loaded in
-//    16-byte chunks along k.  An operand whose m/n index is contiguous
-//    (M- or N-major: the weights of the forward products, and both operands
-//    of the weight-gradient products) is loaded as R x 8 blocks with 16-byte
-//    row loads and transposed in registers with v_perm_b32 before the LDS
-//    write, so global loads stay 16-byte and coalesced in every layout.
-//  * Global loads go through buffer resources: reads past the end of an
-//    operand return zero, which pads the ragged k tail; K-major tails inside a
-//    row are masked explicitly.
-//  * The MFMA's first operand is the B tile and its second the A tile, so the
-//    32x32 accumulator hands each lane 4 consecutive n for one m: epilogues
-//    work on (m, n..n+3) quads and store 8 or 16 bytes at a time.
-//  * Workgroup ids are remapped so that the tiles one XCD (of 8) runs are
-//    contiguous, then grouped along m for L2 reuse of the B panels.
+//  * Workgroup tile BM x BN x 64 computed by WM x WN wavefronts of 64 lanes;
+//    every wave owns a (BM/WM) x (BN/WN) sub-tile of v_mfma_f32_32x32x16_bf16
+//    blocks, accumulators in AGPRs.
+//  * Operand tiles go global -> LDS with buffer_load ... lds (LDS DMA): no
+//    staging registers and no ds_write.  Each wave instruction fills 1 KiB of
+//    LDS, lane L writing bytes [16L, 16L+16); the lane picks which 16-byte
+//    chunk of the tile it fetches, which is how the tiles get their bank
+//    swizzle.  Reads past the end of an operand return zero (buffer range),
+//    which pads ragged k tails; k tails inside a row are sent out of range.
+//  * Two LDS stages: the DMA of k-tile t+1 is in flight while tile t is
+//    multiplied; explicit s_waitcnt vmcnt + s_barrier (no fences) order it.
+//  * A K-major operand (k contiguous in memory) is kept as rows of 64 k
+//    (128 B) with 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7); MFMA
+//    fragments are single ds_read_b128s, bank-conflict free for 16 rows.
+//  * An M/N-major operand (m or n contiguous: the weights of the forward
+//    products, both operands of the weight-gradient products) is kept as it
+//    is in memory, k rows of 128 m/n values (256 B) per sub-tile, chunk c of
+//    row r stored at c ^ (4 (r & 3)), and its fragments are read with two
+//    ds_read_b64_tr_b16 (the gfx950 LDS transpose read): within each 16-lane
+//    group lane q receives element q%4 of the rows addressed by lanes q/4 +
+//    4e, so pointing lane i at row k0 + i/4, columns n0 + 4 (i%4) hands lane q
+//    the four k values of column n0 + q.  No register transposes.
+//  * The MFMA's first operand is the B fragment and its second the A
+//    fragment, so each lane's accumulator holds 4 consecutive n of one m:
+//    epilogues work on (m, n..n+3) quads.
+//  * Workgroup ids are remapped so the tiles one XCD (of 8) runs are
+//    contiguous, then grouped along m for L2 reuse.
 #pragma once
 #include "common.hpp"
 
@@ -47,113 +53,136 @@ struct GemmParams {
   int split_k;         // K-tile ranges over blockIdx.y
 };
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-  static constexpr int NT = WM * WN * 64;
+  static constexpr int BM = BM_, BN = BN_, BK = 64, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  static constexpr int LDK = BK + 8;
-  static constexpr int SMEM_BYTES = 2 * (BM + BN) * LDK * 2;
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0, "tile shape");
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int SMEM_BYTES = 2 * STAGE;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(BM % 128 == 0 && BN % 128 == 0, "M/N-major tiles are 128-wide sub-tiles");
 };
 
-// ----------------------------------------------------------------------------
-// Operand staging (global -> registers -> LDS)
-// ----------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// K-major: 16-byte chunks along k.  Chunk q of the tile is row q / (BK/8),
-// chunk q % (BK/8); eight lanes cover one 128-byte row segment.
-template <int ROWS, int BK, int NT, int LDK>
-struct KMajorStage {
-  static constexpr int CPR = BK / 8;
-  static constexpr int N = ROWS * CPR / NT;
-  static_assert((ROWS * CPR) % NT == 0, "K-major staging split");
-  u32x4 v[N];
+constexpr uint32_t kOOB = 0x80000000u;   // a buffer offset past every tile range
 
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t ld_bytes, int kvalid, int tid) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int q = tid + i * NT;
-      const int row = q / CPR, kc = q % CPR;
-      u32x4 x = buf_load16(r, (uint32_t)row * ld_bytes + (uint32_t)kc * 16u);
-      if (kc * 8 >= kvalid) x = u32x4{0u, 0u, 0u, 0u};
-      v[i] = x;
-    }
-  }
-  __device__ __forceinline__ void store(bf16* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int q = tid + i * NT;
-      const int row = q / CPR, kc = q % CPR;
-      *reinterpret_cast<u32x4*>(lds + row * LDK + kc * 8) = v[i];
-    }
-  }
-};
+// Buffer descriptor words (gfx9 layout: base, stride 0, num_records, flags),
+// kept in SGPRs.
+typedef i32x4 desc_t;
 
-// M/N-major: each thread loads R consecutive k rows of 8 consecutive m/n
-// values (R 16-byte loads), transposes the R x 8 block in registers and
-// writes 8 LDS rows of R k values.  Lanes kb = tid % (BK/R) share a column
-// chunk, so every wave load instruction reads 128-byte row segments and every
-// LDS write instruction covers whole 128-byte row segments.
-template <int ROWS, int BK, int NT, int LDK>
-struct MNMajorStage {
-  static constexpr int R = ROWS * BK / 8 / NT;
-  static constexpr int KB = BK / R;
-  static_assert(R == 2 || R == 4 || R == 8, "M/N-major staging split");
-  static_assert((ROWS / 8) * KB == NT, "M/N-major staging covers the tile");
-  u32x4 v[R];
+__device__ __forceinline__ desc_t make_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  desc_t d;
+  d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  d[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xFFFFu));
+  d[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  d[3] = 0x00020000;
+  return d;
+}
 
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t ld_bytes, int tid) {
-    const int kb = tid % KB, nb = tid / KB;
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-      v[j] = buf_load16(r, (uint32_t)(kb * R + j) * ld_bytes + (uint32_t)nb * 16u);
-  }
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
 
-  __device__ __forceinline__ void store(bf16* lds, int tid) const {
-    const int kb = tid % KB, nb = tid / KB;
-    // element c of row j sits in half (c & 1) of dword c >> 1 of v[j]
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      bf16* dst = lds + (nb * 8 + c) * LDK + kb * R;
-      if constexpr (R == 8) {
-        u32x4 o;
-        o[0] = __builtin_amdgcn_perm(v[1][c >> 1], v[0][c >> 1], sel);
-        o[1] = __builtin_amdgcn_perm(v[3][c >> 1], v[2][c >> 1], sel);
-        o[2] = __builtin_amdgcn_perm(v[5][c >> 1], v[4][c >> 1], sel);
-        o[3] = __builtin_amdgcn_perm(v[7][c >> 1], v[6][c >> 1], sel);
-        *reinterpret_cast<u32x4*>(dst) = o;
-      } else if constexpr (R == 4) {
-        u32x2 o;
-        o[0] = __builtin_amdgcn_perm(v[1][c >> 1], v[0][c >> 1], sel);
-        o[1] = __builtin_amdgcn_perm(v[3][c >> 1], v[2][c >> 1], sel);
-        *reinterpret_cast<u32x2*>(dst) = o;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(v[1][c >> 1], v[0][c >> 1], sel);
-      }
-    }
-  }
-};
+// One 16-byte-per-lane LDS DMA: lane L's 16 bytes from buffer offset voff
+// land at LDS byte lds + 16 L.  Issued as inline assembly so that the
+// compiler does not serialise later LDS reads behind it; the kernel orders
+// it with explicit s_waitcnt vmcnt and s_barrier.
+__device__ __forceinline__ void dma16(desc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               ::"s"(lds), "v"(voff), "s"(r) : "memory", "m0");
+}
 
-template <bool KM, int ROWS, int BK, int NT, int LDK>
-struct StageOf;
-template <int ROWS, int BK, int NT, int LDK>
-struct StageOf<true, ROWS, BK, NT, LDK> { using type = KMajorStage<ROWS, BK, NT, LDK>; };
-template <int ROWS, int BK, int NT, int LDK>
-struct StageOf<false, ROWS, BK, NT, LDK> { using type = MNMajorStage<ROWS, BK, NT, LDK>; };
-
-// Buffer resource for the tile of an operand starting at (row0 in the m/n
+// Buffer descriptor for an operand tile starting at (row0 in the m/n
 // dimension, k0).  K-major: element (r, k) at base[r*ld + k]; M/N-major:
-// element (r, k) at base[k*ld + r].  The resource starts at the tile origin
-// so that in-tile byte offsets stay small for any operand size.
+// base[k*ld + r].  The range ends at the operand's end (clamped below 2 GiB;
+// a tile never spans more, see the ABI limits), so kOOB is always out of
+// range.
 template <bool KM>
-__device__ __forceinline__ rsrc_t tile_rsrc(const bf16* base, int64_t ld, int64_t elems,
+__device__ __forceinline__ desc_t tile_desc(const bf16* base, int64_t ld, int64_t elems,
                                             int64_t row0, int64_t k0) {
   const int64_t off = KM ? row0 * ld + k0 : k0 * ld + row0;
-  const int64_t rem = elems - off;
-  return make_rsrc(base + off, rem > 0 ? (uint64_t)rem * 2u : 0u);
+  const int64_t rem = (elems - off) * 2;
+  const uint32_t n = rem > 0 ? (rem < 0x7FFFFFFF ? (uint32_t)rem : 0x7FFFFFFFu) : 0u;
+  return make_desc(base + off, n);
+}
+
+// DMA of one K-major tile (ROWS x 64 k, 8 rows per 1 KiB instruction).
+template <int ROWS, int NW>
+__device__ __forceinline__ void dma_kmajor(desc_t r, uint32_t ld_bytes, int kvalid, uint32_t lds,
+                                           int wave, int lane) {
+  constexpr int INS = ROWS / 8, PER = INS / NW;
+  static_assert(INS % NW == 0, "K-major DMA split");
+  const int rl = lane >> 3, pc = lane & 7;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int ins = wave * PER + j;
+    const int row = ins * 8 + rl;
+    const int lc = pc ^ ((row >> 1) & 7);
+    const uint32_t voff = lc * 8 < kvalid ? (uint32_t)row * ld_bytes + (uint32_t)lc * 16u : kOOB;
+    dma16(r, lds + ins * 1024, voff);
+  }
+}
+
+// DMA of one M/N-major tile: 64 k rows of ROWS m/n values, stored as
+// ROWS/128 sub-tiles of [64][128]; 4 rows of one sub-tile per instruction.
+// With two resources (dual-B), sub-tile s comes from r[s] at the same columns.
+template <int ROWS, int NW, bool DUAL>
+__device__ __forceinline__ void dma_mnmajor(desc_t r0, desc_t r1, uint32_t ld_bytes, uint32_t lds,
+                                            int wave, int lane) {
+  constexpr int INS = ROWS / 8, PER = INS / NW;
+  static_assert(INS % NW == 0, "M/N-major DMA split");
+  const int kr = lane >> 4, pc = lane & 15;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int ins = wave * PER + j;
+    const int sub = ins >> 4;                 // 16 instructions per 64 x 128 sub-tile
+    const int k = (ins & 15) * 4 + kr;
+    const int lc = pc ^ (4 * (k & 3));
+    const int col = DUAL ? lc * 8 : sub * 128 + lc * 8;
+    const uint32_t voff = (uint32_t)k * ld_bytes + (uint32_t)col * 2u;
+    dma16((DUAL && sub) ? r1 : r0, lds + ins * 1024, voff);
+  }
+}
+
+// Fragment of a K-major tile: rows row..(32 rows by lane), k-substep kk.
+__device__ __forceinline__ bf16x8 frag_kmajor(const char* tile, int row, int kk, int g) {
+  const int pc = (kk * 2 + g) ^ ((row >> 1) & 7);
+  return *reinterpret_cast<const bf16x8*>(tile + row * 128 + pc * 16);
+}
+
+// Fragment of an M/N-major tile for the 32 columns starting at col0.
+__device__ __forceinline__ bf16x8 frag_mnmajor(const char* tile, int col0, int kk, int lane) {
+  const int G = lane >> 4, i = lane & 15;
+  const int col = col0 + 16 * (G & 1) + 4 * (i & 3);
+  const int k = kk * 16 + 8 * (G >> 1) + (i >> 2);
+  const int sub = col >> 7, c = col & 127;
+  const int pc = (c >> 3) ^ (4 * (k & 3));
+  const char* p = tile + sub * 16384 + k * 256 + pc * 16 + (c & 7) * 2;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * 256));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <bool KM>
+__device__ __forceinline__ bf16x8 frag(const char* tile, int rowcol0, int lane, int kk) {
+  if constexpr (KM) return frag_kmajor(tile, rowcol0 + (lane & 31), kk, lane >> 5);
+  else return frag_mnmajor(tile, rowcol0, kk, lane);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_done_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ----------------------------------------------------------------------------
@@ -175,7 +204,7 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, i
 }
 
 // ----------------------------------------------------------------------------
-// The kernel.  DUAL: the B tile's first BN/2 rows come from seg.B and the
+// The kernel.  DUAL: the B tile's first BN/2 columns come from seg.B and the
 // last BN/2 from seg.B2 for the same BN/2 output columns; wave (wm, wn) owns
 // n-blocks j < TN/2 from B and j >= TN/2 from B2 of the same columns, so an
 // epilogue sees both products of an (m, n) in one lane.
@@ -183,15 +212,14 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, i
 template <class Cfg, bool A_KM, bool B_KM, bool DUAL, class Epi>
 __global__ void __launch_bounds__(Cfg::NT)
 gemm_bf16_kernel(const GemmParams p, const Epi epi) {
-  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::NT;
-  constexpr int LDK = Cfg::LDK, TM = Cfg::TM, TN = Cfg::TN;
-  constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN;
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NW = Cfg::NW;
+  constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM, WTN = Cfg::WTN;
   constexpr int BNL = DUAL ? BN / 2 : BN;          // output columns per tile
-  constexpr int BROWS = DUAL ? BN / 2 : BN;        // B rows per staged matrix
-  using AStage = typename StageOf<A_KM, BM, BK, NT, LDK>::type;
-  using BStage = typename StageOf<B_KM, BROWS, BK, NT, LDK>::type;
+  constexpr int NDMA = (BM / 8 + BN / 8) / NW;     // DMA instructions per wave per stage
+  static_assert(!DUAL || !B_KM, "dual-B products take N-major right operands");
+  static_assert(!DUAL || BN == 256, "dual-B tiles hold two 128-column sub-tiles");
 
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * LDK];
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::SMEM_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -204,11 +232,33 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
   const int64_t n0 = (int64_t)tn * BNL;
   const int zb = blockIdx.z;
 
-  // K-tiles of every segment, split over blockIdx.y
-  int kt_seg0 = (p.seg[0].K + BK - 1) / BK;
-  int kt_total = kt_seg0 + (p.nseg > 1 ? (p.seg[1].K + BK - 1) / BK : 0);
+  const int kt_seg0 = (p.seg[0].K + BK - 1) / BK;
+  const int kt_total = kt_seg0 + (p.nseg > 1 ? (p.seg[1].K + BK - 1) / BK : 0);
   const int kt_begin = (int)(((int64_t)kt_total * blockIdx.y) / p.split_k);
   const int kt_end = (int)(((int64_t)kt_total * (blockIdx.y + 1)) / p.split_k);
+  const int T = kt_end - kt_begin;
+
+  auto issue = [&](int kt, int stage) {
+    const int s = kt < kt_seg0 ? 0 : 1;
+    const GemmSeg& g = p.seg[s];
+    const int64_t k0 = (int64_t)(kt - (s ? kt_seg0 : 0)) * BK;
+    const bf16* Bp = (s == 0 && p.Bz[zb]) ? p.Bz[zb] : g.B;
+    const uint32_t As = lds_addr(smem) + stage * Cfg::STAGE;
+    const uint32_t Bs = As + Cfg::A_BYTES;
+    const int kvalid = (int)(g.K - k0);
+    const desc_t ra = tile_desc<A_KM>(g.A, g.lda, g.a_elems, m0, k0);
+    if constexpr (A_KM) dma_kmajor<BM, NW>(ra, (uint32_t)(g.lda * 2), kvalid, As, wave, lane);
+    else dma_mnmajor<BM, NW, false>(ra, ra, (uint32_t)(g.lda * 2), As, wave, lane);
+    const desc_t rb = tile_desc<B_KM>(Bp, g.ldb, g.b_elems, n0, k0);
+    if constexpr (B_KM) {
+      dma_kmajor<BN, NW>(rb, (uint32_t)(g.ldb * 2), kvalid, Bs, wave, lane);
+    } else if constexpr (DUAL) {
+      const desc_t rb2 = tile_desc<false>(g.B2, g.ldb, g.b_elems, n0, k0);
+      dma_mnmajor<BN, NW, true>(rb, rb2, (uint32_t)(g.ldb * 2), Bs, wave, lane);
+    } else {
+      dma_mnmajor<BN, NW, false>(rb, rb, (uint32_t)(g.ldb * 2), Bs, wave, lane);
+    }
+  };
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -216,78 +266,52 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  AStage sa;
-  BStage sb, sb2;
-
-  auto load_tile = [&](int kt) {
-    const int s = kt < kt_seg0 ? 0 : 1;
-    const GemmSeg& g = p.seg[s];
-    const int64_t k0 = (int64_t)(kt - (s ? kt_seg0 : 0)) * BK;
-    const bf16* Bp = (s == 0 && p.Bz[zb]) ? p.Bz[zb] : g.B;
-    const rsrc_t ra = tile_rsrc<A_KM>(g.A, g.lda, g.a_elems, m0, k0);
-    const rsrc_t rb = tile_rsrc<B_KM>(Bp, g.ldb, g.b_elems, n0, k0);
-    const int kvalid = (int)(g.K - k0);
-    if constexpr (A_KM) sa.load(ra, (uint32_t)(g.lda * 2), kvalid, tid);
-    else sa.load(ra, (uint32_t)(g.lda * 2), tid);
-    if constexpr (B_KM) sb.load(rb, (uint32_t)(g.ldb * 2), kvalid, tid);
-    else sb.load(rb, (uint32_t)(g.ldb * 2), tid);
-    if constexpr (DUAL) {
-      const rsrc_t rb2 = tile_rsrc<B_KM>(g.B2, g.ldb, g.b_elems, n0, k0);
-      if constexpr (B_KM) sb2.load(rb2, (uint32_t)(g.ldb * 2), kvalid, tid);
-      else sb2.load(rb2, (uint32_t)(g.ldb * 2), tid);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    bf16* As = smem + buf * (BM + BN) * LDK;
-    bf16* Bs = As + BM * LDK;
-    sa.store(As, tid);
-    sb.store(Bs, tid);
-    if constexpr (DUAL) sb2.store(Bs + BROWS * LDK, tid);
+  // column (within the B tile) of this wave's n-block j
+  auto bcol = [&](int j) {
+    if constexpr (DUAL)
+      return (j < TN / 2) ? wn * (WTN / 2) + j * 32 : 128 + wn * (WTN / 2) + (j - TN / 2) * 32;
+    else
+      return wn * WTN + j * 32;
   };
 
-  if (kt_begin < kt_end) {
-    load_tile(kt_begin);
-    store_tile(0);
-  }
-  __syncthreads();
+  if (T > 0) issue(kt_begin, 0);
+  if (T > 1) issue(kt_begin + 1, 1);
+  for (int t = 0; t < T; ++t) {
+    if (t + 1 < T) wait_vmcnt_barrier<NDMA>();
+    else wait_vmcnt_barrier<0>();
+    const char* As = smem + (t & 1) * Cfg::STAGE;
+    const char* Bs = As + Cfg::A_BYTES;
 
-  const int lrow = lane & 31;
-  const int lk = (lane >> 5) * 8;
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int buf = (kt - kt_begin) & 1;
-    const bool more = kt + 1 < kt_end;
-    if (more) load_tile(kt + 1);
-
-    const bf16* As = smem + buf * (BM + BN) * LDK;
-    const bf16* Bs = As + BM * LDK;
+    bf16x8 fa[2][TM], fb[2][TN];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 af[TM], bfr[TN];
+    for (int i = 0; i < TM; ++i) fa[0][i] = frag<A_KM>(As, wm * WTM + i * 32, lane, 0);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + i * 32 + lrow) * LDK + kk + lk);
+    for (int j = 0; j < TN; ++j) fb[0][j] = frag<B_KM>(Bs, bcol(j), lane, 0);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        int brow;
-        if constexpr (DUAL)
-          brow = (j < TN / 2) ? wn * (WTN / 2) + j * 32 : BROWS + wn * (WTN / 2) + (j - TN / 2) * 32;
-        else
-          brow = wn * WTN + j * 32;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + (brow + lrow) * LDK + kk + lk);
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[nxt][i] = frag<A_KM>(As, wm * WTM + i * 32, lane, kk + 1);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[nxt][j] = frag<B_KM>(Bs, bcol(j), lane, kk + 1);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
     }
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
+    if (t + 2 < T) {
+      lds_done_barrier();
+      issue(kt_begin + t + 2, t & 1);
+    }
   }
 
   // Epilogue: acc[i][j][4*b + q] is C(m, n) with
   //   m = m0 + wm*WTM + i*32 + (lane & 31)
   //   n = n0 + <wave column of block j> + 8*b + 4*(lane >> 5) + q
+  const int lrow = lane & 31;
   const int g4 = (lane >> 5) * 4;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {

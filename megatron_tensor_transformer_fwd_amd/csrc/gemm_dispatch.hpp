@@ -8,12 +8,12 @@
 
 namespace tpk {
 
-// Tile shapes.  L: 256x256 (4 waves of 128x128), the shape for large
-// shards; M: 256x128 (4 waves of 128x64); S: 128x128 (4 waves of 64x64) for
-// narrow outputs such as a TP-8 slice of a 4096-wide feed-forward layer.
-using CfgL = TileCfg<256, 256, 64, 2, 2>;
-using CfgM = TileCfg<256, 128, 64, 2, 2>;
-using CfgS = TileCfg<128, 128, 64, 2, 2>;
+// Tile shapes.  L: 256x256, 8 waves of 128x64 (two per SIMD), the shape for
+// large shards; M: 256x128, 4 waves of 128x64; S: 128x128, 4 waves of 64x64
+// for narrow outputs such as a TP-8 slice of a 4096-wide feed-forward layer.
+using CfgL = TileCfg<256, 256, 2, 4>;
+using CfgM = TileCfg<256, 128, 2, 2>;
+using CfgS = TileCfg<128, 128, 2, 2>;
 
 enum { CFG_L = 0, CFG_M = 1, CFG_S = 2 };
 
@@ -34,10 +34,11 @@ inline int64_t tiles_for(int cfg, int64_t M, int64_t N, bool dual) {
 // Choose the largest tile that still gives every CU (256 of them) at least
 // one tile; products with a small output and a long K (weight gradients of
 // narrow shards) are split along K into a deterministic fp32 workspace.
+// Dual-B products always take the L shape (two 128-column sub-tiles).
 inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow_split) {
   constexpr int64_t CUS = 256;
   GemmPlan p{CFG_S, 1};
-  if (tiles_for(CFG_L, M, N, dual) >= CUS) p.cfg = CFG_L;
+  if (dual || tiles_for(CFG_L, M, N, dual) >= CUS) p.cfg = CFG_L;
   else if (tiles_for(CFG_M, M, N, dual) >= CUS) p.cfg = CFG_M;
   if (allow_split) {
     const int64_t t = tiles_for(p.cfg, M, N, dual);
@@ -65,8 +66,12 @@ hipError_t launch_gemm(hipStream_t st, const char* label, GemmParams p, const Ep
   p.split_k = plan.split;
   switch (plan.cfg) {
     case CFG_L: return launch_gemm_cfg<CfgL, A_KM, B_KM, DUAL, Epi>(st, label, p, epi, nz);
-    case CFG_M: return launch_gemm_cfg<CfgM, A_KM, B_KM, DUAL, Epi>(st, label, p, epi, nz);
-    default: return launch_gemm_cfg<CfgS, A_KM, B_KM, DUAL, Epi>(st, label, p, epi, nz);
+    case CFG_M:
+      if constexpr (DUAL) return hipErrorInvalidValue;
+      else return launch_gemm_cfg<CfgM, A_KM, B_KM, DUAL, Epi>(st, label, p, epi, nz);
+    default:
+      if constexpr (DUAL) return hipErrorInvalidValue;
+      else return launch_gemm_cfg<CfgS, A_KM, B_KM, DUAL, Epi>(st, label, p, epi, nz);
   }
 }
 
