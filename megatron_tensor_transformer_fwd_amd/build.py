@@ -31,10 +31,10 @@ def hipcc() -> str:
 
 def common_flags():
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
         # keep the compiler from forming packed fp32 VALU ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+        "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-DTPK_PINGPONG",
     ]
 
 

@@ -1,8 +1,17 @@
-// GEMM epilogues.  Each receives the fp32 results of one output quad
-// (m, n..n+3) (n is a multiple of 4 and every output width is a multiple of
-// 8, so a quad never straddles a row) and performs the fused elementwise
-// step of the TP shard before a single store.  T is the storage type of the
-// activations (bf16 or float).
+// GEMM epilogues.  An epilogue describes the fused elementwise step of the
+// TP shard that follows a product and where its outputs go:
+//   NOUT                       number of output tensors
+//   OutT<O>                    storage type of output O (bf16 or float)
+//   has_out<O>()               whether output O is wanted (runtime, uniform)
+//   out_ptr<O>(m, n, split, z) address of element (m, n) of output O; eight
+//                              consecutive n starting at a multiple of 8 are
+//                              contiguous
+//   value<O>(m, n, v)          output O's values for the fp32 product quad v
+//                              at (m, n..n+3) (value2<O>(m, n, g, u) for
+//                              dual-B products)
+// Quads never straddle a row (n is a multiple of 4, widths multiples of 8).
+// The GEMM kernels stage each output through LDS and write whole rows with
+// 16-byte stores; the fp32 SIMT kernel stores quads directly.
 #pragma once
 #include "common.hpp"
 
@@ -24,31 +33,41 @@ template <> struct Quad<float> {
   static __device__ __forceinline__ f32x4 load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 };
 
-// C = AB, stored in T.  With split-K, split s writes its partial sum to
+// C = AB stored in T.  With split-K, split s writes its partial sum to
 // C + s * split_stride (fp32 workspace), summed afterwards in split order.
 template <class T>
 struct EpiStore {
+  static constexpr int NOUT = 1;
+  template <int O> using OutT = T;
   T* C;
   int64_t ldc;
   int64_t split_stride;
-  __device__ __forceinline__ void apply(int64_t m, int64_t n, f32x4 v, int split, int) const {
-    Quad<T>::store(C + split * split_stride + m * ldc + n, v);
+  template <int O> __device__ __forceinline__ bool has_out() const { return true; }
+  template <int O> __device__ __forceinline__ T* out_ptr(int64_t m, int64_t n, int split, int) const {
+    return C + split * split_stride + m * ldc + n;
   }
+  template <int O> __device__ __forceinline__ f32x4 value(int64_t, int64_t, f32x4 v) const { return v; }
 };
 
-// Column-parallel product with GeLU ([JY] FFN, [HC] Figure 3.4): keeps the
-// pre-activation A (optional) and writes H = GeLU(A) from the fp32 sum.
+// Column-parallel product with GeLU ([JY] FFN, [HC] Figure 3.4): output 0 is
+// the pre-activation A (optional), output 1 is H = GeLU(A) from the fp32 sum.
 template <class T>
 struct EpiGelu {
+  static constexpr int NOUT = 2;
+  template <int O> using OutT = T;
   T* A;   // may be null
   T* H;
   int64_t ld;
-  __device__ __forceinline__ void apply(int64_t m, int64_t n, f32x4 v, int, int) const {
-    if (A) Quad<T>::store(A + m * ld + n, v);
+  template <int O> __device__ __forceinline__ bool has_out() const { return O == 1 || A != nullptr; }
+  template <int O> __device__ __forceinline__ T* out_ptr(int64_t m, int64_t n, int, int) const {
+    return (O == 0 ? A : H) + m * ld + n;
+  }
+  template <int O> __device__ __forceinline__ f32x4 value(int64_t, int64_t, f32x4 v) const {
+    if constexpr (O == 0) return v;
     f32x4 h;
 #pragma unroll
     for (int q = 0; q < 4; ++q) h[q] = gelu_f(v[q]);
-    Quad<T>::store(H + m * ld + n, h);
+    return h;
   }
 };
 
@@ -56,79 +75,96 @@ struct EpiGelu {
 // dA = (dY W2^T) * GeLU'(A), A read back from the forward's saved copy.
 template <class T>
 struct EpiDGelu {
+  static constexpr int NOUT = 1;
+  template <int O> using OutT = T;
   const T* A;
   T* dA;
   int64_t ld;
-  __device__ __forceinline__ void apply(int64_t m, int64_t n, f32x4 v, int, int) const {
+  template <int O> __device__ __forceinline__ bool has_out() const { return true; }
+  template <int O> __device__ __forceinline__ T* out_ptr(int64_t m, int64_t n, int, int) const {
+    return dA + m * ld + n;
+  }
+  template <int O> __device__ __forceinline__ f32x4 value(int64_t m, int64_t n, f32x4 v) const {
     const f32x4 a = Quad<T>::load(A + m * ld + n);
     f32x4 r;
 #pragma unroll
     for (int q = 0; q < 4; ++q) r[q] = v[q] * gelu_prime_f(a[q]);
-    Quad<T>::store(dA + m * ld + n, r);
+    return r;
   }
 };
 
-// Dual product X [W1 | W3] with SwiGLU: G = X W1, U = X W3, H = Swish(G) * U.
+// Dual product X [W1 | W3] with SwiGLU: outputs G = X W1 (optional),
+// U = X W3 (optional) and H = Swish(G) * U.
 template <class T>
 struct EpiSwiGLU {
+  static constexpr int NOUT = 3;
+  template <int O> using OutT = T;
   T* G;   // may be null
   T* U;   // may be null
   T* H;
   int64_t ld;
-  __device__ __forceinline__ void apply2(int64_t m, int64_t n, f32x4 g, f32x4 u) const {
-    if (G) Quad<T>::store(G + m * ld + n, g);
-    if (U) Quad<T>::store(U + m * ld + n, u);
+  template <int O> __device__ __forceinline__ bool has_out() const {
+    return O == 2 || (O == 0 ? G != nullptr : U != nullptr);
+  }
+  template <int O> __device__ __forceinline__ T* out_ptr(int64_t m, int64_t n, int, int) const {
+    return (O == 0 ? G : O == 1 ? U : H) + m * ld + n;
+  }
+  template <int O> __device__ __forceinline__ f32x4 value2(int64_t, int64_t, f32x4 g, f32x4 u) const {
+    if constexpr (O == 0) return g;
+    if constexpr (O == 1) return u;
     f32x4 h;
 #pragma unroll
     for (int q = 0; q < 4; ++q) h[q] = g[q] * sigmoid_f(g[q]) * u[q];
-    Quad<T>::store(H + m * ld + n, h);
+    return h;
   }
 };
 
-// SwiGLU backward dgrad: given dH = dY W2^T, writes
-// dG = dH * U * Swish'(G) and dU = dH * Swish(G) into the two halves of one
+// SwiGLU backward dgrad: given dH = dY W2^T, outputs dG = dH * U * Swish'(G)
+// (output 0) and dU = dH * Swish(G) (output 1) into the two halves of one
 // [M x 2f] buffer (dG in columns [0, f), dU in [f, 2f)).
 template <class T>
 struct EpiDSwiGLU {
+  static constexpr int NOUT = 2;
+  template <int O> using OutT = T;
   const T* G;
   const T* U;
   T* dGU;
   int64_t ld;    // f
-  __device__ __forceinline__ void apply(int64_t m, int64_t n, f32x4 v, int, int) const {
+  template <int O> __device__ __forceinline__ bool has_out() const { return true; }
+  template <int O> __device__ __forceinline__ T* out_ptr(int64_t m, int64_t n, int, int) const {
+    return dGU + m * (2 * ld) + (O == 0 ? 0 : ld) + n;
+  }
+  template <int O> __device__ __forceinline__ f32x4 value(int64_t m, int64_t n, f32x4 v) const {
     const f32x4 g = Quad<T>::load(G + m * ld + n);
-    const f32x4 u = Quad<T>::load(U + m * ld + n);
-    f32x4 dg, du;
+    f32x4 r;
+    if constexpr (O == 0) {
+      const f32x4 u = Quad<T>::load(U + m * ld + n);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float s = sigmoid_f(g[q]);
-      du[q] = v[q] * g[q] * s;
-      dg[q] = v[q] * u[q] * s * (1.0f + g[q] * (1.0f - s));
+      for (int q = 0; q < 4; ++q) {
+        const float s = sigmoid_f(g[q]);
+        r[q] = v[q] * u[q] * s * (1.0f + g[q] * (1.0f - s));
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[q] = v[q] * g[q] * sigmoid_f(g[q]);
     }
-    T* row = dGU + m * (2 * ld);
-    Quad<T>::store(row + n, dg);
-    Quad<T>::store(row + ld + n, du);
+    return r;
   }
 };
 
 // fp32 output whose columns [0, split_col) go to C1 and the rest to C2 (each
-// with row pitch split_col), e.g. X^T [dG | dU] -> dW1 and dW3.  Split-K
-// partials go to the workspace as one [M x N] matrix per split.
+// with row pitch split_col), e.g. X^T [dG | dU] -> dW1 and dW3.
 struct EpiF32Halves {
+  static constexpr int NOUT = 1;
+  template <int O> using OutT = float;
   float* C1;
   float* C2;
   int64_t split_col;
-  float* ws;              // non-null: split-K partials [split][M][N]
-  int64_t N;
-  int64_t split_stride;
-  __device__ __forceinline__ void apply(int64_t m, int64_t n, f32x4 v, int split, int) const {
-    if (ws) {
-      Quad<float>::store(ws + split * split_stride + m * N + n, v);
-    } else if (n < split_col) {
-      Quad<float>::store(C1 + m * split_col + n, v);
-    } else {
-      Quad<float>::store(C2 + m * split_col + (n - split_col), v);
-    }
+  template <int O> __device__ __forceinline__ bool has_out() const { return true; }
+  template <int O> __device__ __forceinline__ float* out_ptr(int64_t m, int64_t n, int, int) const {
+    return n < split_col ? C1 + m * split_col + n : C2 + m * split_col + (n - split_col);
   }
+  template <int O> __device__ __forceinline__ f32x4 value(int64_t, int64_t, f32x4 v) const { return v; }
 };
 
 // Column-parallel Q/K/V projection ([BM] Megatron_MHA; [JY] Attention): batch
@@ -136,13 +172,39 @@ struct EpiF32Halves {
 // and n = j*d_head + c goes to the head-major [b, h_local, s, d_head] tensor.
 template <class T>
 struct EpiHeadScatter {
+  static constexpr int NOUT = 1;
+  template <int O> using OutT = T;
   T* out[3];
   int s, h_local, d_head;
-  __device__ __forceinline__ void apply(int64_t m, int64_t n, f32x4 v, int, int z) const {
+  template <int O> __device__ __forceinline__ bool has_out() const { return true; }
+  template <int O> __device__ __forceinline__ T* out_ptr(int64_t m, int64_t n, int, int z) const {
     const int64_t bi = m / s, t = m % s;
     const int64_t j = n / d_head, c = n % d_head;
-    Quad<T>::store(out[z] + ((bi * h_local + j) * s + t) * d_head + c, v);
+    return out[z] + ((bi * h_local + j) * s + t) * d_head + c;
   }
+  template <int O> __device__ __forceinline__ f32x4 value(int64_t, int64_t, f32x4 v) const { return v; }
 };
+
+// Direct quad stores of every output (the fp32 SIMT kernel's epilogue).
+template <class Epi>
+__device__ __forceinline__ void epi_store_direct(const Epi& e, int64_t m, int64_t n, f32x4 v, int split,
+                                                 int z) {
+  [&]<int... O>(std::integer_sequence<int, O...>) {
+    ((e.template has_out<O>() ? Quad<typename Epi::template OutT<O>>::store(
+                                    e.template out_ptr<O>(m, n, split, z), e.template value<O>(m, n, v))
+                              : void()),
+     ...);
+  }(std::make_integer_sequence<int, Epi::NOUT>{});
+}
+
+template <class Epi>
+__device__ __forceinline__ void epi_store_direct2(const Epi& e, int64_t m, int64_t n, f32x4 g, f32x4 u) {
+  [&]<int... O>(std::integer_sequence<int, O...>) {
+    ((e.template has_out<O>() ? Quad<typename Epi::template OutT<O>>::store(
+                                    e.template out_ptr<O>(m, n, 0, 0), e.template value2<O>(m, n, g, u))
+                              : void()),
+     ...);
+  }(std::make_integer_sequence<int, Epi::NOUT>{});
+}
 
 }  // namespace tpk

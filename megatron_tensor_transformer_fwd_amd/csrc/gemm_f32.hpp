@@ -5,6 +5,7 @@
 // MFMA kernel, so both paths compute the same quantities.
 #pragma once
 #include "common.hpp"
+#include "epilogues.hpp"
 
 namespace tpk {
 
@@ -87,9 +88,9 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const GemmParamsF32 p, co
       const f32x4 v = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
       if constexpr (DUAL) {
         const f32x4 v2 = {acc2[i][0], acc2[i][1], acc2[i][2], acc2[i][3]};
-        epi.apply2(m, n, v, v2);
+        epi_store_direct2(epi, m, n, v, v2);
       } else {
-        epi.apply(m, n, v, (int)blockIdx.y, 0);
+        epi_store_direct(epi, m, n, v, (int)blockIdx.y, 0);
       }
     }
   }

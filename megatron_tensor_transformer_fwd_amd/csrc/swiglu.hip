@@ -81,7 +81,7 @@ static hipError_t swiglu_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t 
   }
   {  // [dW1 | dW3] = X^T [dG | dU]
     GemmParams p = make_params(d, 2 * f, make_seg(X, d, M * d, dGU, 2 * f, M * 2 * f, M));
-    EpiF32Halves e{dW1, dW3, f, nullptr, 2 * f, 0};
+    EpiF32Halves e{dW1, dW3, f};
     TPK_TRY((launch_gemm<false, false, false>(st, "swiglu_bwd.xtdgu", p, e, plan_gemm(d, 2 * f, M, false, false))));
   }
   return hipSuccess;
@@ -128,7 +128,7 @@ static hipError_t swiglu_bwd_f32(hipStream_t st, int64_t M, int64_t d, int64_t f
   }
   {
     GemmParamsF32 p = make_params_f32(d, 2 * f, make_seg_f32(X, d, d, dGU, 2 * f, 2 * f, M));
-    EpiF32Halves e{dW1, dW3, f, nullptr, 2 * f, 0};
+    EpiF32Halves e{dW1, dW3, f};
     TPK_TRY((launch_gemm_f32<false, false, false>(st, "swiglu_f32.tn", p, e)));
   }
   return hipSuccess;
