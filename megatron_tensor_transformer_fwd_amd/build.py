@@ -34,7 +34,7 @@ def common_flags():
         f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
         # keep the compiler from forming packed fp32 VALU ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-DTPK_PINGPONG",
+        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     ]
 
 

@@ -440,101 +440,4 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
   store_tile<Cfg, DUAL>(acc, p, epi, m0, n0, wm, wn, lane, zb, smem, tid);
 }
 
-// ----------------------------------------------------------------------------
-// Ping-pong schedule for the 8-wave 256x256 tile.  The waves form two groups
-// of four (one wave of each group per SIMD, since waves go to SIMDs round
-// robin).  Each wave alternates a load phase (the MFMA fragments of two
-// k-substeps, LDS -> registers) and a compute phase (those substeps' MFMAs
-// from registers), and group 1 runs one phase behind group 0, so in every
-// phase one wave of each SIMD multiplies while the other reads LDS.
-// A workgroup barrier separates consecutive phases; group 1 takes one extra
-// barrier at the start and group 0 one at the end, so both execute the same
-// number.  Group 0 also owns the DMA: in its first load phase of tile t it
-// issues tile t+1 into the other stage (whose last reader finished before
-// that phase) and waits for it at the end of its last compute phase of tile
-// t, before the barrier after which group 0 first reads it.
-// ----------------------------------------------------------------------------
-template <class Cfg, bool A_KM, bool B_KM, bool DUAL, class Epi>
-__global__ void __launch_bounds__(Cfg::NT)
-gemm_bf16_pingpong_kernel(const GemmParams p, const Epi epi) {
-  constexpr int BK = Cfg::BK;
-  constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM;
-  constexpr int KK = BK / 16;
-  constexpr int PH = 2;                       // k-substeps per phase
-  constexpr int BNL = DUAL ? Cfg::BN / 2 : Cfg::BN;
-  static_assert(Cfg::NW == 8 && Cfg::NSTAGE == 2, "ping-pong takes 8 waves and 2 stages");
-  static_assert(KK % PH == 0, "phases split the k-tile");
-  static_assert(!DUAL || !B_KM, "dual-B products take N-major right operands");
-  static_assert(!DUAL || Cfg::BN == 256, "dual-B tiles hold two 128-column sub-tiles");
-
-  __shared__ __attribute__((aligned(1024))) char smem[Cfg::SMEM_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
-
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * Cfg::BM;
-  const int64_t n0 = (int64_t)tn * BNL;
-  const int zb = blockIdx.z;
-
-  const int kt_seg0 = (p.seg[0].K + BK - 1) / BK;
-  const int kt_total = kt_seg0 + (p.nseg > 1 ? (p.seg[1].K + BK - 1) / BK : 0);
-  const int kt_begin = (int)(((int64_t)kt_total * blockIdx.y) / p.split_k);
-  const int kt_end = (int)(((int64_t)kt_total * (blockIdx.y + 1)) / p.split_k);
-  const int T = kt_end - kt_begin;
-  const uint32_t lds0 = lds_addr(smem);
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-
-  if (grp == 0 && T > 0) {
-    issue_tile<Cfg, A_KM, B_KM, DUAL, 4>(p, kt_begin, kt_seg0, lds0, m0, n0, zb, wave & 3, lane);
-  }
-  dma_lds_barrier<0>();               // tile 0 is in LDS
-  if (grp == 1) dma_lds_barrier<0>();  // group 1 runs one phase behind
-
-  for (int t = 0; t < T; ++t) {
-    const char* As = smem + (t & 1) * Cfg::STAGE;
-    const char* Bs = As + Cfg::A_BYTES;
-#pragma unroll
-    for (int h = 0; h < KK / PH; ++h) {
-      // load phase: PH k-substeps of fragments
-      if (h == 0 && grp == 0 && t + 1 < T)
-        issue_tile<Cfg, A_KM, B_KM, DUAL, 4>(p, kt_begin + t + 1, kt_seg0, lds0 + ((t + 1) & 1) * Cfg::STAGE,
-                                             m0, n0, zb, wave & 3, lane);
-      bf16x8 fa[PH][TM], fb[PH][TN];
-#pragma unroll
-      for (int q = 0; q < PH; ++q) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa[q][i] = frag<A_KM, BK>(As, wm * WTM + i * 32, lane, h * PH + q);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[q][j] = frag<B_KM, BK>(Bs, bcol_of<Cfg, DUAL>(wn, j), lane, h * PH + q);
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      // compute phase
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int q = 0; q < PH; ++q)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q][j], fa[q][i], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_s_setprio(0);
-      if (h == KK / PH - 1 && grp == 0) dma_lds_barrier<0>();   // tile t+1 landed before group 0 reads it
-      else asm volatile("s_barrier" ::: "memory");
-    }
-  }
-  if (grp == 0) asm volatile("s_barrier" ::: "memory");
-
-  store_tile<Cfg, DUAL>(acc, p, epi, m0, n0, wm, wn, lane, zb, smem, tid);
-}
-
 }  // namespace tpk

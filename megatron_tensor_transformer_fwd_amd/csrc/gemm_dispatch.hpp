@@ -11,21 +11,9 @@ namespace tpk {
 // Tile shapes.  L: 256x256, 8 waves of 128x64 (two per SIMD), the shape for
 // large shards; M: 256x128, 4 waves of 128x64; S: 128x128, 4 waves of 64x64
 // for narrow outputs such as a TP-8 slice of a 4096-wide feed-forward layer.
-#ifndef TPK_L_BK
-#define TPK_L_BK 64
-#define TPK_L_NS 2
-#endif
-#ifndef TPK_S_BK
-#define TPK_S_BK 64
-#define TPK_S_NS 2
-#endif
-#ifdef TPK_L_W4
-using CfgL = TileCfg<256, 256, 2, 2, TPK_L_BK, TPK_L_NS>;
-#else
-using CfgL = TileCfg<256, 256, 2, 4, TPK_L_BK, TPK_L_NS>;
-#endif
-using CfgM = TileCfg<256, 128, 2, 2, TPK_S_BK, TPK_S_NS>;
-using CfgS = TileCfg<128, 128, 2, 2, TPK_S_BK, TPK_S_NS>;
+using CfgL = TileCfg<256, 256, 2, 4>;
+using CfgM = TileCfg<256, 128, 2, 2>;
+using CfgS = TileCfg<128, 128, 2, 2>;
 
 enum { CFG_L = 0, CFG_M = 1, CFG_S = 2 };
 
@@ -69,10 +57,6 @@ hipError_t launch_gemm_cfg(hipStream_t st, const char* label, GemmParams p, cons
   p.tiles_m = (int)cdiv(p.M, Cfg::BM);
   p.tiles_n = (int)cdiv(p.N, BNL);
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.split_k, (unsigned)nz);
-#ifdef TPK_PINGPONG
-  if constexpr (Cfg::NW == 8 && Cfg::NSTAGE == 2)
-    return launch(label, gemm_bf16_pingpong_kernel<Cfg, A_KM, B_KM, DUAL, Epi>, grid, dim3(Cfg::NT), st, p, epi);
-#endif
   return launch(label, gemm_bf16_kernel<Cfg, A_KM, B_KM, DUAL, Epi>, grid, dim3(Cfg::NT), st, p, epi);
 }
 
