@@ -11,13 +11,12 @@
 //    chunk of the tile it fetches, which is how the tiles get their bank
 //    swizzle.  Reads past the end of an operand return zero (buffer range),
 //    which pads ragged k tails; k tails inside a row are sent out of range.
-//  * NSTAGE LDS stages in a ring: right after the one barrier of iteration t
-//    the DMA of k-tile t+NSTAGE-1 is issued into the stage tile t-1 used, so
-//    NSTAGE-1 tiles are in flight while tile t is multiplied; explicit
-//    s_waitcnt vmcnt + s_barrier (no fences) order the ring.
-//  * A K-major operand (k contiguous in memory) is kept as rows of 64 k
-//    (128 B) with 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7); MFMA
-//    fragments are single ds_read_b128s, bank-conflict free for 16 rows.
+//  * A and B tiles stream through two LDS rings (NSA and NSB slots) with one
+//    barrier per k-tile (pipeline at the kernel); explicit s_waitcnt vmcnt +
+//    s_barrier (no fences) order the rings.
+//  * A K-major operand (k contiguous in memory) is kept as rows of BK k with
+//    a 16-byte-chunk XOR swizzle (kswz); MFMA fragments are single
+//    ds_read_b128s, bank-conflict free for 16 rows.
 //  * An M/N-major operand (m or n contiguous: the weights of the forward
 //    products, both operands of the weight-gradient products) is kept as it
 //    is in memory, k rows of 128 m/n values (256 B) per sub-tile, chunk c of
@@ -58,19 +57,33 @@ struct GemmParams {
   int split_k;         // K-tile ranges over blockIdx.y
 };
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NSTAGE_ = 2>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NSA_ = 2, int NSB_ = 2, int SPA_ = 1,
+          int SPB_ = 1, int ROT_ = 0, int BARQ_ = -1>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, NSTAGE = NSTAGE_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int NSA = NSA_, NSB = NSB_;          // LDS stages of the A and B rings
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static constexpr int KK = BK / 16;                   // MFMA k-steps per k-tile
+  static constexpr int SPA = SPA_, SPB = SPB_;         // k-steps each ring's DMA is spread over
+  static constexpr bool ROT = ROT_ != 0;               // per-XCD rotation of the k-tile order
+  static constexpr int BARQ = BARQ_ < 0 ? TM * TN / 2 : BARQ_;   // last-k-step MFMAs before the barrier
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int SMEM_BYTES = NSTAGE * STAGE;
+  static constexpr int B_RING = NSA * A_BYTES;         // LDS offset of the B ring
+  static constexpr int SMEM_BYTES = NSA * A_BYTES + NSB * B_BYTES;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(BM % 128 == 0 && BN % 128 == 0, "M/N-major tiles are 128-wide sub-tiles");
   static_assert(BK == 32 || BK == 64, "k-tile");
-  static_assert(NSTAGE >= 2 && SMEM_BYTES <= 160 * 1024, "LDS stages");
+  static_assert(KK % 2 == 0, "fragment double buffer parity");
+  // A ring with one tile of look-ahead must land by this k-tile's barrier,
+  // so its DMA is issued before the last k-step; with more look-ahead it
+  // may spread over the whole k-tile.
+  static_assert(SPA >= 1 && SPA <= KK && (NSA > 2 || SPA < KK), "A DMA spread");
+  static_assert(SPB >= 1 && SPB <= KK && (NSB > 2 || SPB < KK), "B DMA spread");
+  static_assert(NSA == 2 || NSB == 2, "one of the rings has one tile of look-ahead");
+  static_assert(BARQ >= 0 && BARQ < TM * TN, "barrier position");
+  static_assert(NSA >= 2 && NSB >= 2 && SMEM_BYTES <= 160 * 1024, "LDS stages");
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -127,46 +140,6 @@ template <int BK>
 __device__ __forceinline__ int kswz(int row, int c) {
   constexpr int RPW = 256 / (2 * BK), CPR = BK / 8;
   return c ^ ((row / RPW) % CPR);
-}
-
-// DMA of one K-major tile (ROWS x BK; 1024 / (2 BK) rows per 1 KiB instruction).
-template <int ROWS, int BK, int NW>
-__device__ __forceinline__ void dma_kmajor(desc_t r, uint32_t ld_bytes, int kvalid, uint32_t lds,
-                                           int wave, int lane) {
-  constexpr int CPR = BK / 8, RPI = 64 / CPR;           // chunks per row, rows per instruction
-  constexpr int INS = ROWS / RPI, PER = INS / NW;
-  static_assert(INS % NW == 0, "K-major DMA split");
-  const int rl = lane / CPR, pc = lane % CPR;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int ins = wave * PER + j;
-    const int row = ins * RPI + rl;
-    const int lc = kswz<BK>(row, pc);
-    const uint32_t voff = lc * 8 < kvalid ? (uint32_t)row * ld_bytes + (uint32_t)lc * 16u : kOOB;
-    dma16(r, lds + ins * 1024, voff);
-  }
-}
-
-// DMA of one M/N-major tile: BK k rows of ROWS m/n values, stored as
-// ROWS/128 sub-tiles of [BK][128]; 4 rows of one sub-tile per instruction.
-// With two resources (dual-B), sub-tile s comes from r[s] at the same columns.
-template <int ROWS, int BK, int NW, bool DUAL>
-__device__ __forceinline__ void dma_mnmajor(desc_t r0, desc_t r1, uint32_t ld_bytes, uint32_t lds,
-                                            int wave, int lane) {
-  constexpr int IPS = BK / 4;                        // instructions per sub-tile
-  constexpr int INS = ROWS / 128 * IPS, PER = INS / NW;
-  static_assert(INS % NW == 0, "M/N-major DMA split");
-  const int kr = lane >> 4, pc = lane & 15;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int ins = wave * PER + j;
-    const int sub = ins / IPS;
-    const int k = (ins % IPS) * 4 + kr;
-    const int lc = pc ^ (4 * (k & 3));
-    const int col = DUAL ? lc * 8 : sub * 128 + lc * 8;
-    const uint32_t voff = (uint32_t)k * ld_bytes + (uint32_t)col * 2u;
-    dma16((DUAL && sub) ? r1 : r0, lds + ins * 1024, voff);
-  }
 }
 
 // Fragment of a K-major tile: rows row..(32 rows by lane), k-substep kk.
@@ -259,7 +232,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
     static_assert(PASS * ROWB <= Cfg::SMEM_BYTES && BM % PASS == 0, "staging pass fits the LDS");
 #pragma unroll
     for (int pass = 0; pass < BM / PASS; ++pass) {
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // LDS free
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // LDS free
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int rl = wm * WTM + i * 32;           // first tile row of block i (uniform)
@@ -306,31 +279,83 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
   });
 }
 
-// DMA of k-tile kt of a product into one LDS stage, by the NWL waves
-// numbered wl = 0..NWL-1 (each issues its share of the 1 KiB instructions).
-template <class Cfg, bool A_KM, bool B_KM, bool DUAL, int NWL>
-__device__ __forceinline__ void issue_tile(const GemmParams& p, int kt, int kt_seg0, uint32_t As,
-                                           int64_t m0, int64_t n0, int zb, int wl, int lane) {
-  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
-  const int s = kt < kt_seg0 ? 0 : 1;
-  const GemmSeg& g = p.seg[s];
-  const int64_t k0 = (int64_t)(kt - (s ? kt_seg0 : 0)) * BK;
-  const bf16* Bp = (s == 0 && p.Bz[zb]) ? p.Bz[zb] : g.B;
-  const uint32_t Bs = As + Cfg::A_BYTES;
-  const int kvalid = (int)(g.K - k0);
-  const desc_t ra = tile_desc<A_KM>(g.A, g.lda, g.a_elems, m0, k0);
-  if constexpr (A_KM) dma_kmajor<BM, BK, NWL>(ra, (uint32_t)(g.lda * 2), kvalid, As, wl, lane);
-  else dma_mnmajor<BM, BK, NWL, false>(ra, ra, (uint32_t)(g.lda * 2), As, wl, lane);
-  const desc_t rb = tile_desc<B_KM>(Bp, g.ldb, g.b_elems, n0, k0);
-  if constexpr (B_KM) {
-    dma_kmajor<BN, BK, NWL>(rb, (uint32_t)(g.ldb * 2), kvalid, Bs, wl, lane);
-  } else if constexpr (DUAL) {
-    const desc_t rb2 = tile_desc<false>(g.B2, g.ldb, g.b_elems, n0, k0);
-    dma_mnmajor<BN, BK, NWL, true>(rb, rb2, (uint32_t)(g.ldb * 2), Bs, wl, lane);
-  } else {
-    dma_mnmajor<BN, BK, NWL, false>(rb, rb, (uint32_t)(g.ldb * 2), Bs, wl, lane);
-  }
+// Operand description kept in registers for the whole kernel (the kernel
+// argument block is read once).
+struct SegRegs {
+  const bf16* A;
+  const bf16* B;
+  const bf16* B2;
+  int64_t lda, ldb, a_elems, b_elems;
+  int K;
+};
+
+__device__ __forceinline__ SegRegs seg_regs(const GemmSeg& g) {
+  return SegRegs{g.A, g.B, g.B2, g.lda, g.ldb, g.a_elems, g.b_elems, g.K};
 }
+
+// The LDS DMA of one operand's k-tile into one slot of its ring, as N
+// instructions per wave; issue<J0, J1>() sends instructions [J0, J1), so a
+// tile's loads can be spread over several MFMA k-steps.  IS_A selects the
+// left operand (ROWS = BM, layout A_KM) or the right one (ROWS = BN, layout
+// B_KM; dual-B products take their two 128-column halves from B and B2).
+template <class Cfg, bool KM, bool IS_A, bool DUAL>
+struct OperandDma {
+  static constexpr int BK = Cfg::BK, NW = Cfg::NW;
+  static constexpr int ROWS = IS_A ? Cfg::BM : Cfg::BN;
+  static constexpr int N = ROWS * BK * 2 / 1024 / NW;
+  static constexpr bool TWO = !IS_A && DUAL;
+  static_assert(N * NW * 1024 == ROWS * BK * 2, "DMA split");
+  desc_t r0, r1;
+  uint32_t ld_b;
+  uint32_t lds;
+  int kvalid;
+
+  // k-tile kt (counted over both K segments) at tile-local row row0.
+  __device__ __forceinline__ OperandDma(const SegRegs& g0, const SegRegs& g1, const bf16* bz, int kt,
+                                        int kt_seg0, uint32_t lds_slot, int64_t row0) {
+    const bool hi = kt >= kt_seg0;
+    const SegRegs& g = hi ? g1 : g0;
+    const int64_t k0 = (int64_t)(kt - (hi ? kt_seg0 : 0)) * BK;
+    kvalid = (int)(g.K - k0);
+    lds = lds_slot;
+    if constexpr (IS_A) {
+      ld_b = (uint32_t)(g.lda * 2);
+      r0 = tile_desc<KM>(g.A, g.lda, g.a_elems, row0, k0);
+      r1 = r0;
+    } else {
+      const bf16* Bp = (!hi && bz) ? bz : g.B;
+      ld_b = (uint32_t)(g.ldb * 2);
+      r0 = tile_desc<KM>(Bp, g.ldb, g.b_elems, row0, k0);
+      if constexpr (TWO) r1 = tile_desc<false>(g.B2, g.ldb, g.b_elems, row0, k0);
+      else r1 = r0;
+    }
+  }
+
+  template <int J0, int J1>
+  __device__ __forceinline__ void issue(int wave, int lane) const {
+    static_for<J1 - J0>([&]<int I>() {
+      constexpr int J = J0 + I;
+      const int ins = wave * N + J;
+      if constexpr (KM) {
+        // K-major: 1 KiB = 1024 / (2 BK) rows of BK k values.
+        constexpr int CPR = BK / 8, RPI = 64 / CPR;
+        const int row = ins * RPI + lane / CPR;
+        const int lc = kswz<BK>(row, lane % CPR);
+        const uint32_t voff = lc * 8 < kvalid ? (uint32_t)row * ld_b + (uint32_t)lc * 16u : kOOB;
+        dma16(r0, lds + ins * 1024, voff);
+      } else {
+        // M/N-major: 4 k rows of one [BK][128] sub-tile.
+        constexpr int IPS = BK / 4;
+        const int sub = ins / IPS;
+        const int k = (ins % IPS) * 4 + (lane >> 4);
+        const int lc = (lane & 15) ^ (4 * (k & 3));
+        const int col = TWO ? lc * 8 : sub * 128 + lc * 8;
+        const uint32_t voff = (uint32_t)k * ld_b + (uint32_t)col * 2u;
+        dma16((TWO && sub) ? r1 : r0, lds + ins * 1024, voff);
+      }
+    });
+  }
+};
 
 // Column (within the B tile) of wave column wn's n-block j.
 template <class Cfg, bool DUAL>
@@ -347,15 +372,71 @@ __device__ __forceinline__ int bcol_of(int wn, int j) {
 // last BN/2 from seg.B2 for the same BN/2 output columns; wave (wm, wn) owns
 // n-blocks j < TN/2 from B and j >= TN/2 from B2 of the same columns, so an
 // epilogue sees both products of an (m, n) in one lane.
+//
+// Pipeline.  A and B tiles live in two LDS rings of NSA and NSB slots; the
+// DMA of A k-tile t+NSA-1 and of B k-tile t+NSB-1 is issued during k-tile t,
+// so each operand has NS-1 tiles in flight (with the 160 KiB of LDS a
+// 256 x 256 tile affords three A slots and two B slots).  Every k-tile is KK
+// MFMA k-steps of TM x TN MFMAs whose instruction stream is written out in
+// groups the compiler may not reorder across (sched_barrier): after each
+// MFMA, its share of the next k-step's fragment reads and of the DMA
+// (each ring's spread over its first SPA / SPB k-steps, the operand with
+// fewer slots first).  In the last k-step, after BARQ MFMAs, the wave waits until its
+// DMAs of tile t+1 have landed and its LDS reads have returned, then the
+// workgroup barrier; the remaining MFMAs carry the reads of tile t+1's first
+// k-step.  After that barrier no wave reads tile t's slots again, so later
+// DMAs may refill them.  DMAs are issued for every t, past the last tile
+// with an empty or out-of-range source (into slots never read again), which
+// keeps the number of loads in flight, and so every vmcnt, static.  With ROT
+// the k-tile order of a workgroup starts at an offset set by its XCD, so the
+// eight XCDs stream different k-columns of the operands at any moment
+// (deterministic: each tile always sums in the same order).
 // ----------------------------------------------------------------------------
 template <class Cfg, bool A_KM, bool B_KM, bool DUAL, class Epi>
 __global__ void __launch_bounds__(Cfg::NT)
 gemm_bf16_kernel(const GemmParams p, const Epi epi) {
-  constexpr int BK = Cfg::BK, NW = Cfg::NW;
+  constexpr int BK = Cfg::BK;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM;
   constexpr int BNL = DUAL ? Cfg::BN / 2 : Cfg::BN;   // output columns per tile
-  constexpr int NS = Cfg::NSTAGE;
-  constexpr int NDMA = (Cfg::BM + Cfg::BN) * BK / 512 / NW;  // DMA instructions per wave per stage
+  constexpr int NSA = Cfg::NSA, NSB = Cfg::NSB, KK = Cfg::KK, BARQ = Cfg::BARQ;
+  constexpr int LA = NSA - 1, LB = NSB - 1;           // tiles of look-ahead per ring
+  constexpr int Q = TM * TN;                          // MFMAs per k-step
+  constexpr int NRD = TM + TN;                        // fragments per k-step
+  using DmaA = OperandDma<Cfg, A_KM, true, DUAL>;
+  using DmaB = OperandDma<Cfg, B_KM, false, DUAL>;
+  constexpr int NA = DmaA::N, NB = DmaB::N, ND = NA + NB;
+  constexpr bool B_FIRST = LB <= LA;                  // per tile, the nearer tile's DMA first
+  // Issue plan: ring X's N instructions spread evenly over its first SP
+  // k-steps, and within a k-step over the Q MFMAs (after MFMA q).
+  constexpr auto upto = [](int n, int sp, int kk, int q) {   // issued at or before (kk, q)
+    if (kk < 0) return 0;
+    if (kk >= sp) return n;
+    const int c0 = kk * n / sp, c1 = (kk + 1) * n / sp;
+    return c0 + (q + 1) * (c1 - c0) / Q;
+  };
+  constexpr auto before = [upto](int n, int sp, int kk, int q) {   // issued before (kk, q)
+    return q > 0 ? upto(n, sp, kk, q - 1) : upto(n, sp, kk - 1, Q - 1);
+  };
+  // At this k-tile's barrier (before MFMA BARQ of the last k-step) the ring
+  // with one tile of look-ahead must have landed; the own DMAs issued after
+  // its last instruction (the other ring's) may still be in flight.  In the
+  // prologue, whole tiles were issued: the later tiles of each ring.
+  constexpr int VM_PRO = (LA - 1) * NA + (LB - 1) * NB;
+  constexpr int VM_LOOP = [=]() {
+    const int NN = B_FIRST ? NB : NA, SN = B_FIRST ? Cfg::SPB : Cfg::SPA;   // near ring
+    const int NF = B_FIRST ? NA : NB, SF = B_FIRST ? Cfg::SPA : Cfg::SPB;   // far ring
+    const bool far_deadline = (B_FIRST ? LA : LB) == 1;
+    // position of the near ring's last instruction
+    int lk = 0, lq = 0;
+    for (int kk = 0; kk < KK; ++kk)
+      for (int q = 0; q < Q; ++q)
+        if (upto(NN, SN, kk, q) == NN && before(NN, SN, kk, q) < NN) { lk = kk; lq = q; }
+    if (far_deadline) return 0;             // both rings due at this barrier
+    // far-ring instructions after (lk, lq) (those at (lk, lq) come after it)
+    // and before the barrier
+    return upto(NF, SF, KK - 1, BARQ - 1) - before(NF, SF, lk, lq);
+  }();
+  static_assert(VM_PRO <= 63 && VM_LOOP <= 63, "vmcnt range");
   static_assert(!DUAL || !B_KM, "dual-B products take N-major right operands");
   static_assert(!DUAL || Cfg::BN == 256, "dual-B tiles hold two 128-column sub-tiles");
 
@@ -372,12 +453,21 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
   const int64_t n0 = (int64_t)tn * BNL;
   const int zb = blockIdx.z;
 
-  const int kt_seg0 = (p.seg[0].K + BK - 1) / BK;
-  const int kt_total = kt_seg0 + (p.nseg > 1 ? (p.seg[1].K + BK - 1) / BK : 0);
+  const SegRegs g0 = seg_regs(p.seg[0]);
+  const SegRegs g1 = seg_regs(p.seg[1]);
+  const bf16* bz = p.Bz[zb];
+  const int kt_seg0 = (g0.K + BK - 1) / BK;
+  const int kt_total = kt_seg0 + (p.nseg > 1 ? (g1.K + BK - 1) / BK : 0);
   const int kt_begin = (int)(((int64_t)kt_total * blockIdx.y) / p.split_k);
   const int kt_end = (int)(((int64_t)kt_total * (blockIdx.y + 1)) / p.split_k);
   const int T = kt_end - kt_begin;
   const uint32_t lds0 = lds_addr(smem);
+  // k-tile processed at step t (t >= T: past the end, loads that are never read)
+  const int rot = (Cfg::ROT && T > 0) ? (int)(((int64_t)(blockIdx.x % 8) * T) / 8) : 0;
+  auto kt_of = [&](int t) {
+    const int u = t + rot;
+    return kt_begin + (u >= T ? u - T : u);
+  };
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -385,56 +475,80 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  // Prologue: the first NS-1 k-tiles in flight.
+  auto slot_a = [&](int t) { return (uint32_t)((t % NSA) * Cfg::A_BYTES); };
+  auto slot_b = [&](int t) { return (uint32_t)(Cfg::B_RING + (t % NSB) * Cfg::B_BYTES); };
+  auto dma_a = [&](int t) { return DmaA(g0, g1, bz, kt_of(t), kt_seg0, lds0 + slot_a(t), m0); };
+  auto dma_b = [&](int t) { return DmaB(g0, g1, bz, kt_of(t), kt_seg0, lds0 + slot_b(t), n0); };
+  // Fragment r of a k-step, in the order the MFMAs consume them:
+  // A block 0, B blocks 0..TN-1, A blocks 1..TM-1.
+  auto read_frag = [&]<int r>(bf16x8(&fa)[TM], bf16x8(&fb)[TN], const char* As, const char* Bs, int kk) {
+    if constexpr (r == 0) fa[0] = frag<A_KM, BK>(As, wm * WTM, lane, kk);
+    else if constexpr (r <= TN) fb[r - 1] = frag<B_KM, BK>(Bs, bcol_of<Cfg, DUAL>(wn, r - 1), lane, kk);
+    else fa[r - TN] = frag<A_KM, BK>(As, wm * WTM + (r - TN) * 32, lane, kk);
+  };
+
+  bf16x8 fa[2][TM], fb[2][TN];
+  if (T > 0) {
+    // Prologue: A tiles 0..LA-1 and B tiles 0..LB-1 in flight, in the order
+    // the loop keeps, then tile 0 visible to every wave.
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < T)
-      issue_tile<Cfg, A_KM, B_KM, DUAL, NW>(p, kt_begin + s, kt_seg0, lds0 + s * Cfg::STAGE, m0, n0, zb, wave, lane);
+    for (int s = 0; s < (LA > LB ? LA : LB); ++s) {
+      if (B_FIRST) {
+        if (s < LB) dma_b(s).template issue<0, NB>(wave, lane);
+        if (s < LA) dma_a(s).template issue<0, NA>(wave, lane);
+      } else {
+        if (s < LA) dma_a(s).template issue<0, NA>(wave, lane);
+        if (s < LB) dma_b(s).template issue<0, NB>(wave, lane);
+      }
+    }
+    dma_lds_barrier<VM_PRO>();
+    static_for<NRD>([&]<int r>() {
+      read_frag.template operator()<r>(fa[0], fb[0], smem + slot_a(0), smem + slot_b(0), 0);
+    });
+  }
 
   for (int t = 0; t < T; ++t) {
-    // Wait for tile t's DMA (the newer tiles' DMAs stay in flight), then the
-    // barrier: tile t is in LDS everywhere and every wave has finished
-    // multiplying tile t-1, whose stage now takes tile t+NS-1.
-    const int newer = min(NS - 2, T - 1 - t);
-    if constexpr (NS >= 4) {
-      if (newer >= 2) dma_lds_barrier<2 * NDMA>();
-      else if (newer == 1) dma_lds_barrier<NDMA>();
-      else dma_lds_barrier<0>();
-    } else if constexpr (NS == 3) {
-      if (newer >= 1) dma_lds_barrier<NDMA>();
-      else dma_lds_barrier<0>();
-    } else {
-      dma_lds_barrier<0>();
-    }
-    if (t + NS - 1 < T)
-      issue_tile<Cfg, A_KM, B_KM, DUAL, NW>(p, kt_begin + t + NS - 1, kt_seg0,
-                                            lds0 + ((t + NS - 1) % NS) * Cfg::STAGE, m0, n0, zb, wave, lane);
-
-    const char* As = smem + (t % NS) * Cfg::STAGE;
-    const char* Bs = As + Cfg::A_BYTES;
-
-    bf16x8 fa[2][TM], fb[2][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = frag<A_KM, BK>(As, wm * WTM + i * 32, lane, 0);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[0][j] = frag<B_KM, BK>(Bs, bcol_of<Cfg, DUAL>(wn, j), lane, 0);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk + 1 < BK / 16) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa[nxt][i] = frag<A_KM, BK>(As, wm * WTM + i * 32, lane, kk + 1);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[nxt][j] = frag<B_KM, BK>(Bs, bcol_of<Cfg, DUAL>(wn, j), lane, kk + 1);
-      }
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_s_setprio(0);
-    }
+    const DmaA da = dma_a(t + LA);
+    const DmaB db = dma_b(t + LB);
+    const char* a_cur = smem + slot_a(t);
+    const char* b_cur = smem + slot_b(t);
+    const char* a_next = smem + slot_a(t + 1);
+    const char* b_next = smem + slot_b(t + 1);
+    static_for<KK>([&]<int kk>() {
+      constexpr int cur = kk & 1, nxt = cur ^ 1;
+      constexpr bool last = kk + 1 == KK;
+      constexpr int QS = last ? BARQ : 0;             // reads start after MFMA QS
+      const char* ra = last ? a_next : a_cur;
+      const char* rb = last ? b_next : b_cur;
+      constexpr int rkk = last ? 0 : kk + 1;
+      static_for<Q>([&]<int q>() {
+        constexpr int i = q / TN, j = q % TN;
+        if constexpr (last && q == BARQ) dma_lds_barrier<VM_LOOP>();
+        // With two waves per SIMD the MFMA issue is raised above the other
+        // wave's memory instructions; with one wave per SIMD it has no peer.
+        if constexpr (Cfg::NW > 4) __builtin_amdgcn_s_setprio(1);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+        if constexpr (Cfg::NW > 4) __builtin_amdgcn_s_setprio(0);
+        if constexpr (q >= QS) {
+          constexpr int r0 = (q - QS) * NRD / (Q - QS), r1 = (q - QS + 1) * NRD / (Q - QS);
+          static_for<r1 - r0>([&]<int rr>() {
+            read_frag.template operator()<r0 + rr>(fa[nxt], fb[nxt], ra, rb, rkk);
+          });
+        }
+        // This MFMA's share of the DMA: the nearer ring's first, then the
+        // farther ring's.
+        constexpr int b0 = before(NB, Cfg::SPB, kk, q), b1 = upto(NB, Cfg::SPB, kk, q);
+        constexpr int a0 = before(NA, Cfg::SPA, kk, q), a1 = upto(NA, Cfg::SPA, kk, q);
+        if constexpr (B_FIRST) {
+          if constexpr (b1 > b0) db.template issue<b0, b1>(wave, lane);
+          if constexpr (a1 > a0) da.template issue<a0, a1>(wave, lane);
+        } else {
+          if constexpr (a1 > a0) da.template issue<a0, a1>(wave, lane);
+          if constexpr (b1 > b0) db.template issue<b0, b1>(wave, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
   }
 
   store_tile<Cfg, DUAL>(acc, p, epi, m0, n0, wm, wn, lane, zb, smem, tid);

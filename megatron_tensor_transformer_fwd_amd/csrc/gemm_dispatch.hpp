@@ -11,9 +11,20 @@ namespace tpk {
 // Tile shapes.  L: 256x256, 8 waves of 128x64 (two per SIMD), the shape for
 // large shards; M: 256x128, 4 waves of 128x64; S: 128x128, 4 waves of 64x64
 // for narrow outputs such as a TP-8 slice of a 4096-wide feed-forward layer.
-using CfgL = TileCfg<256, 256, 2, 4>;
-using CfgM = TileCfg<256, 128, 2, 2>;
-using CfgS = TileCfg<128, 128, 2, 2>;
+// Wave layout, k-tile depth, A/B ring slots, per-ring DMA spread (k-steps)
+// and k-order rotation of each shape are compile-time tuning knobs.
+#ifndef TPK_L_CFG
+#define TPK_L_CFG 256, 256, 2, 4, 64, 2, 2, 1, 1, 1
+#endif
+#ifndef TPK_M_CFG
+#define TPK_M_CFG 256, 128, 2, 2, 64, 2, 2, 1, 1, 0
+#endif
+#ifndef TPK_S_CFG
+#define TPK_S_CFG 128, 128, 2, 2, 64, 2, 2, 1, 1, 0
+#endif
+using CfgL = TileCfg<TPK_L_CFG>;
+using CfgM = TileCfg<TPK_M_CFG>;
+using CfgS = TileCfg<TPK_S_CFG>;
 
 enum { CFG_L = 0, CFG_M = 1, CFG_S = 2 };
 
