@@ -35,6 +35,9 @@
  *  - Arguments are validated on the host before any HIP call.  Every entry
  *    point returns TP_OK (0) or a negative status; tp_last_error_detail()
  *    then holds a thread-local description.  No exception crosses the ABI.
+ *  - Size limits (TP_E_DIM beyond them): every size <= 2^30; row pitches
+ *    d, f and h_local*d_head <= 2^21 elements (the kernels address a tile of
+ *    up to 256 rows with 32-bit offsets); attention s <= 2^22.
  *  - Outputs must not overlap any input or each other (except where noted).
  */
 #ifndef TP_SHARD_H

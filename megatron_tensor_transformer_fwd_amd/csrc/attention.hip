@@ -10,16 +10,23 @@
 //
 // Attention core, per workgroup: one (batch, head, 128-query tile), four
 // waves of 32 queries.  Key/value tiles of 64 stream through double-buffered
-// LDS (K as rows of d_head, V transposed to rows of keys so both products
-// read 16-byte k-packed fragments).  A wave computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16, so each lane owns one query column and 32 of the
-// tile's keys: the row max and row sum need only one cross-lane exchange
-// (lane l with lane l^32).  The running max/sum rescale the fp32 O^T
-// accumulator (online softmax); P is packed to bf16 straight from the S^T
-// registers and multiplied with V^T in the same key order, so the s x s
-// matrix never leaves registers.  The causal mask keeps key u <= query t;
-// tiles entirely above a wave's diagonal are skipped; the heaviest query
-// tiles are dispatched first.
+// LDS.  A wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so each
+// lane owns one query column and 32 of the tile's keys: the row max and row
+// sum need only one cross-lane exchange (lane l with lane l^32).  The running
+// max/sum rescale the fp32 O^T accumulator (online softmax); P is packed to
+// bf16 straight from the S^T registers and multiplied with V^T in the same
+// key order, so the s x s matrix never leaves registers.  The causal mask
+// keeps key u <= query t; tiles entirely above a wave's diagonal are skipped;
+// the heaviest query tiles are dispatched first.
+//
+// d_head 128 (the workloads' head size): K and V arrive by LDS DMA in their
+// natural row-major layout (K rows of 256 bytes with an XOR chunk swizzle, V
+// as [keys][d] rows read back transposed with ds_read_b64_tr_b16 in the key
+// order the P registers hold), no staging registers or register transposes;
+// at most 256 registers per wave, so two workgroups share a CU and one
+// wave's softmax overlaps another's matrix products.  The O^T rescale is
+// skipped when no running max of the wave changed.  d_head 64 uses the
+// register-staged variant.
 #include "epilogues.hpp"
 #include "gemm_dispatch.hpp"
 #include "stage_regs.hpp"
@@ -185,6 +192,205 @@ flash_attn_fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
 }
 
+// ----------------------------------------------------------------------------
+// d_head = 128 core with LDS-DMA staging.
+// ----------------------------------------------------------------------------
+namespace attn128 {
+constexpr int D = 128, BQ = 128, BKV = 64, NT = 256, NW = 4;
+constexpr int K_BYTES = BKV * D * 2, V_BYTES = BKV * D * 2, STAGE = K_BYTES + V_BYTES;
+constexpr int NK = K_BYTES / 1024 / NW, NV = V_BYTES / 1024 / NW;   // DMA instructions per wave
+
+// K tile: row r (key) of 256 bytes, logical 16-byte chunk c at c ^ (r % 16).
+// V tile: row r (key) of 256 bytes (128 d values), chunk c at c ^ 4 (r & 3).
+__device__ __forceinline__ void dma_kv(desc_t rk, desc_t rv, uint32_t lds, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int ins = wave * NK + j;
+    const int row = ins * 4 + (lane >> 4);
+    const int lc = (lane & 15) ^ (row & 15);
+    dma16(rk, lds + ins * 1024, (uint32_t)row * (D * 2) + (uint32_t)lc * 16u);
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int ins = wave * NV + j;
+    const int row = ins * 4 + (lane >> 4);
+    const int lc = (lane & 15) ^ (4 * (row & 3));
+    dma16(rv, lds + K_BYTES + ins * 1024, (uint32_t)row * (D * 2) + (uint32_t)lc * 16u);
+  }
+}
+
+// K fragment (first MFMA operand of S^T = K Q^T): lane l holds key row0 + l%32,
+// d values kk*16 + 8 (l/32) .. +8.
+__device__ __forceinline__ bf16x8 frag_k(const char* kt, int row0, int kk, int lane) {
+  const int row = row0 + (lane & 31);
+  const int pc = (kk * 2 + (lane >> 5)) ^ (row & 15);
+  return *reinterpret_cast<const bf16x8*>(kt + row * (D * 2) + pc * 16);
+}
+
+// V^T fragment (first MFMA operand of O^T += V^T P^T): lane l holds d value
+// d0 + l%32 for the keys kvb + 4 (l/32) + {0..3} and kvb + 8 + 4 (l/32) + {0..3},
+// the key order of the P registers.  Two transposing reads: within each
+// 16-lane group, lane i addresses key row base + i/4, d columns 4 (i%4)..+3,
+// and lane q receives the four keys of d column q.
+__device__ __forceinline__ bf16x8 frag_v(const char* vt, int d0, int kvb, int lane) {
+  const int G = lane >> 4, i = lane & 15;
+  const int col = d0 + 16 * (G & 1) + 4 * (i & 3);
+  const int k = kvb + 4 * (G >> 1) + (i >> 2);
+  const int pc = (col >> 3) ^ (4 * (k & 3));
+  const char* p = vt + k * (D * 2) + pc * 16 + (col & 7) * 2;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * (D * 2)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+}  // namespace attn128
+
+__global__ void __launch_bounds__(256, 2)
+flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                           const bf16* __restrict__ V, bf16* __restrict__ O,
+                           int nb, int hl, int s, int causal, float scale_log2) {
+  using namespace attn128;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  // Causal work grows with the query tile.  With an even number of query
+  // tiles, blocks [0, G/2) take the heavy half of the tiles, heaviest first,
+  // and block i + G/2 the complement of block i's tile, so the two
+  // workgroups that usually share a CU (blocks i and i + G/2 when every
+  // block is resident) sum to the same work; otherwise heaviest first.
+  const int nqt = (s + BQ - 1) / BQ;
+  const int nbh = nb * hl;
+  const int half = (int)(gridDim.x / 2);
+  const int bid = (int)blockIdx.x;
+  const bool light = (nqt % 2 == 0) && bid >= half;
+  const int rank = light ? bid - half : bid;
+  const int qt = light ? rank / nbh : nqt - 1 - rank / nbh;
+  const int bh = rank % nbh;
+  const int bi = bh / hl, h = bh % hl;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, g = lane >> 5;
+  const int64_t head = (int64_t)bh * s * D;
+  const bf16* Kh = K + head;
+  const bf16* Vh = V + head;
+  const int q0 = qt * BQ;
+  const int qw = q0 + wave * 32;    // first query of this wave
+  const int qme = qw + lq;          // this lane's query
+  const uint32_t lds0 = lds_addr(smem);
+
+  const int kv_end = causal ? min(s, q0 + BQ) : s;
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  auto issue = [&](int t) {
+    const int64_t kv0 = (int64_t)t * BKV;
+    const int64_t rb = (int64_t)(s - kv0) * D * 2;
+    const uint32_t rem = rb < 0x7FFFFFFF ? (uint32_t)rb : 0x7FFFFFFFu;
+    dma_kv(make_desc(Kh + kv0 * D, rem), make_desc(Vh + kv0 * D, rem), lds0 + (t & 1) * STAGE, wave, lane);
+  };
+  issue(0);
+
+  bf16x8 qf[D / 16];
+  {
+    const rsrc_t rq = make_rsrc(Q + head, (uint64_t)s * D * 2);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(((int64_t)qme * D + kk * 16 + g * 8) * 2)));
+  }
+
+  f32x16 acc_o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
+  float m_run = -1e30f, l_run = 0.f;   // running max in log2 units, running sum
+
+  for (int t = 0; t < ntiles; ++t) {
+    // Tile t landed for every wave, and every wave is done with tile t-1,
+    // whose stage takes tile t+1.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 1 < ntiles) issue(t + 1);
+
+    const int kv0 = t * BKV;
+    if (causal && kv0 > qw + 31) continue;
+    const char* Ks = smem + (t & 1) * STAGE;
+    const char* Vs = Ks + K_BYTES;
+    // Two independent accumulator chains (key blocks kb = 0, 1), interleaved.
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_k(Ks, kb * 32, kk, lane), qf[kk], sc[kb], 0, 0, 0);
+    // sc[kb][r] is the raw score of query qme against key kv0 + kb*32 + 8*(r/4) + 4*g + r%4
+    if ((causal && kv0 + BKV - 1 > qw) || (kv0 + BKV > s)) {
+      // keys past this lane's query (causal) or past the sequence are masked
+      const int lim = (causal ? min(qme, s - 1) : s - 1) - (kv0 + 4 * g);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sc[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) <= lim) ? sc[kb][r] : -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    // Rescale O^T and the sum only when a running max of the wave moved.
+    if (__builtin_amdgcn_read_exec() & __ballot(m_new > m_run)) {
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= corr;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc_o[i] *= corr;
+      m_run = m_new;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], scale_log2, -m_run));
+        sc[kb][r] = pv;
+        rs += pv;
+      }
+    rs += __shfl_xor(rs, 32);
+    l_run += rs;
+
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4 wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[e] = pack_bf16x2(sc[kb][8 * hh + 2 * e], sc[kb][8 * hh + 2 * e + 1]);
+        pf[kb][hh] = __builtin_bit_cast(bf16x8, wv);
+      }
+    // O^T[d][q] += V^T[d][kv] P^T[kv][q], keys kv0 + kb*32 + 16*hh + {4g..4g+3, 8+4g..8+4g+3};
+    // the four d blocks are independent accumulator chains, interleaved.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_v(Vs, db * 32, kb * 32 + hh * 16, lane),
+                                                              pf[kb][hh], acc_o[db], 0, 0, 0);
+  }
+
+  if (qme < s) {
+    const float inv = 1.0f / l_run;
+    bf16* orow = O + ((int64_t)bi * s + qme) * ((int64_t)hl * D) + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const f32x4 v = {acc_o[db][4 * b4] * inv, acc_o[db][4 * b4 + 1] * inv,
+                         acc_o[db][4 * b4 + 2] * inv, acc_o[db][4 * b4 + 3] * inv};
+        Quad<bf16>::store(orow + db * 32 + 8 * b4 + 4 * g, v);
+      }
+  }
+}
+
 hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local,
                            int64_t d_head, int causal, float scale,
                            const void* X, const void* Wq, const void* Wk, const void* Wv,
@@ -209,7 +415,7 @@ hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
     const bf16* v = static_cast<const bf16*>(V);
     bf16* o = static_cast<bf16*>(O);
     if (d_head == 128)
-      TPK_TRY(launch("attn.core_d128", flash_attn_fwd_kernel<128>, grid, dim3(256), st, q, k, v, o, (int)b,
+      TPK_TRY(launch("attn.core_d128", flash_attn_fwd_d128_kernel, grid, dim3(256), st, q, k, v, o, (int)b,
                      (int)h_local, (int)s, causal, sl2));
     else
       TPK_TRY(launch("attn.core_d64", flash_attn_fwd_kernel<64>, grid, dim3(256), st, q, k, v, o, (int)b,

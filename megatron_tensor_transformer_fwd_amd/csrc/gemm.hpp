@@ -331,28 +331,38 @@ struct OperandDma {
     }
   }
 
+  // Instruction j of the wave: its buffer offset, resource and LDS block.
+  __device__ __forceinline__ uint32_t voff_of(int j, int wave, int lane) const {
+    const int ins = wave * N + j;
+    if constexpr (KM) {
+      // K-major: 1 KiB = 1024 / (2 BK) rows of BK k values.
+      constexpr int CPR = BK / 8, RPI = 64 / CPR;
+      const int row = ins * RPI + lane / CPR;
+      const int lc = kswz<BK>(row, lane % CPR);
+      return lc * 8 < kvalid ? (uint32_t)row * ld_b + (uint32_t)lc * 16u : kOOB;
+    } else {
+      // M/N-major: 4 k rows of one [BK][128] sub-tile.
+      constexpr int IPS = BK / 4;
+      const int sub = ins / IPS;
+      const int k = (ins % IPS) * 4 + (lane >> 4);
+      const int lc = (lane & 15) ^ (4 * (k & 3));
+      const int col = TWO ? lc * 8 : sub * 128 + lc * 8;
+      return (uint32_t)k * ld_b + (uint32_t)col * 2u;
+    }
+  }
+  __device__ __forceinline__ desc_t rsrc_of(int j, int wave) const {
+    if constexpr (TWO) return ((wave * N + j) / (BK / 4)) ? r1 : r0;
+    else return r0;
+  }
+  __device__ __forceinline__ uint32_t lds_of(int j, int wave) const {
+    return lds + (uint32_t)((wave * N + j) * 1024);
+  }
+
   template <int J0, int J1>
   __device__ __forceinline__ void issue(int wave, int lane) const {
     static_for<J1 - J0>([&]<int I>() {
       constexpr int J = J0 + I;
-      const int ins = wave * N + J;
-      if constexpr (KM) {
-        // K-major: 1 KiB = 1024 / (2 BK) rows of BK k values.
-        constexpr int CPR = BK / 8, RPI = 64 / CPR;
-        const int row = ins * RPI + lane / CPR;
-        const int lc = kswz<BK>(row, lane % CPR);
-        const uint32_t voff = lc * 8 < kvalid ? (uint32_t)row * ld_b + (uint32_t)lc * 16u : kOOB;
-        dma16(r0, lds + ins * 1024, voff);
-      } else {
-        // M/N-major: 4 k rows of one [BK][128] sub-tile.
-        constexpr int IPS = BK / 4;
-        const int sub = ins / IPS;
-        const int k = (ins % IPS) * 4 + (lane >> 4);
-        const int lc = (lane & 15) ^ (4 * (k & 3));
-        const int col = TWO ? lc * 8 : sub * 128 + lc * 8;
-        const uint32_t voff = (uint32_t)k * ld_b + (uint32_t)col * 2u;
-        dma16((TWO && sub) ? r1 : r0, lds + ins * 1024, voff);
-      }
+      dma16(rsrc_of(J, wave), lds_of(J, wave), voff_of(J, wave, lane));
     });
   }
 };

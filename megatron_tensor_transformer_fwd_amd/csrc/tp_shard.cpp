@@ -39,6 +39,19 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
+// The kernels address an operand tile with 32-bit buffer offsets from the
+// tile's first row: 256 rows of a leading dimension up to 2 * 2^21 elements
+// (the SwiGLU [dG | dU] buffer) stay below 2 GiB.  The attention core keeps
+// a head's keys/values (s x 128 bf16) under the same bound.
+constexpr int64_t kMaxLd = int64_t(1) << 21;
+constexpr int64_t kMaxSeq = int64_t(1) << 22;
+
+int check_ld(std::initializer_list<std::pair<const char*, int64_t>> dims) {
+  for (const auto& d : dims)
+    if (d.second > kMaxLd)
+      return fail(TP_E_DIM, "%s = %lld exceeds 2^21 (row pitch limit)", d.first, (long long)d.second);
+  return TP_OK;
+}
 
 size_t esize(int dt) { return dt == TP_DT_BF16 ? 2 : 4; }
 
@@ -108,6 +121,7 @@ int mlp_common(tp_dtype_t dt, int64_t M, int64_t d, int64_t f) {
   if (!dtype_ok(dt)) return fail(TP_E_DTYPE, "dtype %d is not TP_DT_F32 or TP_DT_BF16", (int)dt);
   TP_CHECK(check_dims({{"M", M}, {"d", d}, {"f", f}}));
   TP_CHECK(check_mult8({{"d", d}, {"f", f}}));
+  TP_CHECK(check_ld({{"d", d}, {"f", f}}));
   if ((double)M * (double)std::max(d, f) * 2 > 9.0e15) return fail(TP_E_DIM, "operand too large");
   return TP_OK;
 }
@@ -266,6 +280,8 @@ int tp_attn_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t
   TP_CHECK(check_mult8({{"d", d}}));
   const int64_t M = b * s, N = h_local * d_head;
   TP_CHECK(check_dims({{"b*s", M}, {"h_local*d_head", N}}));
+  TP_CHECK(check_ld({{"d", d}, {"h_local*d_head", N}}));
+  if (s > kMaxSeq) return fail(TP_E_DIM, "s = %lld exceeds 2^22", (long long)s);
   const size_t e = 2;
   TP_CHECK(check_buffers({{"X", X, M * d * e}, {"Wq", Wq, d * N * e}, {"Wk", Wk, d * N * e},
                           {"Wv", Wv, d * N * e}, {"Wo", Wo, N * d * e}},

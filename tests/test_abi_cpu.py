@@ -165,3 +165,25 @@ def test_shard_reduce_validation():
     # an exactly in-place reduce with out's extent inside block 0 passes validation:
     # only the launch (no device here) can then fail, with TP_E_HIP.
     assert L.tp_last_error_detail() != b""
+
+
+def test_row_pitch_and_sequence_limits():
+    """Sizes the kernels cannot address with 32-bit tile offsets are refused
+    on the host: d, f, h_local*d_head above 2^21 and s above 2^22."""
+    L = tp.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    big = (1 << 21) + 8
+    rc = L.tp_mlp_fwd(None, 1, 64, big, 64, fake, fake, fake, None, fake, fake)
+    assert rc == -2 and b"2^21" in L.tp_last_error_detail()
+    rc = L.tp_mlp_fwd(None, 1, 64, 64, big, fake, fake, fake, None, fake, fake)
+    assert rc == -2
+    assert L.tp_swiglu_bwd_workspace_bytes(1, 64, 64, big) == 0
+    rc = L.tp_attn_shard_fwd(None, 1, 1, (1 << 22) + 1, 64, 1, 128, 1, 0.0,
+                             fake, fake, fake, fake, fake, fake, fake, fake, fake, fake)
+    assert rc == -2 and b"2^22" in L.tp_last_error_detail()
+    rc = L.tp_attn_shard_fwd(None, 1, 1, 128, 64, (1 << 21) // 128 + 1, 128, 1, 0.0,
+                             fake, fake, fake, fake, fake, fake, fake, fake, fake, fake)
+    assert rc == -2
+    # the limits themselves are accepted up to the pointer checks
+    rc = L.tp_mlp_fwd(None, 1, 64, 1 << 21, 64, None, fake, fake, None, fake, fake)
+    assert rc == -1
