@@ -46,7 +46,7 @@ __all__ = [
     "gelu", "gelu_prime", "swish", "swish_prime",
     "mlp_shard_fwd", "mlp_shard_bwd", "mlp_unsharded", "mlp_unsharded_bwd",
     "swiglu_shard_fwd", "swiglu_shard_bwd", "swiglu_unsharded",
-    "attn_shard_fwd", "attn_unsharded", "attn_core",
+    "attn_shard_fwd", "attn_unsharded", "attn_core", "attn_core_lse", "attn_core_bwd", "attn_shard_bwd",
     "shard_reduce", "shard_range",
 ]
 
@@ -197,29 +197,106 @@ def attn_core(Q, K, V, causal: bool = True, scale: Optional[float] = None) -> np
     return P @ V
 
 
+def attn_core_lse(Q, K, V, causal: bool = True, scale: Optional[float] = None):
+    """attn_core plus the log-sum-exp of each query's scaled, masked scores:
+    L_t = log sum_{u allowed} exp(S[t, u]), so that P[t, u] = exp(S[t, u] - L_t)."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    s, dh = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(dh)
+    S = (Q @ K.T) * scale
+    if causal:
+        S = np.where(np.tril(np.ones((s, K.shape[0]), dtype=bool)), S, -np.inf)
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    tot = E.sum(axis=1, keepdims=True)
+    L = (m + np.log(tot))[:, 0]
+    return (E / tot) @ V, L
+
+
+def attn_core_bwd(Q, K, V, dO, causal: bool = True, scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Gradients of O = softmax(mask(Q K^T * scale)) V for one head, by the
+    chain rule on that definition: with P the softmax,
+      dV = P^T dO,  dP = dO V^T,
+      dS = P * (dP - rowsum(P * dP))     (the softmax Jacobian applied row by row),
+      dQ = dS K * scale,  dK = dS^T Q * scale.
+    Masked entries have P = 0 and so carry no gradient."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    s, dh = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(dh)
+    S = (Q @ K.T) * scale
+    if causal:
+        S = np.where(np.tril(np.ones((s, K.shape[0]), dtype=bool)), S, -np.inf)
+    S = S - S.max(axis=1, keepdims=True)
+    P = np.exp(S)
+    P = P / P.sum(axis=1, keepdims=True)
+    dV = P.T @ dO
+    dP = dO @ V.T
+    dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+    return {"dQ": dS @ K * scale, "dK": dS.T @ Q * scale, "dV": dV}
+
+
+def _split_heads(T, b, s, h, dh):
+    return T.reshape(b, s, h, dh).transpose(0, 2, 1, 3)
+
+
 def attn_shard_fwd(X, Wq, Wk, Wv, Wo, b: int, s: int, h_local: int, d_head: int,
                    causal: bool = True, scale: Optional[float] = None) -> Dict[str, np.ndarray]:
     """One shard's attention: returns Q, K, V as [b, h_l, s, d_h], the
-    concatenated head outputs O [b*s, h_l*d_h] and the partial Z = O W_O,i.
+    concatenated head outputs O [b*s, h_l*d_h], the partial Z = O W_O,i and
+    the per-query log-sum-exp L [b, h_l, s] (natural log, of the scaled,
+    masked scores).
 
     Local head j uses columns [j*d_h, (j+1)*d_h) of the shard's W_Q/W_K/W_V
     and rows [j*d_h, (j+1)*d_h) of its W_O slice.
     """
     X = _f64(X).reshape(b, s, -1)
     hd = h_local * d_head
-    Qf = X @ _f64(Wq)            # [b, s, hd]
-    Kf = X @ _f64(Wk)
-    Vf = X @ _f64(Wv)
-    Q = Qf.reshape(b, s, h_local, d_head).transpose(0, 2, 1, 3)
-    K = Kf.reshape(b, s, h_local, d_head).transpose(0, 2, 1, 3)
-    V = Vf.reshape(b, s, h_local, d_head).transpose(0, 2, 1, 3)
+    Q = _split_heads(X @ _f64(Wq), b, s, h_local, d_head)
+    K = _split_heads(X @ _f64(Wk), b, s, h_local, d_head)
+    V = _split_heads(X @ _f64(Wv), b, s, h_local, d_head)
     O = np.empty((b, s, h_local, d_head))
+    L = np.empty((b, h_local, s))
     for bi in range(b):
         for j in range(h_local):
-            O[bi, :, j, :] = attn_core(Q[bi, j], K[bi, j], V[bi, j], causal, scale)
+            O[bi, :, j, :], L[bi, j] = attn_core_lse(Q[bi, j], K[bi, j], V[bi, j], causal, scale)
     O = O.reshape(b * s, hd)
     Z = O @ _f64(Wo)
-    return {"Q": Q, "K": K, "V": V, "O": O, "Z": Z}
+    return {"Q": Q, "K": K, "V": V, "O": O, "Z": Z, "L": L}
+
+
+def attn_shard_bwd(X, Wq, Wk, Wv, Wo, dY, b: int, s: int, h_local: int, d_head: int,
+                   causal: bool = True, scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Backward of one attention shard ([BM] Megatron_MHA: the input passes
+    Megatron_f, identity forward, so dX is this shard's summand of the full
+    dX and is summed over shards (the f all-reduce, [HC] 3.4); Z's gradient
+    is the full upstream dY because g's backward is the identity).
+
+      dO = dY W_O^T,  dW_O = O^T dY                      (row-parallel product)
+      per head: dQ, dK, dV from attn_core_bwd
+      dX = dQ W_Q^T + dK W_K^T + dV W_V^T                 (this shard's partial)
+      dW_Q = X^T dQ,  dW_K = X^T dK,  dW_V = X^T dV       (column slices)
+
+    dQ, dK, dV are returned token-major [b*s, h_l*d_h] like O.
+    """
+    f = attn_shard_fwd(X, Wq, Wk, Wv, Wo, b, s, h_local, d_head, causal, scale)
+    X2 = _f64(X).reshape(b * s, -1)
+    dY = _f64(dY)
+    hd = h_local * d_head
+    dO = dY @ _f64(Wo).T
+    dOh = _split_heads(dO, b, s, h_local, d_head)
+    dQ = np.empty((b, s, h_local, d_head))
+    dK = np.empty_like(dQ)
+    dV = np.empty_like(dQ)
+    for bi in range(b):
+        for j in range(h_local):
+            g = attn_core_bwd(f["Q"][bi, j], f["K"][bi, j], f["V"][bi, j], dOh[bi, j], causal, scale)
+            dQ[bi, :, j, :], dK[bi, :, j, :], dV[bi, :, j, :] = g["dQ"], g["dK"], g["dV"]
+    dQ, dK, dV = (t.reshape(b * s, hd) for t in (dQ, dK, dV))
+    return {"dO": dO, "dQ": dQ, "dK": dK, "dV": dV,
+            "dX": dQ @ _f64(Wq).T + dK @ _f64(Wk).T + dV @ _f64(Wv).T,
+            "dWq": X2.T @ dQ, "dWk": X2.T @ dK, "dWv": X2.T @ dV, "dWo": f["O"].T @ dY}
 
 
 def attn_unsharded(X, Wq, Wk, Wv, Wo, b: int, s: int, heads: int, d_head: int,

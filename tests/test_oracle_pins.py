@@ -308,6 +308,75 @@ def test_online_softmax_tiling_equals_direct_softmax():
     np.testing.assert_allclose(out, O.attn_core(Q, K, V), rtol=1e-13, atol=1e-14)
 
 
+# ------------------------------------------------------- attention backward
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_bwd_matches_finite_differences(causal):
+    # The gradients of <dY, Z> with respect to every input, by central
+    # differences of the forward definition alone.
+    b, s, h, dh, d = 1, 5, 2, 4, 6
+    X, Wq, Wk, Wv, Wo = (_tiny((b * s, d), 50), _tiny((d, h * dh), 51, 0.6), _tiny((d, h * dh), 52, 0.6),
+                         _tiny((d, h * dh), 53, 0.6), _tiny((h * dh, d), 54, 0.6))
+    dY = _tiny((b * s, d), 55)
+    loss = lambda: float(np.sum(dY * O.attn_shard_fwd(X, Wq, Wk, Wv, Wo, b, s, h, dh, causal)["Z"]))
+    g = O.attn_shard_bwd(X, Wq, Wk, Wv, Wo, dY, b, s, h, dh, causal)
+    for name, arr in (("dX", X), ("dWq", Wq), ("dWk", Wk), ("dWv", Wv), ("dWo", Wo)):
+        np.testing.assert_allclose(g[name], _fd_grad(loss, arr), atol=2e-8, err_msg=name)
+
+
+def test_attention_lse_brute_force():
+    # L_t = log sum_{u <= t} exp(S[t, u]) written out with math.exp/math.log.
+    rng = np.random.default_rng(56)
+    s, dh = 7, 3
+    Q, K, V = rng.standard_normal((s, dh)), rng.standard_normal((s, dh)), rng.standard_normal((s, dh))
+    _, L = O.attn_core_lse(Q, K, V)
+    sc = 1 / math.sqrt(dh)
+    for t in range(s):
+        ref = math.log(math.fsum(math.exp(math.fsum(Q[t, c] * K[u, c] for c in range(dh)) * sc)
+                                 for u in range(t + 1)))
+        assert abs(L[t] - ref) < 1e-13
+    o, _ = O.attn_core_lse(Q, K, V)
+    np.testing.assert_allclose(o, O.attn_core(Q, K, V), rtol=1e-14, atol=1e-14)
+
+
+def test_attention_bwd_special_cases():
+    rng = np.random.default_rng(57)
+    s, dh = 6, 3
+    Q, K, V, dO = (rng.standard_normal((s, dh)) for _ in range(4))
+    # One key: the softmax is constant 1, so O = V and only V gets gradient.
+    g1 = O.attn_core_bwd(Q[:1], K[:1], V[:1], dO[:1])
+    np.testing.assert_array_equal(g1["dV"], dO[:1])
+    np.testing.assert_array_equal(g1["dQ"], np.zeros((1, dh)))
+    np.testing.assert_array_equal(g1["dK"], np.zeros((1, dh)))
+    # K = 0: every allowed key weighs 1/(t+1), so dV_u = sum_{t >= u} dO_t / (t + 1).
+    g0 = O.attn_core_bwd(Q, np.zeros_like(K), V, dO)
+    w = 1.0 / np.arange(1, s + 1)
+    dv = np.array([np.sum(dO[u:] * w[u:, None], axis=0) for u in range(s)])
+    np.testing.assert_allclose(g0["dV"], dv, rtol=1e-13, atol=1e-14)
+    # Row 0 attends only to key 0 with weight 1: its query gets no gradient.
+    g = O.attn_core_bwd(Q, K, V, dO)
+    np.testing.assert_allclose(g["dQ"][0], np.zeros(dh), atol=1e-15)
+    # Each softmax row's Jacobian sums to zero (sum_u dS[t, u] = 0), so the key
+    # gradients cancel: sum_u dK_u = scale * sum_t (sum_u dS[t, u]) Q_t = 0.
+    np.testing.assert_allclose(g["dK"].sum(axis=0), np.zeros(dh), atol=1e-13)
+
+
+def test_attention_bwd_shards_sum_and_concatenate():
+    # [HC] 3.4 / [BM] Megatron_f: dX is summed over the head-group shards;
+    # the weight gradients are the shards' column (W_Q/W_K/W_V) and row (W_O)
+    # slices of the unsharded gradients.
+    n, h_l, dh, b, s, d = 3, 2, 4, 2, 6, 12
+    inp = tpsynth.random_attn(b, s, d, h_l, dh, "f32", seed=58, w_std=0.3, n_shards=n)
+    dY = _tiny((b * s, d), 59)
+    full = O.attn_shard_bwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], dY, b, s, n * h_l, dh)
+    parts = [O.attn_shard_bwd(inp["X"], inp["Wqs"][i], inp["Wks"][i], inp["Wvs"][i], inp["Wos"][i], dY,
+                              b, s, h_l, dh) for i in range(n)]
+    assert O.max_rel_err(O.shard_reduce([p["dX"] for p in parts]), full["dX"]) < 1e-12
+    for k in ("dWq", "dWk", "dWv"):
+        np.testing.assert_allclose(np.concatenate([p[k] for p in parts], axis=1), full[k], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(np.concatenate([p["dWo"] for p in parts], axis=0), full["dWo"], rtol=1e-12, atol=1e-13)
+
+
 # -------------------------------------------------------------- shard-reduce
 
 def _read_golden_allreduce():
