@@ -294,6 +294,7 @@ def run_c3(tp, torch, steps, warmup):
 
 
 def run_c4(tp, torch, steps, warmup):
+    import numpy as np
     import tpsynth
     wl = tpsynth.WORKLOADS["C4"]
     inp = tpsynth.attn_inputs(wl)
@@ -301,24 +302,43 @@ def run_c4(tp, torch, steps, warmup):
     dev = lambda a: torch.from_numpy(a).to(bf).cuda()
     b, s, d, hl, dh = wl.b, wl.s, wl.d, wl.h_local, wl.d_head
     X, Wq, Wk, Wv, Wo = (dev(inp[k]) for k in ("X", "Wq", "Wk", "Wv", "Wo"))
+    dY = dev(np.random.default_rng(44).standard_normal((b * s, d)).astype(np.float32))
     Q, K, V = (torch.empty((b, hl, s, dh), dtype=bf, device="cuda") for _ in range(3))
     Ob = torch.empty((b * s, hl * dh), dtype=bf, device="cuda")
     Z = torch.empty((b * s, d), dtype=bf, device="cuda")
+    L = torch.empty((b, hl, s), dtype=torch.float32, device="cuda")
+    dX = torch.empty((b * s, d), dtype=bf, device="cuda")
+    dWq, dWk, dWv = (torch.empty((d, hl * dh), dtype=torch.float32, device="cuda") for _ in range(3))
+    dWo = torch.empty((hl * dh, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tp.tp_attn_shard_bwd_workspace_bytes(tp.TP_DT_BF16, b, s, d, hl, dh),
+                     dtype=torch.uint8, device="cuda")
 
-    def step():
-        tp.tp_attn_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, Z, b, s, hl, dh, causal=True)
+    def fwd():
+        tp.tp_attn_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, Z, b, s, hl, dh, causal=True, L=L)
 
-    ms, _, per = timed(tp, torch, step, steps, warmup, 4)
+    def bwd():
+        tp.tp_attn_shard_bwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, L, dY, dX, dWq, dWk, dWv, dWo, ws, b, s, hl, dh,
+                             causal=True)
+
+    ms_f, _, per_f = timed(tp, torch, fwd, steps, warmup, 4)
+    ms_b, _, per_b = timed(tp, torch, bwd, steps, warmup, 12)
     M, N = b * s, hl * dh
     core = 2 * 2.0 * b * hl * (s * (s + 1) / 2) * dh      # causal pairs only: QK^T and PV
-    flops = 3 * gemm_flops(M, N, d) + core + gemm_flops(M, d, N)
-    core_ms = [v for k, v in per.items() if k.startswith("attn.core")]
-    core_avg = sum(core_ms[0]) / len(core_ms[0]) if core_ms else None
-    return {"workload": "C4 causal self-attention shard, b 4 s 2048 d 4096, 8 of 32 heads of 128, fwd",
-            "ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
-            "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-            "core_tflops": round(core / core_avg / 1e9, 1) if core_avg else None,
-            "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in per.items()}}
+    flops_f = 3 * gemm_flops(M, N, d) + core + gemm_flops(M, d, N)
+    # backward: dO and dW_O, dX and dW_{Q,K,V} products; the core's dV, dP, dQ, dK
+    # plus the recomputed S (2.5 x the forward core)
+    flops_b = 2 * gemm_flops(M, N, d) + 2 * 3 * gemm_flops(M, N, d) + 2.5 * core
+    avg = lambda per, names: [sum(v) / len(v) for k, v in per.items() if k in names]
+    core_f = avg(per_f, ("attn.core_d128", "attn.core_d64"))
+    core_b = sum(avg(per_b, ("attn_bwd.dkv", "attn_bwd.dq")))
+    return {"workload": "C4 causal self-attention shard, b 4 s 2048 d 4096, 8 of 32 heads of 128, fwd+bwd",
+            "ms_per_step": round(ms_f + ms_b, 4), "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+            "tflops": round((flops_f + flops_b) / (ms_f + ms_b) / 1e9, 1),
+            "fwd_tflops": round(flops_f / ms_f / 1e9, 1), "bwd_tflops": round(flops_b / ms_b / 1e9, 1),
+            "pct_of_peak": round(100 * (flops_f + flops_b) / (ms_f + ms_b) / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "core_tflops": round(core / core_f[0] / 1e9, 1) if core_f else None,
+            "core_bwd_tflops": round(2.5 * core / core_b / 1e9, 1) if core_b else None,
+            "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in list(per_f.items()) + list(per_b.items())}}
 
 
 def main():

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 1
+#define TP_ABI_VERSION 2
 
 typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype_t;
 
@@ -146,14 +146,45 @@ size_t tp_swiglu_bwd_workspace_bytes(tp_dtype_t dt, int64_t M, int64_t d, int64_
  *   O       = [o_0 | ... | o_{h_local-1}] [b*s x h_local*d_head]
  *   Z       = O Wo                         this shard's partial [b*s x d]
  * X [b*s x d]; Wq, Wk, Wv [d x h_local*d_head]; Wo [h_local*d_head x d].
- * Q, K, V and O are outputs (kept for inspection or a backward pass).
+ *   L[bi,j,t] = log sum_u exp(S[t,u])     fp32 [b, h_local, s], natural log
+ * Q, K, V, O and L are outputs (kept for inspection or the backward pass);
+ * L may be NULL.
  * Supported: dt = TP_DT_BF16, d_head = 64 or 128, d a multiple of 8.
  * scale <= 0 selects 1/sqrt(d_head).  causal is 0 or 1.
  * ------------------------------------------------------------------------- */
 int tp_attn_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
                       int64_t h_local, int64_t d_head, int causal, float scale,
                       const void* X, const void* Wq, const void* Wk, const void* Wv,
-                      const void* Wo, void* Q, void* K, void* V, void* O, void* Z);
+                      const void* Wo, void* Q, void* K, void* V, void* O, void* Z,
+                      float* L);
+
+/* ---------------------------------------------------------------------------
+ * tp_attn_shard_bwd — backward of the attention shard.  The input passes
+ * [BM] Megatron_f (identity forward, all-reduce backward), so dX is this
+ * shard's summand of the full dX (summed over shards by the f all-reduce,
+ * [HC] 3.4); the output projection is row-parallel and g's backward is the
+ * identity, so dY is the full upstream gradient [b*s x d].
+ *   dO = dY Wo^T;  dWo = O^T dY
+ *   per head, with P = exp(S - L) recomputed from Q, K and L:
+ *     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *     dQ = scale dS K,  dK = scale dS^T Q
+ *   dX = dQ Wq^T + dK Wk^T + dV Wv^T  (dQ, dK, dV token-major like O)
+ *   dWq = X^T dQ,  dWk = X^T dK,  dWv = X^T dV
+ * Inputs are the forward's arguments and outputs (Q, K, V, O, L from the
+ * same tp_attn_shard_fwd call).  dX is bf16 [b*s x d]; dWq, dWk, dWv
+ * [d x h_local*d_head] and dWo [h_local*d_head x d] are fp32.  Supported:
+ * dt = TP_DT_BF16, d_head = 128.  ws: device workspace of at least
+ * tp_attn_shard_bwd_workspace_bytes(...) bytes, contents undefined on return.
+ * ------------------------------------------------------------------------- */
+int tp_attn_shard_bwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
+                      int64_t h_local, int64_t d_head, int causal, float scale,
+                      const void* X, const void* Wq, const void* Wk, const void* Wv,
+                      const void* Wo, const void* Q, const void* K, const void* V,
+                      const void* O, const float* L, const void* dY,
+                      void* dX, float* dWq, float* dWk, float* dWv, float* dWo,
+                      void* ws, size_t ws_bytes);
+size_t tp_attn_shard_bwd_workspace_bytes(tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
+                                         int64_t h_local, int64_t d_head);
 
 /* ---------------------------------------------------------------------------
  * tp_shard_reduce — the local stand-in for the g (forward) and f (backward)

@@ -16,7 +16,8 @@ __all__ = [
     "TPError", "lib", "LIB_PATH", "TP_DT_F32", "TP_DT_BF16",
     "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_workspace_bytes",
     "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes",
-    "tp_attn_shard_fwd", "tp_shard_reduce", "tp_shard_range",
+    "tp_attn_shard_fwd", "tp_attn_shard_bwd", "tp_attn_shard_bwd_workspace_bytes",
+    "tp_shard_reduce", "tp_shard_range",
     "tp_abi_version", "EXPORTS",
 ]
 
@@ -44,7 +45,10 @@ EXPORTS = {
     "tp_swiglu_bwd": (_i32, [_p, _i32, _i64, _i64, _i64] + [_p] * 8 + [_p] * 4 + [_p, _sz]),
     "tp_swiglu_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
     "tp_attn_shard_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _i64, _i32, ctypes.c_float]
-                          + [_p] * 5 + [_p] * 5),
+                          + [_p] * 5 + [_p] * 5 + [_p]),
+    "tp_attn_shard_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _i64, _i32, ctypes.c_float]
+                          + [_p] * 5 + [_p] * 5 + [_p] + [_p] * 5 + [_p, _sz]),
+    "tp_attn_shard_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i64, _i64]),
     "tp_shard_reduce": (_i32, [_p, _i32, _i32, _i64, _i64, _p, _i64, _p, _i64, _p]),
     "tp_strerror": (ctypes.c_char_p, [_i32]),
     "tp_last_error_detail": (ctypes.c_char_p, []),
@@ -160,11 +164,25 @@ def tp_swiglu_bwd(X, W1, W3, W2, G, U, H, dY, dX, dW1, dW3, dW2, ws, stream=None
 
 
 def tp_attn_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, O, Z, b: int, s: int, h_local: int, d_head: int,
-                      causal: bool = True, scale: float = 0.0, stream=None) -> None:
+                      causal: bool = True, scale: float = 0.0, L=None, stream=None) -> None:
     d = X.shape[1]
     _check(lib().tp_attn_shard_fwd(_stream(stream), _dt(X), b, s, d, h_local, d_head, int(causal),
                                    float(scale), _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo),
-                                   _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(Z)))
+                                   _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(Z), _ptr(L)))
+
+
+def tp_attn_shard_bwd_workspace_bytes(dtype: int, b: int, s: int, d: int, h_local: int, d_head: int) -> int:
+    return lib().tp_attn_shard_bwd_workspace_bytes(dtype, b, s, d, h_local, d_head)
+
+
+def tp_attn_shard_bwd(X, Wq, Wk, Wv, Wo, Q, K, V, O, L, dY, dX, dWq, dWk, dWv, dWo, ws, b: int, s: int,
+                      h_local: int, d_head: int, causal: bool = True, scale: float = 0.0, stream=None) -> None:
+    d = X.shape[1]
+    _check(lib().tp_attn_shard_bwd(_stream(stream), _dt(X), b, s, d, h_local, d_head, int(causal),
+                                   float(scale), _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo),
+                                   _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), _ptr(dY), _ptr(dX),
+                                   _ptr(dWq), _ptr(dWk), _ptr(dWv), _ptr(dWo), _ptr(ws),
+                                   ws.numel() * ws.element_size()))
 
 
 def tp_shard_reduce(partials, out, n_shards: int, numel: int, shard_stride: Optional[int] = None,

@@ -36,7 +36,7 @@ namespace tpk {
 template <int D>
 __global__ void __launch_bounds__(256)
 flash_attn_fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                      const bf16* __restrict__ V, bf16* __restrict__ O,
+                      const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ L,
                       int nb, int hl, int s, int causal, float scale_log2) {
   constexpr int BQ = 128, BKV = 64, NT = 256;
   constexpr int LDK = D + 8;     // K tile: BKV rows of D
@@ -180,6 +180,8 @@ flash_attn_fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   if (qme < s) {
     const float inv = 1.0f / l_run;
+    // log-sum-exp of the query's scaled scores, natural log (m_run is in log2 units)
+    if (L && g == 0) L[(int64_t)bh * s + qme] = (m_run + __log2f(l_run)) * 0.69314718055994531f;
     bf16* orow = O + ((int64_t)bi * s + qme) * ((int64_t)hl * D) + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -248,7 +250,7 @@ __device__ __forceinline__ bf16x8 frag_v(const char* vt, int d0, int kvb, int la
 
 __global__ void __launch_bounds__(256, 2)
 flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                           const bf16* __restrict__ V, bf16* __restrict__ O,
+                           const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ L,
                            int nb, int hl, int s, int causal, float scale_log2) {
   using namespace attn128;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
@@ -379,6 +381,8 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
 
   if (qme < s) {
     const float inv = 1.0f / l_run;
+    // log-sum-exp of the query's scaled scores, natural log (m_run is in log2 units)
+    if (L && g == 0) L[(int64_t)bh * s + qme] = (m_run + __log2f(l_run)) * 0.69314718055994531f;
     bf16* orow = O + ((int64_t)bi * s + qme) * ((int64_t)hl * D) + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -394,7 +398,7 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
 hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local,
                            int64_t d_head, int causal, float scale,
                            const void* X, const void* Wq, const void* Wk, const void* Wv,
-                           const void* Wo, void* Q, void* K, void* V, void* O, void* Z) {
+                           const void* Wo, void* Q, void* K, void* V, void* O, void* Z, float* L) {
   const int64_t M = b * s, N = h_local * d_head;
   {  // Q, K, V = X W{q,k,v}, scattered to [b, h_local, s, d_head]
     GemmParams p = make_params(M, N, make_seg(X, d, M * d, Wq, N, d * N, d));
@@ -415,10 +419,10 @@ hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
     const bf16* v = static_cast<const bf16*>(V);
     bf16* o = static_cast<bf16*>(O);
     if (d_head == 128)
-      TPK_TRY(launch("attn.core_d128", flash_attn_fwd_d128_kernel, grid, dim3(256), st, q, k, v, o, (int)b,
+      TPK_TRY(launch("attn.core_d128", flash_attn_fwd_d128_kernel, grid, dim3(256), st, q, k, v, o, L, (int)b,
                      (int)h_local, (int)s, causal, sl2));
     else
-      TPK_TRY(launch("attn.core_d64", flash_attn_fwd_kernel<64>, grid, dim3(256), st, q, k, v, o, (int)b,
+      TPK_TRY(launch("attn.core_d64", flash_attn_fwd_kernel<64>, grid, dim3(256), st, q, k, v, o, L, (int)b,
                      (int)h_local, (int)s, causal, sl2));
   }
   {  // Z = O Wo (this shard's partial)

@@ -1,0 +1,472 @@
+// Backward of the head-group attention shard ([BM] Megatron_MHA: the input
+// passes Megatron_f, identity forward and all-reduce backward, so this
+// shard's dX is one summand of the full dX; the output projection is
+// row-parallel and g's backward is the identity, so the shard receives the
+// full upstream dY.  [HC] 3.4: f all-reduces dX in the backward pass.)
+//
+//   dO = dY W_O^T                         (product, bf16 [b*s x h_l*d_h])
+//   dW_O = O^T dY                         (product, fp32)
+//   D[t] = sum_c dO[t, c] O[t, c]         per (batch, head, query)
+//   per head, with P = exp(S - L) recomputed from Q, K and the forward's
+//   log-sum-exp L:
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+//     dK = scale dS^T Q,  dQ = scale dS K
+//   dX = [dQ | dK | dV] [W_Q | W_K | W_V]^T   (one product over K = 3 h_l d_h)
+//   [dW_Q | dW_K | dW_V] = X^T [dQ | dK | dV]  (one product, columns split)
+//
+// The two flash kernels recompute P and dP (no s x s matrix in memory) and
+// are deterministic: the key-tile kernel owns dK and dV of 128 keys (lanes
+// index keys, so P arrives in the layout the dK/dV products consume), the
+// query-tile kernel owns dQ of 128 queries (lanes index queries, as in the
+// forward).  Tiles stream through LDS by DMA with a 16-byte-chunk swizzle
+// c ^ (row % 16) that serves both the row-wise fragment reads and the
+// transposing ds_read_b64_tr_b16 reads.
+#include "epilogues.hpp"
+#include "gemm_dispatch.hpp"
+
+namespace tpk {
+
+namespace attnb {
+constexpr int D = 128, NT = 256, NW = 4;
+constexpr int ROWB = D * 2;                   // bytes per tile row
+constexpr float kLog2e = 1.4426950408889634f;
+
+// DMA of `rows` rows of 128 bf16 (row pitch `ld_b` bytes in memory) into a
+// swizzled LDS tile: 4 rows per 1 KiB instruction; NI instructions per wave.
+template <int ROWS>
+__device__ __forceinline__ void dma_rows(desc_t r, uint32_t ld_b, uint32_t lds, int wave, int lane) {
+  constexpr int NI = ROWS / 4 / NW;
+  static_assert(NI * 4 * NW == ROWS, "tile rows");
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int ins = wave * NI + j;
+    const int row = ins * 4 + (lane >> 4);
+    const int lc = (lane & 15) ^ (row & 15);
+    dma16(r, lds + ins * 1024, (uint32_t)row * ld_b + (uint32_t)lc * 16u);
+  }
+}
+
+// One dword per lane (64 floats) into LDS.
+__device__ __forceinline__ void dma_vec(desc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               ::"s"(lds), "v"(voff), "s"(r) : "memory", "m0");
+}
+
+// Row fragment: lane l holds row row0 + l%32, columns kk*16 + 8 (l/32) .. +8.
+__device__ __forceinline__ bf16x8 frag_row(const char* t, int row0, int kk, int lane) {
+  const int row = row0 + (lane & 31);
+  const int pc = (kk * 2 + (lane >> 5)) ^ (row & 15);
+  return *reinterpret_cast<const bf16x8*>(t + row * ROWB + pc * 16);
+}
+
+// Transposed fragment: lane l holds column d0 + l%32 of the rows
+// r0 + 4 (l/32) + {0..3} and r0 + 8 + 4 (l/32) + {0..3}: the order in which
+// an accumulator (lanes = the other index, registers = these rows) packs its
+// values.  Two ds_read_b64_tr_b16: in each 16-lane group lane i addresses
+// row base + i/4, columns 4 (i%4)..+3, and lane q receives the four rows of
+// column q.
+__device__ __forceinline__ bf16x8 frag_col(const char* t, int d0, int r0, int lane) {
+  const int G = lane >> 4, i = lane & 15;
+  const int col = d0 + 16 * (G & 1) + 4 * (i & 3);
+  const int k = r0 + 4 * (G >> 1) + (i >> 2);
+  const char* plo = t + k * ROWB + (((col >> 3) ^ (k & 15)) * 16) + (col & 7) * 2;
+  const char* phi = t + (k + 8) * ROWB + (((col >> 3) ^ ((k + 8) & 15)) * 16) + (col & 7) * 2;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(plo));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(phi));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(a[base + 2 * e], a[base + 2 * e + 1]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ desc_t range_desc(const void* base, int64_t bytes) {
+  return make_desc(base, bytes <= 0 ? 0u : (bytes < 0x7FFFFFFF ? (uint32_t)bytes : 0x7FFFFFFFu));
+}
+}  // namespace attnb
+
+// D[bh, t] = sum_c dO[t, h*128 + c] * O[t, h*128 + c]; one thread per (t, h).
+__global__ void __launch_bounds__(256) attn_bwd_rowdot_kernel(const bf16* __restrict__ dO,
+                                                              const bf16* __restrict__ O, float* __restrict__ Dv,
+                                                              int64_t rows, int hl, int s, int64_t ld) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * hl) return;
+  const int64_t row = i / hl;
+  const int h = (int)(i % hl);
+  const bf16* a = dO + row * ld + h * attnb::D;
+  const bf16* o = O + row * ld + h * attnb::D;
+  float acc = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < attnb::D; c += 8) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(a + c);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(o + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
+  }
+  const int64_t bi = row / s, t = row % s;
+  Dv[(bi * hl + h) * s + t] = acc;
+}
+
+// Key-tile kernel: dK and dV of 128 keys (four waves of 32) of one (batch,
+// head), streaming 64-query chunks of Q and dO.  Lanes index keys: the
+// accumulators of S = Q K^T and dP = dO V^T hold, per lane, one key and 16
+// queries, exactly the operand layout of dV += P^T dO and dK += dS^T Q.
+__global__ void __launch_bounds__(256, 1)
+attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                    const bf16* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
+                    bf16* __restrict__ dK, bf16* __restrict__ dV, int nb, int hl, int s, int causal,
+                    float scale, int64_t ld_o, int64_t ld_g) {
+  using namespace attnb;
+  constexpr int BKEY = 128, BQ = 64;
+  constexpr int QT = BQ * ROWB, VEC = BQ * 4;
+  constexpr int STAGE = 2 * QT + 2 * VEC;            // Q, dO, L, D
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int nkt = (s + BKEY - 1) / BKEY;
+  const int nbh = nb * hl;
+  const int kt = (int)(blockIdx.x / nbh);            // key tile 0 (most queries) first
+  const int bh = (int)(blockIdx.x % nbh);
+  const int bi = bh / hl, h = bh % hl;
+  (void)nkt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lk = lane & 31, g = lane >> 5;
+  const int k0 = kt * BKEY, kw = k0 + wave * 32, key = kw + lk;
+  const int64_t head = (int64_t)bh * s * D;
+  const uint32_t lds0 = lds_addr(smem);
+  const float sl2 = scale * kLog2e;
+
+  // This wave's keys and values as row fragments (zero past the sequence).
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const rsrc_t rk = make_rsrc(K + head, (uint64_t)s * ROWB);
+    const rsrc_t rv = make_rsrc(V + head, (uint64_t)s * ROWB);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const uint32_t off = (uint32_t)(((int64_t)key * D + kk * 16 + g * 8) * 2);
+      kf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+      vf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+    }
+  }
+
+  const int nqc = (s + BQ - 1) / BQ;
+  const int c_begin = causal ? k0 / BQ : 0;
+  auto issue = [&](int c) {
+    const int q0 = c * BQ;
+    const uint32_t st = lds0 + (uint32_t)((c & 1) * STAGE);
+    dma_rows<BQ>(range_desc(Q + head + (int64_t)q0 * D, (int64_t)(s - q0) * ROWB), ROWB, st, wave, lane);
+    const bf16* dorow = dO + ((int64_t)bi * s + q0) * ld_o + (int64_t)h * D;
+    dma_rows<BQ>(range_desc(dorow, (int64_t)(s - q0 - 1) * ld_o * 2 + ROWB), (uint32_t)(ld_o * 2), st + QT, wave,
+                 lane);
+    if (wave == 0) dma_vec(range_desc(L + (int64_t)bh * s + q0, (int64_t)(s - q0) * 4), st + 2 * QT, lane * 4u);
+    if (wave == 1) dma_vec(range_desc(Dv + (int64_t)bh * s + q0, (int64_t)(s - q0) * 4), st + 2 * QT + VEC, lane * 4u);
+  };
+
+  f32x16 adk[D / 32], adv[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) adk[i] = adv[i] = f32x16{};
+
+  if (c_begin < nqc) issue(c_begin);
+  for (int c = c_begin; c < nqc; ++c) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c + 1 < nqc) issue(c + 1);
+    const int q0 = c * BQ;
+    if (causal && q0 + BQ - 1 < kw) continue;        // every query precedes this wave's keys
+    const char* Qs = smem + (c & 1) * STAGE;
+    const char* dOs = Qs + QT;
+    const float* Ls = reinterpret_cast<const float*>(Qs + 2 * QT);
+    const float* Ds = Ls + BQ;
+
+    // S[key][q] and dP[key][q] for two 32-query blocks (four independent chains)
+    f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Qs, qb * 32, kk, lane), kf[kk], sacc[qb], 0, 0, 0);
+        pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(dOs, qb * 32, kk, lane), vf[kk], pacc[qb], 0, 0, 0);
+      }
+    // register r of block qb: query q0 + qb*32 + 8 (r/4) + 4 g + r%4
+    bf16x8 pf[2][2], sf[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ql = qb * 32 + 8 * r4 + 4 * g;      // first of four consecutive queries
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e, q = q0 + ql + e;
+          const bool ok = q < s && (!causal || key <= q);
+          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], sl2, -l4[e] * kLog2e)) : 0.f;
+          sacc[qb][r] = p;
+          pacc[qb][r] = p * (pacc[qb][r] - d4[e]);
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        pf[qb][hh] = pack8(sacc[qb], 8 * hh);
+        sf[qb][hh] = pack8(pacc[qb], 8 * hh);
+      }
+    }
+    // dV[key][d] += P^T dO, dK[key][d] += dS^T Q (four d blocks each, interleaved)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_col(dOs, db * 32, qb * 32 + hh * 16, lane),
+                                                            pf[qb][hh], adv[db], 0, 0, 0);
+          adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_col(Qs, db * 32, qb * 32 + hh * 16, lane),
+                                                            sf[qb][hh], adk[db], 0, 0, 0);
+        }
+  }
+
+  // register r of block db: d = db*32 + 8 (r/4) + 4 g + r%4 of key `key`
+  if (key < s) {
+    bf16* krow = dK + ((int64_t)bi * s + key) * ld_g + (int64_t)h * D;
+    bf16* vrow = dV + ((int64_t)bi * s + key) * ld_g + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const int c = db * 32 + 8 * b4 + 4 * g;
+        const f32x4 kv = {adk[db][4 * b4] * scale, adk[db][4 * b4 + 1] * scale, adk[db][4 * b4 + 2] * scale,
+                          adk[db][4 * b4 + 3] * scale};
+        const f32x4 vv = {adv[db][4 * b4], adv[db][4 * b4 + 1], adv[db][4 * b4 + 2], adv[db][4 * b4 + 3]};
+        Quad<bf16>::store(krow + c, kv);
+        Quad<bf16>::store(vrow + c, vv);
+      }
+  }
+}
+
+// Query-tile kernel: dQ of 128 queries (four waves of 32) of one (batch,
+// head), streaming 64-key chunks of K and V.  Lanes index queries, as in the
+// forward: S^T = K Q^T and dP^T = V dO^T need row fragments of K and V, and
+// dQ += dS K needs K transposed in the key order of the dS registers.
+__global__ void __launch_bounds__(256, 2)
+attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                   const bf16* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
+                   bf16* __restrict__ dQ, int nb, int hl, int s, int causal, float scale, int64_t ld_o,
+                   int64_t ld_g) {
+  using namespace attnb;
+  constexpr int BQ = 128, BKV = 64;
+  constexpr int KT = BKV * ROWB, STAGE = 2 * KT;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int nqt = (s + BQ - 1) / BQ;
+  const int nbh = nb * hl;
+  const int qt = nqt - 1 - (int)(blockIdx.x / nbh);   // heaviest tiles first
+  const int bh = (int)(blockIdx.x % nbh);
+  const int bi = bh / hl, h = bh % hl;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, g = lane >> 5;
+  const int q0 = qt * BQ, qw = q0 + wave * 32, qme = qw + lq;
+  const int64_t head = (int64_t)bh * s * D;
+  const uint32_t lds0 = lds_addr(smem);
+  const float sl2 = scale * kLog2e;
+
+  bf16x8 qf[D / 16], of[D / 16];
+  {
+    const rsrc_t rq = make_rsrc(Q + head, (uint64_t)s * ROWB);
+    const bf16* dorow = dO + (int64_t)bi * s * ld_o + (int64_t)h * D;
+    const rsrc_t ro = make_rsrc(dorow, (uint64_t)((int64_t)(s - 1) * ld_o * 2 + ROWB));
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(((int64_t)qme * D + kk * 16 + g * 8) * 2)));
+      of[kk] = __builtin_bit_cast(bf16x8,
+                                  buf_load16(ro, (uint32_t)(((int64_t)qme * ld_o + kk * 16 + g * 8) * 2)));
+    }
+  }
+  const bool live = qme < s;
+  const float l2 = live ? L[(int64_t)bh * s + qme] * kLog2e : 0.f;
+  const float dq = live ? Dv[(int64_t)bh * s + qme] : 0.f;
+
+  const int kv_end = causal ? min(s, q0 + BQ) : s;
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  auto issue = [&](int t) {
+    const int kv0 = t * BKV;
+    const uint32_t st = lds0 + (uint32_t)((t & 1) * STAGE);
+    const int64_t rem = (int64_t)(s - kv0) * ROWB;
+    dma_rows<BKV>(range_desc(K + head + (int64_t)kv0 * D, rem), ROWB, st, wave, lane);
+    dma_rows<BKV>(range_desc(V + head + (int64_t)kv0 * D, rem), ROWB, st + KT, wave, lane);
+  };
+
+  f32x16 adq[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) adq[i] = f32x16{};
+
+  if (ntiles > 0) issue(0);
+  for (int t = 0; t < ntiles; ++t) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 1 < ntiles) issue(t + 1);
+    const int kv0 = t * BKV;
+    if (causal && kv0 > qw + 31) continue;
+    const char* Ks = smem + (t & 1) * STAGE;
+    const char* Vs = Ks + KT;
+    f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Ks, kb * 32, kk, lane), qf[kk], sacc[kb], 0, 0, 0);
+        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Vs, kb * 32, kk, lane), of[kk], pacc[kb], 0, 0, 0);
+      }
+    // register r of block kb: key kv0 + kb*32 + 8 (r/4) + 4 g + r%4 of query qme
+    bf16x8 sf[2][2];
+    const int lim = (causal ? min(qme, s - 1) : s - 1) - (kv0 + 4 * g);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = kb * 32 + 8 * (r >> 2) + (r & 3) <= lim;
+        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -l2)) : 0.f;
+        pacc[kb][r] = p * (pacc[kb][r] - dq);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) sf[kb][hh] = pack8(pacc[kb], 8 * hh);
+    }
+    // dQ[q][d] += dS K (four d blocks, interleaved)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          adq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_col(Ks, db * 32, kb * 32 + hh * 16, lane),
+                                                            sf[kb][hh], adq[db], 0, 0, 0);
+  }
+
+  if (live) {
+    bf16* qrow = dQ + ((int64_t)bi * s + qme) * ld_g + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const f32x4 v = {adq[db][4 * b4] * scale, adq[db][4 * b4 + 1] * scale, adq[db][4 * b4 + 2] * scale,
+                         adq[db][4 * b4 + 3] * scale};
+        Quad<bf16>::store(qrow + db * 32 + 8 * b4 + 4 * g, v);
+      }
+  }
+}
+
+// [W_Q | W_K | W_V] side by side: row r of the result is the rows r of the
+// three [d x n] weights, 16 bytes per thread.
+__global__ void __launch_bounds__(256) attn_concat3_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
+                                                           const bf16* __restrict__ C, bf16* __restrict__ out,
+                                                           int64_t rows, int64_t n) {
+  const int64_t chunks = n / 8;                      // n is a multiple of 8
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * 3 * chunks) return;
+  const int64_t r = i / (3 * chunks), j = i % (3 * chunks);
+  const int part = (int)(j / chunks);
+  const int64_t c = (j % chunks) * 8;
+  const bf16* src = (part == 0 ? A : part == 1 ? B : C) + r * n + c;
+  *reinterpret_cast<u32x4*>(out + r * 3 * n + part * n + c) = *reinterpret_cast<const u32x4*>(src);
+}
+
+// fp32 output whose columns [k*part, (k+1)*part) go to C[k] (row pitch part).
+struct EpiF32Thirds {
+  static constexpr int NOUT = 1;
+  template <int O> using OutT = float;
+  float* C[3];
+  int64_t part;
+  template <int O> __device__ __forceinline__ bool has_out() const { return true; }
+  template <int O> __device__ __forceinline__ float* out_ptr(int64_t m, int64_t n, int, int) const {
+    const int k = n < part ? 0 : (n < 2 * part ? 1 : 2);
+    return C[k] + m * part + (n - k * part);
+  }
+  template <int O> __device__ __forceinline__ f32x4 value(int64_t, int64_t, f32x4 v) const { return v; }
+};
+
+static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace: dO [M x N] bf16, [dQ | dK | dV] [M x 3N] bf16, [W_Q | W_K | W_V]
+// [d x 3N] bf16, D [b h s] fp32, then the split-K partials of dW_O.
+size_t attn_bwd_ws_bytes(int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t d_head) {
+  const int64_t M = b * s, N = h_local * d_head;
+  const GemmPlan pwo = plan_gemm(N, d, M, false, true);
+  return up256((size_t)M * N * 2) + up256((size_t)M * 3 * N * 2) + up256((size_t)d * 3 * N * 2) +
+         up256((size_t)b * h_local * s * 4) + (pwo.split > 1 ? up256((size_t)pwo.split * N * d * 4) : 0);
+}
+
+hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local,
+                           int64_t d_head, int causal, float scale,
+                           const void* X, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                           const void* Q, const void* K, const void* V, const void* O, const float* L,
+                           const void* dY, void* dX, float* dWq, float* dWk, float* dWv, float* dWo,
+                           void* ws) {
+  if (d_head != attnb::D) return hipErrorInvalidValue;
+  const int64_t M = b * s, N = h_local * d_head;
+  char* w = static_cast<char*>(ws);
+  bf16* dO = reinterpret_cast<bf16*>(w);
+  w += up256((size_t)M * N * 2);
+  bf16* dQKV = reinterpret_cast<bf16*>(w);           // [M x 3N]: dQ | dK | dV
+  w += up256((size_t)M * 3 * N * 2);
+  bf16* Wcat = reinterpret_cast<bf16*>(w);           // [d x 3N]: W_Q | W_K | W_V
+  w += up256((size_t)d * 3 * N * 2);
+  float* Dv = reinterpret_cast<float*>(w);
+  w += up256((size_t)b * h_local * s * 4);
+  float* split_ws = reinterpret_cast<float*>(w);
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d_head);
+
+  {  // dO = dY W_O^T
+    GemmParams p = make_params(M, N, make_seg(dY, d, M * d, Wo, d, N * d, d));
+    EpiStore<bf16> e{dO, N, 0};
+    TPK_TRY((launch_gemm<true, true, false>(st, "attn_bwd.dy_wot", p, e, plan_gemm(M, N, d, false, false))));
+  }
+  {  // dW_O = O^T dY (fp32; split along K = M when the output is narrow):
+     // A(m, k) = O[k][m], B(k, n) = dY[k][n]
+    GemmParams p = make_params(N, d, make_seg(O, N, M * N, dY, d, M * d, M));
+    TPK_TRY(wgrad_f32_out(st, plan_gemm(N, d, M, false, true), N, d, dWo, split_ws,
+                          [&](const EpiStore<float>& e, GemmPlan g) {
+                            return launch_gemm<false, false, false>(st, "attn_bwd.ot_dy", p, e, g);
+                          }));
+  }
+  {  // D = rowsum(dO * O)
+    const int64_t n = M * h_local;
+    TPK_TRY(launch("attn_bwd.rowdot", attn_bwd_rowdot_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st,
+                   (const bf16*)dO, static_cast<const bf16*>(O), Dv, M, (int)h_local, (int)s, N));
+  }
+  const bf16* q = static_cast<const bf16*>(Q);
+  const bf16* k = static_cast<const bf16*>(K);
+  const bf16* v = static_cast<const bf16*>(V);
+  const int nbh = (int)(b * h_local);
+  {  // dK, dV
+    const unsigned grid = (unsigned)(((s + 127) / 128) * nbh);
+    TPK_TRY(launch("attn_bwd.dkv", attn_bwd_dkv_kernel, dim3(grid), dim3(256), st, q, k, v, (const bf16*)dO, L,
+                   (const float*)Dv, dQKV + N, dQKV + 2 * N, (int)b, (int)h_local, (int)s, causal, sc, N, 3 * N));
+  }
+  {  // dQ
+    const unsigned grid = (unsigned)(((s + 127) / 128) * nbh);
+    TPK_TRY(launch("attn_bwd.dq", attn_bwd_dq_kernel, dim3(grid), dim3(256), st, q, k, v, (const bf16*)dO, L,
+                   (const float*)Dv, dQKV, (int)b, (int)h_local, (int)s, causal, sc, N, 3 * N));
+  }
+  {  // [W_Q | W_K | W_V]
+    const int64_t n = d * 3 * (N / 8);
+    TPK_TRY(launch("attn_bwd.concat_w", attn_concat3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st,
+                   static_cast<const bf16*>(Wq), static_cast<const bf16*>(Wk), static_cast<const bf16*>(Wv), Wcat,
+                   d, N));
+  }
+  {  // dX = [dQ | dK | dV] [W_Q | W_K | W_V]^T
+    GemmParams p = make_params(M, d, make_seg(dQKV, 3 * N, M * 3 * N, Wcat, 3 * N, d * 3 * N, 3 * N));
+    EpiStore<bf16> e{static_cast<bf16*>(dX), d, 0};
+    TPK_TRY((launch_gemm<true, true, false>(st, "attn_bwd.dqkv_wt", p, e, plan_gemm(M, d, 3 * N, false, false))));
+  }
+  {  // [dW_Q | dW_K | dW_V] = X^T [dQ | dK | dV]
+    GemmParams p = make_params(d, 3 * N, make_seg(X, d, M * d, dQKV, 3 * N, M * 3 * N, M));
+    EpiF32Thirds e{{dWq, dWk, dWv}, N};
+    TPK_TRY((launch_gemm<false, false, false>(st, "attn_bwd.xt_dqkv", p, e, plan_gemm(d, 3 * N, M, false, false))));
+  }
+  return hipSuccess;
+}
+
+}  // namespace tpk

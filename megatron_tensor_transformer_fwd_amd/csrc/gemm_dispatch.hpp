@@ -152,4 +152,20 @@ inline GemmParamsF32 make_params_f32(int64_t M, int64_t N, GemmSegF32 s0) {
     if (e_ != hipSuccess) return e_;          \
   } while (0)
 
+// fp32 weight gradient C[Mo x No] = A^T B over K tokens, through the split-K
+// workspace when the plan splits.
+template <class Launch>
+inline hipError_t wgrad_f32_out(hipStream_t st, GemmPlan plan, int64_t Mo, int64_t No,
+                                float* out, float* split_ws, Launch&& run) {
+  if (plan.split > 1) {
+    EpiStore<float> e{split_ws, No, Mo * No};
+    TPK_TRY(run(e, plan));
+    return launch_shard_reduce(st, DT_F32, DT_F32, plan.split, Mo * No, split_ws, Mo * No,
+                               nullptr, 0, out);
+  }
+  EpiStore<float> e{out, No, 0};
+  return run(e, plan);
+}
+
+
 }  // namespace tpk

@@ -55,21 +55,6 @@ size_t mlp_bwd_ws_bytes(int dt, int64_t M, int64_t d, int64_t f) {
   return pl.dA_bytes + pl.split_bytes;
 }
 
-// fp32 weight gradient C[Mo x No] = A^T B over K tokens, through the split-K
-// workspace when the plan splits.
-template <class Launch>
-static hipError_t wgrad_f32_out(hipStream_t st, GemmPlan plan, int64_t Mo, int64_t No,
-                                float* out, float* split_ws, Launch&& run) {
-  if (plan.split > 1) {
-    EpiStore<float> e{split_ws, No, Mo * No};
-    TPK_TRY(run(e, plan));
-    return launch_shard_reduce(st, DT_F32, DT_F32, plan.split, Mo * No, split_ws, Mo * No,
-                               nullptr, 0, out);
-  }
-  EpiStore<float> e{out, No, 0};
-  return run(e, plan);
-}
-
 static hipError_t mlp_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t f,
                                const void* X, const void* W1, const void* W2,
                                const void* A, const void* H, const void* dY,

@@ -268,10 +268,8 @@ int tp_swiglu_bwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
                     "tp_swiglu_bwd");
 }
 
-int tp_attn_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
-                      int64_t h_local, int64_t d_head, int causal, float scale,
-                      const void* X, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
-                      void* Q, void* K, void* V, void* O, void* Z) {
+static int attn_common(tp_dtype_t dt, int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t d_head, int causal,
+                float scale) {
   if (dt != TP_DT_BF16) return fail(TP_E_DTYPE, "attention supports TP_DT_BF16 only");
   TP_CHECK(check_dims({{"b", b}, {"s", s}, {"d", d}, {"h_local", h_local}, {"d_head", d_head}}));
   if (d_head != 64 && d_head != 128) return fail(TP_E_DIM, "d_head = %lld; 64 and 128 are supported", (long long)d_head);
@@ -282,15 +280,55 @@ int tp_attn_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t
   TP_CHECK(check_dims({{"b*s", M}, {"h_local*d_head", N}}));
   TP_CHECK(check_ld({{"d", d}, {"h_local*d_head", N}}));
   if (s > kMaxSeq) return fail(TP_E_DIM, "s = %lld exceeds 2^22", (long long)s);
+  return TP_OK;
+}
+
+int tp_attn_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
+                      int64_t h_local, int64_t d_head, int causal, float scale,
+                      const void* X, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                      void* Q, void* K, void* V, void* O, void* Z, float* L) {
+  TP_CHECK(attn_common(dt, b, s, d, h_local, d_head, causal, scale));
+  const int64_t M = b * s, N = h_local * d_head;
   const size_t e = 2;
   TP_CHECK(check_buffers({{"X", X, M * d * e}, {"Wq", Wq, d * N * e}, {"Wk", Wk, d * N * e},
                           {"Wv", Wv, d * N * e}, {"Wo", Wo, N * d * e}},
                          {{"Q", Q, M * N * e}, {"K", K, M * N * e}, {"V", V, M * N * e},
-                          {"O", O, M * N * e}, {"Z", Z, M * d * e}},
+                          {"O", O, M * N * e}, {"Z", Z, M * d * e}, {"L", L, (size_t)(b * h_local * s) * 4}},
                          {"X", "Wq", "Wk", "Wv", "Wo", "Q", "K", "V", "O", "Z"}));
   return hip_status(tpk::launch_attn_fwd(static_cast<hipStream_t>(stream), b, s, d, h_local, d_head, causal,
-                                         scale, X, Wq, Wk, Wv, Wo, Q, K, V, O, Z),
+                                         scale, X, Wq, Wk, Wv, Wo, Q, K, V, O, Z, L),
                     "tp_attn_shard_fwd");
+}
+
+size_t tp_attn_shard_bwd_workspace_bytes(tp_dtype_t dt, int64_t b, int64_t s, int64_t d, int64_t h_local,
+                                         int64_t d_head) {
+  if (attn_common(dt, b, s, d, h_local, d_head, 0, 1.f) != TP_OK) return 0;
+  return tpk::attn_bwd_ws_bytes(b, s, d, h_local, d_head);
+}
+
+int tp_attn_shard_bwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
+                      int64_t h_local, int64_t d_head, int causal, float scale,
+                      const void* X, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                      const void* Q, const void* K, const void* V, const void* O, const float* L,
+                      const void* dY, void* dX, float* dWq, float* dWk, float* dWv, float* dWo,
+                      void* ws, size_t ws_bytes) {
+  TP_CHECK(attn_common(dt, b, s, d, h_local, d_head, causal, scale));
+  if (d_head != 128) return fail(TP_E_DIM, "the attention backward supports d_head = 128");
+  const int64_t M = b * s, N = h_local * d_head;
+  const size_t e = 2, need = tpk::attn_bwd_ws_bytes(b, s, d, h_local, d_head);
+  TP_CHECK(check_buffers(
+      {{"X", X, M * d * e}, {"Wq", Wq, d * N * e}, {"Wk", Wk, d * N * e}, {"Wv", Wv, d * N * e},
+       {"Wo", Wo, N * d * e}, {"Q", Q, M * N * e}, {"K", K, M * N * e}, {"V", V, M * N * e},
+       {"O", O, M * N * e}, {"L", L, (size_t)(b * h_local * s) * 4}, {"dY", dY, M * d * e}},
+      {{"dX", dX, M * d * e}, {"dWq", dWq, d * N * (size_t)4}, {"dWk", dWk, d * N * (size_t)4},
+       {"dWv", dWv, d * N * (size_t)4}, {"dWo", dWo, N * d * (size_t)4}, {"ws", ws, need}},
+      {"X", "Wq", "Wk", "Wv", "Wo", "Q", "K", "V", "O", "L", "dY", "dX", "dWq", "dWk", "dWv", "dWo"}));
+  if (!ws || ws_bytes < need)
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes given, %zu required", ws ? ws_bytes : (size_t)0, need);
+  return hip_status(tpk::launch_attn_bwd(static_cast<hipStream_t>(stream), b, s, d, h_local, d_head, causal,
+                                         scale, X, Wq, Wk, Wv, Wo, Q, K, V, O, L, dY, dX, dWq, dWk, dWv, dWo,
+                                         ws),
+                    "tp_attn_shard_bwd");
 }
 
 int tp_shard_reduce(void* stream, tp_dtype_t dt_in, tp_dtype_t dt_out, int64_t n_shards, int64_t numel,

@@ -33,7 +33,7 @@ def test_header_and_binding_agree_and_library_exports_all():
 
 
 def test_version_and_strerror():
-    assert tp.tp_abi_version() == 1
+    assert tp.tp_abi_version() == 2
     L = tp.lib()
     for code in (OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP):
         assert L.tp_strerror(code) and L.tp_strerror(code) != b"unknown status"
@@ -133,8 +133,31 @@ def _attn(**kw):
     p = _addrs(10)
     args = dict(stream=None, dt=BF16, b=2, s=64, d=64, h_local=2, d_head=128, causal=1, scale=0.0)
     args.update(dict(zip(["X", "Wq", "Wk", "Wv", "Wo", "Q", "K", "V", "O", "Z"], p)))
+    args["L"] = None
     args.update(kw)
     return tp.lib().tp_attn_shard_fwd(*args.values())
+
+
+def _attn_bwd(**kw):
+    p = _addrs(22)
+    args = dict(stream=None, dt=BF16, b=2, s=64, d=64, h_local=2, d_head=128, causal=1, scale=0.0)
+    names = ["X", "Wq", "Wk", "Wv", "Wo", "Q", "K", "V", "O", "L", "dY", "dX", "dWq", "dWk", "dWv", "dWo", "ws"]
+    args.update(dict(zip(names, p)))
+    args["ws_bytes"] = tp.tp_attn_shard_bwd_workspace_bytes(BF16, 2, 64, 64, 2, 128)
+    args.update(kw)
+    return tp.lib().tp_attn_shard_bwd(*args.values())
+
+
+def test_attention_backward_validation():
+    need = tp.tp_attn_shard_bwd_workspace_bytes(BF16, 2, 64, 64, 2, 128)
+    # dO, [dQ|dK|dV], [Wq|Wk|Wv] and D at least
+    assert need >= 128 * 256 * 2 + 128 * 768 * 2 + 64 * 768 * 2 + 2 * 2 * 64 * 4
+    assert tp.tp_attn_shard_bwd_workspace_bytes(F32, 2, 64, 64, 2, 128) == 0
+    assert _attn_bwd(d_head=64) == E_DIM                 # the backward kernels are written for 128
+    assert _attn_bwd(dt=F32) == E_DTYPE
+    assert _attn_bwd(L=None) == E_NULL
+    assert _attn_bwd(ws_bytes=need - 8) == E_WS
+    assert _attn_bwd(ws=None) == E_WS                    # a missing workspace is a workspace error
 
 
 def test_attention_validation():
@@ -179,10 +202,10 @@ def test_row_pitch_and_sequence_limits():
     assert rc == -2
     assert L.tp_swiglu_bwd_workspace_bytes(1, 64, 64, big) == 0
     rc = L.tp_attn_shard_fwd(None, 1, 1, (1 << 22) + 1, 64, 1, 128, 1, 0.0,
-                             fake, fake, fake, fake, fake, fake, fake, fake, fake, fake)
+                             fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, None)
     assert rc == -2 and b"2^22" in L.tp_last_error_detail()
     rc = L.tp_attn_shard_fwd(None, 1, 1, 128, 64, (1 << 21) // 128 + 1, 128, 1, 0.0,
-                             fake, fake, fake, fake, fake, fake, fake, fake, fake, fake)
+                             fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, None)
     assert rc == -2
     # the limits themselves are accepted up to the pointer checks
     rc = L.tp_mlp_fwd(None, 1, 64, 1 << 21, 64, None, fake, fake, None, fake, fake)

@@ -279,14 +279,26 @@ def test_swiglu_c3_full_size_sampled(tp):
 
 # --------------------------------------------------------------- attention
 
-def run_attn(tp, inp, b, s, h_l, dh, causal=True):
+def run_attn(tp, inp, b, s, h_l, dh, causal=True, dY=None):
     X, Wq, Wk, Wv, Wo = (dev(inp[k], "bf16") for k in ("X", "Wq", "Wk", "Wv", "Wo"))
     d = X.shape[1]
     Q, K, V = (empty((b, h_l, s, dh), "bf16") for _ in range(3))
     Ob, Z = empty((b * s, h_l * dh), "bf16"), empty((b * s, d), "bf16")
-    tp.tp_attn_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, Z, b, s, h_l, dh, causal=causal)
+    L = empty((b, h_l, s), "f32")
+    tp.tp_attn_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, Z, b, s, h_l, dh, causal=causal, L=L)
+    out = dict(Q=Q, K=K, V=V, O=Ob, Z=Z, L=L)
+    if dY is not None:
+        dYd = dev(dY, "bf16")
+        dX = empty((b * s, d), "bf16")
+        dWq, dWk, dWv = (empty((d, h_l * dh), "f32") for _ in range(3))
+        dWo = empty((h_l * dh, d), "f32")
+        ws = torch.empty(tp.tp_attn_shard_bwd_workspace_bytes(tp.TP_DT_BF16, b, s, d, h_l, dh),
+                         dtype=torch.uint8, device="cuda")
+        tp.tp_attn_shard_bwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, L, dYd, dX, dWq, dWk, dWv, dWo, ws,
+                             b, s, h_l, dh, causal=causal)
+        out.update(dX=dX, dWq=dWq, dWk=dWk, dWv=dWv, dWo=dWo)
     torch.cuda.synchronize()
-    return dict(Q=Q, K=K, V=V, O=Ob, Z=Z)
+    return out
 
 
 @pytest.mark.parametrize("b,s,d,h_l,dh,causal", [
@@ -303,6 +315,37 @@ def test_attention_small_shapes(tp, b, s, d, h_l, dh, causal):
     ref = O.attn_shard_fwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], b, s, h_l, dh, causal)
     for k in ("Q", "K", "V", "O", "Z"):
         check(k, out[k], ref[k], "bf16")
+    # L is fp32 from bf16 Q, K: an absolute error relative to the score scale
+    assert np.abs(host(out["L"]) - ref["L"]).max() < 2e-2 * max(1.0, np.abs(ref["L"]).max())
+
+
+@pytest.mark.parametrize("b,s,d,h_l,causal", [
+    (2, 200, 64, 2, True),           # ragged sequence
+    (2, 130, 72, 1, False),
+    (1, 1, 32, 2, True),             # one token: only V gets gradient
+    (1, 257, 96, 2, True),           # ragged key tile and query chunk
+    (1, 384, 64, 1, True),           # several key tiles, query chunks and dQ tiles
+])
+def test_attention_bwd_small_shapes(tp, b, s, d, h_l, causal):
+    dh = 128
+    _say(f"attention bwd b={b} s={s} d={d} h_l={h_l} causal={causal}")
+    inp = tpsynth.random_attn(b, s, d, h_l, dh, "bf16", seed=7 * s + d, w_std=0.1)
+    dY = tpsynth.round_to_bf16(np.random.default_rng(s + 1).standard_normal((b * s, d)).astype(np.float32))
+    out = run_attn(tp, inp, b, s, h_l, dh, causal, dY=dY)
+    ref = O.attn_shard_bwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], dY, b, s, h_l, dh, causal)
+    for k in ("dX", "dWq", "dWk", "dWv", "dWo"):
+        check(k, out[k], ref[k], "bf16")
+
+
+def test_attention_bwd_deterministic(tp):
+    _say("attention bwd bitwise deterministic")
+    b, s, d, h_l, dh = 1, 256, 64, 2, 128
+    inp = tpsynth.random_attn(b, s, d, h_l, dh, "bf16", seed=3, w_std=0.1)
+    dY = tpsynth.round_to_bf16(np.random.default_rng(4).standard_normal((b * s, d)).astype(np.float32))
+    a = run_attn(tp, inp, b, s, h_l, dh, True, dY=dY)
+    c = run_attn(tp, inp, b, s, h_l, dh, True, dY=dY)
+    for k in ("dX", "dWq", "dWk", "dWv", "dWo"):
+        assert torch.equal(a[k], c[k]), k
 
 
 def test_attention_shards_sum_to_unsharded(tp):
@@ -337,3 +380,25 @@ def test_attention_c4_full_size_sampled(tp):
     rows = _sample(s, 32, 31)                  # batch 0: sampled query rows
     ref0 = O.attn_shard_fwd(inp["X"][:s], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], 1, s, h_l, dh)
     check("O[b0]", host(out["O"])[rows], ref0["O"][rows], "bf16")
+
+
+def test_attention_bwd_c4_full_size_sampled(tp):
+    # C4 shapes: dX for one batch row over all heads; dW for one head over
+    # all batch rows (head j's weight gradients depend on head j alone).
+    _say("attention bwd C4 bf16 full size: dX of one batch row, dW of one head")
+    wl = tpsynth.WORKLOADS["C4"]
+    inp = tpsynth.attn_inputs(wl)
+    b, s, h_l, dh = wl.b, wl.s, wl.h_local, wl.d_head
+    dY = tpsynth.round_to_bf16(np.random.default_rng(44).standard_normal((b * s, wl.d)).astype(np.float32))
+    out = run_attn(tp, inp, b, s, h_l, dh, True, dY=dY)
+    bi = 1
+    rows = slice(bi * s, (bi + 1) * s)
+    ref = O.attn_shard_bwd(inp["X"][rows], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], dY[rows], 1, s, h_l, dh)
+    check("dX", host(out["dX"])[rows], ref["dX"], "bf16")
+    j = 5
+    cols = slice(j * dh, (j + 1) * dh)
+    refh = O.attn_shard_bwd(inp["X"], inp["Wq"][:, cols], inp["Wk"][:, cols], inp["Wv"][:, cols],
+                            inp["Wo"][cols], dY, b, s, 1, dh)
+    for k in ("dWq", "dWk", "dWv"):
+        check(k, host(out[k])[:, cols], refh[k], "bf16")
+    check("dWo", host(out["dWo"])[cols], refh["dWo"], "bf16")
