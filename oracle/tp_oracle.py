@@ -47,6 +47,7 @@ __all__ = [
     "mlp_shard_fwd", "mlp_shard_bwd", "mlp_unsharded", "mlp_unsharded_bwd",
     "swiglu_shard_fwd", "swiglu_shard_bwd", "swiglu_unsharded",
     "attn_shard_fwd", "attn_unsharded", "attn_core", "attn_core_lse", "attn_core_bwd", "attn_shard_bwd",
+    "attn_gqa_shard_fwd", "attn_gqa_query_rows",
     "shard_reduce", "shard_range",
 ]
 
@@ -297,6 +298,56 @@ def attn_shard_bwd(X, Wq, Wk, Wv, Wo, dY, b: int, s: int, h_local: int, d_head: 
     return {"dO": dO, "dQ": dQ, "dK": dK, "dV": dV,
             "dX": dQ @ _f64(Wq).T + dK @ _f64(Wk).T + dV @ _f64(Wv).T,
             "dWq": X2.T @ dQ, "dWk": X2.T @ dK, "dWv": X2.T @ dV, "dWo": f["O"].T @ dY}
+
+
+def attn_gqa_shard_fwd(X, Wq, Wk, Wv, Wo, b: int, s: int, h_local: int, h_kv: int, d_head: int,
+                       causal: bool = True, scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Grouped-query attention shard ([HC] 3.4, the Llama-3 example: the
+    shard's query heads share its key/value heads in equal groups).  Query
+    head j uses columns [j*d_h, (j+1)*d_h) of W_Q and K/V head j // (h_local /
+    h_kv), i.e. columns [g*d_h, (g+1)*d_h) of W_K and W_V; everything else is
+    attn_shard_fwd.  Returns Q [b, h_local, s, d_h], K and V [b, h_kv, s, d_h],
+    O, Z and L as attn_shard_fwd."""
+    assert h_local % h_kv == 0
+    group = h_local // h_kv
+    X = _f64(X).reshape(b, s, -1)
+    Q = _split_heads(X @ _f64(Wq), b, s, h_local, d_head)
+    K = _split_heads(X @ _f64(Wk), b, s, h_kv, d_head)
+    V = _split_heads(X @ _f64(Wv), b, s, h_kv, d_head)
+    O = np.empty((b, s, h_local, d_head))
+    L = np.empty((b, h_local, s))
+    for bi in range(b):
+        for j in range(h_local):
+            O[bi, :, j, :], L[bi, j] = attn_core_lse(Q[bi, j], K[bi, j // group], V[bi, j // group], causal, scale)
+    O = O.reshape(b * s, h_local * d_head)
+    return {"Q": Q, "K": K, "V": V, "O": O, "Z": O @ _f64(Wo), "L": L}
+
+
+def attn_gqa_query_rows(Xb, Wq, Wk, Wv, Wo, rows, h_local: int, h_kv: int, d_head: int,
+                        causal: bool = True, scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """attn_gqa_shard_fwd for one batch row Xb [s x d], evaluated only at the
+    query positions `rows` (each query still sees every allowed key of the
+    row): O[rows] and Z[rows], by the same definitions."""
+    Xb = _f64(Xb)
+    rows = np.asarray(rows)
+    s = Xb.shape[0]
+    group = h_local // h_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_head)
+    Qr = (Xb[rows] @ _f64(Wq)).reshape(len(rows), h_local, d_head)
+    K = (Xb @ _f64(Wk)).reshape(s, h_kv, d_head)
+    V = (Xb @ _f64(Wv)).reshape(s, h_kv, d_head)
+    O = np.empty((len(rows), h_local, d_head))
+    for j in range(h_local):
+        Kj, Vj = K[:, j // group], V[:, j // group]
+        S = (Qr[:, j] @ Kj.T) * scale
+        if causal:
+            S = np.where(np.arange(s)[None, :] <= rows[:, None], S, -np.inf)
+        S = S - S.max(axis=1, keepdims=True)
+        P = np.exp(S)
+        O[:, j] = (P / P.sum(axis=1, keepdims=True)) @ Vj
+    O = O.reshape(len(rows), h_local * d_head)
+    return {"O": O, "Z": O @ _f64(Wo)}
 
 
 def attn_unsharded(X, Wq, Wk, Wv, Wo, b: int, s: int, heads: int, d_head: int,

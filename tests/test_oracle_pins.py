@@ -308,6 +308,47 @@ def test_online_softmax_tiling_equals_direct_softmax():
     np.testing.assert_allclose(out, O.attn_core(Q, K, V), rtol=1e-13, atol=1e-14)
 
 
+# ------------------------------------------------------------------ GQA
+
+def test_gqa_with_one_group_is_mha():
+    b, s, d, h, dh = 2, 7, 12, 3, 4
+    inp = tpsynth.random_attn(b, s, d, h, dh, "f32", seed=60, w_std=0.3)
+    g = O.attn_gqa_shard_fwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], b, s, h, h, dh)
+    m = O.attn_shard_fwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], b, s, h, dh)
+    for k in ("O", "Z", "L"):
+        np.testing.assert_allclose(g[k], m[k], rtol=1e-13, atol=1e-14)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    # Sharing a K/V head among a group of query heads is the same as giving
+    # every query head its own copy of that K/V projection.
+    b, s, d, h, hkv, dh = 1, 9, 16, 6, 2, 4
+    rng = np.random.default_rng(61)
+    X = rng.standard_normal((b * s, d))
+    Wq = rng.standard_normal((d, h * dh)) * 0.3
+    Wk = rng.standard_normal((d, hkv * dh)) * 0.3
+    Wv = rng.standard_normal((d, hkv * dh)) * 0.3
+    Wo = rng.standard_normal((h * dh, d)) * 0.3
+    rep = lambda W: np.concatenate([W[:, (j // (h // hkv)) * dh:(j // (h // hkv) + 1) * dh] for j in range(h)], axis=1)
+    g = O.attn_gqa_shard_fwd(X, Wq, Wk, Wv, Wo, b, s, h, hkv, dh)
+    m = O.attn_shard_fwd(X, Wq, rep(Wk), rep(Wv), Wo, b, s, h, dh)
+    for k in ("O", "Z", "L"):
+        np.testing.assert_allclose(g[k], m[k], rtol=1e-13, atol=1e-14)
+
+
+def test_gqa_query_rows_match_full():
+    b, s, d, h, hkv, dh = 1, 11, 16, 4, 1, 4
+    rng = np.random.default_rng(62)
+    X = rng.standard_normal((s, d))
+    Wq, Wk, Wv = (rng.standard_normal((d, n * dh)) * 0.3 for n in (h, hkv, hkv))
+    Wo = rng.standard_normal((h * dh, d)) * 0.3
+    full = O.attn_gqa_shard_fwd(X, Wq, Wk, Wv, Wo, 1, s, h, hkv, dh)
+    rows = [0, 3, 10]
+    r = O.attn_gqa_query_rows(X, Wq, Wk, Wv, Wo, rows, h, hkv, dh)
+    np.testing.assert_allclose(r["O"], full["O"][rows], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(r["Z"], full["Z"][rows], rtol=1e-13, atol=1e-14)
+
+
 # ------------------------------------------------------- attention backward
 
 @pytest.mark.parametrize("causal", [True, False])

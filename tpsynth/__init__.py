@@ -14,6 +14,11 @@ R^{d x h d_h}):
 * ``C3`` SwiGLU bf16 shard, b 4, s 2048, d 4096, d_ff 11008, 4 shards.
 * ``C4`` causal attention bf16 shard, b 4, s 2048, 32 heads of 128, 4 shards.
 * ``C5`` large GeLU MLP bf16 shard, b 2, s 4096, d 8192, d_ff 32768, 8 shards.
+* ``G1`` grouped-query causal attention bf16 shard shaped as the Llama-3-405B
+  example of "Splitting the model" section 3.4 at TP 8: d 16384, 128 query
+  heads and 8 key/value heads of 128, so one GPU holds 16 query heads sharing
+  1 key/value head (W_Q [16384 x 2048], W_K and W_V [16384 x 128]); b 2,
+  s 4096 like C5.
 
 Recipe: ``numpy.random.default_rng(seed)`` (PCG64); normals drawn in float64,
 scaled by the stated standard deviation, cast to float32, and for bf16
@@ -32,7 +37,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "round_to_bf16", "normal",
     "mlp_inputs", "swiglu_inputs", "attn_inputs", "reduce_inputs",
-    "random_mlp", "random_swiglu", "random_attn",
+    "random_mlp", "random_swiglu", "random_attn", "gqa_inputs", "random_gqa",
 ]
 
 
@@ -48,6 +53,7 @@ class Workload:
     d_ff: int = 0
     heads: int = 0
     d_head: int = 0
+    kv_heads: int = 0            # grouped-query attention: key/value heads (0: = heads)
     w_std: float = 0.02
     full_weights: bool = False   # draw every shard's weights (else shard 0 only)
     backward: bool = True
@@ -65,6 +71,10 @@ class Workload:
     def h_local(self) -> int:
         return self.heads // self.n_shards
 
+    @property
+    def h_kv_local(self) -> int:
+        return (self.kv_heads or self.heads) // self.n_shards
+
 
 WORKLOADS: Dict[str, Workload] = {
     "C1": Workload("C1", "mlp", "f32", b=1, s=32, d=64, d_ff=256, n_shards=2,
@@ -80,6 +90,9 @@ WORKLOADS: Dict[str, Workload] = {
                    description="causal self-attention, 8 of 32 heads of 128"),
     "C5": Workload("C5", "mlp", "bf16", b=2, s=4096, d=8192, d_ff=32768, n_shards=8,
                    w_std=0.01, description="large GeLU MLP shard, TP 8, slice 4096"),
+    "G1": Workload("G1", "gqa", "bf16", b=2, s=4096, d=16384, heads=128, kv_heads=8, d_head=128,
+                   n_shards=8, w_std=0.01, backward=False,
+                   description="grouped-query causal attention shard, 16 query heads sharing 1 KV head"),
 }
 
 
@@ -159,6 +172,24 @@ def attn_inputs(wl: Workload, seed: int = 0) -> dict:
     Wk = normal(rng, (wl.d, hd), wl.w_std, wl.dtype)
     Wv = normal(rng, (wl.d, hd), wl.w_std, wl.dtype)
     Wo = normal(rng, (hd, wl.d), wl.w_std, wl.dtype)
+    return {"X": X, "Wq": Wq, "Wk": Wk, "Wv": Wv, "Wo": Wo}
+
+
+def gqa_inputs(wl: Workload, seed: int = 0) -> dict:
+    """Grouped-query shard inputs: X[b*s x d], W_Q [d x h_l*d_h],
+    W_K/W_V [d x h_kv*d_h], W_O [h_l*d_h x d]; draw order X, W_Q, W_K, W_V, W_O."""
+    assert wl.kind == "gqa"
+    return random_gqa(wl.b, wl.s, wl.d, wl.h_local, wl.h_kv_local, wl.d_head, wl.dtype, seed, wl.w_std)
+
+
+def random_gqa(b: int, s: int, d: int, h_local: int, h_kv: int, d_head: int, dtype: str,
+               seed: int = 0, w_std: float = 0.02) -> dict:
+    rng = np.random.default_rng(seed)
+    X = normal(rng, (b * s, d), 1.0, dtype)
+    Wq = normal(rng, (d, h_local * d_head), w_std, dtype)
+    Wk = normal(rng, (d, h_kv * d_head), w_std, dtype)
+    Wv = normal(rng, (d, h_kv * d_head), w_std, dtype)
+    Wo = normal(rng, (h_local * d_head, d), w_std, dtype)
     return {"X": X, "Wq": Wq, "Wk": Wk, "Wv": Wv, "Wo": Wo}
 
 
