@@ -341,6 +341,36 @@ def run_c4(tp, torch, steps, warmup):
             "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in list(per_f.items()) + list(per_b.items())}}
 
 
+def run_g1(tp, torch, steps, warmup):
+    import tpsynth
+    wl = tpsynth.WORKLOADS["G1"]
+    inp = tpsynth.gqa_inputs(wl)
+    bf = torch.bfloat16
+    dev = lambda a: torch.from_numpy(a).to(bf).cuda()
+    b, s, d, hl, hkv, dh = wl.b, wl.s, wl.d, wl.h_local, wl.h_kv_local, wl.d_head
+    X, Wq, Wk, Wv, Wo = (dev(inp[k]) for k in ("X", "Wq", "Wk", "Wv", "Wo"))
+    del inp
+    Q = torch.empty((b, hl, s, dh), dtype=bf, device="cuda")
+    K, V = (torch.empty((b, hkv, s, dh), dtype=bf, device="cuda") for _ in range(2))
+    Ob = torch.empty((b * s, hl * dh), dtype=bf, device="cuda")
+    Z = torch.empty((b * s, d), dtype=bf, device="cuda")
+
+    def step():
+        tp.tp_attn_gqa_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, Z, b, s, hl, hkv, dh, causal=True)
+
+    ms, _, per = timed(tp, torch, step, steps, warmup, 4)
+    M, N, Nkv = b * s, hl * dh, hkv * dh
+    core = 2 * 2.0 * b * hl * (s * (s + 1) / 2) * dh
+    flops = gemm_flops(M, N, d) + 2 * gemm_flops(M, Nkv, d) + core + gemm_flops(M, d, N)
+    core_ms = [sum(v) / len(v) for k, v in per.items() if k in ("attn.core_d128", "attn.core_d64")]
+    return {"workload": "G1 grouped-query causal attention shard (Llama-3-405B TP-8 slice): b 2 s 4096 d 16384, "
+                        "16 query heads sharing 1 KV head of 128, fwd",
+            "ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+            "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "core_tflops": round(core / core_ms[0] / 1e9, 1) if core_ms else None,
+            "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in per.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,7 +446,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         wls = {}
-        for name, fn in (("C2", run_c2), ("C3", run_c3), ("C4", run_c4)):
+        for name, fn in (("C2", run_c2), ("C3", run_c3), ("C4", run_c4), ("G1", run_g1)):
             log(f"timing {name}")
             wls[name] = fn(tp, torch, args.extra_steps, 2)
             torch.cuda.empty_cache()

@@ -159,6 +159,20 @@ int tp_attn_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t
                       float* L);
 
 /* ---------------------------------------------------------------------------
+ * tp_attn_gqa_shard_fwd — grouped-query attention shard forward ([HC] 3.4,
+ * the Llama-3 example: a GPU's query heads share its key/value heads).  As
+ * tp_attn_shard_fwd, except that Wk and Wv are [d x h_kv_local*d_head], K and
+ * V are [b, h_kv_local, s, d_head], and local query head j attends with
+ * key/value head j / (h_local / h_kv_local).  h_kv_local must divide h_local
+ * (TP_E_DIVIS); h_kv_local = h_local is tp_attn_shard_fwd.
+ * ------------------------------------------------------------------------- */
+int tp_attn_gqa_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
+                          int64_t h_local, int64_t h_kv_local, int64_t d_head, int causal, float scale,
+                          const void* X, const void* Wq, const void* Wk, const void* Wv,
+                          const void* Wo, void* Q, void* K, void* V, void* O, void* Z,
+                          float* L);
+
+/* ---------------------------------------------------------------------------
  * tp_attn_shard_bwd — backward of the attention shard.  The input passes
  * [BM] Megatron_f (identity forward, all-reduce backward), so dX is this
  * shard's summand of the full dX (summed over shards by the f all-reduce,

@@ -16,7 +16,7 @@ __all__ = [
     "TPError", "lib", "LIB_PATH", "TP_DT_F32", "TP_DT_BF16",
     "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_workspace_bytes",
     "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes",
-    "tp_attn_shard_fwd", "tp_attn_shard_bwd", "tp_attn_shard_bwd_workspace_bytes",
+    "tp_attn_shard_fwd", "tp_attn_gqa_shard_fwd", "tp_attn_shard_bwd", "tp_attn_shard_bwd_workspace_bytes",
     "tp_shard_reduce", "tp_shard_range",
     "tp_abi_version", "EXPORTS",
 ]
@@ -46,6 +46,8 @@ EXPORTS = {
     "tp_swiglu_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
     "tp_attn_shard_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _i64, _i32, ctypes.c_float]
                           + [_p] * 5 + [_p] * 5 + [_p]),
+    "tp_attn_gqa_shard_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i32, ctypes.c_float]
+                              + [_p] * 5 + [_p] * 5 + [_p]),
     "tp_attn_shard_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _i64, _i32, ctypes.c_float]
                           + [_p] * 5 + [_p] * 5 + [_p] + [_p] * 5 + [_p, _sz]),
     "tp_attn_shard_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i64, _i64]),
@@ -169,6 +171,14 @@ def tp_attn_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, O, Z, b: int, s: int, h_local:
     _check(lib().tp_attn_shard_fwd(_stream(stream), _dt(X), b, s, d, h_local, d_head, int(causal),
                                    float(scale), _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo),
                                    _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(Z), _ptr(L)))
+
+
+def tp_attn_gqa_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, O, Z, b: int, s: int, h_local: int, h_kv_local: int,
+                          d_head: int, causal: bool = True, scale: float = 0.0, L=None, stream=None) -> None:
+    d = X.shape[1]
+    _check(lib().tp_attn_gqa_shard_fwd(_stream(stream), _dt(X), b, s, d, h_local, h_kv_local, d_head, int(causal),
+                                       float(scale), _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo),
+                                       _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(Z), _ptr(L)))
 
 
 def tp_attn_shard_bwd_workspace_bytes(dtype: int, b: int, s: int, d: int, h_local: int, d_head: int) -> int:

@@ -37,7 +37,7 @@ template <int D>
 __global__ void __launch_bounds__(256)
 flash_attn_fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                       const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ L,
-                      int nb, int hl, int s, int causal, float scale_log2) {
+                      int nb, int hl, int group, int s, int causal, float scale_log2) {
   constexpr int BQ = 128, BKV = 64, NT = 256;
   constexpr int LDK = D + 8;     // K tile: BKV rows of D
   constexpr int LDV = BKV + 8;   // V^T tile: D rows of BKV
@@ -55,9 +55,11 @@ flash_attn_fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, g = lane >> 5;
   const int64_t head = (int64_t)bh * s * D;
+  // grouped-query attention: query head h reads key/value head h / group
+  const int64_t kvhead = ((int64_t)bi * (hl / group) + h / group) * s * D;
   const bf16* Qh = Q + head;
-  const bf16* Kh = K + head;
-  const bf16* Vh = V + head;
+  const bf16* Kh = K + kvhead;
+  const bf16* Vh = V + kvhead;
   const int q0 = qt * BQ;
   const int qw = q0 + w * 32;       // first query of this wave
   const int qme = qw + lq;          // this lane's query
@@ -251,7 +253,7 @@ __device__ __forceinline__ bf16x8 frag_v(const char* vt, int d0, int kvb, int la
 __global__ void __launch_bounds__(256, 2)
 flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                            const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ L,
-                           int nb, int hl, int s, int causal, float scale_log2) {
+                           int nb, int hl, int group, int s, int causal, float scale_log2) {
   using namespace attn128;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
@@ -273,8 +275,10 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, g = lane >> 5;
   const int64_t head = (int64_t)bh * s * D;
-  const bf16* Kh = K + head;
-  const bf16* Vh = V + head;
+  // grouped-query attention: query head h reads key/value head h / group
+  const int64_t kvhead = ((int64_t)bi * (hl / group) + h / group) * s * D;
+  const bf16* Kh = K + kvhead;
+  const bf16* Vh = V + kvhead;
   const int q0 = qt * BQ;
   const int qw = q0 + wave * 32;    // first query of this wave
   const int qme = qw + lq;          // this lane's query
@@ -395,12 +399,12 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   }
 }
 
-hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local,
+hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv,
                            int64_t d_head, int causal, float scale,
                            const void* X, const void* Wq, const void* Wk, const void* Wv,
                            const void* Wo, void* Q, void* K, void* V, void* O, void* Z, float* L) {
-  const int64_t M = b * s, N = h_local * d_head;
-  {  // Q, K, V = X W{q,k,v}, scattered to [b, h_local, s, d_head]
+  const int64_t M = b * s, N = h_local * d_head, Nkv = h_kv * d_head;
+  if (h_kv == h_local) {  // Q, K, V = X W{q,k,v}, one batched product scattered to [b, h_local, s, d_head]
     GemmParams p = make_params(M, N, make_seg(X, d, M * d, Wq, N, d * N, d));
     p.Bz[0] = static_cast<const bf16*>(Wq);
     p.Bz[1] = static_cast<const bf16*>(Wk);
@@ -408,22 +412,34 @@ hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
     EpiHeadScatter<bf16> e{{static_cast<bf16*>(Q), static_cast<bf16*>(K), static_cast<bf16*>(V)},
                            (int)s, (int)h_local, (int)d_head};
     TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wqkv_scatter", p, e, plan_gemm(M, 3 * N, d, false, false), 3)));
+  } else {  // grouped-query: Q over h_local heads, then K and V over h_kv heads
+    GemmParams pq = make_params(M, N, make_seg(X, d, M * d, Wq, N, d * N, d));
+    EpiHeadScatter<bf16> eq{{static_cast<bf16*>(Q), nullptr, nullptr}, (int)s, (int)h_local, (int)d_head};
+    TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wq_scatter", pq, eq, plan_gemm(M, N, d, false, false), 1)));
+    GemmParams pk = make_params(M, Nkv, make_seg(X, d, M * d, Wk, Nkv, d * Nkv, d));
+    pk.Bz[0] = static_cast<const bf16*>(Wk);
+    pk.Bz[1] = static_cast<const bf16*>(Wv);
+    EpiHeadScatter<bf16> ek{{static_cast<bf16*>(K), static_cast<bf16*>(V), nullptr}, (int)s, (int)h_kv,
+                            (int)d_head};
+    TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wkv_scatter", pk, ek,
+                                              plan_gemm(M, 2 * Nkv, d, false, false), 2)));
   }
   {
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d_head);
     const float sl2 = sc * 1.4426950408889634f;
     const int64_t nqt = (s + 127) / 128;
     const dim3 grid((unsigned)(nqt * b * h_local));
+    const int group = (int)(h_local / h_kv);
     const bf16* q = static_cast<const bf16*>(Q);
     const bf16* k = static_cast<const bf16*>(K);
     const bf16* v = static_cast<const bf16*>(V);
     bf16* o = static_cast<bf16*>(O);
     if (d_head == 128)
       TPK_TRY(launch("attn.core_d128", flash_attn_fwd_d128_kernel, grid, dim3(256), st, q, k, v, o, L, (int)b,
-                     (int)h_local, (int)s, causal, sl2));
+                     (int)h_local, group, (int)s, causal, sl2));
     else
       TPK_TRY(launch("attn.core_d64", flash_attn_fwd_kernel<64>, grid, dim3(256), st, q, k, v, o, L, (int)b,
-                     (int)h_local, (int)s, causal, sl2));
+                     (int)h_local, group, (int)s, causal, sl2));
   }
   {  // Z = O Wo (this shard's partial)
     GemmParams p = make_params(M, d, make_seg(O, N, M * N, Wo, d, N * d, N));

@@ -31,7 +31,7 @@ hipError_t launch_swiglu_bwd(hipStream_t st, int dt, int64_t M, int64_t d, int64
                              const void* G, const void* U, const void* H, const void* dY,
                              void* dX, float* dW1, float* dW3, float* dW2, void* ws);
 
-hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local,
+hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv,
                            int64_t d_head, int causal, float scale,
                            const void* X, const void* Wq, const void* Wk, const void* Wv,
                            const void* Wo, void* Q, void* K, void* V, void* O, void* Z, float* L);

@@ -283,21 +283,39 @@ static int attn_common(tp_dtype_t dt, int64_t b, int64_t s, int64_t d, int64_t h
   return TP_OK;
 }
 
+static int attn_fwd_impl(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d, int64_t h_local,
+                         int64_t h_kv, int64_t d_head, int causal, float scale, const void* X, const void* Wq,
+                         const void* Wk, const void* Wv, const void* Wo, void* Q, void* K, void* V, void* O,
+                         void* Z, float* L, const char* what) {
+  TP_CHECK(attn_common(dt, b, s, d, h_local, d_head, causal, scale));
+  if (h_kv <= 0 || h_kv > h_local || h_local % h_kv)
+    return fail(TP_E_DIVIS, "h_kv_local = %lld must divide h_local = %lld", (long long)h_kv, (long long)h_local);
+  const int64_t M = b * s, N = h_local * d_head, Nkv = h_kv * d_head;
+  const size_t e = 2;
+  TP_CHECK(check_buffers({{"X", X, M * d * e}, {"Wq", Wq, d * N * e}, {"Wk", Wk, d * Nkv * e},
+                          {"Wv", Wv, d * Nkv * e}, {"Wo", Wo, N * d * e}},
+                         {{"Q", Q, M * N * e}, {"K", K, M * Nkv * e}, {"V", V, M * Nkv * e},
+                          {"O", O, M * N * e}, {"Z", Z, M * d * e}, {"L", L, (size_t)(b * h_local * s) * 4}},
+                         {"X", "Wq", "Wk", "Wv", "Wo", "Q", "K", "V", "O", "Z"}));
+  return hip_status(tpk::launch_attn_fwd(static_cast<hipStream_t>(stream), b, s, d, h_local, h_kv, d_head, causal,
+                                         scale, X, Wq, Wk, Wv, Wo, Q, K, V, O, Z, L),
+                    what);
+}
+
 int tp_attn_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
                       int64_t h_local, int64_t d_head, int causal, float scale,
                       const void* X, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
                       void* Q, void* K, void* V, void* O, void* Z, float* L) {
-  TP_CHECK(attn_common(dt, b, s, d, h_local, d_head, causal, scale));
-  const int64_t M = b * s, N = h_local * d_head;
-  const size_t e = 2;
-  TP_CHECK(check_buffers({{"X", X, M * d * e}, {"Wq", Wq, d * N * e}, {"Wk", Wk, d * N * e},
-                          {"Wv", Wv, d * N * e}, {"Wo", Wo, N * d * e}},
-                         {{"Q", Q, M * N * e}, {"K", K, M * N * e}, {"V", V, M * N * e},
-                          {"O", O, M * N * e}, {"Z", Z, M * d * e}, {"L", L, (size_t)(b * h_local * s) * 4}},
-                         {"X", "Wq", "Wk", "Wv", "Wo", "Q", "K", "V", "O", "Z"}));
-  return hip_status(tpk::launch_attn_fwd(static_cast<hipStream_t>(stream), b, s, d, h_local, d_head, causal,
-                                         scale, X, Wq, Wk, Wv, Wo, Q, K, V, O, Z, L),
-                    "tp_attn_shard_fwd");
+  return attn_fwd_impl(stream, dt, b, s, d, h_local, h_local, d_head, causal, scale, X, Wq, Wk, Wv, Wo, Q, K, V,
+                       O, Z, L, "tp_attn_shard_fwd");
+}
+
+int tp_attn_gqa_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
+                          int64_t h_local, int64_t h_kv_local, int64_t d_head, int causal, float scale,
+                          const void* X, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                          void* Q, void* K, void* V, void* O, void* Z, float* L) {
+  return attn_fwd_impl(stream, dt, b, s, d, h_local, h_kv_local, d_head, causal, scale, X, Wq, Wk, Wv, Wo, Q, K,
+                       V, O, Z, L, "tp_attn_gqa_shard_fwd");
 }
 
 size_t tp_attn_shard_bwd_workspace_bytes(tp_dtype_t dt, int64_t b, int64_t s, int64_t d, int64_t h_local,

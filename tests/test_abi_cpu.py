@@ -210,3 +210,14 @@ def test_row_pitch_and_sequence_limits():
     # the limits themselves are accepted up to the pointer checks
     rc = L.tp_mlp_fwd(None, 1, 64, 1 << 21, 64, None, fake, fake, None, fake, fake)
     assert rc == -1
+
+
+def test_gqa_validation():
+    L = tp.lib()
+    p = _addrs(11)
+    # h_kv_local must divide h_local
+    assert L.tp_attn_gqa_shard_fwd(None, BF16, 1, 64, 64, 6, 4, 128, 1, 0.0, *p[:10], None) == E_DIVIS
+    assert L.tp_attn_gqa_shard_fwd(None, BF16, 1, 64, 64, 4, 0, 128, 1, 0.0, *p[:10], None) == E_DIVIS
+    assert L.tp_attn_gqa_shard_fwd(None, BF16, 1, 64, 64, 4, 8, 128, 1, 0.0, *p[:10], None) == E_DIVIS
+    assert L.tp_attn_gqa_shard_fwd(None, F32, 1, 64, 64, 4, 2, 128, 1, 0.0, *p[:10], None) == E_DTYPE
+    assert L.tp_attn_gqa_shard_fwd(None, BF16, 1, 64, 64, 4, 2, 128, 1, 0.0, None, *p[1:10], None) == E_NULL

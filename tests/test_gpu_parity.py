@@ -402,3 +402,48 @@ def test_attention_bwd_c4_full_size_sampled(tp):
     for k in ("dWq", "dWk", "dWv"):
         check(k, host(out[k])[:, cols], refh[k], "bf16")
     check("dWo", host(out["dWo"])[cols], refh["dWo"], "bf16")
+
+
+# ------------------------------------------------------- grouped-query attention
+
+def run_gqa(tp, inp, b, s, h_l, h_kv, dh, causal=True):
+    X, Wq, Wk, Wv, Wo = (dev(inp[k], "bf16") for k in ("X", "Wq", "Wk", "Wv", "Wo"))
+    d = X.shape[1]
+    Q = empty((b, h_l, s, dh), "bf16")
+    K, V = (empty((b, h_kv, s, dh), "bf16") for _ in range(2))
+    Ob, Z = empty((b * s, h_l * dh), "bf16"), empty((b * s, d), "bf16")
+    L = empty((b, h_l, s), "f32")
+    tp.tp_attn_gqa_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, Z, b, s, h_l, h_kv, dh, causal=causal, L=L)
+    torch.cuda.synchronize()
+    return dict(Q=Q, K=K, V=V, O=Ob, Z=Z, L=L)
+
+
+@pytest.mark.parametrize("b,s,d,h_l,h_kv,dh,causal", [
+    (2, 200, 64, 4, 2, 128, True),
+    (1, 257, 96, 4, 1, 128, True),
+    (2, 130, 64, 6, 3, 64, False),
+    (1, 64, 72, 16, 1, 128, True),    # the G1 grouping, 16 query heads on one K/V head
+])
+def test_gqa_small_shapes(tp, b, s, d, h_l, h_kv, dh, causal):
+    _say(f"gqa b={b} s={s} d={d} h_l={h_l} h_kv={h_kv} dh={dh} causal={causal}")
+    inp = tpsynth.random_gqa(b, s, d, h_l, h_kv, dh, "bf16", seed=s + h_l, w_std=0.1)
+    out = run_gqa(tp, inp, b, s, h_l, h_kv, dh, causal)
+    ref = O.attn_gqa_shard_fwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], b, s, h_l, h_kv, dh, causal)
+    for k in ("Q", "K", "V", "O", "Z"):
+        check(k, out[k], ref[k], "bf16")
+
+
+def test_gqa_g1_full_size_sampled(tp):
+    # G1 (d 16384, 16 query heads on 1 K/V head, b 2, s 4096): sampled query
+    # rows of each batch row, every head, against the definition at those rows.
+    _say("gqa G1 bf16 full size, sampled queries")
+    wl = tpsynth.WORKLOADS["G1"]
+    inp = tpsynth.gqa_inputs(wl)
+    b, s, h_l, h_kv, dh = wl.b, wl.s, wl.h_local, wl.h_kv_local, wl.d_head
+    out = run_gqa(tp, inp, b, s, h_l, h_kv, dh)
+    for bi in range(b):
+        rows = np.unique(np.concatenate([_sample(s, 12, 70 + bi), [0, s - 1]]))
+        Xb = inp["X"][bi * s:(bi + 1) * s]
+        ref = O.attn_gqa_query_rows(Xb, inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], rows, h_l, h_kv, dh)
+        check(f"O[b{bi}]", host(out["O"])[bi * s + rows], ref["O"], "bf16")
+        check(f"Z[b{bi}]", host(out["Z"])[bi * s + rows], ref["Z"], "bf16")
