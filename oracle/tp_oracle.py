@@ -49,6 +49,7 @@ __all__ = [
     "attn_shard_fwd", "attn_unsharded", "attn_core", "attn_core_lse", "attn_core_bwd", "attn_shard_bwd",
     "attn_gqa_shard_fwd", "attn_gqa_query_rows",
     "shard_reduce", "shard_range",
+    "stripe_rows", "reduce_scatter", "all_gather", "layer_norm", "sp_block_end",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -375,6 +376,54 @@ def shard_reduce(partials: Sequence, bias=None) -> np.ndarray:
         flat += np.resize(bias, flat.shape)   # element e gets bias[e % len]
         out = flat.reshape(out.shape)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Sequence parallelism ([HC] 3.4, Figure 3.7; [BM] "Sharding activations to
+# reduce memory"): the all-reduce at g becomes a reduce-scatter that sums the
+# partial outputs and leaves each GPU one stripe of tokens, dropout and the
+# residual add run on that stripe, then LayerNorm for the next block, and an
+# all-gather rebuilds the full input.  all-reduce = reduce-scatter + all-gather.
+# ----------------------------------------------------------------------------
+
+def stripe_rows(rows: int, n_shards: int, index: int):
+    """Token stripe `index` of `rows` tokens over n_shards GPUs (contiguous, equal)."""
+    return shard_range(rows, n_shards, index)
+
+
+def reduce_scatter(partials: Sequence, n_shards: int, index: int, bias=None) -> np.ndarray:
+    """Stripe `index` of sum_i P_i (rows split equally and contiguously), plus
+    the bias once."""
+    P = [_f64(p) for p in partials]
+    r0, k = stripe_rows(P[0].shape[0], n_shards, index)
+    return shard_reduce([p[r0:r0 + k] for p in P], bias)
+
+
+def all_gather(stripes: Sequence) -> np.ndarray:
+    """The stripes of every GPU stacked in order into the full tensor."""
+    return np.concatenate([_f64(x) for x in stripes], axis=0)
+
+
+def layer_norm(h, gamma, beta, eps: float = 1e-5) -> np.ndarray:
+    """Per row: (h - mean) / sqrt(var + eps) * gamma + beta, var the biased
+    (population) variance over the row."""
+    h = _f64(h)
+    mu = h.mean(axis=1, keepdims=True)
+    var = ((h - mu) ** 2).mean(axis=1, keepdims=True)
+    return (h - mu) / np.sqrt(var + eps) * _f64(gamma) + _f64(beta)
+
+
+def sp_block_end(partials: Sequence, n_shards: int, index: int, residual, gamma, beta, bias=None,
+                 keep=None, p_drop: float = 0.0, eps: float = 1e-5) -> Dict[str, np.ndarray]:
+    """One GPU's sequence-parallel block end on its stripe: y = the
+    reduce-scattered sum (+ bias); inverted dropout with the given keep mask,
+    y * keep / (1 - p); the residual stream h = residual + y; and x =
+    LayerNorm(h), the stripe of the next block's input."""
+    y = reduce_scatter(partials, n_shards, index, bias)
+    if keep is not None:
+        y = y * _f64(keep) / (1.0 - p_drop)
+    h = _f64(residual) + y
+    return {"h": h, "x": layer_norm(h, gamma, beta, eps)}
 
 
 def shard_range(total: int, n_shards: int, index: int):

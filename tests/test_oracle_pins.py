@@ -418,6 +418,56 @@ def test_attention_bwd_shards_sum_and_concatenate():
     np.testing.assert_allclose(np.concatenate([p["dWo"] for p in parts], axis=0), full["dWo"], rtol=1e-12, atol=1e-13)
 
 
+# ------------------------------------------------------- sequence parallel
+
+def test_reduce_scatter_then_all_gather_is_all_reduce():
+    # [HC] Figure 3.2: the all-reduce is a reduce-scatter followed by an
+    # all-gather.  The pages' own 4-GPU example: rank r holds [0,1,2,3] + r.
+    P = [np.arange(4.0) + r for r in range(4)]
+    stripes = [O.reduce_scatter([p[:, None] for p in P], 4, j) for j in range(4)]
+    np.testing.assert_array_equal(O.all_gather(stripes)[:, 0], [6, 10, 14, 18])
+    rng = np.random.default_rng(63)
+    Q = [rng.standard_normal((12, 5)) for _ in range(3)]
+    full = O.shard_reduce(Q)
+    np.testing.assert_array_equal(O.all_gather([O.reduce_scatter(Q, 3, j) for j in range(3)]), full)
+    with pytest.raises(ValueError):
+        O.reduce_scatter(Q, 5, 0)                                  # 12 rows over 5 GPUs
+
+
+def test_layer_norm_brute_force_and_properties():
+    rng = np.random.default_rng(64)
+    h = rng.standard_normal((3, 7)) * 3 + 1
+    g, b = rng.standard_normal(7), rng.standard_normal(7)
+    x = O.layer_norm(h, g, b, eps=1e-5)
+    for r in range(3):
+        mu = math.fsum(h[r]) / 7
+        var = math.fsum((v - mu) ** 2 for v in h[r]) / 7
+        for c in range(7):
+            assert abs(x[r, c] - ((h[r, c] - mu) / math.sqrt(var + 1e-5) * g[c] + b[c])) < 1e-12
+    z = O.layer_norm(h, np.ones(7), np.zeros(7), eps=0.0)
+    np.testing.assert_allclose(z.mean(axis=1), 0, atol=1e-14)
+    np.testing.assert_allclose((z ** 2).mean(axis=1), 1, rtol=1e-13)
+    np.testing.assert_allclose(O.layer_norm(np.full((2, 5), 3.0), g[:5], b[:5]), np.tile(b[:5], (2, 1)),
+                               atol=1e-12)                         # a constant row gives beta
+
+
+def test_sp_block_end_definition():
+    rng = np.random.default_rng(65)
+    n, rows, cols, p = 4, 16, 6, 0.25
+    P = [rng.standard_normal((rows, cols)) for _ in range(n)]
+    res, g, b, bias = rng.standard_normal((4, cols)), rng.standard_normal(cols), rng.standard_normal(cols), \
+        rng.standard_normal(cols)
+    keep = (rng.random((4, cols)) >= p).astype(np.float64)
+    out = O.sp_block_end(P, n, 2, res, g, b, bias=bias, keep=keep, p_drop=p)
+    y = sum(q[8:12] for q in P) + bias
+    h = res + y * keep / (1 - p)
+    np.testing.assert_allclose(out["h"], h, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(out["x"], O.layer_norm(h, g, b), rtol=1e-14, atol=1e-14)
+    # p = 0 with no mask: dropout is the identity
+    out0 = O.sp_block_end(P, n, 0, res, g, b)
+    np.testing.assert_allclose(out0["h"], res + sum(q[0:4] for q in P), rtol=1e-14, atol=1e-14)
+
+
 # -------------------------------------------------------------- shard-reduce
 
 def _read_golden_allreduce():
