@@ -8,8 +8,9 @@ tp_mlp_fwd + tp_mlp_bwd on resident synthetic inputs (seed 0).  value is the
 algorithmic FLOP rate: 6 products of 2*M*N*K = 549.76 GFLOP each per step.
 
 Also reported (not the headline): the GPT-2-medium-shaped shard with all 8
-shards and both shard-reduces, the SwiGLU shard and the causal attention
-shard, each timed on its own.  The fp64 oracle runs the same step on the
+shards and both shard-reduces, the SwiGLU shard, the causal attention
+shard (fwd+bwd), the grouped-query attention shard and the sequence-parallel
+block end, each timed on its own.  The fp64 oracle runs the same step on the
 host's cores (cpu_baseline, a baseline and not a target), and its outputs
 give the max relative error of every GPU output tensor.
 
@@ -371,6 +372,73 @@ def run_g1(tp, torch, steps, warmup):
             "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in per.items()}}
 
 
+def run_s1(tp, torch, steps, warmup):
+    """Sequence-parallel block end at 8192 tokens x 8192, TP 8: this GPU's
+    reduce-scatter + dropout + residual + LayerNorm on its 1024-token stripe,
+    then the all-gather of the 8 stripes (HBM-bound, reported in GB/s)."""
+    import tpsynth
+    wl = tpsynth.WORKLOADS["S1"]
+    inp = tpsynth.sp_inputs(wl)
+    bf = torch.bfloat16
+    dev = lambda a: torch.from_numpy(a).to(bf).cuda()
+    n, rows, cols = wl.n_shards, wl.M, wl.d
+    k = rows // n
+    P, res, bias, gamma, beta = (dev(inp[key]) for key in ("P", "residual", "bias", "gamma", "beta"))
+    keep = torch.from_numpy(inp["keep"][:k]).cuda()
+    p_drop = inp["p_drop"]
+    del inp
+    res = res[:k].contiguous()
+    stripes = [torch.empty((k, cols), dtype=bf, device="cuda") for _ in range(n)]
+    x = torch.empty((k, cols), dtype=bf, device="cuda")
+    full = torch.empty((rows, cols), dtype=bf, device="cuda")
+
+    def step():
+        tp.tp_sp_reduce_scatter_ln(P, res, gamma, beta, stripes[0], x, n, 0, rows, cols, bias=bias,
+                                   keep=keep, p_drop=p_drop)
+        tp.tp_sp_all_gather(stripes, full)
+
+    ms, _, per = timed(tp, torch, step, steps, warmup, 2)
+    e = k * cols
+    rs_bytes = (n + 1) * e * 2 + e + 3 * cols * 2 + 2 * e * 2
+    ag_bytes = 2 * n * e * 2
+    avg = lambda lab: (sum(per[lab]) / len(per[lab])) if per.get(lab) else None
+    rs_ms, ag_ms = avg("sp.rs_ln"), avg("sp.all_gather")
+    # cold: evict the 256 MB Infinity Cache before each launch
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    ev = HipEvents(2)
+    cold_rs, cold_ag = [], []
+    for _ in range(3):
+        scratch.fill_(1)
+        torch.cuda.synchronize()
+        tp.lib().tp_profile_begin(ev.start, ev.stop, 2)
+        tp.tp_sp_reduce_scatter_ln(P, res, gamma, beta, stripes[0], x, n, 0, rows, cols, bias=bias,
+                                   keep=keep, p_drop=p_drop)
+        tp.lib().tp_profile_end()
+        torch.cuda.synchronize()
+        cold_rs.append(ev.elapsed_ms(0))
+        scratch.fill_(1)
+        torch.cuda.synchronize()
+        tp.lib().tp_profile_begin(ev.start, ev.stop, 2)
+        tp.tp_sp_all_gather(stripes, full)
+        tp.lib().tp_profile_end()
+        torch.cuda.synchronize()
+        cold_ag.append(ev.elapsed_ms(0))
+    ev.close()
+    del scratch
+    gbs = lambda b, t: round(b / t / 1e6, 1) if t else None
+    return {"workload": "S1 sequence-parallel block end: 8192 tokens x 8192 over TP 8, this GPU's "
+                        "1024-token stripe (reduce-scatter of 8 partials + bias, dropout 0.1, residual, "
+                        "LayerNorm) + all-gather of the 8 stripes",
+            "ms_per_step": round(ms, 4),
+            "rs_ln": {"bytes": rs_bytes, "warm_ms": round(rs_ms, 4) if rs_ms else None,
+                      "warm_GBps": gbs(rs_bytes, rs_ms), "cold_ms": round(min(cold_rs), 4),
+                      "cold_GBps": gbs(rs_bytes, min(cold_rs)), "peak_GBps": PEAK_HBM_GBS},
+            "all_gather": {"bytes": ag_bytes, "warm_ms": round(ag_ms, 4) if ag_ms else None,
+                           "warm_GBps": gbs(ag_bytes, ag_ms), "cold_ms": round(min(cold_ag), 4),
+                           "cold_GBps": gbs(ag_bytes, min(cold_ag)), "peak_GBps": PEAK_HBM_GBS},
+            "kernels_ms": {key: round(sum(v) / len(v), 4) for key, v in per.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,7 +514,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         wls = {}
-        for name, fn in (("C2", run_c2), ("C3", run_c3), ("C4", run_c4), ("G1", run_g1)):
+        for name, fn in (("C2", run_c2), ("C3", run_c3), ("C4", run_c4), ("G1", run_g1), ("S1", run_s1)):
             log(f"timing {name}")
             wls[name] = fn(tp, torch, args.extra_steps, 2)
             torch.cuda.empty_cache()

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 2
+#define TP_ABI_VERSION 3
 
 typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype_t;
 
@@ -199,6 +199,50 @@ int tp_attn_shard_bwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t
                       void* ws, size_t ws_bytes);
 size_t tp_attn_shard_bwd_workspace_bytes(tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
                                          int64_t h_local, int64_t d_head);
+
+/* ---------------------------------------------------------------------------
+ * tp_sp_reduce_scatter_ln — the sequence-parallel block end of one GPU ([HC]
+ * 3.4, the sequence-parallelism paragraph and Figure 3.7; [BM] "Sharding
+ * activations to reduce memory").  Sequence parallelism replaces g's
+ * all-reduce by a reduce-scatter that sums the shards' partial outputs and
+ * keeps this GPU's stripe of tokens; dropout, the residual add and the next
+ * block's LayerNorm then run on that stripe only.  With k = rows / n_shards
+ * and r0 = index * k (stripe `index`, as tp_shard_range), for r in [0, k):
+ *   y[r]  = sum_{i=0}^{n_shards-1} partials[i*shard_stride + (r0+r)*cols + :]
+ *           (+ bias, added once after the sum)
+ *   y[r]  = y[r] * keep[r] / (1 - p_drop)          (only when keep != NULL)
+ *   h[r]  = residual[r] + y[r]                     -> h_out  (dtype dt)
+ *   x[r]  = (h[r] - mean) / sqrt(var + eps) * gamma + beta  -> x_out
+ * with mean and the biased variance var over the row of h as stored in
+ * h_out.  Sums and statistics in fp32, shard sum in order 0..n_shards-1.
+ * partials: n_shards blocks of [rows x cols] (dtype dt), shard_stride
+ * elements apart (>= rows*cols, a multiple of 8).  residual, h_out, x_out:
+ * [k x cols]; keep: [k x cols] bytes, nonzero = kept (the caller draws the
+ * mask: dropout's random numbers are an input); bias, gamma, beta: [cols].
+ * bias and keep may be NULL.  cols must be a multiple of 8 (TP_E_DIVIS),
+ * rows divisible by n_shards (TP_E_DIVIS), k <= 2^24, 0 <= p_drop < 1,
+ * eps > 0.  Outputs may not overlap inputs or each other (TP_E_ALIAS).
+ * ------------------------------------------------------------------------- */
+int tp_sp_reduce_scatter_ln(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t rows,
+                            int64_t cols, int64_t index, const void* partials,
+                            int64_t shard_stride, const void* bias, const void* residual,
+                            const uint8_t* keep, float p_drop, const void* gamma,
+                            const void* beta, float eps, void* h_out, void* x_out);
+
+/* ---------------------------------------------------------------------------
+ * tp_sp_all_gather — the all-gather that rebuilds the full input of the next
+ * TP product from the n_shards token stripes ([HC] 3.2 collectives table and
+ * Figure 3.2; 3.4, Figure 3.7):
+ *   full[j*stripe_rows + r, :] = stripes[j][r, :]   for j < n_shards.
+ * stripes: a HOST array of n_shards DEVICE pointers, each [stripe_rows x
+ * cols] of dtype dt; full: [n_shards*stripe_rows x cols].  A stripe pointer
+ * equal to its own place in full is in place and is not copied; any other
+ * overlap of a stripe with full is TP_E_ALIAS.  1 <= n_shards <= 64, cols a
+ * multiple of 8.  Together with tp_sp_reduce_scatter_ln's sum this is the
+ * all-reduce: reduce-scatter followed by all-gather ([HC] 3.2).
+ * ------------------------------------------------------------------------- */
+int tp_sp_all_gather(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t stripe_rows,
+                     int64_t cols, const void* const* stripes, void* full);
 
 /* ---------------------------------------------------------------------------
  * tp_shard_reduce — the local stand-in for the g (forward) and f (backward)

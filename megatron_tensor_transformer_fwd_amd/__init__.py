@@ -17,7 +17,7 @@ __all__ = [
     "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_workspace_bytes",
     "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes",
     "tp_attn_shard_fwd", "tp_attn_gqa_shard_fwd", "tp_attn_shard_bwd", "tp_attn_shard_bwd_workspace_bytes",
-    "tp_shard_reduce", "tp_shard_range",
+    "tp_shard_reduce", "tp_shard_range", "tp_sp_reduce_scatter_ln", "tp_sp_all_gather",
     "tp_abi_version", "EXPORTS",
 ]
 
@@ -52,6 +52,9 @@ EXPORTS = {
                           + [_p] * 5 + [_p] * 5 + [_p] + [_p] * 5 + [_p, _sz]),
     "tp_attn_shard_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i64, _i64]),
     "tp_shard_reduce": (_i32, [_p, _i32, _i32, _i64, _i64, _p, _i64, _p, _i64, _p]),
+    "tp_sp_reduce_scatter_ln": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, _p, ctypes.c_float,
+                                       _p, _p, ctypes.c_float, _p, _p]),
+    "tp_sp_all_gather": (_i32, [_p, _i32, _i64, _i64, _i64, ctypes.POINTER(_p), _p]),
     "tp_strerror": (ctypes.c_char_p, [_i32]),
     "tp_last_error_detail": (ctypes.c_char_p, []),
     "tp_abi_version": (_i32, []),
@@ -201,3 +204,28 @@ def tp_shard_reduce(partials, out, n_shards: int, numel: int, shard_stride: Opti
     stride = numel if shard_stride is None else shard_stride
     _check(lib().tp_shard_reduce(_stream(stream), _dt(partials), _dt(out), n_shards, numel, _ptr(partials),
                                  stride, _ptr(bias), 0 if bias is None else bias.numel(), _ptr(out)))
+
+
+def tp_sp_reduce_scatter_ln(partials, residual, gamma, beta, h_out, x_out, n_shards: int, index: int,
+                            rows: int, cols: int, shard_stride: Optional[int] = None, bias=None, keep=None,
+                            p_drop: float = 0.0, eps: float = 1e-5, stream=None) -> None:
+    """Stripe `index` of sum_i partials_i (+ bias), inverted dropout with the
+    uint8 mask `keep`, + residual -> h_out, LayerNorm(h) -> x_out."""
+    import torch
+    if keep is not None and keep.dtype != torch.uint8:
+        raise TypeError("keep must be a uint8 tensor")
+    stride = rows * cols if shard_stride is None else shard_stride
+    _check(lib().tp_sp_reduce_scatter_ln(_stream(stream), _dt(partials), n_shards, rows, cols, index,
+                                         _ptr(partials), stride, _ptr(bias), _ptr(residual), _ptr(keep),
+                                         float(p_drop), _ptr(gamma), _ptr(beta), float(eps), _ptr(h_out),
+                                         _ptr(x_out)))
+
+
+def tp_sp_all_gather(stripes, full, stream=None) -> None:
+    """full = concatenation of the [stripe_rows x cols] stripes along rows.
+    A stripe that is already the matching row block of `full` (a view at
+    its place) is not copied."""
+    n = len(stripes)
+    rows, cols = stripes[0].shape
+    arr = (_p * n)(*[_ptr(t) for t in stripes])
+    _check(lib().tp_sp_all_gather(_stream(stream), _dt(full), n, rows, cols, arr, _ptr(full)))

@@ -9,6 +9,10 @@ namespace tpk {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
+// Most stripes one all-gather launch copies (their pointers travel in the
+// kernel arguments).
+constexpr int kSpMaxShards = 64;
+
 hipError_t launch_shard_reduce(hipStream_t st, int dt_in, int dt_out, int n, int64_t numel,
                                const void* P, int64_t stride, const void* bias, int64_t bias_len,
                                void* out);
@@ -42,5 +46,13 @@ hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
                            const void* Q, const void* K, const void* V, const void* O, const float* L,
                            const void* dY, void* dX, float* dWq, float* dWk, float* dWv, float* dWo,
                            void* ws);
+
+hipError_t launch_sp_reduce_scatter_ln(hipStream_t st, int dt, int n, int64_t rows, int64_t cols,
+                                       int64_t index, const void* P, int64_t stride, const void* bias,
+                                       const void* residual, const uint8_t* keep, float p_drop,
+                                       const void* gamma, const void* beta, float eps, void* h_out,
+                                       void* x_out);
+hipError_t launch_sp_all_gather(hipStream_t st, int dt, int n, int64_t stripe_rows, int64_t cols,
+                                const void* const* stripes, void* full);
 
 }  // namespace tpk

@@ -12,33 +12,6 @@
 
 namespace tpk {
 
-template <class T> struct Vec8;
-template <> struct Vec8<bf16> {
-  static __device__ __forceinline__ void load(const bf16* p, float* o) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { o[2 * i] = bf16_lo(w[i]); o[2 * i + 1] = bf16_hi(w[i]); }
-  }
-  static __device__ __forceinline__ void store(bf16* p, const float* v) {
-    u32x4 w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-    *reinterpret_cast<u32x4*>(p) = w;
-  }
-};
-template <> struct Vec8<float> {
-  static __device__ __forceinline__ void load(const float* p, float* o) {
-    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
-    const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[4 + i] = b[i]; }
-  }
-  static __device__ __forceinline__ void store(float* p, const float* v) {
-    reinterpret_cast<f32x4*>(p)[0] = f32x4{v[0], v[1], v[2], v[3]};
-    reinterpret_cast<f32x4*>(p)[1] = f32x4{v[4], v[5], v[6], v[7]};
-  }
-};
-
 // Vector path: numel_vec chunks of 8 elements; every shard base and the
 // output are 16-byte aligned.  `out` may be partials block 0: each element is
 // read by the thread that writes it, before the write.

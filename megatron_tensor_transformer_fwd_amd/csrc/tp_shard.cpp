@@ -375,4 +375,72 @@ int tp_shard_reduce(void* stream, tp_dtype_t dt_in, tp_dtype_t dt_out, int64_t n
                     "tp_shard_reduce");
 }
 
+int tp_sp_reduce_scatter_ln(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t rows, int64_t cols,
+                            int64_t index, const void* partials, int64_t shard_stride, const void* bias,
+                            const void* residual, const uint8_t* keep, float p_drop, const void* gamma,
+                            const void* beta, float eps, void* h_out, void* x_out) {
+  if (!dtype_ok(dt)) return fail(TP_E_DTYPE, "dtype %d is not TP_DT_F32 or TP_DT_BF16", (int)dt);
+  if (n_shards <= 0 || n_shards > 4096) return fail(TP_E_DIM, "n_shards = %lld outside [1, 4096]", (long long)n_shards);
+  TP_CHECK(check_dims({{"rows", rows}, {"cols", cols}}));
+  if (index < 0 || index >= n_shards)
+    return fail(TP_E_DIM, "index = %lld outside [0, %lld)", (long long)index, (long long)n_shards);
+  if (rows % n_shards)
+    return fail(TP_E_DIVIS, "rows = %lld is not divisible by n_shards = %lld", (long long)rows, (long long)n_shards);
+  TP_CHECK(check_mult8({{"cols", cols}}));
+  const int64_t k = rows / n_shards;
+  if (k > (int64_t(1) << 24)) return fail(TP_E_DIM, "stripe of %lld rows exceeds 2^24", (long long)k);
+  const int64_t numel = rows * cols;
+  if (shard_stride < numel)
+    return fail(TP_E_DIM, "shard_stride %lld < rows*cols %lld", (long long)shard_stride, (long long)numel);
+  if (shard_stride % 8) return fail(TP_E_DIVIS, "shard_stride = %lld must be a multiple of 8", (long long)shard_stride);
+  if (keep && !(p_drop >= 0.0f && p_drop < 1.0f))
+    return fail(TP_E_DIM, "p_drop = %g outside [0, 1)", (double)p_drop);
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(TP_E_DIM, "eps = %g must be positive and finite", (double)eps);
+  const size_t e = esize(dt);
+  const size_t stripe = (size_t)(k * cols);
+  TP_CHECK(check_buffers({{"partials", partials, ((size_t)(n_shards - 1) * shard_stride + numel) * e},
+                          {"bias", bias, bias ? cols * e : 0},
+                          {"residual", residual, stripe * e},
+                          {"keep", keep, keep ? stripe : 0},
+                          {"gamma", gamma, cols * e},
+                          {"beta", beta, cols * e}},
+                         {{"h_out", h_out, stripe * e}, {"x_out", x_out, stripe * e}},
+                         {"partials", "residual", "gamma", "beta", "h_out", "x_out"}));
+  return hip_status(tpk::launch_sp_reduce_scatter_ln(static_cast<hipStream_t>(stream), dt, (int)n_shards, rows, cols,
+                                                     index, partials, shard_stride, bias, residual, keep, p_drop,
+                                                     gamma, beta, eps, h_out, x_out),
+                    "tp_sp_reduce_scatter_ln");
+}
+
+int tp_sp_all_gather(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t stripe_rows, int64_t cols,
+                     const void* const* stripes, void* full) {
+  if (!dtype_ok(dt)) return fail(TP_E_DTYPE, "dtype %d is not TP_DT_F32 or TP_DT_BF16", (int)dt);
+  if (n_shards <= 0 || n_shards > tpk::kSpMaxShards)
+    return fail(TP_E_DIM, "n_shards = %lld outside [1, %d]", (long long)n_shards, tpk::kSpMaxShards);
+  TP_CHECK(check_dims({{"stripe_rows", stripe_rows}, {"cols", cols}}));
+  TP_CHECK(check_mult8({{"cols", cols}}));
+  if (!stripes) return fail(TP_E_NULL, "stripes is NULL");
+  const size_t bytes = (size_t)(stripe_rows * cols) * esize(dt);
+  const Span out{"full", full, bytes * n_shards};
+  TP_CHECK(check_buffers({}, {out}, {"full"}));
+  const void* src[tpk::kSpMaxShards];
+  for (int64_t j = 0; j < n_shards; ++j) {
+    char name[32];
+    std::snprintf(name, sizeof name, "stripes[%lld]", (long long)j);
+    const void* p = stripes[j];
+    if (!p) return fail(TP_E_NULL, "%s is NULL", name);
+    if (reinterpret_cast<uintptr_t>(p) & 15u) return fail(TP_E_ALIGN, "%s (%p) is not 16-byte aligned", name, p);
+    const void* home = static_cast<const char*>(full) + bytes * j;
+    if (p == home) {          // already in place: nothing to copy
+      src[j] = nullptr;
+      continue;
+    }
+    if (overlap(out, {name, p, bytes})) return fail(TP_E_ALIAS, "output full overlaps input %s", name);
+    src[j] = p;
+  }
+  return hip_status(tpk::launch_sp_all_gather(static_cast<hipStream_t>(stream), dt, (int)n_shards, stripe_rows, cols,
+                                              src, full),
+                    "tp_sp_all_gather");
+}
+
 }  // extern "C"

@@ -33,7 +33,7 @@ def test_header_and_binding_agree_and_library_exports_all():
 
 
 def test_version_and_strerror():
-    assert tp.tp_abi_version() == 2
+    assert tp.tp_abi_version() == 3
     L = tp.lib()
     for code in (OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP):
         assert L.tp_strerror(code) and L.tp_strerror(code) != b"unknown status"
@@ -221,3 +221,59 @@ def test_gqa_validation():
     assert L.tp_attn_gqa_shard_fwd(None, BF16, 1, 64, 64, 4, 8, 128, 1, 0.0, *p[:10], None) == E_DIVIS
     assert L.tp_attn_gqa_shard_fwd(None, F32, 1, 64, 64, 4, 2, 128, 1, 0.0, *p[:10], None) == E_DTYPE
     assert L.tp_attn_gqa_shard_fwd(None, BF16, 1, 64, 64, 4, 2, 128, 1, 0.0, None, *p[1:10], None) == E_NULL
+
+
+def test_sp_reduce_scatter_ln_validation():
+    L = tp.lib()
+    P, bias, res, keep, g, b, h, x = _addrs(8)
+
+    def rs(dt=BF16, n=4, rows=64, cols=32, index=1, P=P, stride=None, bias=bias, res=res, keep=keep,
+           p_drop=0.1, g=g, b=b, eps=1e-5, h=h, x=x):
+        stride = rows * cols if stride is None else stride
+        return L.tp_sp_reduce_scatter_ln(None, dt, n, rows, cols, index, P, stride, bias, res, keep, p_drop,
+                                         g, b, eps, h, x)
+
+    assert rs(dt=7) == E_DTYPE
+    assert rs(n=0) == E_DIM
+    assert rs(rows=0) == E_DIM
+    assert rs(index=4) == E_DIM and rs(index=-1) == E_DIM
+    assert rs(rows=66) == E_DIVIS                         # rows % n_shards
+    assert rs(cols=36) == E_DIVIS                         # cols % 8
+    assert rs(stride=64 * 32 - 8) == E_DIM                # stride < rows*cols
+    assert rs(stride=64 * 32 + 4) == E_DIVIS
+    assert rs(p_drop=1.0) == E_DIM and rs(p_drop=-0.1) == E_DIM
+    assert rs(eps=0.0) == E_DIM and rs(eps=float("nan")) == E_DIM
+    assert rs(rows=((1 << 24) + 1) * 4) == E_DIM          # stripe rows beyond 2^24
+    for kw in ("P", "res", "g", "b", "h", "x"):
+        assert rs(**{kw: None}) == E_NULL, kw
+    assert rs(keep=keep + 8) == E_ALIGN
+    assert rs(h=res) == E_ALIAS                           # output over the residual
+    assert rs(x=h) == E_ALIAS                             # outputs overlap
+    assert rs(h=P + 2 * 64 * 32 * 2) == E_ALIAS           # output inside the partials
+    # bias and keep are optional; with keep NULL p_drop is not examined.  Such
+    # calls pass validation and fail only at the launch (no device here).
+    assert rs(bias=None, keep=None, p_drop=5.0) == E_HIP
+
+
+def test_sp_all_gather_validation():
+    L = tp.lib()
+    s0, s1, s2, s3, full = _addrs(5)
+    arr = lambda *ps: (ctypes.c_void_p * len(ps))(*ps)
+    st = arr(s0, s1, s2, s3)
+    assert L.tp_sp_all_gather(None, 9, 4, 16, 32, st, full) == E_DTYPE
+    assert L.tp_sp_all_gather(None, BF16, 0, 16, 32, st, full) == E_DIM
+    assert L.tp_sp_all_gather(None, BF16, 65, 16, 32, arr(*([s0] * 65)), full) == E_DIM
+    assert L.tp_sp_all_gather(None, BF16, 4, 0, 32, st, full) == E_DIM
+    assert L.tp_sp_all_gather(None, BF16, 4, 16, 36, st, full) == E_DIVIS
+    assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, None, full) == E_NULL
+    assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, st, None) == E_NULL
+    assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, arr(s0, None, s2, s3), full) == E_NULL
+    assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, arr(s0, s1 + 4, s2, s3), full) == E_ALIGN
+    assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, st, full + 2) == E_ALIGN
+    stripe = 16 * 32 * 2
+    # a stripe that straddles its place in `full` is an overlap ...
+    assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, arr(s0, full + stripe + 16, s2, s3), full) == E_ALIAS
+    # ... another stripe's place as well
+    assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, arr(s0, full, s2, s3), full) == E_ALIAS
+    # exactly in place is accepted (it is not copied); the launch then fails without a device
+    assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, arr(s0, full + stripe, s2, s3), full) == E_HIP

@@ -1,0 +1,198 @@
+"""Parity of the sequence-parallel block end and all-gather (through the C
+ABI) against the fp64 oracle: the reduce-scatter of the partial outputs,
+dropout with the given keep mask, the residual add and LayerNorm on one
+GPU's token stripe ([HC] 3.4, sequence parallelism and Figure 3.7), and the
+all-gather that rebuilds the full tensor.  Bar as for the other paths:
+max_rel_err <= 2e-2 for bf16, <= 1e-5 for fp32.  The decomposition
+all-reduce = reduce-scatter + all-gather ([HC] 3.2, Figure 3.2) is checked
+bitwise against the library's own shard-reduce.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import tpsynth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import megatron_tensor_transformer_fwd_amd as m
+    m.lib()          # raises if the library is missing: no fallback path exists
+    return m
+
+
+def _tdt(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def dev(a, dtype):
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(dtype=_tdt(dtype)).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check(name, got, ref, dtype):
+    err = O.max_rel_err(host(got), ref)
+    assert np.isfinite(err) and err <= TOL[dtype], f"{name}: max_rel_err {err:.3e} > {TOL[dtype]}"
+    return err
+
+
+def run_stripe(tp, g, inp, n, index, dtype, with_bias=True, with_keep=True, h_out=None, x_out=None):
+    """One GPU's block end for stripe `index` on device inputs `g`."""
+    rows, cols = inp["residual"].shape
+    k = rows // n
+    r0 = index * k
+    h = h_out if h_out is not None else torch.empty((k, cols), dtype=_tdt(dtype), device="cuda")
+    x = x_out if x_out is not None else torch.empty((k, cols), dtype=_tdt(dtype), device="cuda")
+    tp.tp_sp_reduce_scatter_ln(g["P"], g["residual"][r0:r0 + k], g["gamma"], g["beta"], h, x, n, index,
+                               rows, cols, bias=g["bias"] if with_bias else None,
+                               keep=g["keep"][r0:r0 + k] if with_keep else None, p_drop=inp["p_drop"])
+    return h, x
+
+
+def upload(inp, dtype):
+    return {"P": dev(inp["P"], dtype), "residual": dev(inp["residual"], dtype),
+            "bias": dev(inp["bias"], dtype), "gamma": dev(inp["gamma"], dtype),
+            "beta": dev(inp["beta"], dtype), "keep": torch.from_numpy(inp["keep"]).cuda()}
+
+
+def oracle_stripe(inp, n, index, with_bias=True, with_keep=True):
+    rows = inp["residual"].shape[0]
+    r0, k = O.stripe_rows(rows, n, index)
+    return O.sp_block_end(list(inp["P"]), n, index, inp["residual"][r0:r0 + k], inp["gamma"], inp["beta"],
+                          bias=inp["bias"] if with_bias else None,
+                          keep=inp["keep"][r0:r0 + k] if with_keep else None,
+                          p_drop=inp["p_drop"] if with_keep else 0.0)
+
+
+@pytest.mark.parametrize("dtype,n,rows,cols,with_bias,with_keep", [
+    ("f32", 2, 64, 96, True, True),          # fp32 end to end
+    ("bf16", 4, 40, 1000, True, True),       # row width not a multiple of the 2048-value sweep
+    ("bf16", 3, 33, 24, False, False),       # no bias, no dropout, 11-row stripes
+    ("bf16", 8, 64, 8192, True, True),       # widest row kept in registers
+    ("bf16", 8, 64, 8200, True, True),       # one chunk past it: LayerNorm re-reads h
+    ("f32", 2, 16, 16392, True, False),      # fp32 re-read path
+    ("bf16", 1, 8, 8, True, True),           # a single shard: no reduction at all
+])
+def test_sp_block_end_small(tp, dtype, n, rows, cols, with_bias, with_keep):
+    _say(f"sp block end {dtype} n={n} rows={rows} cols={cols} bias={with_bias} keep={with_keep}")
+    inp = tpsynth.random_sp(n, rows, cols, dtype, seed=11, p_drop=0.1, with_bias=with_bias)
+    g = upload(inp, dtype)
+    for index in range(n):
+        h, x = run_stripe(tp, g, inp, n, index, dtype, with_bias, with_keep)
+        torch.cuda.synchronize()
+        ref = oracle_stripe(inp, n, index, with_bias, with_keep)
+        check(f"h[{index}]", h, ref["h"], dtype)
+        check(f"x[{index}]", x, ref["x"], dtype)
+
+
+def test_sp_block_end_deterministic(tp):
+    _say("sp block end bitwise determinism")
+    inp = tpsynth.random_sp(8, 256, 4096, "bf16", seed=12)
+    g = upload(inp, "bf16")
+    h1, x1 = run_stripe(tp, g, inp, 8, 5, "bf16")
+    h2, x2 = run_stripe(tp, g, inp, 8, 5, "bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2) and torch.equal(x1, x2)
+
+
+def test_sp_constant_rows_pages_example(tp):
+    """Ranks r = 0..3 hold [0,1,2,3] + r (the pages' all-reduce example,
+    "Chapter 8: Distributed Training", 8.4.2), each element spread over a row
+    of 8: the stripes of the reduce-scatter hold 6, 10, 14, 18, the
+    all-gather returns all four, and LayerNorm of a constant row is beta."""
+    _say("sp pages example")
+    for dtype in ("f32", "bf16"):
+        P = np.stack([np.repeat((np.arange(4) + r)[:, None], 8, axis=1) for r in range(4)]).astype(np.float32)
+        inp = {"P": P, "residual": np.zeros((4, 8), np.float32), "bias": None,
+               "gamma": np.full(8, 2.0, np.float32), "beta": np.arange(8, dtype=np.float32) / 4,
+               "keep": np.ones((4, 8), np.uint8), "p_drop": 0.0}
+        g = upload(inp, dtype)
+        hs = []
+        for index in range(4):
+            h, x = run_stripe(tp, g, inp, 4, index, dtype, with_bias=False, with_keep=False)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(host(h), np.full((1, 8), 6 + 4 * index))
+            np.testing.assert_array_equal(host(x)[0], inp["beta"])
+            hs.append(h)
+        full = torch.empty((4, 8), dtype=_tdt(dtype), device="cuda")
+        tp.tp_sp_all_gather(hs, full)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(full)[:, 0], [6, 10, 14, 18])
+
+
+@pytest.mark.parametrize("dtype,n,rows,cols", [
+    ("bf16", 8, 8192, 1024),     # 8 shards of 8192 tokens x 1024
+    ("f32", 3, 48, 40),
+    ("bf16", 5, 35, 8200),
+])
+def test_sp_rs_plus_ag_is_all_reduce(tp, dtype, n, rows, cols):
+    """With a zero residual and no dropout, h is the reduce-scattered sum; the
+    all-gather of the stripes equals the shard-reduce (the all-reduce's local
+    stand-in) bit for bit, gathered by copy and in place."""
+    _say(f"sp RS+AG == AR {dtype} n={n} rows={rows} cols={cols}")
+    inp = tpsynth.random_sp(n, rows, cols, dtype, seed=13)
+    inp["residual"] = np.zeros_like(inp["residual"])
+    g = upload(inp, dtype)
+    ar = torch.empty((rows, cols), dtype=_tdt(dtype), device="cuda")
+    tp.tp_shard_reduce(g["P"], ar, n, rows * cols, bias=g["bias"])
+    k = rows // n
+    stripes = [run_stripe(tp, g, inp, n, i, dtype, with_keep=False)[0] for i in range(n)]
+    full = torch.empty((rows, cols), dtype=_tdt(dtype), device="cuda")
+    tp.tp_sp_all_gather(stripes, full)
+    torch.cuda.synchronize()
+    assert torch.equal(full, ar)
+    check("all-gather", full, O.shard_reduce(list(inp["P"]), inp["bias"]), dtype)
+    # in place: every GPU's stripe written straight into its rows of the full buffer
+    full2 = torch.full((rows, cols), float("nan"), dtype=_tdt(dtype), device="cuda")
+    views = []
+    for i in range(n):
+        hv = full2[i * k:(i + 1) * k]
+        run_stripe(tp, g, inp, n, i, dtype, with_keep=False, h_out=hv)
+        views.append(hv)
+    tp.tp_sp_all_gather(views, full2)
+    torch.cuda.synchronize()
+    assert torch.equal(full2, ar)
+
+
+def test_sp_s1_full_size_sampled(tp):
+    """8192 tokens x 8192 over 8 shards (1024-token stripes), dropout 0.1:
+    every stripe computed on the GPU, 48 sampled rows of each checked in
+    full against the oracle (a row of the output depends only on that row)."""
+    wl = tpsynth.WORKLOADS["S1"]
+    _say(f"sp S1 full size {wl.M}x{wl.d} n={wl.n_shards}")
+    inp = tpsynth.sp_inputs(wl, seed=0)
+    g = upload(inp, "bf16")
+    n, rows = wl.n_shards, wl.M
+    k = rows // n
+    rng = np.random.default_rng(5)
+    for index in (0, 3, n - 1):
+        h, x = run_stripe(tp, g, inp, n, index, "bf16")
+        torch.cuda.synchronize()
+        sel = np.sort(rng.choice(k, size=48, replace=False))
+        sel[-1] = k - 1
+        r = index * k + sel
+        sub = {"P": inp["P"][:, r], "residual": inp["residual"][r], "bias": inp["bias"], "gamma": inp["gamma"],
+               "beta": inp["beta"], "keep": inp["keep"][r], "p_drop": inp["p_drop"]}
+        ref = oracle_stripe(sub, 1, 0)
+        check(f"h[{index}]", h[torch.from_numpy(sel).cuda()], ref["h"], "bf16")
+        check(f"x[{index}]", x[torch.from_numpy(sel).cuda()], ref["x"], "bf16")

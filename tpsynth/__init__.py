@@ -38,13 +38,14 @@ __all__ = [
     "Workload", "WORKLOADS", "round_to_bf16", "normal",
     "mlp_inputs", "swiglu_inputs", "attn_inputs", "reduce_inputs",
     "random_mlp", "random_swiglu", "random_attn", "gqa_inputs", "random_gqa",
+    "sp_inputs", "random_sp",
 ]
 
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str               # "mlp" | "swiglu" | "attn"
+    kind: str               # "mlp" | "swiglu" | "attn" | "gqa" | "sp"
     dtype: str              # "f32" | "bf16"
     b: int
     s: int
@@ -55,6 +56,7 @@ class Workload:
     d_head: int = 0
     kv_heads: int = 0            # grouped-query attention: key/value heads (0: = heads)
     w_std: float = 0.02
+    p_drop: float = 0.0          # dropout probability (sequence-parallel block end)
     full_weights: bool = False   # draw every shard's weights (else shard 0 only)
     backward: bool = True
     description: str = ""
@@ -93,6 +95,9 @@ WORKLOADS: Dict[str, Workload] = {
     "G1": Workload("G1", "gqa", "bf16", b=2, s=4096, d=16384, heads=128, kv_heads=8, d_head=128,
                    n_shards=8, w_std=0.01, backward=False,
                    description="grouped-query causal attention shard, 16 query heads sharing 1 KV head"),
+    "S1": Workload("S1", "sp", "bf16", b=2, s=4096, d=8192, n_shards=8, p_drop=0.1, backward=False,
+                   description="sequence-parallel block end, 8192 tokens x 8192 over TP 8: "
+                               "reduce-scatter to a 1024-token stripe, dropout, residual, LayerNorm"),
 }
 
 
@@ -245,3 +250,32 @@ def random_attn(b: int, s: int, d: int, h_local: int, d_head: int, dtype: str,
         out["Wvs"] = [_cols(Wv, n, i) for i in range(n)]
         out["Wos"] = [_rows(Wo, n, i) for i in range(n)]
     return out
+
+
+def sp_inputs(wl: Workload, seed: int = 0) -> dict:
+    """Sequence-parallel block end inputs at the workload's shape: rows = b*s
+    tokens of width d, over n_shards GPUs (see random_sp)."""
+    assert wl.kind == "sp"
+    return random_sp(wl.n_shards, wl.M, wl.d, wl.dtype, seed, wl.p_drop)
+
+
+def random_sp(n_shards: int, rows: int, cols: int, dtype: str, seed: int = 0,
+              p_drop: float = 0.1, with_bias: bool = True) -> dict:
+    """P [n_shards x rows x cols] ~ N(0,1): every shard's partial output of the
+    row-parallel product; residual [rows x cols] ~ N(0,1): the residual stream
+    (a GPU uses its stripe); bias ~ N(0, 0.1^2) or None; gamma ~ 1 + N(0,
+    0.1^2), beta ~ N(0, 0.1^2); keep [rows x cols] uint8, 1 with probability
+    1 - p_drop (dropout's random draw, handed to both sides).  Draw order P
+    (shard by shard), residual, bias, gamma, beta, keep."""
+    rng = np.random.default_rng(seed)
+    P = np.empty((n_shards, rows, cols), dtype=np.float32)
+    for i in range(n_shards):
+        P[i] = normal(rng, (rows, cols), 1.0, dtype)
+    residual = normal(rng, (rows, cols), 1.0, dtype)
+    bias = normal(rng, (cols,), 0.1, dtype) if with_bias else None
+    gamma = (1.0 + normal(rng, (cols,), 0.1, "f32")).astype(np.float32)
+    gamma = round_to_bf16(gamma) if dtype == "bf16" else gamma
+    beta = normal(rng, (cols,), 0.1, dtype)
+    keep = (rng.random((rows, cols), dtype=np.float32) >= p_drop).astype(np.uint8)
+    return {"P": P, "residual": residual, "bias": bias, "gamma": gamma, "beta": beta, "keep": keep,
+            "p_drop": p_drop}
