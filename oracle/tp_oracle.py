@@ -11,7 +11,10 @@ from):
 
 * [JY] "Parallelism on Jiang Yi's Homepage", note "megatron-lm": sections
   FFN (Y = GeLU(X W1) W2, the column split of W1 and the row split of W2, the
-  f/g table, the SwiGLU split), Attention (per-head outputs, O = [o_1..o_h] W_O).
+  f/g table, the SwiGLU split), Attention (per-head outputs, O = [o_1..o_h] W_O),
+  Embedding (the vocabulary split of the input embedding with its all-reduce,
+  the output embedding fused with the cross-entropy) and Implementation
+  (ParallelEmbedding: mask, shift, look up, zero the masked rows).
 * [HC] "Splitting the model: five parallelisms and the traffic they make",
   section 3.4 "Tensor parallelism", Figures 3.4-3.6 (Z = sum_k Z_k; g
   all-reduces the partial sums forward, f all-reduces dX backward; heads are
@@ -50,6 +53,8 @@ __all__ = [
     "attn_gqa_shard_fwd", "attn_gqa_query_rows",
     "shard_reduce", "shard_range",
     "stripe_rows", "reduce_scatter", "all_gather", "layer_norm", "sp_block_end",
+    "vocab_embed_shard", "vocab_embed", "vocab_ce_shard", "vocab_ce_combine", "vocab_ce_fwd",
+    "vocab_ce_shard_bwd",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -424,6 +429,89 @@ def sp_block_end(partials: Sequence, n_shards: int, index: int, residual, gamma,
         y = y * _f64(keep) / (1.0 - p_drop)
     h = _f64(residual) + y
     return {"h": h, "x": layer_norm(h, gamma, beta, eps)}
+
+# ----------------------------------------------------------------------------
+# Vocabulary-parallel embeddings ([JY] Embedding and Implementation)
+# ----------------------------------------------------------------------------
+
+def vocab_embed_shard(ids, E_local, vocab_start: int) -> np.ndarray:
+    """One shard's partial of the input embedding: the shard holds rows
+    [vocab_start, vocab_start + V_local) of the table.  Ids outside that range
+    are masked: they are shifted like the rest, looked up at row 0 and their
+    output rows then set to zero; the others read row id - vocab_start."""
+    ids = np.asarray(ids, dtype=np.int64)
+    E = _f64(E_local)
+    mask = (ids < vocab_start) | (ids >= vocab_start + E.shape[0])
+    local = ids - vocab_start
+    local[mask] = 0
+    y = E[local]
+    y[mask] = 0.0
+    return y
+
+
+def vocab_embed(ids, E_shards: Sequence) -> np.ndarray:
+    """The input embedding over all shards: the all-reduce SUM of every
+    shard's partial.  Shard i holds the i-th contiguous block of rows."""
+    start, parts = 0, []
+    for E in E_shards:
+        parts.append(vocab_embed_shard(ids, E, start))
+        start += np.asarray(E).shape[0]
+    return shard_reduce(parts)
+
+
+def vocab_ce_shard(X, E_local, targets, vocab_start: int) -> Dict[str, np.ndarray]:
+    """One shard's part of the output embedding fused with the cross-entropy:
+    logits z = X E_local^T over the shard's V_local vocabulary columns, and per
+    token the shard's three numbers: m = max_v z, s = sum_v exp(z - m), and
+    z_t = the target's logit when the target falls in this shard (else 0)."""
+    z = _f64(X) @ _f64(E_local).T
+    t = np.asarray(targets, dtype=np.int64)
+    m = z.max(axis=1)
+    ssum = np.exp(z - m[:, None]).sum(axis=1)
+    inside = (t >= vocab_start) & (t < vocab_start + z.shape[1])
+    zt = np.zeros(z.shape[0])
+    rows = np.nonzero(inside)[0]
+    zt[rows] = z[rows, t[rows] - vocab_start]
+    return {"logits": z, "m": m, "s": ssum, "zt": zt}
+
+
+def vocab_ce_combine(stats: Sequence[Dict[str, np.ndarray]]) -> Dict[str, np.ndarray]:
+    """The exchange of the fused cross-entropy: per token only (m, s, z_t) of
+    each shard cross GPUs.  M = max_i m_i, S = sum_i s_i exp(m_i - M),
+    log-sum-exp = M + log S, loss = log-sum-exp - sum_i z_t,i."""
+    m = np.stack([_f64(st["m"]) for st in stats])
+    ssum = np.stack([_f64(st["s"]) for st in stats])
+    zt = np.stack([_f64(st["zt"]) for st in stats]).sum(axis=0)
+    M = m.max(axis=0)
+    S = (ssum * np.exp(m - M)).sum(axis=0)
+    lse = M + np.log(S)
+    return {"lse": lse, "loss": lse - zt}
+
+
+def vocab_ce_fwd(X, E_shards: Sequence, targets) -> Dict[str, np.ndarray]:
+    """Per-token cross-entropy of the vocabulary-parallel output embedding."""
+    start, stats = 0, []
+    for E in E_shards:
+        stats.append(vocab_ce_shard(X, E, targets, start))
+        start += np.asarray(E).shape[0]
+    return vocab_ce_combine(stats)
+
+
+def vocab_ce_shard_bwd(X, E_local, targets, vocab_start: int, lse, dloss) -> Dict[str, np.ndarray]:
+    """Backward of one shard given the combined log-sum-exp and the upstream
+    gradient of every token's loss: dz = (softmax(z) - onehot(target)) dloss
+    on the shard's columns, dX_i = dz E_local (this shard's summand of dX),
+    dE_local = dz^T X."""
+    Xf, E = _f64(X), _f64(E_local)
+    z = Xf @ E.T
+    p = np.exp(z - _f64(lse)[:, None])
+    t = np.asarray(targets, dtype=np.int64)
+    inside = (t >= vocab_start) & (t < vocab_start + z.shape[1])
+    rows = np.nonzero(inside)[0]
+    p[rows, t[rows] - vocab_start] -= 1.0
+    dz = p * _f64(dloss)[:, None]
+    return {"dlogits": dz, "dX": dz @ E, "dE": dz.T @ Xf}
+
 
 
 def shard_range(total: int, n_shards: int, index: int):

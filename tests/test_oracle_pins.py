@@ -517,6 +517,136 @@ def test_max_rel_err():
     assert O.max_rel_err([1.0, -2.2], [1.0, -2.0]) == pytest.approx(0.1)
 
 
+# ------------------------------------------------ vocabulary-parallel embedding
+
+def _vocab_case(seed, T=7, d=5, V=24):
+    rng = np.random.default_rng(seed)
+    E = rng.standard_normal((V, d))
+    ids = rng.integers(0, V, size=T)
+    ids[:4] = [0, V - 1, V // 2, V // 2 - 1]          # both ends and a shard boundary
+    return rng, E, ids
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_vocab_embed_equals_one_hot_product(n):
+    """[JY] Embedding: the all-reduce of the shards' partials is the lookup in
+    the whole table, which is onehot(ids) E."""
+    _, E, ids = _vocab_case(60)
+    V = E.shape[0]
+    shards = [E[i * V // n:(i + 1) * V // n] for i in range(n)]
+    onehot = np.zeros((len(ids), V))
+    onehot[np.arange(len(ids)), ids] = 1.0
+    np.testing.assert_array_equal(O.vocab_embed(ids, shards), onehot @ E)
+    # every token's row comes from exactly one shard
+    nonzero = np.stack([np.any(O.vocab_embed_shard(ids, shards[i], i * V // n) != 0, axis=1) for i in range(n)])
+    np.testing.assert_array_equal(nonzero.sum(axis=0), np.ones(len(ids)))
+
+
+def test_vocab_embed_shard_brute_force_and_out_of_range_ids():
+    """[JY] Implementation (ParallelEmbedding): an id outside the shard's rows
+    gives a zero row; an id outside the whole vocabulary is outside every
+    shard, so its embedding is zero."""
+    _, E, ids = _vocab_case(61)
+    ids = np.concatenate([ids, [-1, 24, 1000]])
+    start, El = 8, E[8:16]
+    y = O.vocab_embed_shard(ids, El, start)
+    for t, v in enumerate(ids):
+        want = El[v - start] if start <= v < start + 8 else np.zeros(E.shape[1])
+        np.testing.assert_array_equal(y[t], want)
+    full = O.vocab_embed(ids, [E[0:8], E[8:16], E[16:24]])
+    np.testing.assert_array_equal(full[-3:], np.zeros((3, E.shape[1])))
+
+
+def _ce_brute(X, E, targets):
+    out = []
+    for t in range(X.shape[0]):
+        z = [sum(X[t, k] * E[v, k] for k in range(X.shape[1])) for v in range(E.shape[0])]
+        zmax = max(z)
+        lse = zmax + math.log(sum(math.exp(zv - zmax) for zv in z))
+        out.append((lse - z[targets[t]], lse))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 6])
+def test_vocab_ce_brute_force(n):
+    """Fused output embedding + cross-entropy ([JY] Embedding) equals
+    -log softmax(X E^T)[target] computed with plain loops."""
+    rng = np.random.default_rng(62)
+    T, d, V = 4, 3, 12
+    X, E = rng.standard_normal((T, d)), rng.standard_normal((V, d))
+    targets = np.array([0, 11, 5, 6])
+    got = O.vocab_ce_fwd(X, [E[i * V // n:(i + 1) * V // n] for i in range(n)], targets)
+    ref = _ce_brute(X, E, targets)
+    np.testing.assert_allclose(got["loss"], ref[:, 0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got["lse"], ref[:, 1], rtol=1e-12, atol=1e-12)
+
+
+def test_vocab_ce_closed_forms():
+    rng = np.random.default_rng(63)
+    T, d, V = 5, 4, 16
+    E = rng.standard_normal((V, d))
+    targets = rng.integers(0, V, size=T)
+    shards = [E[0:4], E[4:8], E[8:12], E[12:16]]
+    # zero hidden states: every logit is 0, the loss is log V
+    r = O.vocab_ce_fwd(np.zeros((T, d)), shards, targets)
+    np.testing.assert_allclose(r["loss"], np.full(T, math.log(V)), rtol=1e-14)
+    # one logit 1000 above the rest: the loss of that target vanishes and
+    # the shifted log-sum-exp does not overflow
+    X = np.zeros((1, d))
+    X[0, 0] = 1.0
+    Eb = np.zeros((V, d))
+    Eb[9, 0] = 1000.0
+    r = O.vocab_ce_fwd(X, [Eb[0:8], Eb[8:16]], [9])
+    assert abs(r["loss"][0]) < 1e-300 and r["lse"][0] == pytest.approx(1000.0)
+    r = O.vocab_ce_fwd(X, [Eb[0:8], Eb[8:16]], [3])
+    assert r["loss"][0] == pytest.approx(1000.0)
+
+
+def test_vocab_ce_shard_count_independence():
+    rng = np.random.default_rng(64)
+    T, d, V = 6, 8, 48
+    X, E = rng.standard_normal((T, d)), rng.standard_normal((V, d))
+    targets = rng.integers(0, V, size=T)
+    ref = O.vocab_ce_fwd(X, [E], targets)
+    for n in (2, 4, 8):
+        got = O.vocab_ce_fwd(X, [E[i * V // n:(i + 1) * V // n] for i in range(n)], targets)
+        np.testing.assert_allclose(got["loss"], ref["loss"], rtol=1e-13)
+
+
+def test_vocab_ce_bwd_matches_finite_differences():
+    """Gradients of L = sum_t dloss_t loss_t: the shards' dX summands add up
+    to dL/dX, and dE_i is the i-th row block of dL/dE."""
+    rng = np.random.default_rng(65)
+    T, d, V, n = 5, 4, 12, 3
+    X, E = rng.standard_normal((T, d)), rng.standard_normal((V, d))
+    targets = np.array([0, 11, 4, 7, 3])
+    dloss = rng.uniform(0.5, 1.5, size=T)
+    shards = [E[i * V // n:(i + 1) * V // n] for i in range(n)]
+    lse = O.vocab_ce_fwd(X, shards, targets)["lse"]
+    parts = [O.vocab_ce_shard_bwd(X, shards[i], targets, i * V // n, lse, dloss) for i in range(n)]
+    dX = sum(p["dX"] for p in parts)
+    dE = np.concatenate([p["dE"] for p in parts])
+
+    def L(X_, E_):
+        return float((O.vocab_ce_fwd(X_, [E_[i * V // n:(i + 1) * V // n] for i in range(n)], targets)["loss"]
+                      * dloss).sum())
+
+    h = 1e-6
+    for (t, k) in [(0, 0), (2, 3), (4, 1)]:
+        Xp, Xm = X.copy(), X.copy()
+        Xp[t, k] += h
+        Xm[t, k] -= h
+        assert dX[t, k] == pytest.approx((L(Xp, E) - L(Xm, E)) / (2 * h), rel=1e-6, abs=1e-8)
+    for (v, k) in [(0, 0), (4, 2), (11, 3), (7, 1)]:
+        Ep, Em = E.copy(), E.copy()
+        Ep[v, k] += h
+        Em[v, k] -= h
+        assert dE[v, k] == pytest.approx((L(X, Ep) - L(X, Em)) / (2 * h), rel=1e-6, abs=1e-8)
+    # softmax minus one-hot: each token's gradient over the whole vocabulary sums to 0
+    dz = np.concatenate([p["dlogits"] for p in parts], axis=1)
+    np.testing.assert_allclose(dz.sum(axis=1), np.zeros(T), atol=1e-14)
+
+
 # --------------------------------------------------------------- input recipe
 
 def test_bf16_rounding_ties_to_even():

@@ -38,14 +38,14 @@ __all__ = [
     "Workload", "WORKLOADS", "round_to_bf16", "normal",
     "mlp_inputs", "swiglu_inputs", "attn_inputs", "reduce_inputs",
     "random_mlp", "random_swiglu", "random_attn", "gqa_inputs", "random_gqa",
-    "sp_inputs", "random_sp",
+    "sp_inputs", "random_sp", "vocab_inputs", "random_vocab", "zipf_token_ids",
 ]
 
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str               # "mlp" | "swiglu" | "attn" | "gqa" | "sp"
+    kind: str               # "mlp" | "swiglu" | "attn" | "gqa" | "sp" | "vocab"
     dtype: str              # "f32" | "bf16"
     b: int
     s: int
@@ -57,6 +57,8 @@ class Workload:
     kv_heads: int = 0            # grouped-query attention: key/value heads (0: = heads)
     w_std: float = 0.02
     p_drop: float = 0.0          # dropout probability (sequence-parallel block end)
+    vocab: int = 0               # vocabulary rows of the embedding table (padded)
+    vocab_used: int = 0          # ids drawn below this (the tokenizer's real vocabulary)
     full_weights: bool = False   # draw every shard's weights (else shard 0 only)
     backward: bool = True
     description: str = ""
@@ -98,6 +100,10 @@ WORKLOADS: Dict[str, Workload] = {
     "S1": Workload("S1", "sp", "bf16", b=2, s=4096, d=8192, n_shards=8, p_drop=0.1, backward=False,
                    description="sequence-parallel block end, 8192 tokens x 8192 over TP 8: "
                                "reduce-scatter to a 1024-token stripe, dropout, residual, LayerNorm"),
+    "E1": Workload("E1", "vocab", "bf16", b=8, s=1024, d=1024, n_shards=8, vocab=51200, vocab_used=50257,
+                   w_std=0.02,
+                   description="vocabulary-parallel input embedding and output embedding + cross-entropy, "
+                               "GPT-2-medium width, vocabulary 50257 padded to 51200, TP 8 -> 6400 rows here"),
 }
 
 
@@ -279,3 +285,39 @@ def random_sp(n_shards: int, rows: int, cols: int, dtype: str, seed: int = 0,
     keep = (rng.random((rows, cols), dtype=np.float32) >= p_drop).astype(np.uint8)
     return {"P": P, "residual": residual, "bias": bias, "gamma": gamma, "beta": beta, "keep": keep,
             "p_drop": p_drop}
+
+
+def zipf_token_ids(rng: np.random.Generator, n: int, vocab_used: int, a: float = 1.1) -> np.ndarray:
+    """Token ids with a heavy-tailed (Zipf, exponent a) frequency: rank r has
+    probability proportional to 1 / r^a, and ranks map to ids through one
+    fixed random permutation of [0, vocab_used), so frequent tokens fall in
+    every shard's rows."""
+    ranks = np.arange(1, vocab_used + 1, dtype=np.float64)
+    p = ranks ** -a
+    p /= p.sum()
+    perm = np.random.default_rng(12345).permutation(vocab_used)
+    return perm[rng.choice(vocab_used, size=n, p=p)].astype(np.int64)
+
+
+def vocab_inputs(wl: Workload, seed: int = 0) -> dict:
+    """Vocabulary-parallel inputs at the workload's shape (see random_vocab)."""
+    assert wl.kind == "vocab"
+    return random_vocab(wl.M, wl.d, wl.vocab, wl.vocab_used, wl.n_shards, wl.dtype, seed, wl.w_std)
+
+
+def random_vocab(T: int, d: int, vocab: int, vocab_used: int, n_shards: int, dtype: str, seed: int = 0,
+                 w_std: float = 0.02) -> dict:
+    """E [vocab x d] ~ N(0, w_std^2), the table shared by the input and the
+    output embedding (shard i holds rows [i V/n, (i+1) V/n)); ids and targets
+    [T] Zipf-distributed below vocab_used; X [T x d] ~ N(0,1), the hidden
+    states entering the output embedding; dloss [T] ~ U(0.5, 1.5) / T, the
+    upstream gradient of each token's loss.  Draw order E, ids, targets, X,
+    dloss."""
+    rng = np.random.default_rng(seed)
+    E = normal(rng, (vocab, d), w_std, dtype)
+    ids = zipf_token_ids(rng, T, vocab_used)
+    targets = zipf_token_ids(rng, T, vocab_used)
+    X = normal(rng, (T, d), 1.0, dtype)
+    dloss = (rng.uniform(0.5, 1.5, size=T) / T).astype(np.float32)
+    return {"E": E, "Es": [_rows(E, n_shards, i) for i in range(n_shards)], "ids": ids, "targets": targets,
+            "X": X, "dloss": dloss}
