@@ -9,8 +9,8 @@ algorithmic FLOP rate: 6 products of 2*M*N*K = 549.76 GFLOP each per step.
 
 Also reported (not the headline): the GPT-2-medium-shaped shard with all 8
 shards and both shard-reduces, the SwiGLU shard, the causal attention
-shard (fwd+bwd), the grouped-query attention shard and the sequence-parallel
-block end, each timed on its own.  The fp64 oracle runs the same step on the
+shard (fwd+bwd), the grouped-query attention shard, the sequence-parallel
+block end and the vocabulary-parallel embeddings, each timed on its own.  The fp64 oracle runs the same step on the
 host's cores (cpu_baseline, a baseline and not a target), and its outputs
 give the max relative error of every GPU output tensor.
 
@@ -439,6 +439,60 @@ def run_s1(tp, torch, steps, warmup):
             "kernels_ms": {key: round(sum(v) / len(v), 4) for key, v in per.items()}}
 
 
+def run_e1(tp, torch, steps, warmup):
+    """Vocabulary-parallel embeddings at GPT-2-medium width (vocabulary 51200
+    over TP 8, 8192 tokens): this GPU's input-embedding partial and the
+    shard-reduce of the 8 partials, then its output embedding + cross-entropy
+    forward, the combine of the 8 shards' per-token statistics, and the
+    backward (dlogits, dX summand, dE)."""
+    import tpsynth
+    wl = tpsynth.WORKLOADS["E1"]
+    inp = tpsynth.vocab_inputs(wl)
+    bf = torch.bfloat16
+    dev = lambda a: torch.from_numpy(a).to(bf).cuda()
+    n, T, d = wl.n_shards, wl.M, wl.d
+    vl = wl.vocab // n
+    E0, X = dev(inp["Es"][0]), dev(inp["X"])
+    ids, tg = torch.from_numpy(inp["ids"]).cuda(), torch.from_numpy(inp["targets"]).cuda()
+    dloss = torch.from_numpy(inp["dloss"]).cuda()
+    del inp
+    parts = torch.zeros((n, T, d), dtype=bf, device="cuda")
+    emb = torch.empty((T, d), dtype=bf, device="cuda")
+    logits = torch.empty((T, vl), dtype=bf, device="cuda")
+    stats = torch.zeros((n, T, 3), dtype=torch.float32, device="cuda")
+    stats[:, :, 1] = 1.0
+    loss, lse = (torch.empty(T, dtype=torch.float32, device="cuda") for _ in range(2))
+    dX = torch.empty((T, d), dtype=bf, device="cuda")
+    dE = torch.empty((vl, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tp.tp_vocab_ce_bwd_workspace_bytes(tp.TP_DT_BF16, T, d, vl), dtype=torch.uint8, device="cuda")
+
+    def step():
+        tp.tp_vocab_embed_fwd(ids, E0, parts[0], 0)
+        tp.tp_shard_reduce(parts, emb, n, T * d)
+        tp.tp_vocab_ce_fwd(X, E0, tg, logits, stats[0], 0)
+        tp.tp_vocab_ce_combine(stats, loss, lse)
+        tp.tp_vocab_ce_bwd(X, E0, tg, logits, lse, dloss, dX, dE, ws, 0)
+
+    ms, _, per = timed(tp, torch, step, steps, warmup, 12)
+    flops = 3 * gemm_flops(T, vl, d)
+    avg = lambda lab: (sum(per[lab]) / len(per[lab])) if per.get(lab) else None
+    gemm_ms = sum(avg(k) or 0.0 for k in ("vocab_ce.xet", "vocab_ce.dze", "vocab_ce.dztx"))
+    emb_ms = avg("vocab.embed")
+    # gather: ids + this shard's rows of the tokens it holds + the full partial written
+    own = int(((ids >= 0) & (ids < vl)).sum().item())
+    emb_bytes = T * 8 + own * d * 2 + T * d * 2
+    return {"workload": "E1 vocabulary-parallel embeddings, GPT-2-medium width: 8192 tokens, d 1024, "
+                        "vocabulary 51200 over TP 8 (6400 rows here); input embedding + shard-reduce, "
+                        "output embedding + cross-entropy fwd, combine, bwd",
+            "ms_per_step": round(ms, 4), "gemm_flop_per_step": flops,
+            "tflops": round(flops / ms / 1e9, 1),
+            "gemm_tflops": round(flops / gemm_ms / 1e9, 1) if gemm_ms else None,
+            "pct_of_peak_gemms": round(100 * flops / gemm_ms / 1e9 / PEAK_BF16_TFLOPS, 2) if gemm_ms else None,
+            "embed": {"bytes": emb_bytes, "ms": round(emb_ms, 4) if emb_ms else None,
+                      "GBps": round(emb_bytes / emb_ms / 1e6, 1) if emb_ms else None},
+            "kernels_ms": {key: round(sum(v) / len(v), 4) for key, v in per.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -514,7 +568,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         wls = {}
-        for name, fn in (("C2", run_c2), ("C3", run_c3), ("C4", run_c4), ("G1", run_g1), ("S1", run_s1)):
+        for name, fn in (("C2", run_c2), ("C3", run_c3), ("C4", run_c4), ("G1", run_g1), ("S1", run_s1), ("E1", run_e1)):
             log(f"timing {name}")
             wls[name] = fn(tp, torch, args.extra_steps, 2)
             torch.cuda.empty_cache()

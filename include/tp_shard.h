@@ -24,7 +24,9 @@
  *  - dtype TP_DT_BF16: bf16 operands, activations and partial outputs; every
  *    product accumulates in fp32; weight gradients are fp32.  TP_DT_F32: all
  *    fp32.  bf16 results are rounded to nearest, ties to even.
- *  - Every pointer except `stream` is a device pointer, 16-byte aligned.  The
+ *  - Every pointer except `stream` is a device pointer (tp_sp_all_gather's
+ *    stripe array and tp_shard_range's results are host memory), 16-byte
+ *    aligned unless an entry point says otherwise.  The
  *    caller owns all memory; the library allocates nothing, never
  *    synchronises and never changes the current device.  The only state it
  *    keeps between calls is thread-local: the last error text and the
@@ -50,7 +52,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 3
+#define TP_ABI_VERSION 4
 
 typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype_t;
 
@@ -60,7 +62,7 @@ typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype_t;
 #define TP_E_DIM       -2   /* a size is <= 0, too large, or not supported    */
 #define TP_E_DIVIS     -3   /* a size is not a multiple of what it must be    */
 #define TP_E_DTYPE     -4   /* unsupported dtype for this entry point         */
-#define TP_E_ALIGN     -5   /* a pointer is not 16-byte aligned               */
+#define TP_E_ALIGN     -5   /* a pointer is not aligned as required           */
 #define TP_E_ALIAS     -6   /* an output overlaps an input or another output  */
 #define TP_E_WORKSPACE -7   /* workspace NULL or smaller than required        */
 #define TP_E_HIP       -8   /* a HIP launch failed (text in the detail)       */
@@ -243,6 +245,74 @@ int tp_sp_reduce_scatter_ln(void* stream, tp_dtype_t dt, int64_t n_shards, int64
  * ------------------------------------------------------------------------- */
 int tp_sp_all_gather(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t stripe_rows,
                      int64_t cols, const void* const* stripes, void* full);
+
+/* ---------------------------------------------------------------------------
+ * tp_vocab_embed_fwd — one shard's partial of the vocabulary-parallel input
+ * embedding ([JY] Embedding: the table is split by vocabulary rows and the
+ * shards' results are all-reduced; Implementation, ParallelEmbedding).  The
+ * shard holds rows [vocab_start, vocab_start + vocab_local) of the table as
+ * E_local [vocab_local x d]:
+ *   Y[t, :] = E_local[ids[t] - vocab_start, :]  if the id is in that range,
+ *   Y[t, :] = 0                                 otherwise.
+ * The embedding is the SUM of the shards' Y (tp_shard_reduce on one GPU);
+ * an id outside [0, V) is in no shard and embeds as a zero row.  ids: int64
+ * [n_tokens] on the device; Y: [n_tokens x d] of dtype dt.  d and
+ * vocab_local multiples of 8 (TP_E_DIVIS), each <= 2^21; n_tokens <= 2^24.
+ * Token-id arrays need 8-byte and per-token fp32 arrays (stats, loss, lse,
+ * dloss) 4-byte alignment; tables and matrices 16 bytes.
+ * ------------------------------------------------------------------------- */
+int tp_vocab_embed_fwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d,
+                       int64_t vocab_local, int64_t vocab_start, const int64_t* ids,
+                       const void* E_local, void* Y);
+
+/* ---------------------------------------------------------------------------
+ * tp_vocab_ce_fwd — one shard of the output embedding fused with the
+ * cross-entropy ([JY] Embedding: fusing the loss into the output embedding
+ * leaves only per-token values to exchange instead of [bs x V] logits).
+ *   logits = X E_local^T                  [n_tokens x vocab_local], dtype dt
+ *   stats[t] = (m, s, z_t):  m = max_v logits[t, v],
+ *                            s = sum_v exp(logits[t, v] - m),
+ *                            z_t = logits[t, targets[t] - vocab_start] when
+ *                                  the target is one of the shard's rows, else 0
+ * with the statistics taken from the logits as stored (fp32 arithmetic).
+ * X: [n_tokens x d]; E_local: [vocab_local x d] (the same table slice as the
+ * input embedding's); targets: int64 [n_tokens]; stats: fp32 [n_tokens x 3].
+ * logits is kept for tp_vocab_ce_bwd.  Sizes as tp_vocab_embed_fwd.
+ * ------------------------------------------------------------------------- */
+int tp_vocab_ce_fwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d,
+                    int64_t vocab_local, int64_t vocab_start, const void* X,
+                    const void* E_local, const int64_t* targets, void* logits, float* stats);
+
+/* ---------------------------------------------------------------------------
+ * tp_vocab_ce_combine — the exchange of the fused cross-entropy on one GPU:
+ * the n_shards stats blocks (shard i at stats + i * shard_stride floats,
+ * shard_stride >= 3 * n_tokens) are merged per token, in shard order:
+ *   M = max_i m_i,  S = sum_i s_i exp(m_i - M),
+ *   lse[t] = M + log S,  loss[t] = lse[t] - sum_i z_t,i.
+ * A target outside [0, V) has no logit and its loss is lse.  loss, lse:
+ * fp32 [n_tokens].
+ * ------------------------------------------------------------------------- */
+int tp_vocab_ce_combine(void* stream, int64_t n_shards, int64_t n_tokens, const float* stats,
+                        int64_t shard_stride, float* loss, float* lse);
+
+/* ---------------------------------------------------------------------------
+ * tp_vocab_ce_bwd — backward of one shard of the fused output embedding and
+ * cross-entropy, given lse from tp_vocab_ce_combine and dloss[t] = dL/dloss[t]
+ * (fp32 [n_tokens]; a loss mask or the mean's 1/n_tokens goes here):
+ *   dz = (exp(logits - lse) - onehot(targets - vocab_start)) * dloss
+ *   dX = dz E_local     [n_tokens x d], dtype dt: this shard's summand of dX
+ *                        (summed over shards by the backward all-reduce)
+ *   dE = dz^T X          [vocab_local x d], fp32
+ * logits: tp_vocab_ce_fwd's output.  ws: device workspace of at least
+ * tp_vocab_ce_bwd_workspace_bytes(...) bytes, contents undefined on return.
+ * ------------------------------------------------------------------------- */
+int tp_vocab_ce_bwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d,
+                    int64_t vocab_local, int64_t vocab_start, const void* X,
+                    const void* E_local, const int64_t* targets, const void* logits,
+                    const float* lse, const float* dloss, void* dX, float* dE,
+                    void* ws, size_t ws_bytes);
+size_t tp_vocab_ce_bwd_workspace_bytes(tp_dtype_t dt, int64_t n_tokens, int64_t d,
+                                       int64_t vocab_local);
 
 /* ---------------------------------------------------------------------------
  * tp_shard_reduce — the local stand-in for the g (forward) and f (backward)

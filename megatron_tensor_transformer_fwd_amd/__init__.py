@@ -18,6 +18,8 @@ __all__ = [
     "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes",
     "tp_attn_shard_fwd", "tp_attn_gqa_shard_fwd", "tp_attn_shard_bwd", "tp_attn_shard_bwd_workspace_bytes",
     "tp_shard_reduce", "tp_shard_range", "tp_sp_reduce_scatter_ln", "tp_sp_all_gather",
+    "tp_vocab_embed_fwd", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
+    "tp_vocab_ce_bwd_workspace_bytes",
     "tp_abi_version", "EXPORTS",
 ]
 
@@ -55,6 +57,11 @@ EXPORTS = {
     "tp_sp_reduce_scatter_ln": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, _p, ctypes.c_float,
                                        _p, _p, ctypes.c_float, _p, _p]),
     "tp_sp_all_gather": (_i32, [_p, _i32, _i64, _i64, _i64, ctypes.POINTER(_p), _p]),
+    "tp_vocab_embed_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p]),
+    "tp_vocab_ce_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    "tp_vocab_ce_combine": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p]),
+    "tp_vocab_ce_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64] + [_p] * 6 + [_p, _p, _p, _sz]),
+    "tp_vocab_ce_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
     "tp_strerror": (ctypes.c_char_p, [_i32]),
     "tp_last_error_detail": (ctypes.c_char_p, []),
     "tp_abi_version": (_i32, []),
@@ -229,3 +236,45 @@ def tp_sp_all_gather(stripes, full, stream=None) -> None:
     rows, cols = stripes[0].shape
     arr = (_p * n)(*[_ptr(t) for t in stripes])
     _check(lib().tp_sp_all_gather(_stream(stream), _dt(full), n, rows, cols, arr, _ptr(full)))
+
+
+def _ids(t):
+    import torch
+    if t.dtype != torch.int64:
+        raise TypeError("token ids must be an int64 tensor")
+    return _ptr(t)
+
+
+def tp_vocab_embed_fwd(ids, E_local, Y, vocab_start: int, stream=None) -> None:
+    """Y = this shard's partial of the input embedding (rows of E_local for
+    the ids it holds, zero rows for the rest)."""
+    vl, d = E_local.shape
+    _check(lib().tp_vocab_embed_fwd(_stream(stream), _dt(E_local), ids.numel(), d, vl, vocab_start, _ids(ids),
+                                    _ptr(E_local), _ptr(Y)))
+
+
+def tp_vocab_ce_fwd(X, E_local, targets, logits, stats, vocab_start: int, stream=None) -> None:
+    """logits = X E_local^T and the per-token (max, sum-exp, target logit)."""
+    n_tokens, d = X.shape
+    vl = E_local.shape[0]
+    _check(lib().tp_vocab_ce_fwd(_stream(stream), _dt(X), n_tokens, d, vl, vocab_start, _ptr(X), _ptr(E_local),
+                                 _ids(targets), _ptr(logits), _ptr(stats)))
+
+
+def tp_vocab_ce_combine(stats, loss, lse, stream=None) -> None:
+    """stats [n_shards x n_tokens x 3] fp32 -> per-token loss and log-sum-exp."""
+    n, n_tokens = stats.shape[0], stats.shape[1]
+    _check(lib().tp_vocab_ce_combine(_stream(stream), n, n_tokens, _ptr(stats), n_tokens * 3, _ptr(loss),
+                                     _ptr(lse)))
+
+
+def tp_vocab_ce_bwd_workspace_bytes(dtype: int, n_tokens: int, d: int, vocab_local: int) -> int:
+    return lib().tp_vocab_ce_bwd_workspace_bytes(dtype, n_tokens, d, vocab_local)
+
+
+def tp_vocab_ce_bwd(X, E_local, targets, logits, lse, dloss, dX, dE, ws, vocab_start: int, stream=None) -> None:
+    n_tokens, d = X.shape
+    vl = E_local.shape[0]
+    _check(lib().tp_vocab_ce_bwd(_stream(stream), _dt(X), n_tokens, d, vl, vocab_start, _ptr(X), _ptr(E_local),
+                                 _ids(targets), _ptr(logits), _ptr(lse), _ptr(dloss), _ptr(dX), _ptr(dE),
+                                 _ptr(ws), ws.numel() * ws.element_size()))

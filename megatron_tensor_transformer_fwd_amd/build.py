@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtpshard.so")
 ARCH = "gfx950"
 
-SOURCES = ["shard_reduce.hip", "mlp.hip", "swiglu.hip", "attention.hip", "attention_bwd.hip", "sp.hip", "tp_shard.cpp"]
+SOURCES = ["shard_reduce.hip", "mlp.hip", "swiglu.hip", "attention.hip", "attention_bwd.hip", "sp.hip", "vocab.hip", "tp_shard.cpp"]
 
 
 def hipcc() -> str:

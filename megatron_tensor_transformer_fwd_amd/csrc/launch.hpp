@@ -55,4 +55,17 @@ hipError_t launch_sp_reduce_scatter_ln(hipStream_t st, int dt, int n, int64_t ro
 hipError_t launch_sp_all_gather(hipStream_t st, int dt, int n, int64_t stripe_rows, int64_t cols,
                                 const void* const* stripes, void* full);
 
+hipError_t launch_vocab_embed_fwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
+                                  int64_t vstart, const int64_t* ids, const void* E, void* Y);
+hipError_t launch_vocab_ce_fwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
+                               int64_t vstart, const void* X, const void* E, const int64_t* targets,
+                               void* logits, float* stats);
+hipError_t launch_vocab_ce_combine(hipStream_t st, int n, int64_t n_tokens, const float* stats,
+                                   int64_t shard_stride, float* loss, float* lse);
+size_t vocab_ce_bwd_ws_bytes(int dt, int64_t n_tokens, int64_t d, int64_t vlocal);
+hipError_t launch_vocab_ce_bwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
+                               int64_t vstart, const void* X, const void* E, const int64_t* targets,
+                               const void* logits, const float* lse, const float* dloss, void* dX, float* dE,
+                               void* ws);
+
 }  // namespace tpk

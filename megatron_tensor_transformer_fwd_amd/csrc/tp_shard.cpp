@@ -61,6 +61,7 @@ struct Span {
   const char* name;
   const void* p;
   size_t bytes;
+  size_t align = 16;   // required alignment in bytes
 };
 
 bool overlap(const Span& a, const Span& b) {
@@ -85,8 +86,8 @@ int check_buffers(const std::vector<Span>& ins, const std::vector<Span>& outs,
   }
   for (const auto* v : {&ins, &outs})
     for (const auto& s : *v)
-      if (s.p && (reinterpret_cast<uintptr_t>(s.p) & 15u))
-        return fail(TP_E_ALIGN, "%s (%p) is not 16-byte aligned", s.name, s.p);
+      if (s.p && (reinterpret_cast<uintptr_t>(s.p) & (s.align - 1)))
+        return fail(TP_E_ALIGN, "%s (%p) is not %zu-byte aligned", s.name, s.p, s.align);
   for (size_t i = 0; i < outs.size(); ++i) {
     for (const auto& in : ins)
       if (overlap(outs[i], in)) return fail(TP_E_ALIAS, "output %s overlaps input %s", outs[i].name, in.name);
@@ -123,6 +124,18 @@ int mlp_common(tp_dtype_t dt, int64_t M, int64_t d, int64_t f) {
   TP_CHECK(check_mult8({{"d", d}, {"f", f}}));
   TP_CHECK(check_ld({{"d", d}, {"f", f}}));
   if ((double)M * (double)std::max(d, f) * 2 > 9.0e15) return fail(TP_E_DIM, "operand too large");
+  return TP_OK;
+}
+
+int vocab_common(tp_dtype_t dt, int64_t n_tokens, int64_t d, int64_t vocab_local, int64_t vocab_start) {
+  if (!dtype_ok(dt)) return fail(TP_E_DTYPE, "dtype %d is not TP_DT_F32 or TP_DT_BF16", (int)dt);
+  TP_CHECK(check_dims({{"n_tokens", n_tokens}, {"d", d}, {"vocab_local", vocab_local}}));
+  TP_CHECK(check_mult8({{"d", d}, {"vocab_local", vocab_local}}));
+  TP_CHECK(check_ld({{"d", d}, {"vocab_local", vocab_local}}));
+  if (n_tokens > (int64_t(1) << 24)) return fail(TP_E_DIM, "n_tokens = %lld exceeds 2^24", (long long)n_tokens);
+  if (vocab_start < 0 || vocab_start > (int64_t(1) << 40))
+    return fail(TP_E_DIM, "vocab_start = %lld outside [0, 2^40]", (long long)vocab_start);
+  if ((double)n_tokens * (double)std::max(d, vocab_local) * 2 > 9.0e15) return fail(TP_E_DIM, "operand too large");
   return TP_OK;
 }
 
@@ -173,7 +186,7 @@ const char* tp_strerror(int status) {
     case TP_E_DIM: return "size is non-positive, too large or unsupported";
     case TP_E_DIVIS: return "size is not a multiple of what it must be";
     case TP_E_DTYPE: return "unsupported dtype";
-    case TP_E_ALIGN: return "pointer is not 16-byte aligned";
+    case TP_E_ALIGN: return "pointer is not aligned as required";
     case TP_E_ALIAS: return "output overlaps an input or another output";
     case TP_E_WORKSPACE: return "workspace missing or too small";
     case TP_E_HIP: return "HIP launch failed";
@@ -441,6 +454,76 @@ int tp_sp_all_gather(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t stri
   return hip_status(tpk::launch_sp_all_gather(static_cast<hipStream_t>(stream), dt, (int)n_shards, stripe_rows, cols,
                                               src, full),
                     "tp_sp_all_gather");
+}
+
+int tp_vocab_embed_fwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d, int64_t vocab_local,
+                       int64_t vocab_start, const int64_t* ids, const void* E_local, void* Y) {
+  TP_CHECK(vocab_common(dt, n_tokens, d, vocab_local, vocab_start));
+  const size_t e = esize(dt);
+  TP_CHECK(check_buffers({{"ids", ids, (size_t)n_tokens * 8, 8}, {"E_local", E_local, (size_t)(vocab_local * d) * e}},
+                         {{"Y", Y, (size_t)(n_tokens * d) * e}}, {"ids", "E_local", "Y"}));
+  return hip_status(tpk::launch_vocab_embed_fwd(static_cast<hipStream_t>(stream), dt, n_tokens, d, vocab_local,
+                                                vocab_start, ids, E_local, Y),
+                    "tp_vocab_embed_fwd");
+}
+
+int tp_vocab_ce_fwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d, int64_t vocab_local,
+                    int64_t vocab_start, const void* X, const void* E_local, const int64_t* targets,
+                    void* logits, float* stats) {
+  TP_CHECK(vocab_common(dt, n_tokens, d, vocab_local, vocab_start));
+  const size_t e = esize(dt);
+  TP_CHECK(check_buffers({{"X", X, (size_t)(n_tokens * d) * e},
+                          {"E_local", E_local, (size_t)(vocab_local * d) * e},
+                          {"targets", targets, (size_t)n_tokens * 8, 8}},
+                         {{"logits", logits, (size_t)(n_tokens * vocab_local) * e},
+                          {"stats", stats, (size_t)n_tokens * 12, 4}},
+                         {"X", "E_local", "targets", "logits", "stats"}));
+  return hip_status(tpk::launch_vocab_ce_fwd(static_cast<hipStream_t>(stream), dt, n_tokens, d, vocab_local,
+                                             vocab_start, X, E_local, targets, logits, stats),
+                    "tp_vocab_ce_fwd");
+}
+
+int tp_vocab_ce_combine(void* stream, int64_t n_shards, int64_t n_tokens, const float* stats,
+                        int64_t shard_stride, float* loss, float* lse) {
+  if (n_shards <= 0 || n_shards > 4096) return fail(TP_E_DIM, "n_shards = %lld outside [1, 4096]", (long long)n_shards);
+  TP_CHECK(check_dims({{"n_tokens", n_tokens}}));
+  if (shard_stride < 3 * n_tokens)
+    return fail(TP_E_DIM, "shard_stride %lld < 3 * n_tokens %lld", (long long)shard_stride, (long long)(3 * n_tokens));
+  TP_CHECK(check_buffers({{"stats", stats, ((size_t)(n_shards - 1) * shard_stride + 3 * n_tokens) * 4, 4}},
+                         {{"loss", loss, (size_t)n_tokens * 4, 4}, {"lse", lse, (size_t)n_tokens * 4, 4}},
+                         {"stats", "loss", "lse"}));
+  return hip_status(tpk::launch_vocab_ce_combine(static_cast<hipStream_t>(stream), (int)n_shards, n_tokens, stats,
+                                                 shard_stride, loss, lse),
+                    "tp_vocab_ce_combine");
+}
+
+size_t tp_vocab_ce_bwd_workspace_bytes(tp_dtype_t dt, int64_t n_tokens, int64_t d, int64_t vocab_local) {
+  if (vocab_common(dt, n_tokens, d, vocab_local, 0) != TP_OK) return 0;
+  return tpk::vocab_ce_bwd_ws_bytes(dt, n_tokens, d, vocab_local);
+}
+
+int tp_vocab_ce_bwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d, int64_t vocab_local,
+                    int64_t vocab_start, const void* X, const void* E_local, const int64_t* targets,
+                    const void* logits, const float* lse, const float* dloss, void* dX, float* dE,
+                    void* ws, size_t ws_bytes) {
+  TP_CHECK(vocab_common(dt, n_tokens, d, vocab_local, vocab_start));
+  const size_t e = esize(dt);
+  const size_t need = tpk::vocab_ce_bwd_ws_bytes(dt, n_tokens, d, vocab_local);
+  TP_CHECK(check_buffers({{"X", X, (size_t)(n_tokens * d) * e},
+                          {"E_local", E_local, (size_t)(vocab_local * d) * e},
+                          {"targets", targets, (size_t)n_tokens * 8, 8},
+                          {"logits", logits, (size_t)(n_tokens * vocab_local) * e},
+                          {"lse", lse, (size_t)n_tokens * 4, 4},
+                          {"dloss", dloss, (size_t)n_tokens * 4, 4}},
+                         {{"dX", dX, (size_t)(n_tokens * d) * e},
+                          {"dE", dE, (size_t)(vocab_local * d) * 4},
+                          {"ws", ws, need}},
+                         {"X", "E_local", "targets", "logits", "lse", "dloss", "dX", "dE"}));
+  if (!ws || ws_bytes < need)
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes, %zu needed", ws ? ws_bytes : (size_t)0, need);
+  return hip_status(tpk::launch_vocab_ce_bwd(static_cast<hipStream_t>(stream), dt, n_tokens, d, vocab_local,
+                                             vocab_start, X, E_local, targets, logits, lse, dloss, dX, dE, ws),
+                    "tp_vocab_ce_bwd");
 }
 
 }  // extern "C"

@@ -1,0 +1,230 @@
+// Vocabulary-parallel embeddings ([JY] Embedding and Implementation).
+//
+// Input embedding.  Shard i holds rows [vocab_start, vocab_start + V_local)
+// of the table E.  A token whose id falls in that range reads its row; every
+// other token gets a zero row; the all-reduce SUM over shards (the
+// shard-reduce on one GPU) then yields E[id] for every token.  HBM-bound
+// gather: each 16-byte chunk of an output row is one thread's copy (or zero
+// fill), so a row is written by consecutive lanes.
+//
+// Output embedding fused with the cross-entropy.  The shard's logits
+// z = X E_local^T come from the bf16 MFMA GEMM; a row pass then reduces every
+// token's logits to three numbers, m = max z, s = sum exp(z - m) and the
+// target's logit when the target is one of the shard's rows.  Only these
+// 3 * n_tokens values per shard cross GPUs (the combine kernel is the
+// exchange), not the [n_tokens x V] logits.  The statistics are taken from the
+// logits as stored (bf16 in the bf16 path), the values the backward reads.
+// Backward: dz = (exp(z - lse) - onehot(target)) dloss per row, then
+// dX_i = dz E_local (this shard's summand of dX) and dE_local = dz^T X.
+#include <cfloat>
+
+#include "epilogues.hpp"
+#include "gemm_dispatch.hpp"
+
+namespace tpk {
+
+// ----------------------------------------------------------- input embedding
+
+// Y[t, :] = E_local[ids[t] - vstart, :] when the id is in the shard, else 0.
+// `rowvec` 16-byte vectors per row.
+__global__ void __launch_bounds__(256)
+vocab_embed_kernel(const int64_t* __restrict__ ids, int64_t n_tokens, int64_t rowvec, int64_t vstart,
+                   int64_t vlocal, const u32x4* __restrict__ E, u32x4* __restrict__ Y) {
+  const int64_t total = n_tokens * rowvec;
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < total; v += step) {
+    const int64_t t = v / rowvec, c = v - t * rowvec;
+    const int64_t local = ids[t] - vstart;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (local >= 0 && local < vlocal) w = E[local * rowvec + c];
+    Y[v] = w;
+  }
+}
+
+// ------------------------------------------------------ cross-entropy rows
+
+// (m, s) pairs with s = sum exp(z - m), merged without overflow.
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  s = s * __expf(m - M) + s2 * __expf(m2 - M);
+  m = M;
+}
+
+// One workgroup per token row of the shard's logits [n_tokens x vlocal].
+template <class T>
+__global__ void __launch_bounds__(256)
+ce_row_stats_kernel(const T* __restrict__ logits, int64_t vlocal, const int64_t* __restrict__ targets,
+                    int64_t vstart, float* __restrict__ stats) {
+  __shared__ float red_m[4], red_s[4];
+  const int64_t t = blockIdx.x;
+  const T* row = logits + t * vlocal;
+  float m = -FLT_MAX, s = 0.f;
+  for (int64_t c = (int64_t)threadIdx.x * 8; c < vlocal; c += 256 * 8) {
+    float z[8];
+    Vec8<T>::load(row + c, z);
+    float cm = z[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, z[e]);
+    if (cm > m) {
+      s *= __expf(m - cm);
+      m = cm;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += __expf(z[e] - m);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+    ms_merge(m, s, m2, s2);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red_m[threadIdx.x >> 6] = m;
+    red_s[threadIdx.x >> 6] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = red_m[0];
+    s = red_s[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) ms_merge(m, s, red_m[w], red_s[w]);
+    const int64_t local = targets[t] - vstart;
+    const float zt = (local >= 0 && local < vlocal) ? to_f32(row[local]) : 0.f;
+    stats[t * 3 + 0] = m;
+    stats[t * 3 + 1] = s;
+    stats[t * 3 + 2] = zt;
+  }
+}
+
+// The exchange: per token, the shards' (m, s, z_t) -> log-sum-exp and loss.
+// Shards are merged in order 0..n-1.
+__global__ void __launch_bounds__(256)
+ce_combine_kernel(const float* __restrict__ stats, int64_t shard_stride, int n, int64_t n_tokens,
+                  float* __restrict__ loss, float* __restrict__ lse) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n_tokens) return;
+  float M = -FLT_MAX;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, stats[i * shard_stride + t * 3]);
+  float S = 0.f, zt = 0.f;
+  for (int i = 0; i < n; ++i) {
+    const float* p = stats + i * shard_stride + t * 3;
+    S += p[1] * __expf(p[0] - M);
+    zt += p[2];
+  }
+  const float l = M + __logf(S);
+  lse[t] = l;
+  loss[t] = l - zt;
+}
+
+// dz[t, v] = (exp(z[t, v] - lse[t]) - [v == target - vstart]) * dloss[t].
+template <class T>
+__global__ void __launch_bounds__(256)
+ce_dlogits_kernel(const T* __restrict__ logits, int64_t n_tokens, int64_t vlocal,
+                  const int64_t* __restrict__ targets, int64_t vstart, const float* __restrict__ lse,
+                  const float* __restrict__ dloss, T* __restrict__ dz) {
+  const int64_t rowvec = vlocal / 8, total = n_tokens * rowvec;
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < total; v += step) {
+    const int64_t t = v / rowvec, c = (v - t * rowvec) * 8;
+    const float l = lse[t], g = dloss[t];
+    const int64_t hit = targets[t] - vstart - c;   // in [0, 8) when the target is in this chunk
+    float z[8];
+    Vec8<T>::load(logits + t * vlocal + c, z);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (__expf(z[e] - l) - (hit == e ? 1.f : 0.f)) * g;
+    Vec8<T>::store(dz + t * vlocal + c, z);
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+static size_t up256v(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static unsigned flat_blocks(int64_t work) {
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(work, 256), 256 * 16));
+}
+
+hipError_t launch_vocab_embed_fwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
+                                  int64_t vstart, const int64_t* ids, const void* E, void* Y) {
+  const int64_t rowvec = d * (dt == DT_BF16 ? 2 : 4) / 16;
+  return launch("vocab.embed", vocab_embed_kernel, dim3(flat_blocks(n_tokens * rowvec)), dim3(256), st, ids,
+                n_tokens, rowvec, vstart, vlocal, static_cast<const u32x4*>(E), static_cast<u32x4*>(Y));
+}
+
+hipError_t launch_vocab_ce_fwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
+                               int64_t vstart, const void* X, const void* E, const int64_t* targets,
+                               void* logits, float* stats) {
+  if (dt == DT_BF16) {  // z = X E^T:  B(k, n) = E[n][k]
+    GemmParams p = make_params(n_tokens, vlocal, make_seg(X, d, n_tokens * d, E, d, vlocal * d, d));
+    EpiStore<bf16> e{static_cast<bf16*>(logits), vlocal, 0};
+    TPK_TRY((launch_gemm<true, true, false>(st, "vocab_ce.xet", p, e, plan_gemm(n_tokens, vlocal, d, false, false))));
+    return launch("vocab_ce.row_stats", ce_row_stats_kernel<bf16>, dim3((unsigned)n_tokens), dim3(256), st,
+                  static_cast<const bf16*>(logits), vlocal, targets, vstart, stats);
+  }
+  GemmParamsF32 p = make_params_f32(n_tokens, vlocal, make_seg_f32(X, d, n_tokens, E, d, vlocal, d));
+  EpiStore<float> e{static_cast<float*>(logits), vlocal, 0};
+  TPK_TRY((launch_gemm_f32<true, true, false>(st, "vocab_ce_f32.nt", p, e)));
+  return launch("vocab_ce.row_stats", ce_row_stats_kernel<float>, dim3((unsigned)n_tokens), dim3(256), st,
+                static_cast<const float*>(logits), vlocal, targets, vstart, stats);
+}
+
+hipError_t launch_vocab_ce_combine(hipStream_t st, int n, int64_t n_tokens, const float* stats,
+                                   int64_t shard_stride, float* loss, float* lse) {
+  return launch("vocab_ce.combine", ce_combine_kernel, dim3((unsigned)cdiv(n_tokens, 256)), dim3(256), st, stats,
+                shard_stride, n, n_tokens, loss, lse);
+}
+
+struct VocabBwdPlan {
+  GemmPlan dE;
+  size_t dz_bytes, split_bytes;
+};
+
+static VocabBwdPlan vocab_bwd_plan(int dt, int64_t n_tokens, int64_t d, int64_t vlocal) {
+  VocabBwdPlan pl;
+  pl.dz_bytes = up256v((size_t)n_tokens * vlocal * (dt == DT_BF16 ? 2 : 4));
+  pl.dE = dt == DT_BF16 ? plan_gemm(vlocal, d, n_tokens, false, true) : GemmPlan{CFG_S, 1};
+  pl.split_bytes = pl.dE.split > 1 ? up256v((size_t)pl.dE.split * vlocal * d * 4) : 0;
+  return pl;
+}
+
+size_t vocab_ce_bwd_ws_bytes(int dt, int64_t n_tokens, int64_t d, int64_t vlocal) {
+  const VocabBwdPlan pl = vocab_bwd_plan(dt, n_tokens, d, vlocal);
+  return pl.dz_bytes + pl.split_bytes;
+}
+
+hipError_t launch_vocab_ce_bwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
+                               int64_t vstart, const void* X, const void* E, const int64_t* targets,
+                               const void* logits, const float* lse, const float* dloss, void* dX, float* dE,
+                               void* ws) {
+  const VocabBwdPlan pl = vocab_bwd_plan(dt, n_tokens, d, vlocal);
+  const dim3 grid(flat_blocks(n_tokens * vlocal / 8));
+  if (dt == DT_BF16) {
+    bf16* dz = static_cast<bf16*>(ws);
+    float* split_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.dz_bytes);
+    TPK_TRY(launch("vocab_ce.dlogits", ce_dlogits_kernel<bf16>, grid, dim3(256), st,
+                   static_cast<const bf16*>(logits), n_tokens, vlocal, targets, vstart, lse, dloss, dz));
+    {  // dX = dz E:  B(k, n) = E[k][n]
+      GemmParams p = make_params(n_tokens, d, make_seg(dz, vlocal, n_tokens * vlocal, E, d, vlocal * d, vlocal));
+      EpiStore<bf16> e{static_cast<bf16*>(dX), d, 0};
+      TPK_TRY((launch_gemm<true, false, false>(st, "vocab_ce.dze", p, e, plan_gemm(n_tokens, d, vlocal, false, false))));
+    }
+    {  // dE = dz^T X:  A(m, k) = dz[k][m], B(k, n) = X[k][n]
+      GemmParams p = make_params(vlocal, d, make_seg(dz, vlocal, n_tokens * vlocal, X, d, n_tokens * d, n_tokens));
+      return wgrad_f32_out(st, pl.dE, vlocal, d, dE, split_ws, [&](const EpiStore<float>& e, GemmPlan g) {
+        return launch_gemm<false, false, false>(st, "vocab_ce.dztx", p, e, g);
+      });
+    }
+  }
+  float* dz = static_cast<float*>(ws);
+  TPK_TRY(launch("vocab_ce.dlogits", ce_dlogits_kernel<float>, grid, dim3(256), st,
+                 static_cast<const float*>(logits), n_tokens, vlocal, targets, vstart, lse, dloss, dz));
+  {
+    GemmParamsF32 p = make_params_f32(n_tokens, d, make_seg_f32(dz, vlocal, n_tokens, E, d, d, vlocal));
+    EpiStore<float> e{static_cast<float*>(dX), d, 0};
+    TPK_TRY((launch_gemm_f32<true, false, false>(st, "vocab_ce_f32.nn", p, e)));
+  }
+  GemmParamsF32 p = make_params_f32(vlocal, d, make_seg_f32(dz, vlocal, vlocal, X, d, d, n_tokens));
+  EpiStore<float> e{dE, d, 0};
+  return launch_gemm_f32<false, false, false>(st, "vocab_ce_f32.tn", p, e);
+}
+
+}  // namespace tpk

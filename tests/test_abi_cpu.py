@@ -33,7 +33,7 @@ def test_header_and_binding_agree_and_library_exports_all():
 
 
 def test_version_and_strerror():
-    assert tp.tp_abi_version() == 3
+    assert tp.tp_abi_version() == 4
     L = tp.lib()
     for code in (OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP):
         assert L.tp_strerror(code) and L.tp_strerror(code) != b"unknown status"
@@ -277,3 +277,40 @@ def test_sp_all_gather_validation():
     assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, arr(s0, full, s2, s3), full) == E_ALIAS
     # exactly in place is accepted (it is not copied); the launch then fails without a device
     assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, arr(s0, full + stripe, s2, s3), full) == E_HIP
+
+
+def test_vocab_validation():
+    L = tp.lib()
+    ids, E, Y, X, tg, lg, st, loss, lse, dl, dX, dE, ws = _addrs(13)
+    # input embedding
+    assert L.tp_vocab_embed_fwd(None, 3, 16, 64, 128, 0, ids, E, Y) == E_DTYPE
+    assert L.tp_vocab_embed_fwd(None, BF16, 0, 64, 128, 0, ids, E, Y) == E_DIM
+    assert L.tp_vocab_embed_fwd(None, BF16, 16, 60, 128, 0, ids, E, Y) == E_DIVIS
+    assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 100, 0, ids, E, Y) == E_DIVIS
+    assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, -1, ids, E, Y) == E_DIM
+    assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, None, E, Y) == E_NULL
+    assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, ids + 4, E, Y) == E_ALIGN
+    assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, ids + 8, E, Y) == E_HIP   # 8 bytes suffice
+    assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, ids, E + 8, Y) == E_ALIGN
+    assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, ids, E, E + 64) == E_ALIAS
+    assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, (1 << 21) + 8, 0, ids, E, Y) == E_DIM
+    assert L.tp_vocab_embed_fwd(None, BF16, (1 << 24) + 1, 64, 128, 0, ids, E, Y) == E_DIM
+    # fused output embedding + cross-entropy
+    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, lg, None) == E_NULL
+    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, None, lg, st) == E_NULL
+    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, lg, lg + 16) == E_ALIAS
+    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, X, st) == E_ALIAS
+    assert L.tp_vocab_ce_combine(None, 0, 16, st, 48, loss, lse) == E_DIM
+    assert L.tp_vocab_ce_combine(None, 4, 16, st, 40, loss, lse) == E_DIM       # stride < 3 * n_tokens
+    assert L.tp_vocab_ce_combine(None, 4, 16, st, 48, loss, loss) == E_ALIAS
+    assert L.tp_vocab_ce_combine(None, 4, 16, st + 2, 48, loss, lse) == E_ALIGN
+    assert L.tp_vocab_ce_combine(None, 4, 16, st + 4, 49, loss + 12, lse + 4) == E_HIP
+    assert L.tp_vocab_ce_combine(None, 4, 16, st, 48, st + 64, lse) == E_ALIAS
+    need = L.tp_vocab_ce_bwd_workspace_bytes(BF16, 16, 64, 128)
+    assert need >= 16 * 128 * 2
+    assert L.tp_vocab_ce_bwd_workspace_bytes(BF16, 16, 64, 100) == 0
+    args = [X, E, tg, lg, lse, dl, dX, dE]
+    assert L.tp_vocab_ce_bwd(None, BF16, 16, 64, 128, 0, *args, None, 0) == E_WS
+    assert L.tp_vocab_ce_bwd(None, BF16, 16, 64, 128, 0, *args, ws, need - 1) == E_WS
+    assert L.tp_vocab_ce_bwd(None, BF16, 16, 64, 128, 0, *args[:6], X, dE, ws, need) == E_ALIAS
+    assert L.tp_vocab_ce_bwd(None, BF16, 16, 64, 128, 0, *args[:7], None, ws, need) == E_NULL

@@ -1,0 +1,183 @@
+"""Parity of the vocabulary-parallel embeddings (through the C ABI) against
+the fp64 oracle ([JY] Embedding and Implementation).  The input embedding is
+byte work and must match bit for bit, per shard and after the shard-reduce
+(the all-reduce's stand-in).  The fused output embedding + cross-entropy is
+floating point: max_rel_err <= 2e-2 for bf16, <= 1e-5 for fp32, on the loss,
+the log-sum-exp, the logits and both gradients.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import tpsynth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import megatron_tensor_transformer_fwd_amd as m
+    m.lib()          # raises if the library is missing: no fallback path exists
+    return m
+
+
+def _tdt(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(dtype=_tdt(dtype)).cuda()
+
+
+def dev_i64(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check(name, got, ref, dtype):
+    err = O.max_rel_err(host(got) if torch.is_tensor(got) else got, ref)
+    assert np.isfinite(err) and err <= TOL[dtype], f"{name}: max_rel_err {err:.3e} > {TOL[dtype]}"
+    return err
+
+
+# ------------------------------------------------------------ input embedding
+
+@pytest.mark.parametrize("dtype,T,d,V,n", [
+    ("f32", 37, 24, 64, 2),
+    ("bf16", 100, 1000, 96, 3),        # row width not a multiple of a 16-byte sweep of 256 lanes
+    ("bf16", 1, 8, 8, 1),              # one token, one shard
+    ("bf16", 8192, 1024, 51200, 8),    # GPT-2-medium width, padded vocabulary, TP 8
+])
+def test_vocab_embed_bit_exact(tp, dtype, T, d, V, n):
+    _say(f"vocab embed {dtype} T={T} d={d} V={V} n={n}")
+    rng = np.random.default_rng(70)
+    E = tpsynth.normal(rng, (V, d), 0.02, dtype)
+    ids = tpsynth.zipf_token_ids(rng, T, V) if T > 16 else rng.integers(0, V, size=T)
+    ids[: min(T, 3)] = [V - 1, -1, V][: min(T, 3)]        # last row, and two ids in no shard
+    g_ids = dev_i64(ids)
+    vl = V // n
+    parts = torch.empty((n, T, d), dtype=_tdt(dtype), device="cuda")
+    for i in range(n):
+        tp.tp_vocab_embed_fwd(g_ids, dev(E[i * vl:(i + 1) * vl], dtype), parts[i], i * vl)
+    full = torch.empty((T, d), dtype=_tdt(dtype), device="cuda")
+    tp.tp_shard_reduce(parts, full, n, T * d)
+    torch.cuda.synchronize()
+    for i in range(n):
+        np.testing.assert_array_equal(host(parts[i]), O.vocab_embed_shard(ids, E[i * vl:(i + 1) * vl], i * vl))
+    np.testing.assert_array_equal(host(full), O.vocab_embed(ids, [E[i * vl:(i + 1) * vl] for i in range(n)]))
+
+
+# ------------------------------------------- output embedding + cross-entropy
+
+def run_ce(tp, inp, n, dtype, dloss=None, backward=True):
+    X, E, targets = inp["X"], inp["E"], inp["targets"]
+    T, d = X.shape
+    vl = E.shape[0] // n
+    gX, gt = dev(X, dtype), dev_i64(targets)
+    gE = [dev(E[i * vl:(i + 1) * vl], dtype) for i in range(n)]
+    logits = torch.empty((n, T, vl), dtype=_tdt(dtype), device="cuda")
+    stats = torch.empty((n, T, 3), dtype=torch.float32, device="cuda")
+    for i in range(n):
+        tp.tp_vocab_ce_fwd(gX, gE[i], gt, logits[i], stats[i], i * vl)
+    loss = torch.empty(T, dtype=torch.float32, device="cuda")
+    lse = torch.empty(T, dtype=torch.float32, device="cuda")
+    tp.tp_vocab_ce_combine(stats, loss, lse)
+    out = {"logits": logits, "stats": stats, "loss": loss, "lse": lse}
+    if backward:
+        gdl = torch.from_numpy(np.ascontiguousarray(dloss, dtype=np.float32)).cuda()
+        dt = tp.TP_DT_BF16 if dtype == "bf16" else tp.TP_DT_F32
+        ws = torch.empty(tp.tp_vocab_ce_bwd_workspace_bytes(dt, T, d, vl), dtype=torch.uint8, device="cuda")
+        dX = torch.empty((n, T, d), dtype=_tdt(dtype), device="cuda")
+        dE = torch.empty((n, vl, d), dtype=torch.float32, device="cuda")
+        for i in range(n):
+            tp.tp_vocab_ce_bwd(gX, gE[i], gt, logits[i], lse, gdl, dX[i], dE[i], ws, i * vl)
+        dXsum = torch.empty((T, d), dtype=_tdt(dtype), device="cuda")
+        tp.tp_shard_reduce(dX, dXsum, n, T * d)
+        out.update(dX=dX, dE=dE, dXsum=dXsum)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("dtype,T,d,V,n", [
+    ("f32", 64, 32, 96, 3),
+    ("bf16", 100, 64, 200, 5),        # 40 vocabulary rows per shard: ragged tiles everywhere
+    ("bf16", 257, 128, 1024, 2),
+    ("bf16", 512, 1024, 6400, 1),     # one shard holds the whole vocabulary
+])
+def test_vocab_ce_small(tp, dtype, T, d, V, n):
+    _say(f"vocab ce {dtype} T={T} d={d} V={V} n={n}")
+    inp = tpsynth.random_vocab(T, d, V, V, n, dtype, seed=71, w_std=0.05)
+    inp["targets"][:2] = [0, V - 1]
+    out = run_ce(tp, inp, n, dtype, dloss=inp["dloss"] * T)
+    vl = V // n
+    Es = [inp["E"][i * vl:(i + 1) * vl] for i in range(n)]
+    ref = O.vocab_ce_fwd(inp["X"], Es, inp["targets"])
+    check("loss", out["loss"], ref["loss"], dtype)
+    check("lse", out["lse"], ref["lse"], dtype)
+    dXs = []
+    for i in range(n):
+        sh = O.vocab_ce_shard(inp["X"], Es[i], inp["targets"], i * vl)
+        check(f"logits[{i}]", out["logits"][i], sh["logits"], dtype)
+        check(f"m[{i}]", out["stats"][i, :, 0], sh["m"], dtype)
+        check(f"zt[{i}]", out["stats"][i, :, 2], sh["zt"], dtype)
+        bw = O.vocab_ce_shard_bwd(inp["X"], Es[i], inp["targets"], i * vl, ref["lse"], inp["dloss"] * T)
+        check(f"dX[{i}]", out["dX"][i], bw["dX"], dtype)
+        check(f"dE[{i}]", out["dE"][i], bw["dE"], dtype)
+        dXs.append(bw["dX"])
+    check("dX summed", out["dXsum"], O.shard_reduce(dXs), dtype)
+
+
+def test_vocab_ce_deterministic(tp):
+    _say("vocab ce bitwise determinism")
+    inp = tpsynth.random_vocab(300, 256, 2048, 2000, 4, "bf16", seed=72)
+    a = run_ce(tp, inp, 4, "bf16", dloss=inp["dloss"])
+    b = run_ce(tp, inp, 4, "bf16", dloss=inp["dloss"])
+    for k in ("logits", "stats", "loss", "lse", "dX", "dE"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_vocab_e1_full_size_sampled(tp):
+    """GPT-2-medium width, vocabulary 51200 over 8 shards, 8192 tokens.  The
+    loss, log-sum-exp and dX of 64 sampled tokens are checked against the
+    oracle (a token's values depend only on its own row).  dE needs every
+    token's softmax, so a second backward runs with dloss masked to those 64
+    tokens: dE is then theirs alone, and every other token's dX is zero."""
+    wl = tpsynth.WORKLOADS["E1"]
+    _say(f"vocab ce E1 full size T={wl.M} d={wl.d} V={wl.vocab} n={wl.n_shards}")
+    inp = tpsynth.vocab_inputs(wl, seed=0)
+    n, vl, T = wl.n_shards, wl.vocab // wl.n_shards, wl.M
+    rng = np.random.default_rng(6)
+    sel = np.sort(rng.choice(T, size=64, replace=False))
+    sel[-1] = T - 1
+    Es = inp["Es"]
+    sub = O.vocab_ce_fwd(inp["X"][sel], Es, inp["targets"][sel])
+    out = run_ce(tp, inp, n, "bf16", dloss=inp["dloss"])
+    check("loss", host(out["loss"])[sel], sub["loss"], "bf16")
+    check("lse", host(out["lse"])[sel], sub["lse"], "bf16")
+    dXs = [O.vocab_ce_shard_bwd(inp["X"][sel], Es[i], inp["targets"][sel], i * vl, sub["lse"],
+                                inp["dloss"][sel])["dX"] for i in range(n)]
+    check("dX summed", host(out["dXsum"])[sel], O.shard_reduce(dXs), "bf16")
+    masked = np.zeros(T, dtype=np.float32)
+    masked[sel] = inp["dloss"][sel] * T
+    out = run_ce(tp, inp, n, "bf16", dloss=masked)
+    rest = np.setdiff1d(np.arange(T), sel)
+    assert not torch.any(out["dXsum"][torch.from_numpy(rest).cuda()] != 0)
+    for i in (0, 3, n - 1):
+        bw = O.vocab_ce_shard_bwd(inp["X"][sel], Es[i], inp["targets"][sel], i * vl, sub["lse"], masked[sel])
+        check(f"dE[{i}]", out["dE"][i], bw["dE"], "bf16")
