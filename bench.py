@@ -501,6 +501,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--only", choices=["C2", "C3", "C4", "G1", "S1", "E1"],
+                    help="for kernel traces: time only this workload (--steps/--warmup apply) and print "
+                         "its JSON object")
     ap.add_argument("--profile", action="store_true",
                     help="for counter runs: headline steps only, then one plain 1 GiB device copy "
                          "whose FETCH_SIZE/WRITE_SIZE calibrate the counters")
@@ -520,6 +523,10 @@ def main():
     tp.lib()
     torch.cuda.set_device(0)
 
+    extras = {"C2": run_c2, "C3": run_c3, "C4": run_c4, "G1": run_g1, "S1": run_s1, "E1": run_e1}
+    if args.only:
+        print(json.dumps({args.only: extras[args.only](tp, torch, args.steps, args.warmup)}), flush=True)
+        return
     wl = tpsynth.WORKLOADS["C5"]
     ms, wall, per, flops, inp, outs = run_headline(tp, torch, wl, args.steps, args.warmup)
     if args.profile:
@@ -568,7 +575,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         wls = {}
-        for name, fn in (("C2", run_c2), ("C3", run_c3), ("C4", run_c4), ("G1", run_g1), ("S1", run_s1), ("E1", run_e1)):
+        for name, fn in extras.items():
             log(f"timing {name}")
             wls[name] = fn(tp, torch, args.extra_steps, 2)
             torch.cuda.empty_cache()
