@@ -1,6 +1,7 @@
 // Host-side tile-shape choice and launch of the GEMM kernels.
 #pragma once
 #include <algorithm>
+#include <cmath>
 #include "gemm.hpp"
 #include "gemm_f32.hpp"
 #include "launch.hpp"
@@ -42,24 +43,46 @@ inline int64_t tiles_for(int cfg, int64_t M, int64_t N, bool dual) {
   return cdiv(M, bm) * cdiv(N, bn);
 }
 
-// Choose the largest tile that still gives every CU (256 of them) at least
-// one tile; products with a small output and a long K (weight gradients of
-// narrow shards) are split along K into a deterministic fp32 workspace.
+// Relative MFMA rate of a CU running the M and S shapes, against the L shape
+// (tuning constants, measured on the workloads' products).
+#ifndef TPK_RATE_M
+#define TPK_RATE_M 0.75
+#endif
+#ifndef TPK_RATE_S
+#define TPK_RATE_S 0.60
+#endif
+
+// Tile shape and K split of a product: the choice with the smallest
+// estimated duration, where a launch takes ceil(tiles / 256) rounds of tiles
+// (one per CU at a time; a partly filled last round costs a whole one) times
+// a tile's work over its shape's rate, and a K split adds the deterministic
+// fp32 reduce of its partials (split + 1 passes over the output at about
+// 4 TB/s).  Splitting is allowed only where the caller has an fp32 workspace
+// (weight gradients).  Near-ties go to the larger tile and the smaller split.
 // Dual-B products always take the L shape (two 128-column sub-tiles).
 inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow_split) {
-  constexpr int64_t CUS = 256;
-  GemmPlan p{CFG_S, 1};
-  if (dual || tiles_for(CFG_L, M, N, dual) >= CUS) p.cfg = CFG_L;
-  else if (tiles_for(CFG_M, M, N, dual) >= CUS) p.cfg = CFG_M;
-  if (allow_split) {
-    const int64_t t = tiles_for(p.cfg, M, N, dual);
-    if (t < CUS / 2) {
-      int64_t s = CUS / t;
-      s = std::min<int64_t>(s, std::max<int64_t>(1, K / 1024));
-      p.split = (int)std::max<int64_t>(1, std::min<int64_t>(s, 16));
+  constexpr double CUS = 256.0, CU_FLOPS = 4.4e12, REDUCE_BPS = 4.0e12, LAUNCH_S = 4e-6;
+  const double rate[3] = {1.0, TPK_RATE_M, TPK_RATE_S};
+  GemmPlan best{CFG_L, 1};
+  double best_t = 1e30;
+  for (int cfg = CFG_L; cfg <= CFG_S; ++cfg) {
+    if (dual && cfg != CFG_L) break;
+    const int64_t bm = cfg == CFG_S ? 128 : 256;
+    const int64_t bn = cfg == CFG_L ? 256 : 128;   // output columns per tile (dual: two halves)
+    const int64_t tiles = cdiv(M, bm) * cdiv(N, dual ? bn / 2 : bn);
+    for (int s = 1; s <= (allow_split ? 16 : 1); s *= 2) {
+      const int64_t kc = cdiv(K, s);
+      if (s > 1 && kc < 512) break;
+      const double rounds = std::ceil((double)(tiles * s) / CUS);
+      double t = rounds * 2.0 * (double)(bm * bn * kc) / (rate[cfg] * CU_FLOPS);
+      if (s > 1) t += (double)(s + 1) * (double)M * (double)N * 4.0 / REDUCE_BPS + LAUNCH_S;
+      if (t < best_t * 0.97) {
+        best_t = t;
+        best = GemmPlan{cfg, s};
+      }
     }
   }
-  return p;
+  return best;
 }
 
 template <class Cfg, bool A_KM, bool B_KM, bool DUAL, class Epi>
