@@ -104,6 +104,33 @@ def timed(tp, torch, step, steps: int, warmup: int, kernels_per_step: int):
     return t0.elapsed_time(t1) / steps, wall, per
 
 
+def graph_timed(torch, step, steps: int) -> float:
+    """ms per step of the same step captured once as a HIP graph (through
+    torch.cuda.CUDAGraph, on a side stream of default priority) and replayed
+    `steps` times: the eager loop's per-launch host and queue overhead is
+    gone, the kernels are the same."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del g
+    return ms
+
+
 def gemm_flops(M, N, K):
     return 2.0 * M * N * K
 
@@ -236,6 +263,7 @@ def run_c2(tp, torch, steps, warmup):
         tp.tp_shard_reduce(dXp, dX, n, M * d)
 
     ms, _, per = timed(tp, torch, step, steps, warmup, 8 * 10 + 2)
+    gms = graph_timed(torch, step, steps)
     flops = n * 6 * gemm_flops(M, f, d)
     red = per.get("shard_reduce.vec8", [])
     # the reduce reads 8 partials and writes 1 output: (n + 1) * M * d * 2 bytes
@@ -260,6 +288,7 @@ def run_c2(tp, torch, steps, warmup):
                         "fwd+bwd + Z and dX shard-reduce",
             "ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
             "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "graph_ms_per_step": round(gms, 4), "graph_tflops": round(flops / gms / 1e9, 1),
             "shard_reduce": {"bytes": rbytes, "warm_ms": round(red_ms, 4) if red_ms else None,
                              "warm_GBps": round(rbytes / red_ms / 1e6, 1) if red_ms else None,
                              "cold_ms": round(cold_ms, 4), "cold_GBps": round(rbytes / cold_ms / 1e6, 1),
@@ -323,6 +352,12 @@ def run_c4(tp, torch, steps, warmup):
 
     ms_f, _, per_f = timed(tp, torch, fwd, steps, warmup, 4)
     ms_b, _, per_b = timed(tp, torch, bwd, steps, warmup, 12)
+
+    def both():
+        fwd()
+        bwd()
+
+    gms = graph_timed(torch, both, steps)
     M, N = b * s, hl * dh
     core = 2 * 2.0 * b * hl * (s * (s + 1) / 2) * dh      # causal pairs only: QK^T and PV
     flops_f = 3 * gemm_flops(M, N, d) + core + gemm_flops(M, d, N)
@@ -334,6 +369,7 @@ def run_c4(tp, torch, steps, warmup):
     core_b = sum(avg(per_b, ("attn_bwd.dkv", "attn_bwd.dq")))
     return {"workload": "C4 causal self-attention shard, b 4 s 2048 d 4096, 8 of 32 heads of 128, fwd+bwd",
             "ms_per_step": round(ms_f + ms_b, 4), "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+            "graph_ms_per_step": round(gms, 4),
             "tflops": round((flops_f + flops_b) / (ms_f + ms_b) / 1e9, 1),
             "fwd_tflops": round(flops_f / ms_f / 1e9, 1), "bwd_tflops": round(flops_b / ms_b / 1e9, 1),
             "pct_of_peak": round(100 * (flops_f + flops_b) / (ms_f + ms_b) / 1e9 / PEAK_BF16_TFLOPS, 2),
@@ -398,6 +434,7 @@ def run_s1(tp, torch, steps, warmup):
         tp.tp_sp_all_gather(stripes, full)
 
     ms, _, per = timed(tp, torch, step, steps, warmup, 2)
+    gms = graph_timed(torch, step, steps)
     e = k * cols
     rs_bytes = (n + 1) * e * 2 + e + 3 * cols * 2 + 2 * e * 2
     ag_bytes = 2 * n * e * 2
@@ -429,7 +466,7 @@ def run_s1(tp, torch, steps, warmup):
     return {"workload": "S1 sequence-parallel block end: 8192 tokens x 8192 over TP 8, this GPU's "
                         "1024-token stripe (reduce-scatter of 8 partials + bias, dropout 0.1, residual, "
                         "LayerNorm) + all-gather of the 8 stripes",
-            "ms_per_step": round(ms, 4),
+            "ms_per_step": round(ms, 4), "graph_ms_per_step": round(gms, 4),
             "rs_ln": {"bytes": rs_bytes, "warm_ms": round(rs_ms, 4) if rs_ms else None,
                       "warm_GBps": gbs(rs_bytes, rs_ms), "cold_ms": round(min(cold_rs), 4),
                       "cold_GBps": gbs(rs_bytes, min(cold_rs)), "peak_GBps": PEAK_HBM_GBS},
@@ -474,6 +511,7 @@ def run_e1(tp, torch, steps, warmup):
         tp.tp_vocab_ce_bwd(X, E0, tg, logits, lse, dloss, dX, dE, ws, 0)
 
     ms, _, per = timed(tp, torch, step, steps, warmup, 12)
+    gms = graph_timed(torch, step, steps)
     flops = 3 * gemm_flops(T, vl, d)
     avg = lambda lab: (sum(per[lab]) / len(per[lab])) if per.get(lab) else None
     gemm_ms = sum(avg(k) or 0.0 for k in ("vocab_ce.xet", "vocab_ce.dze", "vocab_ce.dztx"))
@@ -486,6 +524,7 @@ def run_e1(tp, torch, steps, warmup):
                         "output embedding + cross-entropy fwd, combine, bwd",
             "ms_per_step": round(ms, 4), "gemm_flop_per_step": flops,
             "tflops": round(flops / ms / 1e9, 1),
+            "graph_ms_per_step": round(gms, 4), "graph_tflops": round(flops / gms / 1e9, 1),
             "gemm_tflops": round(flops / gemm_ms / 1e9, 1) if gemm_ms else None,
             "pct_of_peak_gemms": round(100 * flops / gemm_ms / 1e9 / PEAK_BF16_TFLOPS, 2) if gemm_ms else None,
             "embed": {"bytes": emb_bytes, "ms": round(emb_ms, 4) if emb_ms else None,
