@@ -16,7 +16,8 @@
 // variance around it.  Rows of up to 8192 values stay in registers between
 // the passes; longer rows re-read h, each thread its own writes.
 // HBM-bound: (n_shards + 1) row reads plus 2 row writes per token, and the
-// keep mask at one byte per value when dropout is on.
+// keep mask at one byte per value when dropout is on; the streamed rows use
+// nontemporal accesses (bias, gamma and beta, shared by every row, do not).
 #include <algorithm>
 #include <type_traits>
 
@@ -76,7 +77,7 @@ sp_rs_ln_kernel(const T* __restrict__ P, int64_t stride, int n, int64_t row0, in
     for (; i + 8 <= n; i += 8) {
       float t[8][8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) Vec8<T>::load(p + (int64_t)(i + u) * stride, t[u]);
+      for (int u = 0; u < 8; ++u) Vec8<T>::template load<kNtIn>(p + (int64_t)(i + u) * stride, t[u]);
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
@@ -84,7 +85,7 @@ sp_rs_ln_kernel(const T* __restrict__ P, int64_t stride, int n, int64_t row0, in
     }
     for (; i < n; ++i) {
       float t[8];
-      Vec8<T>::load(p + (int64_t)i * stride, t);
+      Vec8<T>::template load<kNtIn>(p + (int64_t)i * stride, t);
 #pragma unroll
       for (int e = 0; e < 8; ++e) s[e] += t[e];
     }
@@ -95,7 +96,7 @@ sp_rs_ln_kernel(const T* __restrict__ P, int64_t stride, int n, int64_t row0, in
       for (int e = 0; e < 8; ++e) s[e] += b[e];
     }
     if (keep) {
-      const u32x2 m = *reinterpret_cast<const u32x2*>(keep + dst + c);
+      const u32x2 m = ld16<kNtIn>(reinterpret_cast<const u32x2*>(keep + dst + c));
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t byte = (m[e >> 2] >> (8 * (e & 3))) & 0xFFu;
@@ -103,13 +104,13 @@ sp_rs_ln_kernel(const T* __restrict__ P, int64_t stride, int n, int64_t row0, in
       }
     }
     float res[8];
-    Vec8<T>::load(residual + dst + c, res);
+    Vec8<T>::template load<kNtIn>(residual + dst + c, res);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       s[e] = round_to(s[e] + res[e], (T*)nullptr);
       sum += s[e];
     }
-    Vec8<T>::store(h_out + dst + c, s);
+    Vec8<T>::template store<REG && kNtOut>(h_out + dst + c, s);   // re-read below when !REG
     if constexpr (REG) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) hv[k][e] = s[e];
@@ -142,7 +143,7 @@ sp_rs_ln_kernel(const T* __restrict__ P, int64_t stride, int n, int64_t row0, in
     Vec8<T>::load(beta + c, b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (h[e] - mean) * rstd * g[e] + b[e];
-    Vec8<T>::store(x_out + dst + c, x);
+    Vec8<T>::template store<kNtOut>(x_out + dst + c, x);
   });
 }
 
@@ -158,7 +159,10 @@ sp_all_gather_kernel(SpStripes s, int64_t nvec, u32x4* __restrict__ full) {
   if (!src) return;  // the stripe already sits at its place in `full`
   u32x4* dst = full + (int64_t)blockIdx.y * nvec;
   const int64_t step = (int64_t)gridDim.x * 256;
-  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += step) dst[v] = src[v];
+  // Streaming reads; ordinary stores, since the next TP product reads the
+  // gathered tensor right away and finds it in the Infinity Cache.
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += step)
+    st16<false>(dst + v, ld16<kNtIn>(src + v));
 }
 
 hipError_t launch_sp_reduce_scatter_ln(hipStream_t st, int dt, int n, int64_t rows, int64_t cols,

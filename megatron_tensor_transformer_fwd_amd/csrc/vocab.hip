@@ -37,7 +37,7 @@ vocab_embed_kernel(const int64_t* __restrict__ ids, int64_t n_tokens, int64_t ro
     const int64_t local = ids[t] - vstart;
     u32x4 w = {0u, 0u, 0u, 0u};
     if (local >= 0 && local < vlocal) w = E[local * rowvec + c];
-    Y[v] = w;
+    st16<kNtOut>(Y + v, w);
   }
 }
 
@@ -61,7 +61,7 @@ ce_row_stats_kernel(const T* __restrict__ logits, int64_t vlocal, const int64_t*
   float m = -FLT_MAX, s = 0.f;
   for (int64_t c = (int64_t)threadIdx.x * 8; c < vlocal; c += 256 * 8) {
     float z[8];
-    Vec8<T>::load(row + c, z);
+    Vec8<T>::template load<kNtIn>(row + c, z);
     float cm = z[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) cm = fmaxf(cm, z[e]);
@@ -128,7 +128,7 @@ ce_dlogits_kernel(const T* __restrict__ logits, int64_t n_tokens, int64_t vlocal
     const float l = lse[t], g = dloss[t];
     const int64_t hit = targets[t] - vstart - c;   // in [0, 8) when the target is in this chunk
     float z[8];
-    Vec8<T>::load(logits + t * vlocal + c, z);
+    Vec8<T>::template load<kNtIn>(logits + t * vlocal + c, z);
 #pragma unroll
     for (int e = 0; e < 8; ++e) z[e] = (__expf(z[e] - l) - (hit == e ? 1.f : 0.f)) * g;
     Vec8<T>::store(dz + t * vlocal + c, z);
