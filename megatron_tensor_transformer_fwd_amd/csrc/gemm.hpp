@@ -272,7 +272,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
         const int64_t n = n0 + c * (16 / ES);
         if (m < p.M && n < p.N) {
           const u32x4 w = *reinterpret_cast<const u32x4*>(smem + r * ROWB + ((c ^ (r & (CPR - 1))) * 16));
-          *reinterpret_cast<u32x4*>(epi.template out_ptr<O>(m, n, split, zb)) = w;
+          // streaming store: the tile is not read again by this product, and
+          // its dirty lines would otherwise compete with the operand stream
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(epi.template out_ptr<O>(m, n, split, zb)));
         }
       }
     }
