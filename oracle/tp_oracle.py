@@ -50,7 +50,7 @@ __all__ = [
     "mlp_shard_fwd", "mlp_shard_bwd", "mlp_unsharded", "mlp_unsharded_bwd",
     "swiglu_shard_fwd", "swiglu_shard_bwd", "swiglu_unsharded",
     "attn_shard_fwd", "attn_unsharded", "attn_core", "attn_core_lse", "attn_core_bwd", "attn_shard_bwd",
-    "attn_gqa_shard_fwd", "attn_gqa_query_rows",
+    "attn_gqa_shard_fwd", "attn_gqa_query_rows", "attn_gqa_shard_bwd",
     "shard_reduce", "shard_range",
     "stripe_rows", "reduce_scatter", "all_gather", "layer_norm", "sp_block_end",
     "vocab_embed_shard", "vocab_embed", "vocab_ce_shard", "vocab_ce_combine", "vocab_ce_fwd",
@@ -327,6 +327,37 @@ def attn_gqa_shard_fwd(X, Wq, Wk, Wv, Wo, b: int, s: int, h_local: int, h_kv: in
             O[bi, :, j, :], L[bi, j] = attn_core_lse(Q[bi, j], K[bi, j // group], V[bi, j // group], causal, scale)
     O = O.reshape(b * s, h_local * d_head)
     return {"Q": Q, "K": K, "V": V, "O": O, "Z": O @ _f64(Wo), "L": L}
+
+
+def attn_gqa_shard_bwd(X, Wq, Wk, Wv, Wo, dY, b: int, s: int, h_local: int, h_kv: int, d_head: int,
+                       causal: bool = True, scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Backward of the grouped-query shard: attn_shard_bwd's chain rule with
+    query head j reading K/V head j // (h_local / h_kv).  A K/V head feeds
+    every query head of its group, so its dK and dV are the sums of the
+    group's per-head contributions.  dQ is [b*s, h_local*d_h]; dK and dV are
+    [b*s, h_kv*d_h]; dX, dW_Q, dW_K, dW_V, dW_O as attn_shard_bwd."""
+    assert h_local % h_kv == 0
+    group = h_local // h_kv
+    f = attn_gqa_shard_fwd(X, Wq, Wk, Wv, Wo, b, s, h_local, h_kv, d_head, causal, scale)
+    X2 = _f64(X).reshape(b * s, -1)
+    dY = _f64(dY)
+    dO = dY @ _f64(Wo).T
+    dOh = _split_heads(dO, b, s, h_local, d_head)
+    dQ = np.zeros((b, s, h_local, d_head))
+    dK = np.zeros((b, s, h_kv, d_head))
+    dV = np.zeros((b, s, h_kv, d_head))
+    for bi in range(b):
+        for j in range(h_local):
+            g = attn_core_bwd(f["Q"][bi, j], f["K"][bi, j // group], f["V"][bi, j // group], dOh[bi, j], causal,
+                              scale)
+            dQ[bi, :, j, :] = g["dQ"]
+            dK[bi, :, j // group, :] += g["dK"]
+            dV[bi, :, j // group, :] += g["dV"]
+    dQ = dQ.reshape(b * s, h_local * d_head)
+    dK, dV = (t.reshape(b * s, h_kv * d_head) for t in (dK, dV))
+    return {"dO": dO, "dQ": dQ, "dK": dK, "dV": dV,
+            "dX": dQ @ _f64(Wq).T + dK @ _f64(Wk).T + dV @ _f64(Wv).T,
+            "dWq": X2.T @ dQ, "dWk": X2.T @ dK, "dWv": X2.T @ dV, "dWo": f["O"].T @ dY}
 
 
 def attn_gqa_query_rows(Xb, Wq, Wk, Wv, Wo, rows, h_local: int, h_kv: int, d_head: int,

@@ -418,6 +418,59 @@ def test_attention_bwd_shards_sum_and_concatenate():
     np.testing.assert_allclose(np.concatenate([p["dWo"] for p in parts], axis=0), full["dWo"], rtol=1e-12, atol=1e-13)
 
 
+def test_gqa_bwd_one_group_is_mha_bwd():
+    rng = np.random.default_rng(90)
+    b, s, d, h, dh = 1, 6, 5, 3, 4
+    X = rng.standard_normal((b * s, d))
+    Wq, Wk, Wv = (rng.standard_normal((d, h * dh)) * 0.5 for _ in range(3))
+    Wo = rng.standard_normal((h * dh, d)) * 0.5
+    dY = rng.standard_normal((b * s, d))
+    g = O.attn_gqa_shard_bwd(X, Wq, Wk, Wv, Wo, dY, b, s, h, h, dh)
+    m = O.attn_shard_bwd(X, Wq, Wk, Wv, Wo, dY, b, s, h, dh)
+    for k in ("dX", "dWq", "dWk", "dWv", "dWo"):
+        np.testing.assert_allclose(g[k], m[k], rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_bwd_matches_finite_differences_and_repeated_kv_mha():
+    """Gradients of <dY, Z> by central differences; and the grouped backward
+    equals multi-head attention's with each K/V head's weight columns
+    repeated over its group, the repeated copies' gradients summed."""
+    rng = np.random.default_rng(91)
+    b, s, d, h, hkv, dh = 2, 5, 4, 4, 2, 3
+    group = h // hkv
+    X = rng.standard_normal((b * s, d))
+    Wq = rng.standard_normal((d, h * dh)) * 0.6
+    Wk, Wv = (rng.standard_normal((d, hkv * dh)) * 0.6 for _ in range(2))
+    Wo = rng.standard_normal((h * dh, d)) * 0.6
+    dY = rng.standard_normal((b * s, d))
+    g = O.attn_gqa_shard_bwd(X, Wq, Wk, Wv, Wo, dY, b, s, h, hkv, dh)
+
+    def f(X_, Wq_, Wk_, Wv_, Wo_):
+        return float((O.attn_gqa_shard_fwd(X_, Wq_, Wk_, Wv_, Wo_, b, s, h, hkv, dh)["Z"] * dY).sum())
+
+    eps = 1e-6
+    args = [X, Wq, Wk, Wv, Wo]
+    names = ["dX", "dWq", "dWk", "dWv", "dWo"]
+    for ai, (r, c) in [(0, (3, 1)), (1, (2, 5)), (2, (1, 4)), (3, (0, 2)), (4, (7, 3))]:
+        p, m = [a.copy() for a in args], [a.copy() for a in args]
+        p[ai][r, c] += eps
+        m[ai][r, c] -= eps
+        assert g[names[ai]][r, c] == pytest.approx((f(*p) - f(*m)) / (2 * eps), rel=1e-6, abs=1e-8)
+
+    def rep(W):
+        return np.concatenate([W[:, (j // group) * dh:(j // group + 1) * dh] for j in range(h)], axis=1)
+
+    def fold(G):
+        return np.concatenate([sum(G[:, (k * group + i) * dh:(k * group + i + 1) * dh] for i in range(group))
+                               for k in range(hkv)], axis=1)
+
+    mh = O.attn_shard_bwd(X, Wq, rep(Wk), rep(Wv), Wo, dY, b, s, h, dh)
+    np.testing.assert_allclose(g["dX"], mh["dX"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(g["dWq"], mh["dWq"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(g["dWk"], fold(mh["dWk"]), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(g["dWv"], fold(mh["dWv"]), rtol=1e-11, atol=1e-12)
+
+
 # ------------------------------------------------------- sequence parallel
 
 def test_reduce_scatter_then_all_gather_is_all_reduce():
