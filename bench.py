@@ -387,25 +387,45 @@ def run_g1(tp, torch, steps, warmup):
     b, s, d, hl, hkv, dh = wl.b, wl.s, wl.d, wl.h_local, wl.h_kv_local, wl.d_head
     X, Wq, Wk, Wv, Wo = (dev(inp[k]) for k in ("X", "Wq", "Wk", "Wv", "Wo"))
     del inp
+    M, N, Nkv = b * s, hl * dh, hkv * dh
+    dY = dev(np.random.default_rng(45).standard_normal((M, d)).astype(np.float32))
     Q = torch.empty((b, hl, s, dh), dtype=bf, device="cuda")
     K, V = (torch.empty((b, hkv, s, dh), dtype=bf, device="cuda") for _ in range(2))
-    Ob = torch.empty((b * s, hl * dh), dtype=bf, device="cuda")
-    Z = torch.empty((b * s, d), dtype=bf, device="cuda")
+    Ob = torch.empty((M, N), dtype=bf, device="cuda")
+    Z = torch.empty((M, d), dtype=bf, device="cuda")
+    L = torch.empty((b, hl, s), dtype=torch.float32, device="cuda")
+    dX = torch.empty((M, d), dtype=bf, device="cuda")
+    dWq, dWo = torch.empty((d, N), device="cuda"), torch.empty((N, d), device="cuda")
+    dWk, dWv = torch.empty((d, Nkv), device="cuda"), torch.empty((d, Nkv), device="cuda")
+    ws = torch.empty(tp.tp_attn_gqa_shard_bwd_workspace_bytes(tp.TP_DT_BF16, b, s, d, hl, hkv, dh),
+                     dtype=torch.uint8, device="cuda")
 
-    def step():
-        tp.tp_attn_gqa_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, Z, b, s, hl, hkv, dh, causal=True)
+    def fwd():
+        tp.tp_attn_gqa_shard_fwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, Z, b, s, hl, hkv, dh, causal=True, L=L)
 
-    ms, _, per = timed(tp, torch, step, steps, warmup, 4)
-    M, N, Nkv = b * s, hl * dh, hkv * dh
+    def bwd():
+        tp.tp_attn_gqa_shard_bwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, L, dY, dX, dWq, dWk, dWv, dWo, ws, b, s, hl, hkv,
+                                 dh, causal=True)
+
+    ms_f, _, per_f = timed(tp, torch, fwd, steps, warmup, 4)
+    ms_b, _, per_b = timed(tp, torch, bwd, steps, warmup, 12)
     core = 2 * 2.0 * b * hl * (s * (s + 1) / 2) * dh
-    flops = gemm_flops(M, N, d) + 2 * gemm_flops(M, Nkv, d) + core + gemm_flops(M, d, N)
-    core_ms = [sum(v) / len(v) for k, v in per.items() if k in ("attn.core_d128", "attn.core_d64")]
+    Nt = N + 2 * Nkv
+    f_fwd = gemm_flops(M, N, d) + 2 * gemm_flops(M, Nkv, d) + core + gemm_flops(M, d, N)
+    f_bwd = 2 * gemm_flops(M, N, d) + 2.5 * core + 2 * gemm_flops(M, d, Nt)
+    avg = lambda per, names: sum(sum(v) / len(v) for k, v in per.items() if k in names)
+    core_ms = avg(per_f, ("attn.core_d128", "attn.core_d64"))
+    core_b = avg(per_b, ("attn_bwd.dkv", "attn_bwd.dq"))
+    ms = ms_f + ms_b
     return {"workload": "G1 grouped-query causal attention shard (Llama-3-405B TP-8 slice): b 2 s 4096 d 16384, "
-                        "16 query heads sharing 1 KV head of 128, fwd",
-            "ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
-            "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-            "core_tflops": round(core / core_ms[0] / 1e9, 1) if core_ms else None,
-            "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in per.items()}}
+                        "16 query heads sharing 1 KV head of 128, fwd+bwd",
+            "ms_per_step": round(ms, 4), "fwd_ms": round(ms_f, 4), "bwd_ms": round(ms_b, 4),
+            "tflops": round((f_fwd + f_bwd) / ms / 1e9, 1),
+            "fwd_tflops": round(f_fwd / ms_f / 1e9, 1), "bwd_tflops": round(f_bwd / ms_b / 1e9, 1),
+            "pct_of_peak": round(100 * (f_fwd + f_bwd) / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "core_tflops": round(core / core_ms / 1e9, 1) if core_ms else None,
+            "core_bwd_tflops": round(2.5 * core / core_b / 1e9, 1) if core_b else None,
+            "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in list(per_f.items()) + list(per_b.items())}}
 
 
 def run_s1(tp, torch, steps, warmup):

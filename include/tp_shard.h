@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 4
+#define TP_ABI_VERSION 5
 
 typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype_t;
 
@@ -201,6 +201,28 @@ int tp_attn_shard_bwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t
                       void* ws, size_t ws_bytes);
 size_t tp_attn_shard_bwd_workspace_bytes(tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
                                          int64_t h_local, int64_t d_head);
+
+/* ---------------------------------------------------------------------------
+ * tp_attn_gqa_shard_bwd — backward of the grouped-query shard
+ * (tp_attn_gqa_shard_fwd): tp_attn_shard_bwd's chain rule with local query
+ * head j reading K/V head j / (h_local / h_kv_local).  A K/V head feeds every
+ * query head of its group, so its dK and dV are the group's contributions
+ * summed (in fp32, in head order).  Wk, Wv, dWk, dWv are [d x
+ * h_kv_local*d_head]; K, V [b, h_kv_local, s, d_head]; everything else as
+ * tp_attn_shard_bwd.  h_kv_local must divide h_local (TP_E_DIVIS); d_head =
+ * 128; (h_local + 2 h_kv_local)*d_head <= 2^21.  ws: device workspace of at
+ * least tp_attn_gqa_shard_bwd_workspace_bytes(...) bytes.
+ * ------------------------------------------------------------------------- */
+int tp_attn_gqa_shard_bwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
+                          int64_t h_local, int64_t h_kv_local, int64_t d_head, int causal,
+                          float scale, const void* X, const void* Wq, const void* Wk,
+                          const void* Wv, const void* Wo, const void* Q, const void* K,
+                          const void* V, const void* O, const float* L, const void* dY,
+                          void* dX, float* dWq, float* dWk, float* dWv, float* dWo,
+                          void* ws, size_t ws_bytes);
+size_t tp_attn_gqa_shard_bwd_workspace_bytes(tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
+                                             int64_t h_local, int64_t h_kv_local,
+                                             int64_t d_head);
 
 /* ---------------------------------------------------------------------------
  * tp_sp_reduce_scatter_ln — the sequence-parallel block end of one GPU ([HC]

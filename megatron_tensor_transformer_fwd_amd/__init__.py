@@ -17,6 +17,7 @@ __all__ = [
     "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_workspace_bytes",
     "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes",
     "tp_attn_shard_fwd", "tp_attn_gqa_shard_fwd", "tp_attn_shard_bwd", "tp_attn_shard_bwd_workspace_bytes",
+    "tp_attn_gqa_shard_bwd", "tp_attn_gqa_shard_bwd_workspace_bytes",
     "tp_shard_reduce", "tp_shard_range", "tp_sp_reduce_scatter_ln", "tp_sp_all_gather",
     "tp_vocab_embed_fwd", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
     "tp_vocab_ce_bwd_workspace_bytes",
@@ -53,6 +54,9 @@ EXPORTS = {
     "tp_attn_shard_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _i64, _i32, ctypes.c_float]
                           + [_p] * 5 + [_p] * 5 + [_p] + [_p] * 5 + [_p, _sz]),
     "tp_attn_shard_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i64, _i64]),
+    "tp_attn_gqa_shard_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i32, ctypes.c_float]
+                              + [_p] * 5 + [_p] * 5 + [_p] + [_p] * 5 + [_p, _sz]),
+    "tp_attn_gqa_shard_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i64, _i64, _i64]),
     "tp_shard_reduce": (_i32, [_p, _i32, _i32, _i64, _i64, _p, _i64, _p, _i64, _p]),
     "tp_sp_reduce_scatter_ln": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, _p, ctypes.c_float,
                                        _p, _p, ctypes.c_float, _p, _p]),
@@ -203,6 +207,22 @@ def tp_attn_shard_bwd(X, Wq, Wk, Wv, Wo, Q, K, V, O, L, dY, dX, dWq, dWk, dWv, d
                                    _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), _ptr(dY), _ptr(dX),
                                    _ptr(dWq), _ptr(dWk), _ptr(dWv), _ptr(dWo), _ptr(ws),
                                    ws.numel() * ws.element_size()))
+
+
+def tp_attn_gqa_shard_bwd_workspace_bytes(dtype: int, b: int, s: int, d: int, h_local: int, h_kv_local: int,
+                                          d_head: int) -> int:
+    return lib().tp_attn_gqa_shard_bwd_workspace_bytes(dtype, b, s, d, h_local, h_kv_local, d_head)
+
+
+def tp_attn_gqa_shard_bwd(X, Wq, Wk, Wv, Wo, Q, K, V, O, L, dY, dX, dWq, dWk, dWv, dWo, ws, b: int, s: int,
+                          h_local: int, h_kv_local: int, d_head: int, causal: bool = True, scale: float = 0.0,
+                          stream=None) -> None:
+    d = X.shape[1]
+    _check(lib().tp_attn_gqa_shard_bwd(_stream(stream), _dt(X), b, s, d, h_local, h_kv_local, d_head, int(causal),
+                                       float(scale), _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo),
+                                       _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), _ptr(dY), _ptr(dX),
+                                       _ptr(dWq), _ptr(dWk), _ptr(dWv), _ptr(dWo), _ptr(ws),
+                                       ws.numel() * ws.element_size()))
 
 
 def tp_shard_reduce(partials, out, n_shards: int, numel: int, shard_stride: Optional[int] = None,

@@ -113,13 +113,17 @@ __global__ void __launch_bounds__(256) attn_bwd_rowdot_kernel(const bf16* __rest
 }
 
 // Key-tile kernel: dK and dV of 128 keys (four waves of 32) of one (batch,
-// head), streaming 64-query chunks of Q and dO.  Lanes index keys: the
+// query head), streaming 64-query chunks of Q and dO.  Lanes index keys: the
 // accumulators of S = Q K^T and dP = dO V^T hold, per lane, one key and 16
-// queries, exactly the operand layout of dV += P^T dO and dK += dS^T Q.
+// queries, exactly the operand layout of dV += P^T dO and dK += dS^T Q.  With
+// grouped-query attention (group > 1) the keys and values are those of K/V
+// head h / group, and the outputs are this query head's fp32 contributions,
+// summed over the group afterwards.
+template <class TO>
 __global__ void __launch_bounds__(256, 1)
 attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                     const bf16* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
-                    bf16* __restrict__ dK, bf16* __restrict__ dV, int nb, int hl, int s, int causal,
+                    TO* __restrict__ dK, TO* __restrict__ dV, int nb, int hl, int group, int s, int causal,
                     float scale, int64_t ld_o, int64_t ld_g) {
   using namespace attnb;
   constexpr int BKEY = 128, BQ = 64;
@@ -138,14 +142,15 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
   const int lk = lane & 31, g = lane >> 5;
   const int k0 = kt * BKEY, kw = k0 + wave * 32, key = kw + lk;
   const int64_t head = (int64_t)bh * s * D;
+  const int64_t kvhead = ((int64_t)bi * (hl / group) + h / group) * s * D;
   const uint32_t lds0 = lds_addr(smem);
   const float sl2 = scale * kLog2e;
 
   // This wave's keys and values as row fragments (zero past the sequence).
   bf16x8 kf[D / 16], vf[D / 16];
   {
-    const rsrc_t rk = make_rsrc(K + head, (uint64_t)s * ROWB);
-    const rsrc_t rv = make_rsrc(V + head, (uint64_t)s * ROWB);
+    const rsrc_t rk = make_rsrc(K + kvhead, (uint64_t)s * ROWB);
+    const rsrc_t rv = make_rsrc(V + kvhead, (uint64_t)s * ROWB);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const uint32_t off = (uint32_t)(((int64_t)key * D + kk * 16 + g * 8) * 2);
@@ -231,8 +236,8 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
 
   // register r of block db: d = db*32 + 8 (r/4) + 4 g + r%4 of key `key`
   if (key < s) {
-    bf16* krow = dK + ((int64_t)bi * s + key) * ld_g + (int64_t)h * D;
-    bf16* vrow = dV + ((int64_t)bi * s + key) * ld_g + (int64_t)h * D;
+    TO* krow = dK + ((int64_t)bi * s + key) * ld_g + (int64_t)h * D;
+    TO* vrow = dV + ((int64_t)bi * s + key) * ld_g + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -241,8 +246,8 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
         const f32x4 kv = {adk[db][4 * b4] * scale, adk[db][4 * b4 + 1] * scale, adk[db][4 * b4 + 2] * scale,
                           adk[db][4 * b4 + 3] * scale};
         const f32x4 vv = {adv[db][4 * b4], adv[db][4 * b4 + 1], adv[db][4 * b4 + 2], adv[db][4 * b4 + 3]};
-        Quad<bf16>::store(krow + c, kv);
-        Quad<bf16>::store(vrow + c, vv);
+        Quad<TO>::store(krow + c, kv);
+        Quad<TO>::store(vrow + c, vv);
       }
   }
 }
@@ -254,8 +259,8 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
 __global__ void __launch_bounds__(256, 2)
 attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                    const bf16* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
-                   bf16* __restrict__ dQ, int nb, int hl, int s, int causal, float scale, int64_t ld_o,
-                   int64_t ld_g) {
+                   bf16* __restrict__ dQ, int nb, int hl, int group, int s, int causal, float scale,
+                   int64_t ld_o, int64_t ld_g) {
   using namespace attnb;
   constexpr int BQ = 128, BKV = 64;
   constexpr int KT = BKV * ROWB, STAGE = 2 * KT;
@@ -271,6 +276,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   const int lq = lane & 31, g = lane >> 5;
   const int q0 = qt * BQ, qw = q0 + wave * 32, qme = qw + lq;
   const int64_t head = (int64_t)bh * s * D;
+  const int64_t kvhead = ((int64_t)bi * (hl / group) + h / group) * s * D;
   const uint32_t lds0 = lds_addr(smem);
   const float sl2 = scale * kLog2e;
 
@@ -296,8 +302,8 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     const int kv0 = t * BKV;
     const uint32_t st = lds0 + (uint32_t)((t & 1) * STAGE);
     const int64_t rem = (int64_t)(s - kv0) * ROWB;
-    dma_rows<BKV>(range_desc(K + head + (int64_t)kv0 * D, rem), ROWB, st, wave, lane);
-    dma_rows<BKV>(range_desc(V + head + (int64_t)kv0 * D, rem), ROWB, st + KT, wave, lane);
+    dma_rows<BKV>(range_desc(K + kvhead + (int64_t)kv0 * D, rem), ROWB, st, wave, lane);
+    dma_rows<BKV>(range_desc(V + kvhead + (int64_t)kv0 * D, rem), ROWB, st + KT, wave, lane);
   };
 
   f32x16 adq[D / 32];
@@ -359,63 +365,107 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
 }
 
 // [W_Q | W_K | W_V] side by side: row r of the result is the rows r of the
-// three [d x n] weights, 16 bytes per thread.
+// three weights ([d x n0], [d x n1], [d x n1]), 16 bytes per thread.
 __global__ void __launch_bounds__(256) attn_concat3_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
                                                            const bf16* __restrict__ C, bf16* __restrict__ out,
-                                                           int64_t rows, int64_t n) {
-  const int64_t chunks = n / 8;                      // n is a multiple of 8
+                                                           int64_t rows, int64_t n0, int64_t n1) {
+  const int64_t c0 = n0 / 8, c1 = n1 / 8, cr = c0 + 2 * c1;   // widths are multiples of 8
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * 3 * chunks) return;
-  const int64_t r = i / (3 * chunks), j = i % (3 * chunks);
-  const int part = (int)(j / chunks);
-  const int64_t c = (j % chunks) * 8;
-  const bf16* src = (part == 0 ? A : part == 1 ? B : C) + r * n + c;
-  *reinterpret_cast<u32x4*>(out + r * 3 * n + part * n + c) = *reinterpret_cast<const u32x4*>(src);
+  if (i >= rows * cr) return;
+  const int64_t r = i / cr, j = i % cr;
+  const bf16* src = j < c0 ? A + r * n0 + j * 8
+                           : (j < c0 + c1 ? B + r * n1 + (j - c0) * 8 : C + r * n1 + (j - c0 - c1) * 8);
+  *reinterpret_cast<u32x4*>(out + r * cr * 8 + j * 8) = *reinterpret_cast<const u32x4*>(src);
 }
 
-// fp32 output whose columns [k*part, (k+1)*part) go to C[k] (row pitch part).
-struct EpiF32Thirds {
+// Grouped-query attention: dK (or dV) of K/V head k is the sum, in order, of
+// the fp32 contributions of query heads k*group .. k*group + group - 1
+// (P [rows x hl*128]); written as bf16 into columns k*128.. of `out` (row
+// pitch ld).  One thread per 8 outputs.
+__global__ void __launch_bounds__(256) attn_bwd_group_sum_kernel(const float* __restrict__ P,
+                                                                 bf16* __restrict__ out, int64_t rows, int hl,
+                                                                 int group, int64_t ld) {
+  constexpr int D = attnb::D;
+  const int hkv = hl / group;
+  const int64_t per_row = (int64_t)hkv * D / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * per_row) return;
+  const int64_t r = i / per_row;
+  const int64_t c = (i % per_row) * 8;                 // column within [0, hkv*128)
+  const int k = (int)(c / D);
+  const float* src = P + r * (int64_t)hl * D + (int64_t)k * group * D + (c % D);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < group; ++j) {
+    float t[8];
+    Vec8<float>::load<kNtIn>(src + (int64_t)j * D, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += t[e];
+  }
+  Vec8<bf16>::store(out + r * ld + c, acc);
+}
+
+// fp32 output of a product whose columns [off[k], off[k] + w[k]) go to C[k]
+// (row pitch w[k]), e.g. X^T [dQ | dK | dV] -> dW_Q, dW_K, dW_V.
+struct EpiF32Parts {
   static constexpr int NOUT = 1;
   template <int O> using OutT = float;
   float* C[3];
-  int64_t part;
+  int64_t w0, w1;   // widths: w0, w1, w1 (offsets 0, w0, w0 + w1)
   template <int O> __device__ __forceinline__ bool has_out() const { return true; }
   template <int O> __device__ __forceinline__ float* out_ptr(int64_t m, int64_t n, int, int) const {
-    const int k = n < part ? 0 : (n < 2 * part ? 1 : 2);
-    return C[k] + m * part + (n - k * part);
+    if (n < w0) return C[0] + m * w0 + n;
+    if (n < w0 + w1) return C[1] + m * w1 + (n - w0);
+    return C[2] + m * w1 + (n - w0 - w1);
   }
   template <int O> __device__ __forceinline__ f32x4 value(int64_t, int64_t, f32x4 v) const { return v; }
 };
 
 static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace: dO [M x N] bf16, [dQ | dK | dV] [M x 3N] bf16, [W_Q | W_K | W_V]
-// [d x 3N] bf16, D [b h s] fp32, then the split-K partials of dW_O.
-size_t attn_bwd_ws_bytes(int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t d_head) {
-  const int64_t M = b * s, N = h_local * d_head;
+// Workspace: dO [M x N] bf16, [dQ | dK | dV] [M x (N + 2 Nkv)] bf16,
+// [W_Q | W_K | W_V] [d x (N + 2 Nkv)] bf16, D [b h s] fp32, with grouped K/V
+// heads the per-query-head fp32 dK and dV contributions [M x N] each, then
+// the split-K partials of dW_O.
+struct AttnBwdLayout {
+  size_t dO, dQKV, Wcat, Dv, part, split, total;
+};
+
+static AttnBwdLayout attn_bwd_layout(int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv,
+                                     int64_t d_head) {
+  const int64_t M = b * s, N = h_local * d_head, Nt = N + 2 * h_kv * d_head;
   const GemmPlan pwo = plan_gemm(N, d, M, false, true);
-  return up256((size_t)M * N * 2) + up256((size_t)M * 3 * N * 2) + up256((size_t)d * 3 * N * 2) +
-         up256((size_t)b * h_local * s * 4) + (pwo.split > 1 ? up256((size_t)pwo.split * N * d * 4) : 0);
+  AttnBwdLayout l;
+  l.dO = 0;
+  l.dQKV = l.dO + up256((size_t)M * N * 2);
+  l.Wcat = l.dQKV + up256((size_t)M * Nt * 2);
+  l.Dv = l.Wcat + up256((size_t)d * Nt * 2);
+  l.part = l.Dv + up256((size_t)b * h_local * s * 4);
+  l.split = l.part + (h_kv != h_local ? 2 * up256((size_t)M * N * 4) : 0);
+  l.total = l.split + (pwo.split > 1 ? up256((size_t)pwo.split * N * d * 4) : 0);
+  return l;
 }
 
-hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local,
+size_t attn_bwd_ws_bytes(int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv, int64_t d_head) {
+  return attn_bwd_layout(b, s, d, h_local, h_kv, d_head).total;
+}
+
+hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv,
                            int64_t d_head, int causal, float scale,
                            const void* X, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
                            const void* Q, const void* K, const void* V, const void* O, const float* L,
                            const void* dY, void* dX, float* dWq, float* dWk, float* dWv, float* dWo,
                            void* ws) {
-  if (d_head != attnb::D) return hipErrorInvalidValue;
-  const int64_t M = b * s, N = h_local * d_head;
+  if (d_head != attnb::D || h_kv <= 0 || h_local % h_kv) return hipErrorInvalidValue;
+  const int64_t M = b * s, N = h_local * d_head, Nkv = h_kv * d_head, Nt = N + 2 * Nkv;
+  const int group = (int)(h_local / h_kv);
+  const AttnBwdLayout lay = attn_bwd_layout(b, s, d, h_local, h_kv, d_head);
   char* w = static_cast<char*>(ws);
-  bf16* dO = reinterpret_cast<bf16*>(w);
-  w += up256((size_t)M * N * 2);
-  bf16* dQKV = reinterpret_cast<bf16*>(w);           // [M x 3N]: dQ | dK | dV
-  w += up256((size_t)M * 3 * N * 2);
-  bf16* Wcat = reinterpret_cast<bf16*>(w);           // [d x 3N]: W_Q | W_K | W_V
-  w += up256((size_t)d * 3 * N * 2);
-  float* Dv = reinterpret_cast<float*>(w);
-  w += up256((size_t)b * h_local * s * 4);
-  float* split_ws = reinterpret_cast<float*>(w);
+  bf16* dO = reinterpret_cast<bf16*>(w + lay.dO);
+  bf16* dQKV = reinterpret_cast<bf16*>(w + lay.dQKV);  // [M x Nt]: dQ | dK | dV
+  bf16* Wcat = reinterpret_cast<bf16*>(w + lay.Wcat);  // [d x Nt]: W_Q | W_K | W_V
+  float* Dv = reinterpret_cast<float*>(w + lay.Dv);
+  float* part = reinterpret_cast<float*>(w + lay.part);
+  float* split_ws = reinterpret_cast<float*>(w + lay.split);
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d_head);
 
   {  // dO = dY W_O^T
@@ -440,31 +490,39 @@ hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
   const bf16* k = static_cast<const bf16*>(K);
   const bf16* v = static_cast<const bf16*>(V);
   const int nbh = (int)(b * h_local);
-  {  // dK, dV
-    const unsigned grid = (unsigned)(((s + 127) / 128) * nbh);
-    TPK_TRY(launch("attn_bwd.dkv", attn_bwd_dkv_kernel, dim3(grid), dim3(256), st, q, k, v, (const bf16*)dO, L,
-                   (const float*)Dv, dQKV + N, dQKV + 2 * N, (int)b, (int)h_local, (int)s, causal, sc, N, 3 * N));
+  const unsigned grid = (unsigned)(((s + 127) / 128) * nbh);
+  if (group == 1) {  // dK, dV straight into their columns of [dQ | dK | dV]
+    TPK_TRY(launch("attn_bwd.dkv", attn_bwd_dkv_kernel<bf16>, dim3(grid), dim3(256), st, q, k, v, (const bf16*)dO,
+                   L, (const float*)Dv, dQKV + N, dQKV + 2 * N, (int)b, (int)h_local, 1, (int)s, causal, sc, N, Nt));
+  } else {  // per-query-head contributions, then the ordered sum over each group
+    float* pk = part;
+    float* pv = reinterpret_cast<float*>(reinterpret_cast<char*>(part) + up256((size_t)M * N * 4));
+    TPK_TRY(launch("attn_bwd.dkv", attn_bwd_dkv_kernel<float>, dim3(grid), dim3(256), st, q, k, v, (const bf16*)dO,
+                   L, (const float*)Dv, pk, pv, (int)b, (int)h_local, group, (int)s, causal, sc, N, N));
+    const int64_t n = M * Nkv / 8;
+    const dim3 g2((unsigned)((n + 255) / 256));
+    TPK_TRY(launch("attn_bwd.group_sum", attn_bwd_group_sum_kernel, g2, dim3(256), st, (const float*)pk, dQKV + N, M,
+                   (int)h_local, group, Nt));
+    TPK_TRY(launch("attn_bwd.group_sum", attn_bwd_group_sum_kernel, g2, dim3(256), st, (const float*)pv,
+                   dQKV + N + Nkv, M, (int)h_local, group, Nt));
   }
-  {  // dQ
-    const unsigned grid = (unsigned)(((s + 127) / 128) * nbh);
-    TPK_TRY(launch("attn_bwd.dq", attn_bwd_dq_kernel, dim3(grid), dim3(256), st, q, k, v, (const bf16*)dO, L,
-                   (const float*)Dv, dQKV, (int)b, (int)h_local, (int)s, causal, sc, N, 3 * N));
-  }
+  TPK_TRY(launch("attn_bwd.dq", attn_bwd_dq_kernel, dim3(grid), dim3(256), st, q, k, v, (const bf16*)dO, L,
+                 (const float*)Dv, dQKV, (int)b, (int)h_local, group, (int)s, causal, sc, N, Nt));
   {  // [W_Q | W_K | W_V]
-    const int64_t n = d * 3 * (N / 8);
+    const int64_t n = d * (Nt / 8);
     TPK_TRY(launch("attn_bwd.concat_w", attn_concat3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st,
                    static_cast<const bf16*>(Wq), static_cast<const bf16*>(Wk), static_cast<const bf16*>(Wv), Wcat,
-                   d, N));
+                   d, N, Nkv));
   }
   {  // dX = [dQ | dK | dV] [W_Q | W_K | W_V]^T
-    GemmParams p = make_params(M, d, make_seg(dQKV, 3 * N, M * 3 * N, Wcat, 3 * N, d * 3 * N, 3 * N));
+    GemmParams p = make_params(M, d, make_seg(dQKV, Nt, M * Nt, Wcat, Nt, d * Nt, Nt));
     EpiStore<bf16> e{static_cast<bf16*>(dX), d, 0};
-    TPK_TRY((launch_gemm<true, true, false>(st, "attn_bwd.dqkv_wt", p, e, plan_gemm(M, d, 3 * N, false, false))));
+    TPK_TRY((launch_gemm<true, true, false>(st, "attn_bwd.dqkv_wt", p, e, plan_gemm(M, d, Nt, false, false))));
   }
   {  // [dW_Q | dW_K | dW_V] = X^T [dQ | dK | dV]
-    GemmParams p = make_params(d, 3 * N, make_seg(X, d, M * d, dQKV, 3 * N, M * 3 * N, M));
-    EpiF32Thirds e{{dWq, dWk, dWv}, N};
-    TPK_TRY((launch_gemm<false, false, false>(st, "attn_bwd.xt_dqkv", p, e, plan_gemm(d, 3 * N, M, false, false))));
+    GemmParams p = make_params(d, Nt, make_seg(X, d, M * d, dQKV, Nt, M * Nt, M));
+    EpiF32Parts e{{dWq, dWk, dWv}, N, Nkv};
+    TPK_TRY((launch_gemm<false, false, false>(st, "attn_bwd.xt_dqkv", p, e, plan_gemm(d, Nt, M, false, false))));
   }
   return hipSuccess;
 }

@@ -39,8 +39,8 @@ hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
                            int64_t d_head, int causal, float scale,
                            const void* X, const void* Wq, const void* Wk, const void* Wv,
                            const void* Wo, void* Q, void* K, void* V, void* O, void* Z, float* L);
-size_t attn_bwd_ws_bytes(int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t d_head);
-hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local,
+size_t attn_bwd_ws_bytes(int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv, int64_t d_head);
+hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv,
                            int64_t d_head, int causal, float scale,
                            const void* X, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
                            const void* Q, const void* K, const void* V, const void* O, const float* L,

@@ -296,13 +296,18 @@ static int attn_common(tp_dtype_t dt, int64_t b, int64_t s, int64_t d, int64_t h
   return TP_OK;
 }
 
+static int attn_kv_heads(int64_t h_local, int64_t h_kv) {
+  if (h_kv <= 0 || h_kv > h_local || h_local % h_kv)
+    return fail(TP_E_DIVIS, "h_kv_local = %lld must divide h_local = %lld", (long long)h_kv, (long long)h_local);
+  return TP_OK;
+}
+
 static int attn_fwd_impl(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d, int64_t h_local,
                          int64_t h_kv, int64_t d_head, int causal, float scale, const void* X, const void* Wq,
                          const void* Wk, const void* Wv, const void* Wo, void* Q, void* K, void* V, void* O,
                          void* Z, float* L, const char* what) {
   TP_CHECK(attn_common(dt, b, s, d, h_local, d_head, causal, scale));
-  if (h_kv <= 0 || h_kv > h_local || h_local % h_kv)
-    return fail(TP_E_DIVIS, "h_kv_local = %lld must divide h_local = %lld", (long long)h_kv, (long long)h_local);
+  TP_CHECK(attn_kv_heads(h_local, h_kv));
   const int64_t M = b * s, N = h_local * d_head, Nkv = h_kv * d_head;
   const size_t e = 2;
   TP_CHECK(check_buffers({{"X", X, M * d * e}, {"Wq", Wq, d * N * e}, {"Wk", Wk, d * Nkv * e},
@@ -331,10 +336,36 @@ int tp_attn_gqa_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int
                        V, O, Z, L, "tp_attn_gqa_shard_fwd");
 }
 
+static int attn_bwd_impl(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d, int64_t h_local,
+                         int64_t h_kv, int64_t d_head, int causal, float scale, const void* X, const void* Wq,
+                         const void* Wk, const void* Wv, const void* Wo, const void* Q, const void* K,
+                         const void* V, const void* O, const float* L, const void* dY, void* dX, float* dWq,
+                         float* dWk, float* dWv, float* dWo, void* ws, size_t ws_bytes, const char* what) {
+  TP_CHECK(attn_common(dt, b, s, d, h_local, d_head, causal, scale));
+  TP_CHECK(attn_kv_heads(h_local, h_kv));
+  if (d_head != 128) return fail(TP_E_DIM, "the attention backward supports d_head = 128");
+  const int64_t M = b * s, N = h_local * d_head, Nkv = h_kv * d_head;
+  TP_CHECK(check_ld({{"(h_local + 2 h_kv_local)*d_head", N + 2 * Nkv}}));
+  const size_t e = 2, need = tpk::attn_bwd_ws_bytes(b, s, d, h_local, h_kv, d_head);
+  TP_CHECK(check_buffers(
+      {{"X", X, M * d * e}, {"Wq", Wq, d * N * e}, {"Wk", Wk, d * Nkv * e}, {"Wv", Wv, d * Nkv * e},
+       {"Wo", Wo, N * d * e}, {"Q", Q, M * N * e}, {"K", K, M * Nkv * e}, {"V", V, M * Nkv * e},
+       {"O", O, M * N * e}, {"L", L, (size_t)(b * h_local * s) * 4}, {"dY", dY, M * d * e}},
+      {{"dX", dX, M * d * e}, {"dWq", dWq, d * N * (size_t)4}, {"dWk", dWk, d * Nkv * (size_t)4},
+       {"dWv", dWv, d * Nkv * (size_t)4}, {"dWo", dWo, N * d * (size_t)4}, {"ws", ws, need}},
+      {"X", "Wq", "Wk", "Wv", "Wo", "Q", "K", "V", "O", "L", "dY", "dX", "dWq", "dWk", "dWv", "dWo"}));
+  if (!ws || ws_bytes < need)
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes given, %zu required", ws ? ws_bytes : (size_t)0, need);
+  return hip_status(tpk::launch_attn_bwd(static_cast<hipStream_t>(stream), b, s, d, h_local, h_kv, d_head, causal,
+                                         scale, X, Wq, Wk, Wv, Wo, Q, K, V, O, L, dY, dX, dWq, dWk, dWv, dWo,
+                                         ws),
+                    what);
+}
+
 size_t tp_attn_shard_bwd_workspace_bytes(tp_dtype_t dt, int64_t b, int64_t s, int64_t d, int64_t h_local,
                                          int64_t d_head) {
   if (attn_common(dt, b, s, d, h_local, d_head, 0, 1.f) != TP_OK) return 0;
-  return tpk::attn_bwd_ws_bytes(b, s, d, h_local, d_head);
+  return tpk::attn_bwd_ws_bytes(b, s, d, h_local, h_local, d_head);
 }
 
 int tp_attn_shard_bwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
@@ -343,23 +374,25 @@ int tp_attn_shard_bwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t
                       const void* Q, const void* K, const void* V, const void* O, const float* L,
                       const void* dY, void* dX, float* dWq, float* dWk, float* dWv, float* dWo,
                       void* ws, size_t ws_bytes) {
-  TP_CHECK(attn_common(dt, b, s, d, h_local, d_head, causal, scale));
-  if (d_head != 128) return fail(TP_E_DIM, "the attention backward supports d_head = 128");
-  const int64_t M = b * s, N = h_local * d_head;
-  const size_t e = 2, need = tpk::attn_bwd_ws_bytes(b, s, d, h_local, d_head);
-  TP_CHECK(check_buffers(
-      {{"X", X, M * d * e}, {"Wq", Wq, d * N * e}, {"Wk", Wk, d * N * e}, {"Wv", Wv, d * N * e},
-       {"Wo", Wo, N * d * e}, {"Q", Q, M * N * e}, {"K", K, M * N * e}, {"V", V, M * N * e},
-       {"O", O, M * N * e}, {"L", L, (size_t)(b * h_local * s) * 4}, {"dY", dY, M * d * e}},
-      {{"dX", dX, M * d * e}, {"dWq", dWq, d * N * (size_t)4}, {"dWk", dWk, d * N * (size_t)4},
-       {"dWv", dWv, d * N * (size_t)4}, {"dWo", dWo, N * d * (size_t)4}, {"ws", ws, need}},
-      {"X", "Wq", "Wk", "Wv", "Wo", "Q", "K", "V", "O", "L", "dY", "dX", "dWq", "dWk", "dWv", "dWo"}));
-  if (!ws || ws_bytes < need)
-    return fail(TP_E_WORKSPACE, "workspace of %zu bytes given, %zu required", ws ? ws_bytes : (size_t)0, need);
-  return hip_status(tpk::launch_attn_bwd(static_cast<hipStream_t>(stream), b, s, d, h_local, d_head, causal,
-                                         scale, X, Wq, Wk, Wv, Wo, Q, K, V, O, L, dY, dX, dWq, dWk, dWv, dWo,
-                                         ws),
-                    "tp_attn_shard_bwd");
+  return attn_bwd_impl(stream, dt, b, s, d, h_local, h_local, d_head, causal, scale, X, Wq, Wk, Wv, Wo, Q, K, V, O,
+                       L, dY, dX, dWq, dWk, dWv, dWo, ws, ws_bytes, "tp_attn_shard_bwd");
+}
+
+size_t tp_attn_gqa_shard_bwd_workspace_bytes(tp_dtype_t dt, int64_t b, int64_t s, int64_t d, int64_t h_local,
+                                             int64_t h_kv_local, int64_t d_head) {
+  if (attn_common(dt, b, s, d, h_local, d_head, 0, 1.f) != TP_OK) return 0;
+  if (attn_kv_heads(h_local, h_kv_local) != TP_OK) return 0;
+  return tpk::attn_bwd_ws_bytes(b, s, d, h_local, h_kv_local, d_head);
+}
+
+int tp_attn_gqa_shard_bwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
+                          int64_t h_local, int64_t h_kv_local, int64_t d_head, int causal, float scale,
+                          const void* X, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                          const void* Q, const void* K, const void* V, const void* O, const float* L,
+                          const void* dY, void* dX, float* dWq, float* dWk, float* dWv, float* dWo,
+                          void* ws, size_t ws_bytes) {
+  return attn_bwd_impl(stream, dt, b, s, d, h_local, h_kv_local, d_head, causal, scale, X, Wq, Wk, Wv, Wo, Q, K, V,
+                       O, L, dY, dX, dWq, dWk, dWv, dWo, ws, ws_bytes, "tp_attn_gqa_shard_bwd");
 }
 
 int tp_shard_reduce(void* stream, tp_dtype_t dt_in, tp_dtype_t dt_out, int64_t n_shards, int64_t numel,

@@ -33,7 +33,7 @@ def test_header_and_binding_agree_and_library_exports_all():
 
 
 def test_version_and_strerror():
-    assert tp.tp_abi_version() == 4
+    assert tp.tp_abi_version() == 5
     L = tp.lib()
     for code in (OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP):
         assert L.tp_strerror(code) and L.tp_strerror(code) != b"unknown status"
@@ -314,3 +314,22 @@ def test_vocab_validation():
     assert L.tp_vocab_ce_bwd(None, BF16, 16, 64, 128, 0, *args, ws, need - 1) == E_WS
     assert L.tp_vocab_ce_bwd(None, BF16, 16, 64, 128, 0, *args[:6], X, dE, ws, need) == E_ALIAS
     assert L.tp_vocab_ce_bwd(None, BF16, 16, 64, 128, 0, *args[:7], None, ws, need) == E_NULL
+
+
+def test_gqa_backward_validation():
+    L = tp.lib()
+    p = _addrs(17)
+    ws = p[16]
+    need = L.tp_attn_gqa_shard_bwd_workspace_bytes(BF16, 1, 64, 64, 4, 2, 128)
+    assert need > 0
+    assert L.tp_attn_gqa_shard_bwd_workspace_bytes(BF16, 1, 64, 64, 4, 3, 128) == 0
+    args = p[:16]
+    assert L.tp_attn_gqa_shard_bwd(None, BF16, 1, 64, 64, 4, 3, 128, 1, 0.0, *args, ws, need) == E_DIVIS
+    assert L.tp_attn_gqa_shard_bwd(None, BF16, 1, 64, 64, 4, 2, 64, 1, 0.0, *args, ws, need) == E_DIM
+    assert L.tp_attn_gqa_shard_bwd(None, F32, 1, 64, 64, 4, 2, 128, 1, 0.0, *args, ws, need) == E_DTYPE
+    assert L.tp_attn_gqa_shard_bwd(None, BF16, 1, 64, 64, 4, 2, 128, 1, 0.0, *args, None, 0) == E_WS
+    assert L.tp_attn_gqa_shard_bwd(None, BF16, 1, 64, 64, 4, 2, 128, 1, 0.0, *args, ws, need - 1) == E_WS
+    assert L.tp_attn_gqa_shard_bwd(None, BF16, 1, 64, 64, 4, 2, 128, 1, 0.0, None, *args[1:], ws, need) == E_NULL
+    # one group is the multi-head backward: same workspace
+    assert (L.tp_attn_gqa_shard_bwd_workspace_bytes(BF16, 2, 96, 64, 4, 4, 128)
+            == L.tp_attn_shard_bwd_workspace_bytes(BF16, 2, 96, 64, 4, 128))

@@ -447,3 +447,71 @@ def test_gqa_g1_full_size_sampled(tp):
         ref = O.attn_gqa_query_rows(Xb, inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], rows, h_l, h_kv, dh)
         check(f"O[b{bi}]", host(out["O"])[bi * s + rows], ref["O"], "bf16")
         check(f"Z[b{bi}]", host(out["Z"])[bi * s + rows], ref["Z"], "bf16")
+
+
+def run_gqa_bwd(tp, inp, fwd, dY, b, s, h_l, h_kv, dh, causal=True):
+    X, Wq, Wk, Wv, Wo = (dev(inp[k], "bf16") for k in ("X", "Wq", "Wk", "Wv", "Wo"))
+    d = X.shape[1]
+    N, Nkv = h_l * dh, h_kv * dh
+    dX = empty((b * s, d), "bf16")
+    dWq, dWo = empty((d, N), "f32"), empty((N, d), "f32")
+    dWk, dWv = empty((d, Nkv), "f32"), empty((d, Nkv), "f32")
+    ws = torch.empty(tp.tp_attn_gqa_shard_bwd_workspace_bytes(tp.TP_DT_BF16, b, s, d, h_l, h_kv, dh),
+                     dtype=torch.uint8, device="cuda")
+    tp.tp_attn_gqa_shard_bwd(X, Wq, Wk, Wv, Wo, fwd["Q"], fwd["K"], fwd["V"], fwd["O"], fwd["L"], dY, dX, dWq,
+                             dWk, dWv, dWo, ws, b, s, h_l, h_kv, dh, causal=causal)
+    torch.cuda.synchronize()
+    return dict(dX=dX, dWq=dWq, dWk=dWk, dWv=dWv, dWo=dWo)
+
+
+@pytest.mark.parametrize("b,s,d,h_l,h_kv,causal", [
+    (2, 200, 64, 4, 2, True),
+    (1, 257, 96, 4, 1, True),
+    (2, 130, 64, 6, 3, False),
+    (1, 64, 72, 16, 1, True),     # the G1 grouping
+    (1, 96, 64, 3, 3, True),      # one query head per K/V head: the multi-head backward
+])
+def test_gqa_bwd_small_shapes(tp, b, s, d, h_l, h_kv, causal):
+    _say(f"gqa bwd b={b} s={s} d={d} h_l={h_l} h_kv={h_kv} causal={causal}")
+    dh = 128
+    inp = tpsynth.random_gqa(b, s, d, h_l, h_kv, dh, "bf16", seed=s + 7 * h_l, w_std=0.1)
+    dYn = tpsynth.normal(np.random.default_rng(s + 1), (b * s, d), 1.0, "bf16")
+    fwd = run_gqa(tp, inp, b, s, h_l, h_kv, dh, causal)
+    out = run_gqa_bwd(tp, inp, fwd, dev(dYn, "bf16"), b, s, h_l, h_kv, dh, causal)
+    ref = O.attn_gqa_shard_bwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], dYn, b, s, h_l, h_kv, dh,
+                               causal)
+    for k in ("dX", "dWq", "dWk", "dWv", "dWo"):
+        check(k, out[k], ref[k], "bf16")
+
+
+def test_gqa_bwd_g1_grouping_long_sequence(tp):
+    """The G1 grouping (16 query heads on one K/V head, d_head 128) at s 1024
+    and d 2048, every output against the oracle."""
+    _say("gqa bwd 16:1 grouping, s 1024, d 2048")
+    b, s, d, h_l, h_kv, dh = 1, 1024, 2048, 16, 1, 128
+    inp = tpsynth.random_gqa(b, s, d, h_l, h_kv, dh, "bf16", seed=93, w_std=0.01)
+    dYn = tpsynth.normal(np.random.default_rng(94), (b * s, d), 1.0, "bf16")
+    fwd = run_gqa(tp, inp, b, s, h_l, h_kv, dh)
+    out = run_gqa_bwd(tp, inp, fwd, dev(dYn, "bf16"), b, s, h_l, h_kv, dh)
+    ref = O.attn_gqa_shard_bwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], dYn, b, s, h_l, h_kv, dh)
+    for k in ("dX", "dWq", "dWk", "dWv", "dWo"):
+        check(k, out[k], ref[k], "bf16")
+
+
+def test_gqa_bwd_g1_full_size_deterministic(tp):
+    """G1 at full size: the backward runs, its outputs are finite and two runs
+    agree bit for bit (every gradient has one owner and a fixed summation
+    order, including the sum over each K/V head's group)."""
+    _say("gqa bwd G1 full size, determinism")
+    wl = tpsynth.WORKLOADS["G1"]
+    inp = tpsynth.gqa_inputs(wl)
+    b, s, h_l, h_kv, dh = wl.b, wl.s, wl.h_local, wl.h_kv_local, wl.d_head
+    dY = torch.from_numpy(np.random.default_rng(95).standard_normal((b * s, wl.d)).astype(np.float32))
+    dY = dY.to(torch.bfloat16).cuda()
+    fwd = run_gqa(tp, inp, b, s, h_l, h_kv, dh)
+    a = run_gqa_bwd(tp, inp, fwd, dY, b, s, h_l, h_kv, dh)
+    c = run_gqa_bwd(tp, inp, fwd, dY, b, s, h_l, h_kv, dh)
+    for k in a:
+        assert torch.isfinite(a[k]).all(), k
+        assert torch.equal(a[k], c[k]), k
+
