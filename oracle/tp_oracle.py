@@ -52,7 +52,8 @@ __all__ = [
     "attn_shard_fwd", "attn_unsharded", "attn_core", "attn_core_lse", "attn_core_bwd", "attn_shard_bwd",
     "attn_gqa_shard_fwd", "attn_gqa_query_rows", "attn_gqa_shard_bwd",
     "shard_reduce", "shard_range",
-    "stripe_rows", "reduce_scatter", "all_gather", "layer_norm", "sp_block_end",
+    "stripe_rows", "reduce_scatter", "all_gather", "layer_norm", "sp_block_end", "layer_norm_bwd",
+    "sp_block_end_bwd",
     "vocab_embed_shard", "vocab_embed", "vocab_ce_shard", "vocab_ce_combine", "vocab_ce_fwd",
     "vocab_ce_shard_bwd",
 ]
@@ -460,6 +461,41 @@ def sp_block_end(partials: Sequence, n_shards: int, index: int, residual, gamma,
         y = y * _f64(keep) / (1.0 - p_drop)
     h = _f64(residual) + y
     return {"h": h, "x": layer_norm(h, gamma, beta, eps)}
+
+def layer_norm_bwd(dx, h, gamma, eps: float = 1e-5) -> Dict[str, np.ndarray]:
+    """Backward of layer_norm by the chain rule on its definition, per row:
+    with xhat = (h - mean) / sqrt(var + eps) and g = dx * gamma,
+      dh = (g - mean(g) - xhat * mean(g * xhat)) / sqrt(var + eps),
+      dgamma = sum over rows of dx * xhat,  dbeta = sum over rows of dx."""
+    dx, h, gamma = _f64(dx), _f64(h), _f64(gamma)
+    mu = h.mean(axis=1, keepdims=True)
+    var = ((h - mu) ** 2).mean(axis=1, keepdims=True)
+    rstd = 1.0 / np.sqrt(var + eps)
+    xhat = (h - mu) * rstd
+    g = dx * gamma
+    dh = (g - g.mean(axis=1, keepdims=True) - xhat * (g * xhat).mean(axis=1, keepdims=True)) * rstd
+    return {"dh": dh, "dgamma": (dx * xhat).sum(axis=0), "dbeta": dx.sum(axis=0)}
+
+
+def sp_block_end_bwd(dx_partials: Sequence, n_shards: int, index: int, h, gamma, keep=None,
+                     p_drop: float = 0.0, dres=None, eps: float = 1e-5) -> Dict[str, np.ndarray]:
+    """Backward of sp_block_end on one GPU's stripe ([HC] Figure 3.7: the
+    backward pass mirrors the forward, a reduce-scatter where the forward
+    gathered).  dx: the stripe of the sum of every shard's gradient of the
+    next block's input (reduce_scatter of the summands); h: the stripe's
+    residual stream as the forward produced it; dres: gradient reaching h
+    through the skip connection (or None).
+      dh = LayerNorm backward of dx (+ dres)      -> the previous residual's gradient
+      dy = dh * keep / (1 - p)                    -> the gradient of the reduce-scattered sum
+      dbias = sum over the stripe's rows of dy; dgamma, dbeta this stripe's parts.
+    Every shard's row-parallel partial then receives the all-gather of the
+    stripes' dy as its output gradient."""
+    dx = reduce_scatter(dx_partials, n_shards, index)
+    ln = layer_norm_bwd(dx, h, gamma, eps)
+    dh = ln["dh"] + (_f64(dres) if dres is not None else 0.0)
+    dy = dh * _f64(keep) / (1.0 - p_drop) if keep is not None else dh
+    return {"dh": dh, "dy": dy, "dbias": dy.sum(axis=0), "dgamma": ln["dgamma"], "dbeta": ln["dbeta"]}
+
 
 # ----------------------------------------------------------------------------
 # Vocabulary-parallel embeddings ([JY] Embedding and Implementation)

@@ -521,6 +521,80 @@ def test_sp_block_end_definition():
     np.testing.assert_allclose(out0["h"], res + sum(q[0:4] for q in P), rtol=1e-14, atol=1e-14)
 
 
+def test_layer_norm_bwd_matches_finite_differences():
+    rng = np.random.default_rng(96)
+    h = rng.standard_normal((3, 7)) * 2 + 0.5
+    g, b = rng.standard_normal(7), rng.standard_normal(7)
+    G = rng.standard_normal((3, 7))
+    r = O.layer_norm_bwd(G, h, g)
+    L = lambda h_, g_, b_: float((O.layer_norm(h_, g_, b_) * G).sum())
+    eps = 1e-6
+    for (i, j) in [(0, 0), (1, 3), (2, 6)]:
+        hp, hm = h.copy(), h.copy()
+        hp[i, j] += eps
+        hm[i, j] -= eps
+        assert r["dh"][i, j] == pytest.approx((L(hp, g, b) - L(hm, g, b)) / (2 * eps), rel=1e-6, abs=1e-9)
+    for j in (0, 4):
+        gp, gm = g.copy(), g.copy()
+        gp[j] += eps
+        gm[j] -= eps
+        assert r["dgamma"][j] == pytest.approx((L(h, gp, b) - L(h, gm, b)) / (2 * eps), rel=1e-6, abs=1e-9)
+        bp, bm = b.copy(), b.copy()
+        bp[j] += eps
+        bm[j] -= eps
+        assert r["dbeta"][j] == pytest.approx((L(h, g, bp) - L(h, g, bm)) / (2 * eps), rel=1e-6, abs=1e-9)
+    # a row's input gradient is orthogonal to the constant and to xhat (LayerNorm's invariances)
+    np.testing.assert_allclose(r["dh"].sum(axis=1), 0, atol=1e-12)
+
+
+def test_sp_block_end_bwd_matches_finite_differences():
+    """Gradients of <Gx, x> + <Gh, h> through sp_block_end, with Gx the
+    reduce-scattered stripe of the shards' summands."""
+    rng = np.random.default_rng(97)
+    n, rows, cols, index, p = 3, 6, 5, 1, 0.25
+    P = rng.standard_normal((n, rows, cols))
+    r0, k = O.stripe_rows(rows, n, index)
+    res = rng.standard_normal((k, cols))
+    g, b, bias = rng.standard_normal(cols), rng.standard_normal(cols), rng.standard_normal(cols)
+    keep = (rng.random((k, cols)) > p).astype(np.uint8)
+    Gp = rng.standard_normal((n, rows, cols))            # next block's input-gradient summands
+    Gh = rng.standard_normal((k, cols))
+    Gx = Gp.sum(axis=0)[r0:r0 + k]
+    fw = O.sp_block_end(list(P), n, index, res, g, b, bias, keep, p)
+    bw = O.sp_block_end_bwd(list(Gp), n, index, fw["h"], g, keep, p, dres=Gh)
+
+    def L(P_, res_, g_, b_, bias_):
+        o = O.sp_block_end(list(P_), n, index, res_, g_, b_, bias_, keep, p)
+        return float((o["x"] * Gx).sum() + (o["h"] * Gh).sum())
+
+    eps = 1e-6
+    for (sh, i, j) in [(0, r0, 0), (2, r0 + 1, 3)]:       # any shard's partial at a stripe row gets dy
+        Pp, Pm = P.copy(), P.copy()
+        Pp[sh, i, j] += eps
+        Pm[sh, i, j] -= eps
+        num = (L(Pp, res, g, b, bias) - L(Pm, res, g, b, bias)) / (2 * eps)
+        assert bw["dy"][i - r0, j] == pytest.approx(num, rel=1e-6, abs=1e-9)
+    for (i, j) in [(0, 2), (1, 4)]:
+        rp, rm = res.copy(), res.copy()
+        rp[i, j] += eps
+        rm[i, j] -= eps
+        assert bw["dh"][i, j] == pytest.approx((L(P, rp, g, b, bias) - L(P, rm, g, b, bias)) / (2 * eps),
+                                               rel=1e-6, abs=1e-9)
+    for j in (1, 3):
+        e = np.zeros(cols)
+        e[j] = eps
+        assert bw["dgamma"][j] == pytest.approx((L(P, res, g + e, b, bias) - L(P, res, g - e, b, bias)) / (2 * eps),
+                                                rel=1e-6, abs=1e-9)
+        assert bw["dbeta"][j] == pytest.approx((L(P, res, g, b + e, bias) - L(P, res, g, b - e, bias)) / (2 * eps),
+                                               rel=1e-6, abs=1e-9)
+        assert bw["dbias"][j] == pytest.approx((L(P, res, g, b, bias + e) - L(P, res, g, b, bias - e)) / (2 * eps),
+                                               rel=1e-6, abs=1e-9)
+    # a partial outside the stripe does not touch this GPU's outputs
+    Pp = P.copy()
+    Pp[0, 0 if r0 else rows - 1, 0] += 1.0
+    assert L(Pp, res, g, b, bias) == pytest.approx(L(P, res, g, b, bias), abs=1e-12)
+
+
 # -------------------------------------------------------------- shard-reduce
 
 def _read_golden_allreduce():
