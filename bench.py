@@ -455,10 +455,26 @@ def run_s1(tp, torch, steps, warmup):
 
     ms, _, per = timed(tp, torch, step, steps, warmup, 2)
     gms = graph_timed(torch, step, steps)
+    # backward: this stripe's LayerNorm/dropout backward of the 8 shards' input gradients, then the
+    # all-gather of the 8 stripes' dy (the row-parallel products' output gradient)
+    dres = torch.randn((k, cols), device="cuda").to(bf)
+    dh_b, dy_b = torch.empty((k, cols), dtype=bf, device="cuda"), torch.empty((k, cols), dtype=bf, device="cuda")
+    dgam, dbet, dbias = (torch.empty(cols, device="cuda") for _ in range(3))
+    ws = torch.empty(tp.tp_sp_ln_bwd_workspace_bytes(tp.TP_DT_BF16, n, rows, cols), dtype=torch.uint8,
+                     device="cuda")
+    dys = [dy_b] + [torch.zeros((k, cols), dtype=bf, device="cuda") for _ in range(n - 1)]
+
+    def bwd():
+        tp.tp_sp_ln_bwd_reduce_scatter(P, stripes[0], gamma, dh_b, dy_b, dgam, dbet, ws, n, 0, rows, cols,
+                                       keep=keep, p_drop=p_drop, dres=dres, dbias=dbias)
+        tp.tp_sp_all_gather(dys, full)
+
+    ms_b, _, per_b = timed(tp, torch, bwd, steps, warmup, 3)
     e = k * cols
     rs_bytes = (n + 1) * e * 2 + e + 3 * cols * 2 + 2 * e * 2
     ag_bytes = 2 * n * e * 2
     avg = lambda lab: (sum(per[lab]) / len(per[lab])) if per.get(lab) else None
+    avg_b = lambda lab, pp: (sum(pp[lab]) / len(pp[lab])) if pp.get(lab) else None
     rs_ms, ag_ms = avg("sp.rs_ln"), avg("sp.all_gather")
     # cold: evict the 256 MB Infinity Cache before each launch
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -483,17 +499,23 @@ def run_s1(tp, torch, steps, warmup):
     ev.close()
     del scratch
     gbs = lambda b, t: round(b / t / 1e6, 1) if t else None
+    bwd_bytes = n * e * 2 + e * 2 + e + e * 2 + 2 * e * 2 + cols * 2
+    bwd_ms = avg_b("sp.ln_bwd", per_b)
     return {"workload": "S1 sequence-parallel block end: 8192 tokens x 8192 over TP 8, this GPU's "
                         "1024-token stripe (reduce-scatter of 8 partials + bias, dropout 0.1, residual, "
-                        "LayerNorm) + all-gather of the 8 stripes",
-            "ms_per_step": round(ms, 4), "graph_ms_per_step": round(gms, 4),
+                        "LayerNorm) + all-gather of the 8 stripes; backward: LayerNorm/dropout backward of "
+                        "the 8 shards' input gradients on the stripe + all-gather of dy",
+            "ms_per_step": round(ms, 4), "graph_ms_per_step": round(gms, 4), "bwd_ms_per_step": round(ms_b, 4),
+            "ln_bwd": {"bytes": bwd_bytes, "warm_ms": round(bwd_ms, 4) if bwd_ms else None,
+                       "warm_GBps": gbs(bwd_bytes, bwd_ms), "peak_GBps": PEAK_HBM_GBS},
             "rs_ln": {"bytes": rs_bytes, "warm_ms": round(rs_ms, 4) if rs_ms else None,
                       "warm_GBps": gbs(rs_bytes, rs_ms), "cold_ms": round(min(cold_rs), 4),
                       "cold_GBps": gbs(rs_bytes, min(cold_rs)), "peak_GBps": PEAK_HBM_GBS},
             "all_gather": {"bytes": ag_bytes, "warm_ms": round(ag_ms, 4) if ag_ms else None,
                            "warm_GBps": gbs(ag_bytes, ag_ms), "cold_ms": round(min(cold_ag), 4),
                            "cold_GBps": gbs(ag_bytes, min(cold_ag)), "peak_GBps": PEAK_HBM_GBS},
-            "kernels_ms": {key: round(sum(v) / len(v), 4) for key, v in per.items()}}
+            "kernels_ms": {key: round(sum(v) / len(v), 4) for key, v in list(per.items()) +
+                           [("bwd." + kk, vv) for kk, vv in per_b.items()]}}
 
 
 def run_e1(tp, torch, steps, warmup):

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 5
+#define TP_ABI_VERSION 6
 
 typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype_t;
 
@@ -252,6 +252,31 @@ int tp_sp_reduce_scatter_ln(void* stream, tp_dtype_t dt, int64_t n_shards, int64
                             int64_t shard_stride, const void* bias, const void* residual,
                             const uint8_t* keep, float p_drop, const void* gamma,
                             const void* beta, float eps, void* h_out, void* x_out);
+
+/* ---------------------------------------------------------------------------
+ * tp_sp_ln_bwd_reduce_scatter — backward of tp_sp_reduce_scatter_ln on one
+ * stripe ([HC] Figure 3.7: the backward pass mirrors the forward, a
+ * reduce-scatter where the forward gathered).  With k = rows / n_shards:
+ *   dx[r]  = sum_i dx_partials[i*shard_stride + (index*k + r)*cols + :]
+ *            (every shard's gradient of the next block's input, this stripe)
+ *   dh[r]  = LayerNorm backward of dx[r] at h[r] (statistics recomputed from
+ *            h as stored, biased variance, eps) + dres[r]     -> dh_out
+ *   dy[r]  = dh[r] * keep[r] / (1 - p_drop)  (dh[r] when keep is NULL) -> dy_out
+ *   dgamma = sum_r dx[r] * xhat[r],  dbeta = sum_r dx[r],  dbias = sum_r dy[r]
+ * (fp32 [cols], this stripe's parts; summed in a fixed order).  dh_out is
+ * the gradient of the previous residual stream; the all-gather of the
+ * stripes' dy_out (tp_sp_all_gather) is the output gradient of every
+ * shard's row-parallel product.  h, keep, dres, dh_out, dy_out: [k x cols];
+ * dres and dbias may be NULL.  cols a multiple of 8 and <= 16384.  ws:
+ * device workspace of tp_sp_ln_bwd_workspace_bytes(...) bytes.
+ * ------------------------------------------------------------------------- */
+int tp_sp_ln_bwd_reduce_scatter(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t rows,
+                                int64_t cols, int64_t index, const void* dx_partials,
+                                int64_t shard_stride, const void* h, const void* gamma, float eps,
+                                const uint8_t* keep, float p_drop, const void* dres, void* dh_out,
+                                void* dy_out, float* dgamma, float* dbeta, float* dbias, void* ws,
+                                size_t ws_bytes);
+size_t tp_sp_ln_bwd_workspace_bytes(tp_dtype_t dt, int64_t n_shards, int64_t rows, int64_t cols);
 
 /* ---------------------------------------------------------------------------
  * tp_sp_all_gather — the all-gather that rebuilds the full input of the next

@@ -18,7 +18,8 @@ __all__ = [
     "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes",
     "tp_attn_shard_fwd", "tp_attn_gqa_shard_fwd", "tp_attn_shard_bwd", "tp_attn_shard_bwd_workspace_bytes",
     "tp_attn_gqa_shard_bwd", "tp_attn_gqa_shard_bwd_workspace_bytes",
-    "tp_shard_reduce", "tp_shard_range", "tp_sp_reduce_scatter_ln", "tp_sp_all_gather",
+    "tp_shard_reduce", "tp_shard_range", "tp_sp_reduce_scatter_ln", "tp_sp_all_gather", "tp_sp_ln_bwd_reduce_scatter",
+    "tp_sp_ln_bwd_workspace_bytes",
     "tp_vocab_embed_fwd", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
     "tp_vocab_ce_bwd_workspace_bytes",
     "tp_abi_version", "EXPORTS",
@@ -61,6 +62,9 @@ EXPORTS = {
     "tp_sp_reduce_scatter_ln": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, _p, ctypes.c_float,
                                        _p, _p, ctypes.c_float, _p, _p]),
     "tp_sp_all_gather": (_i32, [_p, _i32, _i64, _i64, _i64, ctypes.POINTER(_p), _p]),
+    "tp_sp_ln_bwd_reduce_scatter": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _i64, _p, _p, ctypes.c_float, _p,
+                                           ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _sz]),
+    "tp_sp_ln_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
     "tp_vocab_embed_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p]),
     "tp_vocab_ce_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "tp_vocab_ce_combine": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p]),
@@ -246,6 +250,27 @@ def tp_sp_reduce_scatter_ln(partials, residual, gamma, beta, h_out, x_out, n_sha
                                          _ptr(partials), stride, _ptr(bias), _ptr(residual), _ptr(keep),
                                          float(p_drop), _ptr(gamma), _ptr(beta), float(eps), _ptr(h_out),
                                          _ptr(x_out)))
+
+
+def tp_sp_ln_bwd_workspace_bytes(dtype: int, n_shards: int, rows: int, cols: int) -> int:
+    return lib().tp_sp_ln_bwd_workspace_bytes(dtype, n_shards, rows, cols)
+
+
+def tp_sp_ln_bwd_reduce_scatter(dx_partials, h, gamma, dh_out, dy_out, dgamma, dbeta, ws, n_shards: int,
+                                index: int, rows: int, cols: int, shard_stride: Optional[int] = None, keep=None,
+                                p_drop: float = 0.0, dres=None, dbias=None, eps: float = 1e-5,
+                                stream=None) -> None:
+    """Backward of tp_sp_reduce_scatter_ln on stripe `index`: the stripe's
+    LayerNorm backward of the summed input gradients (+ dres) -> dh_out,
+    dropout backward -> dy_out, and this stripe's gamma/beta/bias gradients."""
+    import torch
+    if keep is not None and keep.dtype != torch.uint8:
+        raise TypeError("keep must be a uint8 tensor")
+    stride = rows * cols if shard_stride is None else shard_stride
+    _check(lib().tp_sp_ln_bwd_reduce_scatter(_stream(stream), _dt(h), n_shards, rows, cols, index,
+                                             _ptr(dx_partials), stride, _ptr(h), _ptr(gamma), float(eps), _ptr(keep),
+                                             float(p_drop), _ptr(dres), _ptr(dh_out), _ptr(dy_out), _ptr(dgamma),
+                                             _ptr(dbeta), _ptr(dbias), _ptr(ws), ws.numel() * ws.element_size()))
 
 
 def tp_sp_all_gather(stripes, full, stream=None) -> None:

@@ -52,6 +52,11 @@ hipError_t launch_sp_reduce_scatter_ln(hipStream_t st, int dt, int n, int64_t ro
                                        const void* residual, const uint8_t* keep, float p_drop,
                                        const void* gamma, const void* beta, float eps, void* h_out,
                                        void* x_out);
+size_t sp_ln_bwd_ws_bytes(int64_t rows, int64_t cols, int n);
+hipError_t launch_sp_ln_bwd(hipStream_t st, int dt, int n, int64_t rows, int64_t cols, int64_t index,
+                            const void* P, int64_t stride, const void* h, const void* gamma, float eps,
+                            const uint8_t* keep, float p_drop, const void* dres, void* dh_out, void* dy_out,
+                            float* dgamma, float* dbeta, float* dbias, void* ws);
 hipError_t launch_sp_all_gather(hipStream_t st, int dt, int n, int64_t stripe_rows, int64_t cols,
                                 const void* const* stripes, void* full);
 

@@ -458,6 +458,60 @@ int tp_sp_reduce_scatter_ln(void* stream, tp_dtype_t dt, int64_t n_shards, int64
                     "tp_sp_reduce_scatter_ln");
 }
 
+static int sp_bwd_common(tp_dtype_t dt, int64_t n_shards, int64_t rows, int64_t cols) {
+  if (!dtype_ok(dt)) return fail(TP_E_DTYPE, "dtype %d is not TP_DT_F32 or TP_DT_BF16", (int)dt);
+  if (n_shards <= 0 || n_shards > 4096) return fail(TP_E_DIM, "n_shards = %lld outside [1, 4096]", (long long)n_shards);
+  TP_CHECK(check_dims({{"rows", rows}, {"cols", cols}}));
+  if (rows % n_shards)
+    return fail(TP_E_DIVIS, "rows = %lld is not divisible by n_shards = %lld", (long long)rows, (long long)n_shards);
+  TP_CHECK(check_mult8({{"cols", cols}}));
+  if (cols > 16384) return fail(TP_E_DIM, "cols = %lld exceeds 16384 (the backward keeps a row in registers)",
+                                (long long)cols);
+  if (rows / n_shards > (int64_t(1) << 24))
+    return fail(TP_E_DIM, "stripe of %lld rows exceeds 2^24", (long long)(rows / n_shards));
+  return TP_OK;
+}
+
+size_t tp_sp_ln_bwd_workspace_bytes(tp_dtype_t dt, int64_t n_shards, int64_t rows, int64_t cols) {
+  if (sp_bwd_common(dt, n_shards, rows, cols) != TP_OK) return 0;
+  return tpk::sp_ln_bwd_ws_bytes(rows, cols, (int)n_shards);
+}
+
+int tp_sp_ln_bwd_reduce_scatter(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t rows, int64_t cols,
+                                int64_t index, const void* dx_partials, int64_t shard_stride, const void* h,
+                                const void* gamma, float eps, const uint8_t* keep, float p_drop,
+                                const void* dres, void* dh_out, void* dy_out, float* dgamma, float* dbeta,
+                                float* dbias, void* ws, size_t ws_bytes) {
+  TP_CHECK(sp_bwd_common(dt, n_shards, rows, cols));
+  if (index < 0 || index >= n_shards)
+    return fail(TP_E_DIM, "index = %lld outside [0, %lld)", (long long)index, (long long)n_shards);
+  const int64_t numel = rows * cols;
+  if (shard_stride < numel)
+    return fail(TP_E_DIM, "shard_stride %lld < rows*cols %lld", (long long)shard_stride, (long long)numel);
+  if (shard_stride % 8) return fail(TP_E_DIVIS, "shard_stride = %lld must be a multiple of 8", (long long)shard_stride);
+  if (keep && !(p_drop >= 0.0f && p_drop < 1.0f))
+    return fail(TP_E_DIM, "p_drop = %g outside [0, 1)", (double)p_drop);
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(TP_E_DIM, "eps = %g must be positive and finite", (double)eps);
+  const size_t e = esize(dt);
+  const size_t stripe = (size_t)(rows / n_shards * cols);
+  const size_t need = tpk::sp_ln_bwd_ws_bytes(rows, cols, (int)n_shards);
+  TP_CHECK(check_buffers({{"dx_partials", dx_partials, ((size_t)(n_shards - 1) * shard_stride + numel) * e},
+                          {"h", h, stripe * e},
+                          {"gamma", gamma, cols * e},
+                          {"keep", keep, keep ? stripe : 0},
+                          {"dres", dres, dres ? stripe * e : 0}},
+                         {{"dh_out", dh_out, stripe * e}, {"dy_out", dy_out, stripe * e},
+                          {"dgamma", dgamma, (size_t)cols * 4, 4}, {"dbeta", dbeta, (size_t)cols * 4, 4},
+                          {"dbias", dbias, dbias ? (size_t)cols * 4 : 0, 4}, {"ws", ws, need}},
+                         {"dx_partials", "h", "gamma", "dh_out", "dy_out", "dgamma", "dbeta"}));
+  if (!ws || ws_bytes < need)
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes given, %zu required", ws ? ws_bytes : (size_t)0, need);
+  return hip_status(tpk::launch_sp_ln_bwd(static_cast<hipStream_t>(stream), dt, (int)n_shards, rows, cols, index,
+                                          dx_partials, shard_stride, h, gamma, eps, keep, p_drop, dres, dh_out,
+                                          dy_out, dgamma, dbeta, dbias, ws),
+                    "tp_sp_ln_bwd_reduce_scatter");
+}
+
 int tp_sp_all_gather(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t stripe_rows, int64_t cols,
                      const void* const* stripes, void* full) {
   if (!dtype_ok(dt)) return fail(TP_E_DTYPE, "dtype %d is not TP_DT_F32 or TP_DT_BF16", (int)dt);

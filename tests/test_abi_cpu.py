@@ -33,7 +33,7 @@ def test_header_and_binding_agree_and_library_exports_all():
 
 
 def test_version_and_strerror():
-    assert tp.tp_abi_version() == 5
+    assert tp.tp_abi_version() == 6
     L = tp.lib()
     for code in (OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP):
         assert L.tp_strerror(code) and L.tp_strerror(code) != b"unknown status"
@@ -333,3 +333,29 @@ def test_gqa_backward_validation():
     # one group is the multi-head backward: same workspace
     assert (L.tp_attn_gqa_shard_bwd_workspace_bytes(BF16, 2, 96, 64, 4, 4, 128)
             == L.tp_attn_shard_bwd_workspace_bytes(BF16, 2, 96, 64, 4, 128))
+
+
+def test_sp_ln_bwd_validation():
+    L = tp.lib()
+    P, h, g, keep, dres, dh, dy, dg, db, dbi, ws = _addrs(11)
+    need = L.tp_sp_ln_bwd_workspace_bytes(BF16, 4, 64, 32)
+    assert need > 0
+    assert L.tp_sp_ln_bwd_workspace_bytes(BF16, 4, 66, 32) == 0
+    assert L.tp_sp_ln_bwd_workspace_bytes(BF16, 4, 64, 16392) == 0     # rows kept in registers: <= 16384
+
+    def bw(dt=BF16, n=4, rows=64, cols=32, index=1, P=P, stride=None, h=h, g=g, eps=1e-5, keep=keep, p=0.1,
+           dres=dres, dh=dh, dy=dy, dg=dg, db=db, dbi=dbi, ws=ws, wsb=None):
+        stride = rows * cols if stride is None else stride
+        return L.tp_sp_ln_bwd_reduce_scatter(None, dt, n, rows, cols, index, P, stride, h, g, eps, keep, p, dres,
+                                             dh, dy, dg, db, dbi, ws, need if wsb is None else wsb)
+
+    assert bw(dt=9) == E_DTYPE
+    assert bw(rows=66) == E_DIVIS and bw(cols=36) == E_DIVIS
+    assert bw(cols=16392) == E_DIM and bw(index=4) == E_DIM and bw(p=1.0) == E_DIM and bw(eps=0.0) == E_DIM
+    assert bw(stride=64 * 32 - 8) == E_DIM
+    for kw in ("P", "h", "g", "dh", "dy", "dg", "db"):
+        assert bw(**{kw: None}) == E_NULL, kw
+    assert bw(ws=None) == E_WS and bw(wsb=need - 1) == E_WS
+    assert bw(dh=h) == E_ALIAS and bw(dy=dh) == E_ALIAS
+    assert bw(dg=dg + 2) == E_ALIGN
+    assert bw(dg=dg + 4, dbi=None, dres=None, keep=None, p=3.0) == E_HIP      # 4-byte fp32 arrays; optional inputs

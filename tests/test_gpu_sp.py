@@ -196,3 +196,77 @@ def test_sp_s1_full_size_sampled(tp):
         ref = oracle_stripe(sub, 1, 0)
         check(f"h[{index}]", h[torch.from_numpy(sel).cuda()], ref["h"], "bf16")
         check(f"x[{index}]", x[torch.from_numpy(sel).cuda()], ref["x"], "bf16")
+
+
+# ------------------------------------------------------------------ backward
+
+def sp_bwd_inputs(n, rows, cols, dtype, seed, p_drop=0.1):
+    rng = np.random.default_rng(seed)
+    k = rows // n
+    Gp = np.stack([tpsynth.normal(rng, (rows, cols), 1.0, dtype) for _ in range(n)])
+    h = tpsynth.normal(rng, (k, cols), 2.0, dtype)
+    dres = tpsynth.normal(rng, (k, cols), 1.0, dtype)
+    gamma = (1.0 + tpsynth.normal(rng, (cols,), 0.1, "f32")).astype(np.float32)
+    gamma = tpsynth.round_to_bf16(gamma) if dtype == "bf16" else gamma
+    keep = (rng.random((k, cols), dtype=np.float32) >= p_drop).astype(np.uint8)
+    return {"Gp": Gp, "h": h, "dres": dres, "gamma": gamma, "keep": keep, "p_drop": p_drop}
+
+
+def run_sp_bwd(tp, g, n, index, rows, cols, dtype, p_drop, with_keep=True, with_dres=True, with_bias=True):
+    k = rows // n
+    dt = tp.TP_DT_BF16 if dtype == "bf16" else tp.TP_DT_F32
+    ws = torch.empty(tp.tp_sp_ln_bwd_workspace_bytes(dt, n, rows, cols), dtype=torch.uint8, device="cuda")
+    dh = torch.empty((k, cols), dtype=_tdt(dtype), device="cuda")
+    dy = torch.empty((k, cols), dtype=_tdt(dtype), device="cuda")
+    dgam, dbet = torch.empty(cols, device="cuda"), torch.empty(cols, device="cuda")
+    dbias = torch.empty(cols, device="cuda") if with_bias else None
+    tp.tp_sp_ln_bwd_reduce_scatter(g["Gp"], g["h"], g["gamma"], dh, dy, dgam, dbet, ws, n, index, rows, cols,
+                                   keep=g["keep"] if with_keep else None, p_drop=p_drop,
+                                   dres=g["dres"] if with_dres else None, dbias=dbias)
+    torch.cuda.synchronize()
+    return {"dh": dh, "dy": dy, "dgamma": dgam, "dbeta": dbet, "dbias": dbias}
+
+
+@pytest.mark.parametrize("dtype,n,rows,cols,with_keep,with_dres", [
+    ("f32", 2, 64, 96, True, True),
+    ("bf16", 4, 40, 1000, True, True),
+    ("bf16", 3, 33, 24, False, False),
+    ("bf16", 8, 64, 8192, True, True),      # widest row of the two-chunk kernel
+    ("bf16", 8, 64, 8200, True, False),     # the four-chunk kernel
+    ("bf16", 2, 16, 16384, False, True),    # its widest row
+    ("f32", 2, 2048, 64, True, True),       # many rows per workgroup (partials summed over workgroups)
+])
+def test_sp_block_end_bwd_small(tp, dtype, n, rows, cols, with_keep, with_dres):
+    _say(f"sp block end bwd {dtype} n={n} rows={rows} cols={cols} keep={with_keep} dres={with_dres}")
+    inp = sp_bwd_inputs(n, rows, cols, dtype, seed=rows + cols)
+    g = {"Gp": dev(inp["Gp"], dtype), "h": None, "gamma": dev(inp["gamma"], dtype),
+         "keep": torch.from_numpy(inp["keep"]).cuda(), "dres": dev(inp["dres"], dtype)}
+    g["h"] = dev(inp["h"], dtype)
+    for index in sorted({0, n - 1}):
+        out = run_sp_bwd(tp, g, n, index, rows, cols, dtype, inp["p_drop"], with_keep, with_dres)
+        ref = O.sp_block_end_bwd(list(inp["Gp"]), n, index, inp["h"], inp["gamma"],
+                                 keep=inp["keep"] if with_keep else None, p_drop=inp["p_drop"] if with_keep else 0.0,
+                                 dres=inp["dres"] if with_dres else None)
+        for key in ("dh", "dy", "dgamma", "dbeta", "dbias"):
+            check(f"{key}[{index}]", out[key], ref[key], dtype)
+
+
+def test_sp_block_end_bwd_s1_full_size(tp):
+    """S1's shape (8192 tokens x 8192, 8 shards, 1024-token stripes), stripe 3
+    checked whole against the oracle, and bitwise determinism."""
+    wl = tpsynth.WORKLOADS["S1"]
+    _say(f"sp bwd S1 full size {wl.M}x{wl.d} n={wl.n_shards}")
+    n, rows, cols = wl.n_shards, wl.M, wl.d
+    k, index = rows // n, 3
+    inp = sp_bwd_inputs(n, rows, cols, "bf16", seed=98, p_drop=wl.p_drop)
+    g = {"Gp": dev(inp["Gp"], "bf16"), "h": dev(inp["h"], "bf16"), "gamma": dev(inp["gamma"], "bf16"),
+         "keep": torch.from_numpy(inp["keep"]).cuda(), "dres": dev(inp["dres"], "bf16")}
+    a = run_sp_bwd(tp, g, n, index, rows, cols, "bf16", inp["p_drop"])
+    b = run_sp_bwd(tp, g, n, index, rows, cols, "bf16", inp["p_drop"])
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+    stripe = [inp["Gp"][i, index * k:(index + 1) * k] for i in range(n)]
+    ref = O.sp_block_end_bwd(stripe, 1, 0, inp["h"], inp["gamma"], keep=inp["keep"], p_drop=inp["p_drop"],
+                             dres=inp["dres"])
+    for key in ("dh", "dy", "dgamma", "dbeta", "dbias"):
+        check(key, a[key], ref[key], "bf16")
