@@ -24,8 +24,11 @@
 // as [keys][d] rows read back transposed with ds_read_b64_tr_b16 in the key
 // order the P registers hold), no staging registers or register transposes;
 // at most 256 registers per wave, so two workgroups share a CU and one
-// wave's softmax overlaps another's matrix products.  The O^T rescale is
-// skipped when no running max of the wave changed.  d_head 64 uses the
+// wave's softmax overlaps another's matrix products.  Within a wave the
+// loop is software-pipelined: the next key tile's score MFMAs are issued
+// before this tile's softmax, so both kinds of work are in flight (K and V
+// have separate two-stage LDS rings for that).  The O^T rescale is skipped
+// when no running max of the wave changed.  d_head 64 uses the
 // register-staged variant.
 #include "epilogues.hpp"
 #include "gemm_dispatch.hpp"
@@ -201,12 +204,12 @@ flash_attn_fwd_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 // ----------------------------------------------------------------------------
 namespace attn128 {
 constexpr int D = 128, BQ = 128, BKV = 64, NT = 256, NW = 4;
-constexpr int K_BYTES = BKV * D * 2, V_BYTES = BKV * D * 2, STAGE = K_BYTES + V_BYTES;
+constexpr int K_BYTES = BKV * D * 2, V_BYTES = BKV * D * 2;
 constexpr int NK = K_BYTES / 1024 / NW, NV = V_BYTES / 1024 / NW;   // DMA instructions per wave
 
 // K tile: row r (key) of 256 bytes, logical 16-byte chunk c at c ^ (r % 16).
 // V tile: row r (key) of 256 bytes (128 d values), chunk c at c ^ 4 (r & 3).
-__device__ __forceinline__ void dma_kv(desc_t rk, desc_t rv, uint32_t lds, int wave, int lane) {
+__device__ __forceinline__ void dma_k(desc_t rk, uint32_t lds, int wave, int lane) {
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
     const int ins = wave * NK + j;
@@ -214,12 +217,15 @@ __device__ __forceinline__ void dma_kv(desc_t rk, desc_t rv, uint32_t lds, int w
     const int lc = (lane & 15) ^ (row & 15);
     dma16(rk, lds + ins * 1024, (uint32_t)row * (D * 2) + (uint32_t)lc * 16u);
   }
+}
+
+__device__ __forceinline__ void dma_v(desc_t rv, uint32_t lds, int wave, int lane) {
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int ins = wave * NV + j;
     const int row = ins * 4 + (lane >> 4);
     const int lc = (lane & 15) ^ (4 * (row & 3));
-    dma16(rv, lds + K_BYTES + ins * 1024, (uint32_t)row * (D * 2) + (uint32_t)lc * 16u);
+    dma16(rv, lds + ins * 1024, (uint32_t)row * (D * 2) + (uint32_t)lc * 16u);
   }
 }
 
@@ -250,18 +256,20 @@ __device__ __forceinline__ bf16x8 frag_v(const char* vt, int d0, int kvb, int la
 }
 }  // namespace attn128
 
+// d_head 128.  Software-pipelined: a wave computes the next key tile's scores
+// S^T_{t+1} = K_{t+1} Q^T (MFMA) while it turns tile t's scores into
+// probabilities (VALU) and multiplies them with V_t, so the matrix cores and
+// the vector units work on independent data.  K and V have separate
+// two-stage rings: at the top of iteration t (one barrier) K_{t+1} and V_t
+// have landed, and the DMAs of K_{t+2} and V_{t+1} go into the stages that
+// held K_t (consumed at iteration t-1) and V_{t-1}.
 __global__ void __launch_bounds__(256, 2)
 flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                           const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ L,
-                           int nb, int hl, int group, int s, int causal, float scale_log2) {
+                              const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ L,
+                              int nb, int hl, int group, int s, int causal, float scale_log2) {
   using namespace attn128;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * K_BYTES + 2 * V_BYTES];
 
-  // Causal work grows with the query tile.  With an even number of query
-  // tiles, blocks [0, G/2) take the heavy half of the tiles, heaviest first,
-  // and block i + G/2 the complement of block i's tile, so the two
-  // workgroups that usually share a CU (blocks i and i + G/2 when every
-  // block is resident) sum to the same work; otherwise heaviest first.
   const int nqt = (s + BQ - 1) / BQ;
   const int nbh = nb * hl;
   const int half = (int)(gridDim.x / 2);
@@ -275,24 +283,26 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, g = lane >> 5;
   const int64_t head = (int64_t)bh * s * D;
-  // grouped-query attention: query head h reads key/value head h / group
   const int64_t kvhead = ((int64_t)bi * (hl / group) + h / group) * s * D;
   const bf16* Kh = K + kvhead;
   const bf16* Vh = V + kvhead;
   const int q0 = qt * BQ;
-  const int qw = q0 + wave * 32;    // first query of this wave
-  const int qme = qw + lq;          // this lane's query
+  const int qw = q0 + wave * 32;
+  const int qme = qw + lq;
   const uint32_t lds0 = lds_addr(smem);
+  const uint32_t kring = lds0, vring = lds0 + 2 * K_BYTES;
 
   const int kv_end = causal ? min(s, q0 + BQ) : s;
   const int ntiles = (kv_end + BKV - 1) / BKV;
-  auto issue = [&](int t) {
+  // last key tile this wave needs (every tile for non-causal attention)
+  const int wlast = causal ? min(ntiles - 1, (qw + 31) / BKV) : ntiles - 1;
+  auto desc_of = [&](const bf16* base, int t) {
     const int64_t kv0 = (int64_t)t * BKV;
     const int64_t rb = (int64_t)(s - kv0) * D * 2;
-    const uint32_t rem = rb < 0x7FFFFFFF ? (uint32_t)rb : 0x7FFFFFFFu;
-    dma_kv(make_desc(Kh + kv0 * D, rem), make_desc(Vh + kv0 * D, rem), lds0 + (t & 1) * STAGE, wave, lane);
+    return make_desc(base + kv0 * D, rb < 0x7FFFFFFF ? (uint32_t)rb : 0x7FFFFFFFu);
   };
-  issue(0);
+  auto issue_k = [&](int t) { dma_k(desc_of(Kh, t), kring + (t & 1) * K_BYTES, wave, lane); };
+  auto issue_v = [&](int t) { dma_v(desc_of(Vh, t), vring + (t & 1) * V_BYTES, wave, lane); };
 
   bf16x8 qf[D / 16];
   {
@@ -301,32 +311,41 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
     for (int kk = 0; kk < D / 16; ++kk)
       qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(((int64_t)qme * D + kk * 16 + g * 8) * 2)));
   }
+  issue_k(0);
+  issue_v(0);
+  if (ntiles > 1) issue_k(1);
 
-  f32x16 acc_o[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
-  float m_run = -1e30f, l_run = 0.f;   // running max in log2 units, running sum
-
-  for (int t = 0; t < ntiles; ++t) {
-    // Tile t landed for every wave, and every wave is done with tile t-1,
-    // whose stage takes tile t+1.
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (t + 1 < ntiles) issue(t + 1);
-
-    const int kv0 = t * BKV;
-    if (causal && kv0 > qw + 31) continue;
-    const char* Ks = smem + (t & 1) * STAGE;
-    const char* Vs = Ks + K_BYTES;
-    // Two independent accumulator chains (key blocks kb = 0, 1), interleaved.
-    f32x16 sc[2] = {f32x16{}, f32x16{}};
+  auto scores = [&](int t, f32x16 (&sc)[2]) {
+    const char* Ks = smem + (t & 1) * K_BYTES;
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_k(Ks, kb * 32, kk, lane), qf[kk], sc[kb], 0, 0, 0);
-    // sc[kb][r] is the raw score of query qme against key kv0 + kb*32 + 8*(r/4) + 4*g + r%4
+  };
+
+  f32x16 acc_o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
+  float m_run = -1e30f, l_run = 0.f;
+
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  f32x16 sc[2];
+  scores(0, sc);
+
+  for (int t = 0; t < ntiles; ++t) {
+    // K_{t+1} and V_t have landed for every wave; every wave is done with K_t and V_{t-1}.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 1 < ntiles) issue_v(t + 1);
+    if (t + 2 < ntiles) issue_k(t + 2);
+    if (t > wlast) continue;                        // uniform per wave
+    f32x16 sn[2];
+    if (t + 1 <= wlast) scores(t + 1, sn);          // next tile's scores, independent of this softmax
+
+    const int kv0 = t * BKV;
     if ((causal && kv0 + BKV - 1 > qw) || (kv0 + BKV > s)) {
-      // keys past this lane's query (causal) or past the sequence are masked
       const int lim = (causal ? min(qme, s - 1) : s - 1) - (kv0 + 4 * g);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -341,7 +360,7 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx * scale_log2);
-    // Rescale O^T and the sum only when a running max of the wave moved.
+    // rescale O^T and the sum only when a running max of the wave moved
     if (__builtin_amdgcn_read_exec() & __ballot(m_new > m_run)) {
       const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= corr;
@@ -350,17 +369,6 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
       m_run = m_new;
     }
     float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], scale_log2, -m_run));
-        sc[kb][r] = pv;
-        rs += pv;
-      }
-    rs += __shfl_xor(rs, 32);
-    l_run += rs;
-
     bf16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -368,11 +376,18 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
       for (int hh = 0; hh < 2; ++hh) {
         u32x4 wv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wv[e] = pack_bf16x2(sc[kb][8 * hh + 2 * e], sc[kb][8 * hh + 2 * e + 1]);
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hh + 2 * e], scale_log2, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hh + 2 * e + 1], scale_log2, -m_run));
+          rs += p0 + p1;
+          wv[e] = pack_bf16x2(p0, p1);
+        }
         pf[kb][hh] = __builtin_bit_cast(bf16x8, wv);
       }
-    // O^T[d][q] += V^T[d][kv] P^T[kv][q], keys kv0 + kb*32 + 16*hh + {4g..4g+3, 8+4g..8+4g+3};
-    // the four d blocks are independent accumulator chains, interleaved.
+    rs += __shfl_xor(rs, 32);
+    l_run += rs;
+
+    const char* Vs = smem + 2 * K_BYTES + (t & 1) * V_BYTES;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -381,11 +396,14 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
         for (int db = 0; db < D / 32; ++db)
           acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_v(Vs, db * 32, kb * 32 + hh * 16, lane),
                                                               pf[kb][hh], acc_o[db], 0, 0, 0);
+    if (t + 1 <= wlast) {
+      sc[0] = sn[0];
+      sc[1] = sn[1];
+    }
   }
 
   if (qme < s) {
     const float inv = 1.0f / l_run;
-    // log-sum-exp of the query's scaled scores, natural log (m_run is in log2 units)
     if (L && g == 0) L[(int64_t)bh * s + qme] = (m_run + __log2f(l_run)) * 0.69314718055994531f;
     bf16* orow = O + ((int64_t)bi * s + qme) * ((int64_t)hl * D) + (int64_t)h * D;
 #pragma unroll
