@@ -54,7 +54,7 @@ __all__ = [
     "shard_reduce", "shard_range",
     "stripe_rows", "reduce_scatter", "all_gather", "layer_norm", "sp_block_end", "layer_norm_bwd",
     "sp_block_end_bwd",
-    "vocab_embed_shard", "vocab_embed", "vocab_ce_shard", "vocab_ce_combine", "vocab_ce_fwd",
+    "vocab_embed_shard", "vocab_embed", "vocab_embed_shard_bwd", "vocab_ce_shard", "vocab_ce_combine", "vocab_ce_fwd",
     "vocab_ce_shard_bwd",
 ]
 
@@ -524,6 +524,21 @@ def vocab_embed(ids, E_shards: Sequence) -> np.ndarray:
         parts.append(vocab_embed_shard(ids, E, start))
         start += np.asarray(E).shape[0]
     return shard_reduce(parts)
+
+
+def vocab_embed_shard_bwd(ids, dY, vocab_local: int, vocab_start: int) -> np.ndarray:
+    """Gradient of the shard's table rows: the forward's all-reduce has an
+    identity backward, so every shard receives the whole output gradient dY
+    and row v of dE_local is the sum of dY over the tokens whose id is
+    vocab_start + v (ids outside the shard contribute nothing).  Summed in
+    token order."""
+    ids = np.asarray(ids, dtype=np.int64)
+    dY = _f64(dY)
+    dE = np.zeros((vocab_local, dY.shape[1]))
+    for t, v in enumerate(ids):
+        if vocab_start <= v < vocab_start + vocab_local:
+            dE[v - vocab_start] += dY[t]
+    return dE
 
 
 def vocab_ce_shard(X, E_local, targets, vocab_start: int) -> Dict[str, np.ndarray]:

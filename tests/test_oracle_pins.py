@@ -684,6 +684,29 @@ def test_vocab_embed_shard_brute_force_and_out_of_range_ids():
     np.testing.assert_array_equal(full[-3:], np.zeros((3, E.shape[1])))
 
 
+def test_vocab_embed_bwd_one_hot_product_and_finite_differences():
+    """dE_local = onehot(ids - start)^T dY over the shard's rows; the gradient
+    of <dY, Y_i> with respect to the shard's table; the shards' gradients
+    stacked are the whole table's."""
+    rng, E, ids = _vocab_case(66, T=9, d=4, V=12)
+    ids = np.concatenate([ids, [5, 5, -1, 12]])         # a repeated id and two in no shard
+    dY = rng.standard_normal((len(ids), 4))
+    n, V = 3, 12
+    parts = [O.vocab_embed_shard_bwd(ids, dY, V // n, i * V // n) for i in range(n)]
+    onehot = np.zeros((len(ids), V))
+    ok = (ids >= 0) & (ids < V)
+    onehot[np.nonzero(ok)[0], ids[ok]] = 1.0
+    np.testing.assert_allclose(np.concatenate(parts), onehot.T @ dY, rtol=1e-14, atol=1e-14)
+    eps = 1e-6
+    for (i, r, c) in [(0, 0, 1), (1, 1, 3), (2, 3, 0)]:
+        Es = [E[k * V // n:(k + 1) * V // n].copy() for k in range(n)]
+        Ep, Em = Es[i].copy(), Es[i].copy()
+        Ep[r, c] += eps
+        Em[r, c] -= eps
+        f = lambda El: float((O.vocab_embed_shard(ids, El, i * V // n) * dY).sum())
+        assert parts[i][r, c] == pytest.approx((f(Ep) - f(Em)) / (2 * eps), rel=1e-7, abs=1e-9)
+
+
 def _ce_brute(X, E, targets):
     out = []
     for t in range(X.shape[0]):
