@@ -545,14 +545,18 @@ def run_e1(tp, torch, steps, warmup):
     dE = torch.empty((vl, d), dtype=torch.float32, device="cuda")
     ws = torch.empty(tp.tp_vocab_ce_bwd_workspace_bytes(tp.TP_DT_BF16, T, d, vl), dtype=torch.uint8, device="cuda")
 
+    dEmb = torch.randn((T, d), device="cuda").to(bf)          # gradient of the embedding output
+    dE_in = torch.empty((vl, d), dtype=torch.float32, device="cuda")
+
     def step():
         tp.tp_vocab_embed_fwd(ids, E0, parts[0], 0)
         tp.tp_shard_reduce(parts, emb, n, T * d)
         tp.tp_vocab_ce_fwd(X, E0, tg, logits, stats[0], 0)
         tp.tp_vocab_ce_combine(stats, loss, lse)
         tp.tp_vocab_ce_bwd(X, E0, tg, logits, lse, dloss, dX, dE, ws, 0)
+        tp.tp_vocab_embed_bwd(ids, dEmb, dE_in, 0)
 
-    ms, _, per = timed(tp, torch, step, steps, warmup, 12)
+    ms, _, per = timed(tp, torch, step, steps, warmup, 13)
     gms = graph_timed(torch, step, steps)
     flops = 3 * gemm_flops(T, vl, d)
     avg = lambda lab: (sum(per[lab]) / len(per[lab])) if per.get(lab) else None
@@ -561,9 +565,13 @@ def run_e1(tp, torch, steps, warmup):
     # gather: ids + this shard's rows of the tokens it holds + the full partial written
     own = int(((ids >= 0) & (ids < vl)).sum().item())
     emb_bytes = T * 8 + own * d * 2 + T * d * 2
+    eb_ms = avg("vocab.embed_bwd")
+    eb_bytes = T * 8 + T * d * 2 + vl * d * 4 + (vl // 8) * T * 8   # ids, dY, dE, and the ids each workgroup scans
     return {"workload": "E1 vocabulary-parallel embeddings, GPT-2-medium width: 8192 tokens, d 1024, "
                         "vocabulary 51200 over TP 8 (6400 rows here); input embedding + shard-reduce, "
-                        "output embedding + cross-entropy fwd, combine, bwd",
+                        "output embedding + cross-entropy fwd, combine, bwd; input embedding bwd",
+            "embed_bwd": {"bytes": eb_bytes, "ms": round(eb_ms, 4) if eb_ms else None,
+                          "GBps": round(eb_bytes / eb_ms / 1e6, 1) if eb_ms else None},
             "ms_per_step": round(ms, 4), "gemm_flop_per_step": flops,
             "tflops": round(flops / ms / 1e9, 1),
             "graph_ms_per_step": round(gms, 4), "graph_tflops": round(flops / gms / 1e9, 1),

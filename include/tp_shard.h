@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 6
+#define TP_ABI_VERSION 7
 
 typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype_t;
 
@@ -311,6 +311,19 @@ int tp_sp_all_gather(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t stri
 int tp_vocab_embed_fwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d,
                        int64_t vocab_local, int64_t vocab_start, const int64_t* ids,
                        const void* E_local, void* Y);
+
+/* ---------------------------------------------------------------------------
+ * tp_vocab_embed_bwd — backward of tp_vocab_embed_fwd: the table gradient of
+ * the shard's rows.  The forward's all-reduce has an identity backward, so
+ * the shard receives the whole output gradient dY [n_tokens x d] (dtype dt):
+ *   dE_local[v, :] = sum over tokens t with ids[t] == vocab_start + v of dY[t, :]
+ * summed in token order (bitwise deterministic; no atomics); rows no token
+ * hits are zero.  dE_local: fp32 [vocab_local x d], overwritten.  Sizes as
+ * tp_vocab_embed_fwd.
+ * ------------------------------------------------------------------------- */
+int tp_vocab_embed_bwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d,
+                       int64_t vocab_local, int64_t vocab_start, const int64_t* ids,
+                       const void* dY, float* dE_local);
 
 /* ---------------------------------------------------------------------------
  * tp_vocab_ce_fwd — one shard of the output embedding fused with the

@@ -20,7 +20,7 @@ __all__ = [
     "tp_attn_gqa_shard_bwd", "tp_attn_gqa_shard_bwd_workspace_bytes",
     "tp_shard_reduce", "tp_shard_range", "tp_sp_reduce_scatter_ln", "tp_sp_all_gather", "tp_sp_ln_bwd_reduce_scatter",
     "tp_sp_ln_bwd_workspace_bytes",
-    "tp_vocab_embed_fwd", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
+    "tp_vocab_embed_fwd", "tp_vocab_embed_bwd", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
     "tp_vocab_ce_bwd_workspace_bytes",
     "tp_abi_version", "EXPORTS",
 ]
@@ -66,6 +66,7 @@ EXPORTS = {
                                            ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _sz]),
     "tp_sp_ln_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
     "tp_vocab_embed_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p]),
+    "tp_vocab_embed_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p]),
     "tp_vocab_ce_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     "tp_vocab_ce_combine": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p]),
     "tp_vocab_ce_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64] + [_p] * 6 + [_p, _p, _p, _sz]),
@@ -296,6 +297,13 @@ def tp_vocab_embed_fwd(ids, E_local, Y, vocab_start: int, stream=None) -> None:
     vl, d = E_local.shape
     _check(lib().tp_vocab_embed_fwd(_stream(stream), _dt(E_local), ids.numel(), d, vl, vocab_start, _ids(ids),
                                     _ptr(E_local), _ptr(Y)))
+
+
+def tp_vocab_embed_bwd(ids, dY, dE_local, vocab_start: int, stream=None) -> None:
+    """dE_local[v] = sum of dY over the tokens whose id is vocab_start + v."""
+    vl, d = dE_local.shape
+    _check(lib().tp_vocab_embed_bwd(_stream(stream), _dt(dY), ids.numel(), d, vl, vocab_start, _ids(ids), _ptr(dY),
+                                    _ptr(dE_local)))
 
 
 def tp_vocab_ce_fwd(X, E_local, targets, logits, stats, vocab_start: int, stream=None) -> None:

@@ -62,6 +62,8 @@ hipError_t launch_sp_all_gather(hipStream_t st, int dt, int n, int64_t stripe_ro
 
 hipError_t launch_vocab_embed_fwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
                                   int64_t vstart, const int64_t* ids, const void* E, void* Y);
+hipError_t launch_vocab_embed_bwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
+                                  int64_t vstart, const int64_t* ids, const void* dY, float* dE);
 hipError_t launch_vocab_ce_fwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
                                int64_t vstart, const void* X, const void* E, const int64_t* targets,
                                void* logits, float* stats);

@@ -554,6 +554,17 @@ int tp_vocab_embed_fwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d,
                     "tp_vocab_embed_fwd");
 }
 
+int tp_vocab_embed_bwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d, int64_t vocab_local,
+                       int64_t vocab_start, const int64_t* ids, const void* dY, float* dE_local) {
+  TP_CHECK(vocab_common(dt, n_tokens, d, vocab_local, vocab_start));
+  const size_t e = esize(dt);
+  TP_CHECK(check_buffers({{"ids", ids, (size_t)n_tokens * 8, 8}, {"dY", dY, (size_t)(n_tokens * d) * e}},
+                         {{"dE_local", dE_local, (size_t)(vocab_local * d) * 4}}, {"ids", "dY", "dE_local"}));
+  return hip_status(tpk::launch_vocab_embed_bwd(static_cast<hipStream_t>(stream), dt, n_tokens, d, vocab_local,
+                                                vocab_start, ids, dY, dE_local),
+                    "tp_vocab_embed_bwd");
+}
+
 int tp_vocab_ce_fwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d, int64_t vocab_local,
                     int64_t vocab_start, const void* X, const void* E_local, const int64_t* targets,
                     void* logits, float* stats) {

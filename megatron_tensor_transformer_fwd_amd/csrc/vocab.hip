@@ -41,6 +41,150 @@ vocab_embed_kernel(const int64_t* __restrict__ ids, int64_t n_tokens, int64_t ro
   }
 }
 
+// ---------------------------------------------------------- input embedding backward
+
+// dE_local[v, :] = sum of dY[t, :] over the tokens t whose id is vstart + v.
+// A workgroup owns EB_R table rows, so no two workgroups write the same row
+// and no atomics are needed.  It scans the ids in windows of EB_W tokens and
+// compacts the window's hits on its rows into LDS in token order (a
+// block-wide prefix sum of per-thread hit counts).  Threads own 8 columns
+// each; when a row has fewer 8-column chunks than the workgroup has
+// threads, HL groups of threads ("hit lanes") take every HL-th hit, each
+// keeping per-row register accumulators and issuing four hits' loads at a
+// time.  The lanes' sums are added in lane order at the end, so the
+// summation order is fixed (bitwise deterministic).  Rows wider than the
+// workgroup's columns take several column passes over the same windows.
+constexpr int EB_R = 8, EB_NT = 256, EB_W = 4096;
+
+template <class T>
+__global__ void __launch_bounds__(EB_NT)
+vocab_embed_bwd_kernel(const int64_t* __restrict__ ids, int64_t n_tokens, const T* __restrict__ dY, int64_t d,
+                       int64_t vstart, int64_t vlocal, float* __restrict__ dE, int HL) {
+  __shared__ int hits[EB_W];
+  __shared__ int wave_base[EB_NT / 64 + 1];
+  __shared__ float red[EB_NT * 8];
+  constexpr int PER = EB_W / EB_NT;                // tokens per thread per window
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t v0 = vstart + (int64_t)blockIdx.x * EB_R;
+  const int rows = (int)std::min<int64_t>(EB_R, vlocal - (int64_t)blockIdx.x * EB_R);
+  const int cols_t = EB_NT / HL;                    // threads per hit lane
+  const int hl = tid / cols_t, ct = tid % cols_t;
+
+  for (int64_t cp = 0; cp < d; cp += (int64_t)cols_t * 8) {
+    const int64_t c = cp + (int64_t)ct * 8;
+    const bool mine = c < d;
+    float acc[EB_R][8];
+#pragma unroll
+    for (int r = 0; r < EB_R; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+
+    for (int64_t w0 = 0; w0 < n_tokens; w0 += EB_W) {
+      // ordered compaction of this window's hits: entry = token * EB_R + row
+      const int64_t t0 = w0 + (int64_t)tid * PER;
+      int cnt = 0;
+      uint32_t rowbits[PER / 8];                   // 4 bits per token: row, 0xF = no hit
+#pragma unroll
+      for (int j = 0; j < PER / 8; ++j) rowbits[j] = 0xFFFFFFFFu;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int64_t t = t0 + j;
+        if (t < n_tokens) {
+          const int64_t r = ids[t] - v0;
+          if (r >= 0 && r < rows) {
+            rowbits[j >> 3] = (rowbits[j >> 3] & ~(0xFu << (4 * (j & 7)))) | ((uint32_t)r << (4 * (j & 7)));
+            ++cnt;
+          }
+        }
+      }
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      __syncthreads();                              // hits[] and wave_base[] free from the previous window
+      if (lane == 63) wave_base[wv + 1] = incl;
+      if (tid == 0) wave_base[0] = 0;
+      __syncthreads();
+      if (tid == 0)
+        for (int k = 1; k <= EB_NT / 64; ++k) wave_base[k] += wave_base[k - 1];
+      __syncthreads();
+      int pos = wave_base[wv] + incl - cnt;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const uint32_t r = (rowbits[j >> 3] >> (4 * (j & 7))) & 0xFu;
+        if (r != 0xFu) hits[pos++] = (int)((t0 + j - w0) * EB_R + r);
+      }
+      const int nh = wave_base[EB_NT / 64];
+      __syncthreads();
+      if (mine) {
+        int k = hl;
+        for (; k + 3 * HL < nh; k += 4 * HL) {      // four hits' loads in flight
+          float v[4][8];
+          int rr4[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int e = hits[k + u * HL];
+            rr4[u] = e % EB_R;
+            Vec8<T>::template load<kNtIn>(dY + (w0 + e / EB_R) * d + c, v[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int rr = 0; rr < EB_R; ++rr)
+              if (rr == rr4[u]) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[rr][q] += v[u][q];
+              }
+        }
+        for (; k < nh; k += HL) {
+          const int e = hits[k];
+          const int r = e % EB_R;
+          float v[8];
+          Vec8<T>::template load<kNtIn>(dY + (w0 + e / EB_R) * d + c, v);
+#pragma unroll
+          for (int rr = 0; rr < EB_R; ++rr)
+            if (rr == r) {
+#pragma unroll
+              for (int q = 0; q < 8; ++q) acc[rr][q] += v[q];
+            }
+        }
+      }
+    }
+    // the hit lanes' sums, added in lane order
+#pragma unroll
+    for (int r = 0; r < EB_R; ++r) {
+      if (r >= rows) break;                         // uniform
+      if (HL > 1) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 8; ++q) red[tid * 8 + q] = acc[r][q];
+        __syncthreads();
+        if (hl == 0) {
+          for (int l = 1; l < HL; ++l)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[r][q] += red[(l * cols_t + ct) * 8 + q];
+        }
+      }
+      if (hl == 0 && mine) Vec8<float>::template store<kNtOut>(dE + ((int64_t)blockIdx.x * EB_R + r) * d + c, acc[r]);
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_vocab_embed_bwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
+                                  int64_t vstart, const int64_t* ids, const void* dY, float* dE) {
+  const dim3 grid((unsigned)cdiv(vlocal, EB_R));
+  const int64_t chunks = d / 8;
+  const int HL = chunks >= EB_NT ? 1 : (chunks >= EB_NT / 2 ? 2 : 4);   // hit lanes
+  if (dt == DT_BF16)
+    return launch("vocab.embed_bwd", vocab_embed_bwd_kernel<bf16>, grid, dim3(EB_NT), st, ids, n_tokens,
+                  static_cast<const bf16*>(dY), d, vstart, vlocal, dE, HL);
+  return launch("vocab.embed_bwd", vocab_embed_bwd_kernel<float>, grid, dim3(EB_NT), st, ids, n_tokens,
+                static_cast<const float*>(dY), d, vstart, vlocal, dE, HL);
+}
+
 // ------------------------------------------------------ cross-entropy rows
 
 // (m, s) pairs with s = sum exp(z - m), merged without overflow.

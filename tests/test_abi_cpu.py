@@ -33,7 +33,7 @@ def test_header_and_binding_agree_and_library_exports_all():
 
 
 def test_version_and_strerror():
-    assert tp.tp_abi_version() == 6
+    assert tp.tp_abi_version() == 7
     L = tp.lib()
     for code in (OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP):
         assert L.tp_strerror(code) and L.tp_strerror(code) != b"unknown status"
@@ -295,6 +295,12 @@ def test_vocab_validation():
     assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, ids, E, E + 64) == E_ALIAS
     assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, (1 << 21) + 8, 0, ids, E, Y) == E_DIM
     assert L.tp_vocab_embed_fwd(None, BF16, (1 << 24) + 1, 64, 128, 0, ids, E, Y) == E_DIM
+    # input embedding backward
+    assert L.tp_vocab_embed_bwd(None, BF16, 16, 64, 128, 0, ids, Y, E) == E_HIP
+    assert L.tp_vocab_embed_bwd(None, BF16, 16, 64, 100, 0, ids, Y, E) == E_DIVIS
+    assert L.tp_vocab_embed_bwd(None, BF16, 16, 64, 128, 0, None, Y, E) == E_NULL
+    assert L.tp_vocab_embed_bwd(None, BF16, 16, 64, 128, 0, ids, Y, Y + 64) == E_ALIAS
+    assert L.tp_vocab_embed_bwd(None, BF16, 16, 64, 128, 0, ids + 4, Y, E) == E_ALIGN
     # fused output embedding + cross-entropy
     assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, lg, None) == E_NULL
     assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, None, lg, st) == E_NULL

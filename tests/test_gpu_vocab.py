@@ -181,3 +181,29 @@ def test_vocab_e1_full_size_sampled(tp):
     for i in (0, 3, n - 1):
         bw = O.vocab_ce_shard_bwd(inp["X"][sel], Es[i], inp["targets"][sel], i * vl, sub["lse"], masked[sel])
         check(f"dE[{i}]", out["dE"][i], bw["dE"], "bf16")
+
+@pytest.mark.parametrize("dtype,T,d,V,n", [
+    ("f32", 37, 24, 64, 2),
+    ("bf16", 100, 1000, 96, 3),
+    ("bf16", 5000, 2056, 64, 2),       # two column passes; many hits per row
+    ("bf16", 9000, 64, 40, 5),         # three id windows; 8-row shards (one workgroup each)
+    ("bf16", 8192, 1024, 51200, 8),    # E1
+])
+def test_vocab_embed_bwd(tp, dtype, T, d, V, n):
+    _say(f"vocab embed bwd {dtype} T={T} d={d} V={V} n={n}")
+    rng = np.random.default_rng(73)
+    ids = tpsynth.zipf_token_ids(rng, T, V)
+    ids[: 3] = [V - 1, -1, V]                           # the last row and two ids in no shard
+    dY = tpsynth.normal(rng, (T, d), 1.0, dtype)
+    g_ids, g_dY = dev_i64(ids), dev(dY, dtype)
+    vl = V // n
+    for i in range(n):
+        dE = torch.empty((vl, d), device="cuda")
+        tp.tp_vocab_embed_bwd(g_ids, g_dY, dE, i * vl)
+        torch.cuda.synchronize()
+        check(f"dE[{i}]", dE, O.vocab_embed_shard_bwd(ids, dY, vl, i * vl), dtype)
+        if i == 0:
+            dE2 = torch.empty_like(dE)
+            tp.tp_vocab_embed_bwd(g_ids, g_dY, dE2, 0)
+            torch.cuda.synchronize()
+            assert torch.equal(dE, dE2), "embedding backward is not bitwise deterministic"
