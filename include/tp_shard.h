@@ -166,7 +166,10 @@ int tp_attn_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t
  * tp_attn_shard_fwd, except that Wk and Wv are [d x h_kv_local*d_head], K and
  * V are [b, h_kv_local, s, d_head], and local query head j attends with
  * key/value head j / (h_local / h_kv_local).  h_kv_local must divide h_local
- * (TP_E_DIVIS); h_kv_local = h_local is tp_attn_shard_fwd.
+ * (TP_E_DIVIS); h_kv_local = h_local is tp_attn_shard_fwd.  When the K/V
+ * projection is narrow and d long, its K split keeps fp32 partials in Z's
+ * memory before Z itself is written (Z must be device memory of its full
+ * size, as for every output).
  * ------------------------------------------------------------------------- */
 int tp_attn_gqa_shard_fwd(void* stream, tp_dtype_t dt, int64_t b, int64_t s, int64_t d,
                           int64_t h_local, int64_t h_kv_local, int64_t d_head, int causal, float scale,

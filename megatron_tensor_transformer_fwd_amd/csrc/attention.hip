@@ -417,6 +417,45 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   }
 }
 
+// fp32 split-K partials of a z-batched product: split s, batch z at
+// C + s * split_stride + z * z_stride + m * ldc + n.
+struct EpiSplitZ {
+  static constexpr int NOUT = 1;
+  template <int O> using OutT = float;
+  float* C;
+  int64_t ldc, split_stride, z_stride;
+  template <int O> __device__ __forceinline__ bool has_out() const { return true; }
+  template <int O> __device__ __forceinline__ float* out_ptr(int64_t m, int64_t n, int split, int z) const {
+    return C + split * split_stride + z * z_stride + m * ldc + n;
+  }
+  template <int O> __device__ __forceinline__ f32x4 value(int64_t, int64_t, f32x4 v) const { return v; }
+};
+
+// Sum of the split partials (in split order) of the K (z = 0) and V (z = 1)
+// projections, scattered to head-major [b, h_kv, s, d_head] bf16.  One
+// thread per 8 outputs.
+__global__ void __launch_bounds__(256)
+attn_kv_split_sum_kernel(const float* __restrict__ P, int splits, int64_t M, int64_t nkv, int s, int h_kv,
+                         int d_head, bf16* __restrict__ Kout, bf16* __restrict__ Vout) {
+  const int64_t per_z = M * nkv / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * per_z) return;
+  const int z = (int)(i / per_z);
+  const int64_t e = (i % per_z) * 8;
+  const int64_t m = e / nkv, n = e % nkv;
+  const float* src = P + z * M * nkv + e;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < splits; ++k) {
+    float t[8];
+    Vec8<float>::load<kNtIn>(src + (int64_t)k * 2 * M * nkv, t);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += t[q];
+  }
+  const int64_t bi = m / s, t = m % s, j = n / d_head, c = n % d_head;
+  bf16* out = (z == 0 ? Kout : Vout) + ((bi * h_kv + j) * s + t) * d_head + c;
+  Vec8<bf16>::store(out, acc);
+}
+
 hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv,
                            int64_t d_head, int causal, float scale,
                            const void* X, const void* Wq, const void* Wk, const void* Wv,
@@ -437,10 +476,27 @@ hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
     GemmParams pk = make_params(M, Nkv, make_seg(X, d, M * d, Wk, Nkv, d * Nkv, d));
     pk.Bz[0] = static_cast<const bf16*>(Wk);
     pk.Bz[1] = static_cast<const bf16*>(Wv);
-    EpiHeadScatter<bf16> ek{{static_cast<bf16*>(K), static_cast<bf16*>(V), nullptr}, (int)s, (int)h_kv,
-                            (int)d_head};
-    TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wkv_scatter", pk, ek,
-                                              plan_gemm(M, 2 * Nkv, d, false, false), 2)));
+    // K and V are narrow (h_kv * d_head columns) and K = d is long: split K when
+    // that fills the CUs, with fp32 partials in Z's memory (Z is written only by
+    // the output projection at the end, and holds M * d bf16).
+    const int64_t tiles = cdiv(M, 256) * cdiv(Nkv, 128) * 2;
+    int split = 1;
+    while (split < 16 && tiles * split * 2 <= 256 && d / (split * 2) >= 1024) split *= 2;
+    if ((int64_t)split * 2 * M * Nkv * 4 > M * d * 2) split = 1;
+    if (split > 1) {
+      float* part = static_cast<float*>(Z);
+      EpiSplitZ e{part, Nkv, 2 * M * Nkv, M * Nkv};
+      TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wkv_split", pk, e, GemmPlan{CFG_M, split}, 2)));
+      const int64_t n = 2 * M * Nkv / 8;
+      TPK_TRY(launch("attn.kv_split_sum", attn_kv_split_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st,
+                     (const float*)part, split, M, Nkv, (int)s, (int)h_kv, (int)d_head, static_cast<bf16*>(K),
+                     static_cast<bf16*>(V)));
+    } else {
+      EpiHeadScatter<bf16> ek{{static_cast<bf16*>(K), static_cast<bf16*>(V), nullptr}, (int)s, (int)h_kv,
+                              (int)d_head};
+      TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wkv_scatter", pk, ek,
+                                                plan_gemm(M, 2 * Nkv, d, false, false), 2)));
+    }
   }
   {
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d_head);

@@ -423,10 +423,13 @@ def run_gqa(tp, inp, b, s, h_l, h_kv, dh, causal=True):
     (1, 257, 96, 4, 1, 128, True),
     (2, 130, 64, 6, 3, 64, False),
     (1, 64, 72, 16, 1, 128, True),    # the G1 grouping, 16 query heads on one K/V head
+    (1, 256, 2048, 4, 1, 128, True),  # long d: the K/V projection splits K (2 ways) through Z's memory
+    (2, 128, 4096, 4, 2, 128, True),  # 4-way split, two K/V heads scattered
 ])
 def test_gqa_small_shapes(tp, b, s, d, h_l, h_kv, dh, causal):
     _say(f"gqa b={b} s={s} d={d} h_l={h_l} h_kv={h_kv} dh={dh} causal={causal}")
-    inp = tpsynth.random_gqa(b, s, d, h_l, h_kv, dh, "bf16", seed=s + h_l, w_std=0.1)
+    # weights ~ N(0, min(0.1, 1/sqrt(d))^2): scores of order one at every width
+    inp = tpsynth.random_gqa(b, s, d, h_l, h_kv, dh, "bf16", seed=s + h_l, w_std=min(0.1, d ** -0.5))
     out = run_gqa(tp, inp, b, s, h_l, h_kv, dh, causal)
     ref = O.attn_gqa_shard_fwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], b, s, h_l, h_kv, dh, causal)
     for k in ("Q", "K", "V", "O", "Z"):
