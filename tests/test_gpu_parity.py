@@ -164,6 +164,26 @@ def test_mlp_ragged_shapes(tp, dtype, M, d, f):
         check(k, out[k], refb[k], dtype)
 
 
+def test_mlp_row_pitch_limit(tp):
+    """d at the ABI's row-pitch limit (2^21 elements): every operand tile spans
+    256 rows of 4 MiB, the widest the kernels address with 32-bit offsets
+    from a tile's first row.  M 64, f 64, forward and backward, every tensor."""
+    M, d, f = 64, 1 << 21, 64
+    _say(f"mlp row-pitch limit bf16 M={M} d={d} f={f}")
+    rng = np.random.default_rng(99)
+    X = tpsynth.normal(rng, (M, d), 1.0, "bf16")
+    W1 = tpsynth.normal(rng, (d, f), d ** -0.5, "bf16")
+    W2 = tpsynth.normal(rng, (f, d), 0.1, "bf16")
+    dY = tpsynth.normal(rng, (M, d), 1.0, "bf16")
+    out = run_mlp_shard(tp, dev(X, "bf16"), dev(W1, "bf16"), dev(W2, "bf16"), dev(dY, "bf16"), "bf16")
+    ref = O.mlp_shard_fwd(X, W1, W2)
+    for k in ("A", "H", "Z"):
+        check(k, out[k], ref[k], "bf16")
+    refb = O.mlp_shard_bwd(X, W1, W2, dY)
+    for k in ("dX", "dW1", "dW2"):
+        check(k, out[k], refb[k], "bf16")
+
+
 def test_mlp_c2_all_shards_and_reduces(tp):
     _say("mlp C2 bf16, 8 shards + Z/dX shard-reduce")
     wl = tpsynth.WORKLOADS["C2"]
@@ -405,6 +425,21 @@ def test_attention_bwd_c4_full_size_sampled(tp):
 
 
 # ------------------------------------------------------- grouped-query attention
+
+def test_attention_sequence_limit(tp):
+    """s at the ABI's sequence limit (2^22 tokens, one head of 128: 1 GiB per
+    head of K or V, the most the core's 32-bit key/value offsets address),
+    causal; sampled queries across the sequence, O and Z, and L finite."""
+    b, s, d, h_l, dh = 1, 1 << 22, 64, 1, 128
+    _say(f"attention sequence limit s={s}")
+    inp = tpsynth.random_gqa(b, s, d, h_l, h_l, dh, "bf16", seed=100, w_std=0.1)
+    out = run_attn(tp, inp, b, s, h_l, dh)
+    assert torch.isfinite(out["L"]).all()
+    rows = np.unique(np.concatenate([_sample(s, 6, 101), [1 << 21, (1 << 22) - 2]]))
+    ref = O.attn_gqa_query_rows(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], rows, h_l, h_l, dh)
+    check("O", host(out["O"][torch.from_numpy(rows).cuda()]), ref["O"], "bf16")
+    check("Z", host(out["Z"][torch.from_numpy(rows).cuda()]), ref["Z"], "bf16")
+
 
 def run_gqa(tp, inp, b, s, h_l, h_kv, dh, causal=True):
     X, Wq, Wk, Wv, Wo = (dev(inp[k], "bf16") for k in ("X", "Wq", "Wk", "Wv", "Wo"))
