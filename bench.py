@@ -544,6 +544,7 @@ def run_e1(tp, torch, steps, warmup):
     dX = torch.empty((T, d), dtype=bf, device="cuda")
     dE = torch.empty((vl, d), dtype=torch.float32, device="cuda")
     ws = torch.empty(tp.tp_vocab_ce_bwd_workspace_bytes(tp.TP_DT_BF16, T, d, vl), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(tp.tp_vocab_ce_fwd_workspace_bytes(tp.TP_DT_BF16, T, d, vl), dtype=torch.uint8, device="cuda")
 
     dEmb = torch.randn((T, d), device="cuda").to(bf)          # gradient of the embedding output
     dE_in = torch.empty((vl, d), dtype=torch.float32, device="cuda")
@@ -551,7 +552,7 @@ def run_e1(tp, torch, steps, warmup):
     def step():
         tp.tp_vocab_embed_fwd(ids, E0, parts[0], 0)
         tp.tp_shard_reduce(parts, emb, n, T * d)
-        tp.tp_vocab_ce_fwd(X, E0, tg, logits, stats[0], 0)
+        tp.tp_vocab_ce_fwd(X, E0, tg, logits, stats[0], 0, ws=fws)
         tp.tp_vocab_ce_combine(stats, loss, lse)
         tp.tp_vocab_ce_bwd(X, E0, tg, logits, lse, dloss, dX, dE, ws, 0)
         tp.tp_vocab_embed_bwd(ids, dEmb, dE_in, 0)

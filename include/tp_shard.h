@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 7
+#define TP_ABI_VERSION 8
 
 typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype_t;
 
@@ -337,14 +337,20 @@ int tp_vocab_embed_bwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d,
  *                            s = sum_v exp(logits[t, v] - m),
  *                            z_t = logits[t, targets[t] - vocab_start] when
  *                                  the target is one of the shard's rows, else 0
- * with the statistics taken from the logits as stored (fp32 arithmetic).
+ * with the statistics taken from the logits as stored (fp32 arithmetic); in
+ * the bf16 path the product's epilogue computes them as it stores the logits.
  * X: [n_tokens x d]; E_local: [vocab_local x d] (the same table slice as the
  * input embedding's); targets: int64 [n_tokens]; stats: fp32 [n_tokens x 3].
- * logits is kept for tp_vocab_ce_bwd.  Sizes as tp_vocab_embed_fwd.
+ * logits is kept for tp_vocab_ce_bwd.  ws: device workspace of
+ * tp_vocab_ce_fwd_workspace_bytes(...) bytes (0 for TP_DT_F32: ws may then be
+ * NULL).  Sizes as tp_vocab_embed_fwd.
  * ------------------------------------------------------------------------- */
 int tp_vocab_ce_fwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d,
                     int64_t vocab_local, int64_t vocab_start, const void* X,
-                    const void* E_local, const int64_t* targets, void* logits, float* stats);
+                    const void* E_local, const int64_t* targets, void* logits, float* stats,
+                    void* ws, size_t ws_bytes);
+size_t tp_vocab_ce_fwd_workspace_bytes(tp_dtype_t dt, int64_t n_tokens, int64_t d,
+                                       int64_t vocab_local);
 
 /* ---------------------------------------------------------------------------
  * tp_vocab_ce_combine — the exchange of the fused cross-entropy on one GPU:

@@ -20,7 +20,7 @@ __all__ = [
     "tp_attn_gqa_shard_bwd", "tp_attn_gqa_shard_bwd_workspace_bytes",
     "tp_shard_reduce", "tp_shard_range", "tp_sp_reduce_scatter_ln", "tp_sp_all_gather", "tp_sp_ln_bwd_reduce_scatter",
     "tp_sp_ln_bwd_workspace_bytes",
-    "tp_vocab_embed_fwd", "tp_vocab_embed_bwd", "tp_vocab_ce_fwd", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
+    "tp_vocab_embed_fwd", "tp_vocab_embed_bwd", "tp_vocab_ce_fwd", "tp_vocab_ce_fwd_workspace_bytes", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
     "tp_vocab_ce_bwd_workspace_bytes",
     "tp_abi_version", "EXPORTS",
 ]
@@ -67,7 +67,8 @@ EXPORTS = {
     "tp_sp_ln_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
     "tp_vocab_embed_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p]),
     "tp_vocab_embed_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p]),
-    "tp_vocab_ce_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    "tp_vocab_ce_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz]),
+    "tp_vocab_ce_fwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
     "tp_vocab_ce_combine": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p]),
     "tp_vocab_ce_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _i64] + [_p] * 6 + [_p, _p, _p, _sz]),
     "tp_vocab_ce_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
@@ -306,12 +307,17 @@ def tp_vocab_embed_bwd(ids, dY, dE_local, vocab_start: int, stream=None) -> None
                                     _ptr(dE_local)))
 
 
-def tp_vocab_ce_fwd(X, E_local, targets, logits, stats, vocab_start: int, stream=None) -> None:
+def tp_vocab_ce_fwd_workspace_bytes(dtype: int, n_tokens: int, d: int, vocab_local: int) -> int:
+    return lib().tp_vocab_ce_fwd_workspace_bytes(dtype, n_tokens, d, vocab_local)
+
+
+def tp_vocab_ce_fwd(X, E_local, targets, logits, stats, vocab_start: int, ws=None, stream=None) -> None:
     """logits = X E_local^T and the per-token (max, sum-exp, target logit)."""
     n_tokens, d = X.shape
     vl = E_local.shape[0]
     _check(lib().tp_vocab_ce_fwd(_stream(stream), _dt(X), n_tokens, d, vl, vocab_start, _ptr(X), _ptr(E_local),
-                                 _ids(targets), _ptr(logits), _ptr(stats)))
+                                 _ids(targets), _ptr(logits), _ptr(stats), _ptr(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size()))
 
 
 def tp_vocab_ce_combine(stats, loss, lse, stream=None) -> None:

@@ -31,6 +31,7 @@
 //  * Workgroup ids are remapped so the tiles one XCD (of 8) runs are
 //    contiguous, then grouped along m for L2 reuse.
 #pragma once
+#include <type_traits>
 #include <utility>
 
 #include "common.hpp"
@@ -203,6 +204,11 @@ __device__ __forceinline__ void static_for(F&& f) {
       std::make_integer_sequence<int, N>{});
 }
 
+// An epilogue may also reduce each staged output row of the tile (its values
+// as stored) by defining ROW_REDUCE and row_reduce<O, NT, PASS, CPR, BNL>().
+template <class E, class = void> struct epi_row_reduce : std::false_type {};
+template <class E> struct epi_row_reduce<E, std::void_t<decltype(E::ROW_REDUCE)>> : std::true_type {};
+
 // Epilogue.  acc[i][j][4*b + q] is C(m, n) with
 //   m = m0 + wm*WTM + i*32 + (lane & 31)
 //   n = n0 + <wave column of block j> + 8*b + 4*(lane >> 5) + q
@@ -264,6 +270,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
           }
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // staged tile complete
+      if constexpr (epi_row_reduce<Epi>::value)     // per-row statistics of the staged (stored) values
+        epi.template row_reduce<O, Cfg::NT, PASS, CPR, BNL>(smem, pass * PASS, m0, n0, p, tid);
       constexpr int TOTAL = PASS * CPR;
 #pragma unroll 4
       for (int idx = tid; idx < TOTAL; idx += Cfg::NT) {

@@ -64,9 +64,10 @@ hipError_t launch_vocab_embed_fwd(hipStream_t st, int dt, int64_t n_tokens, int6
                                   int64_t vstart, const int64_t* ids, const void* E, void* Y);
 hipError_t launch_vocab_embed_bwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
                                   int64_t vstart, const int64_t* ids, const void* dY, float* dE);
+size_t vocab_ce_fwd_ws_bytes(int dt, int64_t n_tokens, int64_t vlocal);
 hipError_t launch_vocab_ce_fwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
                                int64_t vstart, const void* X, const void* E, const int64_t* targets,
-                               void* logits, float* stats);
+                               void* logits, float* stats, void* ws);
 hipError_t launch_vocab_ce_combine(hipStream_t st, int n, int64_t n_tokens, const float* stats,
                                    int64_t shard_stride, float* loss, float* lse);
 size_t vocab_ce_bwd_ws_bytes(int dt, int64_t n_tokens, int64_t d, int64_t vlocal);

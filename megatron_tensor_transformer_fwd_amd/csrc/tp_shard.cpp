@@ -565,19 +565,27 @@ int tp_vocab_embed_bwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d,
                     "tp_vocab_embed_bwd");
 }
 
+size_t tp_vocab_ce_fwd_workspace_bytes(tp_dtype_t dt, int64_t n_tokens, int64_t d, int64_t vocab_local) {
+  if (vocab_common(dt, n_tokens, d, vocab_local, 0) != TP_OK) return 0;
+  return tpk::vocab_ce_fwd_ws_bytes(dt, n_tokens, vocab_local);
+}
+
 int tp_vocab_ce_fwd(void* stream, tp_dtype_t dt, int64_t n_tokens, int64_t d, int64_t vocab_local,
                     int64_t vocab_start, const void* X, const void* E_local, const int64_t* targets,
-                    void* logits, float* stats) {
+                    void* logits, float* stats, void* ws, size_t ws_bytes) {
   TP_CHECK(vocab_common(dt, n_tokens, d, vocab_local, vocab_start));
   const size_t e = esize(dt);
+  const size_t need = tpk::vocab_ce_fwd_ws_bytes(dt, n_tokens, vocab_local);
   TP_CHECK(check_buffers({{"X", X, (size_t)(n_tokens * d) * e},
                           {"E_local", E_local, (size_t)(vocab_local * d) * e},
                           {"targets", targets, (size_t)n_tokens * 8, 8}},
                          {{"logits", logits, (size_t)(n_tokens * vocab_local) * e},
-                          {"stats", stats, (size_t)n_tokens * 12, 4}},
+                          {"stats", stats, (size_t)n_tokens * 12, 4}, {"ws", ws, need}},
                          {"X", "E_local", "targets", "logits", "stats"}));
+  if (need && (!ws || ws_bytes < need))
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes given, %zu required", ws ? ws_bytes : (size_t)0, need);
   return hip_status(tpk::launch_vocab_ce_fwd(static_cast<hipStream_t>(stream), dt, n_tokens, d, vocab_local,
-                                             vocab_start, X, E_local, targets, logits, stats),
+                                             vocab_start, X, E_local, targets, logits, stats, ws),
                     "tp_vocab_ce_fwd");
 }
 

@@ -8,9 +8,12 @@
 // fill), so a row is written by consecutive lanes.
 //
 // Output embedding fused with the cross-entropy.  The shard's logits
-// z = X E_local^T come from the bf16 MFMA GEMM; a row pass then reduces every
-// token's logits to three numbers, m = max z, s = sum exp(z - m) and the
-// target's logit when the target is one of the shard's rows.  Only these
+// z = X E_local^T come from the bf16 MFMA GEMM, whose epilogue also reduces
+// each output tile's rows to (max, sum exp) pairs; a small per-token kernel
+// merges a row's tile pairs and reads the target's logit, giving every
+// token's three numbers, m = max z, s = sum exp(z - m) and the target's logit
+// when the target is one of the shard's rows.  (The fp32 path keeps a
+// separate row pass.)  Only these
 // 3 * n_tokens values per shard cross GPUs (the combine kernel is the
 // exchange), not the [n_tokens x V] logits.  The statistics are taken from the
 // logits as stored (bf16 in the bf16 path), the values the backward reads.
@@ -279,6 +282,86 @@ ce_dlogits_kernel(const T* __restrict__ logits, int64_t n_tokens, int64_t vlocal
   }
 }
 
+// The logits product's epilogue: stores the bf16 logits and, from the
+// staged tile (the values as stored), each row's max and sum of exp over the
+// tile's columns, written as one (m, s) pair per (token, tile column).  The
+// loss is thereby fused into the output-embedding product: the logits are
+// not read back for the forward statistics.
+struct EpiCeLogits {
+  static constexpr int NOUT = 1;
+  static constexpr bool ROW_REDUCE = true;
+  template <int O> using OutT = bf16;
+  bf16* C;
+  int64_t ldc;
+  f32x2* part;      // [M x tiles_n]
+  template <int O> __device__ __forceinline__ bool has_out() const { return true; }
+  template <int O> __device__ __forceinline__ bf16* out_ptr(int64_t m, int64_t n, int, int) const {
+    return C + m * ldc + n;
+  }
+  template <int O> __device__ __forceinline__ f32x4 value(int64_t, int64_t, f32x4 v) const { return v; }
+  template <int O, int NT, int PASS, int CPR, int BNL>
+  __device__ __forceinline__ void row_reduce(const char* smem, int r_base, int64_t m0, int64_t n0,
+                                             const GemmParams& p, int tid) const {
+    constexpr int TPR = NT >= PASS ? NT / PASS : 1;     // threads per staged row
+    constexpr int RPT = PASS > NT ? PASS / NT : 1;      // staged rows per thread
+    const int ncv = (int)std::min<int64_t>(CPR, (p.N - n0) / 8);   // chunks of 8 valid columns
+    const int part_idx = tid % TPR;
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) {
+      const int r = tid / TPR + rr * (NT / TPR);
+      float mx = -FLT_MAX, sm = 0.f;
+      for (int c = part_idx; c < ncv; c += TPR) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(smem + r * (CPR * 16) + ((c ^ (r & (CPR - 1))) * 16));
+        float z[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          z[2 * i] = bf16_lo(w[i]);
+          z[2 * i + 1] = bf16_hi(w[i]);
+        }
+        float cm = z[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) cm = fmaxf(cm, z[e]);
+        if (cm > mx) {
+          sm *= __expf(mx - cm);
+          mx = cm;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm += __expf(z[e] - mx);
+      }
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) {
+        const float m2 = __shfl_xor(mx, o), s2 = __shfl_xor(sm, o);
+        const float M = fmaxf(mx, m2);
+        sm = sm * __expf(mx - M) + s2 * __expf(m2 - M);
+        mx = M;
+      }
+      const int64_t m = m0 + r_base + r;
+      if (part_idx == 0 && m < p.M) part[m * p.tiles_n + n0 / BNL] = f32x2{mx, sm};
+    }
+  }
+};
+
+// Per token: the tile columns' (m, s) pairs merged in order, and the target's
+// logit when the target is one of the shard's rows.
+__global__ void __launch_bounds__(256)
+ce_tile_stats_kernel(const f32x2* __restrict__ part, int ntn, const bf16* __restrict__ logits, int64_t vlocal,
+                     const int64_t* __restrict__ targets, int64_t vstart, int64_t n_tokens,
+                     float* __restrict__ stats) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n_tokens) return;
+  float m = -FLT_MAX, s = 0.f;
+  for (int j = 0; j < ntn; ++j) {
+    const f32x2 q = part[t * ntn + j];
+    const float M = fmaxf(m, q[0]);
+    s = s * __expf(m - M) + q[1] * __expf(q[0] - M);
+    m = M;
+  }
+  const int64_t local = targets[t] - vstart;
+  stats[t * 3 + 0] = m;
+  stats[t * 3 + 1] = s;
+  stats[t * 3 + 2] = (local >= 0 && local < vlocal) ? to_f32(logits[t * vlocal + local]) : 0.f;
+}
+
 // ------------------------------------------------------------------ launchers
 
 static size_t up256v(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -294,15 +377,23 @@ hipError_t launch_vocab_embed_fwd(hipStream_t st, int dt, int64_t n_tokens, int6
                 n_tokens, rowvec, vstart, vlocal, static_cast<const u32x4*>(E), static_cast<u32x4*>(Y));
 }
 
+size_t vocab_ce_fwd_ws_bytes(int dt, int64_t n_tokens, int64_t vlocal) {
+  return dt == DT_BF16 ? (size_t)n_tokens * (size_t)cdiv(vlocal, 128) * 8 : 0;
+}
+
 hipError_t launch_vocab_ce_fwd(hipStream_t st, int dt, int64_t n_tokens, int64_t d, int64_t vlocal,
                                int64_t vstart, const void* X, const void* E, const int64_t* targets,
-                               void* logits, float* stats) {
-  if (dt == DT_BF16) {  // z = X E^T:  B(k, n) = E[n][k]
+                               void* logits, float* stats, void* ws) {
+  if (dt == DT_BF16) {  // z = X E^T:  B(k, n) = E[n][k]; row statistics fused into the epilogue
     GemmParams p = make_params(n_tokens, vlocal, make_seg(X, d, n_tokens * d, E, d, vlocal * d, d));
-    EpiStore<bf16> e{static_cast<bf16*>(logits), vlocal, 0};
-    TPK_TRY((launch_gemm<true, true, false>(st, "vocab_ce.xet", p, e, plan_gemm(n_tokens, vlocal, d, false, false))));
-    return launch("vocab_ce.row_stats", ce_row_stats_kernel<bf16>, dim3((unsigned)n_tokens), dim3(256), st,
-                  static_cast<const bf16*>(logits), vlocal, targets, vstart, stats);
+    const GemmPlan plan = plan_gemm(n_tokens, vlocal, d, false, false);
+    const int ntn = (int)cdiv(vlocal, plan.cfg == CFG_L ? 256 : 128);
+    f32x2* part = static_cast<f32x2*>(ws);
+    EpiCeLogits e{static_cast<bf16*>(logits), vlocal, part};
+    TPK_TRY((launch_gemm<true, true, false>(st, "vocab_ce.xet", p, e, plan)));
+    return launch("vocab_ce.tile_stats", ce_tile_stats_kernel, dim3((unsigned)cdiv(n_tokens, 256)), dim3(256), st,
+                  (const f32x2*)part, ntn, static_cast<const bf16*>(logits), vlocal, targets, vstart, n_tokens,
+                  stats);
   }
   GemmParamsF32 p = make_params_f32(n_tokens, vlocal, make_seg_f32(X, d, n_tokens, E, d, vlocal, d));
   EpiStore<float> e{static_cast<float*>(logits), vlocal, 0};

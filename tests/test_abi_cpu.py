@@ -33,7 +33,7 @@ def test_header_and_binding_agree_and_library_exports_all():
 
 
 def test_version_and_strerror():
-    assert tp.tp_abi_version() == 7
+    assert tp.tp_abi_version() == 8
     L = tp.lib()
     for code in (OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP):
         assert L.tp_strerror(code) and L.tp_strerror(code) != b"unknown status"
@@ -302,10 +302,15 @@ def test_vocab_validation():
     assert L.tp_vocab_embed_bwd(None, BF16, 16, 64, 128, 0, ids, Y, Y + 64) == E_ALIAS
     assert L.tp_vocab_embed_bwd(None, BF16, 16, 64, 128, 0, ids + 4, Y, E) == E_ALIGN
     # fused output embedding + cross-entropy
-    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, lg, None) == E_NULL
-    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, None, lg, st) == E_NULL
-    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, lg, lg + 16) == E_ALIAS
-    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, X, st) == E_ALIAS
+    fws = L.tp_vocab_ce_fwd_workspace_bytes(BF16, 16, 64, 128)
+    assert fws >= 16 * 8 and L.tp_vocab_ce_fwd_workspace_bytes(F32, 16, 64, 128) == 0
+    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, lg, None, ws, fws) == E_NULL
+    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, None, lg, st, ws, fws) == E_NULL
+    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, lg, lg + 16, ws, fws) == E_ALIAS
+    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, X, st, ws, fws) == E_ALIAS
+    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, lg, st, None, 0) == E_WS
+    assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, lg, st, ws, fws - 1) == E_WS
+    assert L.tp_vocab_ce_fwd(None, F32, 16, 64, 128, 0, X, E, tg, lg, st, None, 0) == E_HIP   # fp32: no workspace
     assert L.tp_vocab_ce_combine(None, 0, 16, st, 48, loss, lse) == E_DIM
     assert L.tp_vocab_ce_combine(None, 4, 16, st, 40, loss, lse) == E_DIM       # stride < 3 * n_tokens
     assert L.tp_vocab_ce_combine(None, 4, 16, st, 48, loss, loss) == E_ALIAS

@@ -147,6 +147,8 @@ def test_graph_sequence_parallel_and_vocab(tp):
     dXv = torch.empty((nv, T, d), dtype=torch.bfloat16, device="cuda")
     dE = torch.empty((nv, vl, d), device="cuda")
     ws = torch.empty(tp.tp_vocab_ce_bwd_workspace_bytes(tp.TP_DT_BF16, T, d, vl), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(tp.tp_vocab_ce_fwd_workspace_bytes(tp.TP_DT_BF16, T, d, vl), dtype=torch.uint8,
+                      device="cuda")
 
     def step():
         for i in range(n):
@@ -155,7 +157,7 @@ def test_graph_sequence_parallel_and_vocab(tp):
         tp.tp_sp_all_gather(hs, full)
         for i in range(nv):
             tp.tp_vocab_embed_fwd(ids, Es[i], emb_p[i], i * vl)
-            tp.tp_vocab_ce_fwd(Xv, Es[i], tg, logits[i], stats[i], i * vl)
+            tp.tp_vocab_ce_fwd(Xv, Es[i], tg, logits[i], stats[i], i * vl, ws=fws)
         tp.tp_shard_reduce(emb_p, emb, nv, T * d)
         tp.tp_vocab_ce_combine(stats, loss, lse)
         for i in range(nv):

@@ -93,15 +93,17 @@ def run_ce(tp, inp, n, dtype, dloss=None, backward=True):
     gE = [dev(E[i * vl:(i + 1) * vl], dtype) for i in range(n)]
     logits = torch.empty((n, T, vl), dtype=_tdt(dtype), device="cuda")
     stats = torch.empty((n, T, 3), dtype=torch.float32, device="cuda")
+    dt = tp.TP_DT_BF16 if dtype == "bf16" else tp.TP_DT_F32
+    fb = tp.tp_vocab_ce_fwd_workspace_bytes(dt, T, d, vl)
+    fws = torch.empty(fb, dtype=torch.uint8, device="cuda") if fb else None
     for i in range(n):
-        tp.tp_vocab_ce_fwd(gX, gE[i], gt, logits[i], stats[i], i * vl)
+        tp.tp_vocab_ce_fwd(gX, gE[i], gt, logits[i], stats[i], i * vl, ws=fws)
     loss = torch.empty(T, dtype=torch.float32, device="cuda")
     lse = torch.empty(T, dtype=torch.float32, device="cuda")
     tp.tp_vocab_ce_combine(stats, loss, lse)
     out = {"logits": logits, "stats": stats, "loss": loss, "lse": lse}
     if backward:
         gdl = torch.from_numpy(np.ascontiguousarray(dloss, dtype=np.float32)).cuda()
-        dt = tp.TP_DT_BF16 if dtype == "bf16" else tp.TP_DT_F32
         ws = torch.empty(tp.tp_vocab_ce_bwd_workspace_bytes(dt, T, d, vl), dtype=torch.uint8, device="cuda")
         dX = torch.empty((n, T, d), dtype=_tdt(dtype), device="cuda")
         dE = torch.empty((n, vl, d), dtype=torch.float32, device="cuda")
