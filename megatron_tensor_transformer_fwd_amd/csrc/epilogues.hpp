@@ -19,18 +19,23 @@ namespace tpk {
 
 template <class T> struct Quad;
 template <> struct Quad<bf16> {
+  using Raw = u32x2;
   static __device__ __forceinline__ void store(bf16* p, f32x4 v) {
     u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     *reinterpret_cast<u32x2*>(p) = w;
   }
-  static __device__ __forceinline__ f32x4 load(const bf16* p) {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  static __device__ __forceinline__ Raw load_raw(const bf16* p) { return *reinterpret_cast<const u32x2*>(p); }
+  static __device__ __forceinline__ f32x4 unpack(Raw w) {
     return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
   }
+  static __device__ __forceinline__ f32x4 load(const bf16* p) { return unpack(load_raw(p)); }
 };
 template <> struct Quad<float> {
+  using Raw = f32x4;
   static __device__ __forceinline__ void store(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
-  static __device__ __forceinline__ f32x4 load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  static __device__ __forceinline__ Raw load_raw(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  static __device__ __forceinline__ f32x4 unpack(Raw w) { return w; }
+  static __device__ __forceinline__ f32x4 load(const float* p) { return load_raw(p); }
 };
 
 // C = AB stored in T.  With split-K, split s writes its partial sum to
@@ -84,12 +89,19 @@ struct EpiDGelu {
   template <int O> __device__ __forceinline__ T* out_ptr(int64_t m, int64_t n, int, int) const {
     return dA + m * ld + n;
   }
-  template <int O> __device__ __forceinline__ f32x4 value(int64_t m, int64_t n, f32x4 v) const {
-    const f32x4 a = Quad<T>::load(A + m * ld + n);
+  struct Aux { typename Quad<T>::Raw a; };
+  template <int O> __device__ __forceinline__ Aux aux_load(int64_t m, int64_t n) const {
+    return Aux{Quad<T>::load_raw(A + m * ld + n)};
+  }
+  template <int O> __device__ __forceinline__ f32x4 value_aux(int64_t, int64_t, f32x4 v, const Aux& x) const {
+    const f32x4 a = Quad<T>::unpack(x.a);
     f32x4 r;
 #pragma unroll
     for (int q = 0; q < 4; ++q) r[q] = v[q] * gelu_prime_f(a[q]);
     return r;
+  }
+  template <int O> __device__ __forceinline__ f32x4 value(int64_t m, int64_t n, f32x4 v) const {
+    return value_aux<O>(m, n, v, aux_load<O>(m, n));
   }
 };
 
@@ -134,11 +146,22 @@ struct EpiDSwiGLU {
   template <int O> __device__ __forceinline__ T* out_ptr(int64_t m, int64_t n, int, int) const {
     return dGU + m * (2 * ld) + (O == 0 ? 0 : ld) + n;
   }
+  // output 0 reads G and U, output 1 only G
+  struct Aux { typename Quad<T>::Raw g, u; };
+  template <int O> __device__ __forceinline__ Aux aux_load(int64_t m, int64_t n) const {
+    Aux x;
+    x.g = Quad<T>::load_raw(G + m * ld + n);
+    if constexpr (O == 0) x.u = Quad<T>::load_raw(U + m * ld + n);
+    return x;
+  }
   template <int O> __device__ __forceinline__ f32x4 value(int64_t m, int64_t n, f32x4 v) const {
-    const f32x4 g = Quad<T>::load(G + m * ld + n);
+    return value_aux<O>(m, n, v, aux_load<O>(m, n));
+  }
+  template <int O> __device__ __forceinline__ f32x4 value_aux(int64_t, int64_t, f32x4 v, const Aux& x) const {
+    const f32x4 g = Quad<T>::unpack(x.g);
     f32x4 r;
     if constexpr (O == 0) {
-      const f32x4 u = Quad<T>::load(U + m * ld + n);
+      const f32x4 u = Quad<T>::unpack(x.u);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float s = sigmoid_f(g[q]);

@@ -209,6 +209,15 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <class E, class = void> struct epi_row_reduce : std::false_type {};
 template <class E> struct epi_row_reduce<E, std::void_t<decltype(E::ROW_REDUCE)>> : std::true_type {};
 
+// An epilogue that reads other tensors at the output positions (a saved
+// activation) defines Aux, aux_load<O>(m, n) and value_aux<O>(m, n, v, aux):
+// the staging loop then issues one 32-row block's loads together before
+// using any of them, instead of one load-and-wait per quad.
+template <class E, class = void> struct epi_aux : std::false_type {};
+template <class E> struct epi_aux<E, std::void_t<typename E::Aux>> : std::true_type {};
+template <class E, bool = epi_aux<E>::value> struct epi_aux_type { struct type {}; };
+template <class E> struct epi_aux_type<E, true> { using type = typename E::Aux; };
+
 // Epilogue.  acc[i][j][4*b + q] is C(m, n) with
 //   m = m0 + wm*WTM + i*32 + (lane & 31)
 //   n = n0 + <wave column of block j> + 8*b + 4*(lane >> 5) + q
@@ -246,15 +255,31 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
         const int r = rl + lrow - pass * PASS;
         const int64_t m = m0 + rl + lrow;
         char* rowp = smem + r * ROWB;
+        constexpr int JN = DUAL ? TN / 2 : TN;
+        using AuxT = typename epi_aux_type<Epi>::type;
+        [[maybe_unused]] AuxT ax[JN][4];
+        if constexpr (epi_aux<Epi>::value) {
 #pragma unroll
-        for (int j = 0; j < (DUAL ? TN / 2 : TN); ++j)
+          for (int j = 0; j < JN; ++j)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const int64_t n = n0 + wn * WTN + j * 32 + 8 * b + g4;
+              if (m < p.M && n < p.N) ax[j][b] = epi.template aux_load<O>(m, n);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < JN; ++j)
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const int nl = (DUAL ? wn * (WTN / 2) : wn * WTN) + j * 32 + 8 * b + g4;
             const int64_t n = n0 + nl;
             if (m < p.M && n < p.N) {
               f32x4 v;
-              if constexpr (DUAL) {
+              if constexpr (epi_aux<Epi>::value) {
+                static_assert(!DUAL, "auxiliary inputs in single-B products only");
+                const f32x4 a = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2], acc[i][j][4 * b + 3]};
+                v = epi.template value_aux<O>(m, n, a, ax[j][b]);
+              } else if constexpr (DUAL) {
                 const int jj = j + TN / 2;
                 const f32x4 g = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2], acc[i][j][4 * b + 3]};
                 const f32x4 u = {acc[i][jj][4 * b], acc[i][jj][4 * b + 1], acc[i][jj][4 * b + 2], acc[i][jj][4 * b + 3]};
