@@ -40,10 +40,10 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-try:  # scipy's erf; math.erf is the fallback and the brute-force cross-check
-    from scipy.special import erf as _erf
+try:  # scipy's erfc; math.erfc is the fallback and the brute-force cross-check
+    from scipy.special import erfc as _erfc
 except Exception:  # pragma: no cover
-    _erf = np.vectorize(math.erf, otypes=[np.float64])
+    _erfc = np.vectorize(math.erfc, otypes=[np.float64])
 
 __all__ = [
     "gelu", "gelu_prime", "swish", "swish_prime",
@@ -71,16 +71,23 @@ def _f64(a) -> np.ndarray:
 # block) and called as PyTorch's default (erf) form in the code listings.
 # ----------------------------------------------------------------------------
 
+def _norm_cdf(x):
+    """Phi(x) = (1 + erf(x / sqrt 2)) / 2, written as erfc(-x / sqrt 2) / 2: the
+    same function, without the cancellation of 1 + erf in the lower tail
+    (below x = -6 the sum rounds to 0 in fp64 while Phi(-10) is 7.6e-24)."""
+    return 0.5 * _erfc(-_f64(x) / _SQRT2)
+
+
 def gelu(x):
     """GeLU(x) = x * Phi(x), Phi the standard normal CDF (exact erf form)."""
     x = _f64(x)
-    return x * 0.5 * (1.0 + _erf(x / _SQRT2))
+    return x * _norm_cdf(x)
 
 
 def gelu_prime(x):
     """dGeLU/dx = Phi(x) + x * phi(x), phi the standard normal density."""
     x = _f64(x)
-    return 0.5 * (1.0 + _erf(x / _SQRT2)) + x * _INV_SQRT_2PI * np.exp(-0.5 * x * x)
+    return _norm_cdf(x) + x * _INV_SQRT_2PI * np.exp(-0.5 * x * x)
 
 
 def _sigmoid(x):

@@ -33,6 +33,19 @@ def test_gelu_textbook_values():
     assert abs(O.gelu(-10.0)) < 1e-20
 
 
+def test_gelu_lower_tail_relative():
+    # Upper-tail probabilities Q(x) = Phi(-x) of the standard normal from
+    # tables of the normal distribution: Q(5) = 2.8665157187919e-7,
+    # Q(10) = 7.6198530241605e-24.  GeLU(-x) = -x Q(x) must hold to relative
+    # accuracy, not just be small, because the products store these values
+    # in floating point with their own exponent.
+    assert O.gelu(-5.0) == pytest.approx(-5 * 2.8665157187919e-7, rel=1e-12)
+    assert O.gelu(-10.0) == pytest.approx(-10 * 7.6198530241605e-24, rel=1e-12)
+    # GeLU'(-10) = Phi(-10) - 10 phi(-10), phi(10) = exp(-50) / sqrt(2 pi)
+    phi10 = math.exp(-50.0) / math.sqrt(2 * math.pi)
+    assert O.gelu_prime(-10.0) == pytest.approx(7.6198530241605e-24 - 10 * phi10, rel=1e-12)
+
+
 def test_swish_closed_forms():
     sig1 = 1.0 / (1.0 + math.exp(-1.0))
     assert O.swish(1.0) == pytest.approx(sig1, abs=1e-15)
