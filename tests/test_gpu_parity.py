@@ -184,6 +184,77 @@ def test_mlp_row_pitch_limit(tp):
         check(k, out[k], refb[k], "bf16")
 
 
+def _act_grid(n, lo=-10.0, hi=10.0, seed=0):
+    """n x n values spread over [lo, hi] in shuffled order (the activations' tails included)."""
+    v = np.linspace(lo, hi, n * n)
+    np.random.default_rng(seed).shuffle(v)
+    return v.reshape(n, n)
+
+
+def _as_dtype(a, dtype):
+    """The values the device holds: rounded to bf16 (or fp32) on the host."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.float().numpy().astype(np.float64)
+
+
+def _elementwise(name, got, ref, scale, rtol):
+    g = host(got)
+    bad = np.abs(g - ref) > rtol * scale
+    assert not bad.any(), (f"{name}: {int(bad.sum())} elements off, worst at x-index "
+                           f"{np.unravel_index(np.argmax(np.abs(g - ref) / scale), ref.shape)}")
+
+
+_ACT_RTOL = {"bf16": 2.0 ** -8, "f32": 1e-5}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gelu_elementwise_tails(tp, dtype):
+    """GeLU and GeLU' value by value over [-10, 10]: with X = W2 = I the forward
+    gives A = W1 and H = GeLU(W1), and the backward's dW1 = X^T dA is
+    dA = dY * GeLU'(W1) itself, each rounded once to the output type.  The
+    bound is relative to each value (to |dY| (Phi + |x| phi) for GeLU', which
+    crosses zero), so the lower tail, where GeLU is tiny, is checked too."""
+    _say(f"gelu elementwise tails {dtype}")
+    n = 64
+    I = np.eye(n)
+    W1 = _as_dtype(_act_grid(n, seed=1), dtype)
+    dY = _as_dtype(np.random.default_rng(2).standard_normal((n, n)), dtype)
+    out = run_mlp_shard(tp, dev(I, dtype), dev(W1, dtype), dev(I, dtype), dev(dY, dtype), dtype)
+    rtol = _ACT_RTOL[dtype]
+    np.testing.assert_array_equal(host(out["A"]), W1)
+    H = O.gelu(W1)
+    _elementwise("H", out["H"], H, np.abs(H), rtol)
+    _elementwise("Z", out["Z"], H, np.abs(H), rtol)
+    phi = np.exp(-0.5 * W1 * W1) / math.sqrt(2 * math.pi)
+    cdf = 0.5 * np.vectorize(math.erfc)(-W1 / math.sqrt(2))
+    _elementwise("dA (dW1)", out["dW1"], dY * O.gelu_prime(W1), np.abs(dY) * (cdf + np.abs(W1) * phi), rtol)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_swiglu_elementwise_tails(tp, dtype):
+    """Swish and Swish' value by value: with X = W2 = I, G = W1 and U = W3, so
+    H = Swish(W1) * W3, and the weight gradients are dW1 = dG = dY * U * Swish'(G)
+    and dW3 = dU = dY * Swish(G) themselves."""
+    _say(f"swiglu elementwise tails {dtype}")
+    n = 64
+    I = np.eye(n)
+    W1 = _as_dtype(_act_grid(n, seed=3), dtype)
+    W3 = _as_dtype(np.random.default_rng(4).standard_normal((n, n)), dtype)
+    dY = _as_dtype(np.random.default_rng(5).standard_normal((n, n)), dtype)
+    inp = {"X": I, "W1": W1, "W3": W3, "W2": I, "dY": dY}
+    out = run_swiglu(tp, inp, dtype)
+    rtol = _ACT_RTOL[dtype]
+    H = O.swish(W1) * W3
+    _elementwise("H", out["H"], H, np.abs(H), rtol)
+    sig = 1.0 / (1.0 + np.exp(-W1))
+    dU = dY * O.swish(W1)
+    _elementwise("dU (dW3)", out["dW3"], dU, np.abs(dU), rtol)
+    dG = dY * W3 * O.swish_prime(W1)
+    _elementwise("dG (dW1)", out["dW1"], dG, np.abs(dY * W3) * sig * (1 + np.abs(W1) * (1 - sig)), rtol)
+
+
 def test_mlp_c2_all_shards_and_reduces(tp):
     _say("mlp C2 bf16, 8 shards + Z/dX shard-reduce")
     wl = tpsynth.WORKLOADS["C2"]
