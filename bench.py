@@ -74,24 +74,28 @@ class HipEvents:
             self.hip.hipEventDestroy(self.stop[i])
 
 
-def timed(tp, torch, step, steps: int, warmup: int, kernels_per_step: int):
+def timed(tp, torch, step, steps: int, warmup: int, kernels_per_step: int, per_step: bool = False):
     """Warm up, then time exactly `steps` steps between two synchronisations;
     per-kernel durations come from the library's hipEvent hook on the same
-    stream."""
+    stream.  With per_step, an event between consecutive steps also gives
+    each step's duration (returned as the fifth value)."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     ev = HipEvents(steps * kernels_per_step + 8)
     L = tp.lib()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps - 1)] if per_step else []
     torch.cuda.synchronize()
     rc = L.tp_profile_begin(ev.start, ev.stop, ev.n)
     if rc != 0:
         raise RuntimeError("tp_profile_begin failed")
     t0.record()
     wall0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
         step()
+        if per_step and i < steps - 1:
+            marks[i].record()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -101,7 +105,11 @@ def timed(tp, torch, step, steps: int, warmup: int, kernels_per_step: int):
         lab = L.tp_profile_label(i).decode()
         per.setdefault(lab, []).append(ev.elapsed_ms(i))
     ev.close()
-    return t0.elapsed_time(t1) / steps, wall, per
+    if not per_step:
+        return t0.elapsed_time(t1) / steps, wall, per
+    bounds = [t0] + marks + [t1]
+    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps)]
+    return t0.elapsed_time(t1) / steps, wall, per, step_ms
 
 
 def graph_timed(torch, step, steps: int) -> float:
@@ -157,10 +165,10 @@ def run_headline(tp, torch, wl, steps, warmup):
         tp.tp_mlp_bwd(X, W1, W2, A, H, dY, dX, dW1, dW2, ws)
 
     log(f"timing {wl.name}: warmup {warmup}, steps {steps}")
-    ms, wall, per = timed(tp, torch, step, steps, warmup, 8)
+    ms, wall, per, step_ms = timed(tp, torch, step, steps, warmup, 8, per_step=True)
     flops = 6 * gemm_flops(M, f, d)
     outs = {"A": A, "H": H, "Z": Z, "dX": dX, "dW1": dW1, "dW2": dW2}
-    return ms, wall, per, flops, inp, outs
+    return ms, wall, per, flops, inp, outs, step_ms
 
 
 KERNEL_SOURCES = ["common.hpp", "gemm.hpp", "epilogues.hpp", "gemm_dispatch.hpp", "mlp.hip"]
@@ -202,6 +210,54 @@ def roofline_for(per, M, d, f):
 
 
 # ------------------------------------------------------------- CPU baseline
+def step_percentiles(step_ms):
+    q = np.percentile(np.asarray(step_ms, dtype=np.float64), [10, 50, 90])
+    return {"p10": round(float(q[0]), 4), "median": round(float(q[1]), 4), "p90": round(float(q[2]), 4),
+            "steps": len(step_ms)}
+
+
+CLOCK_FILE = os.path.join(ROOT, "profiles", "clock_c5_mlp.json")
+
+
+def sustained_clock():
+    """The products' sustained GFX clock from the committed counter run
+    (GRBM_GUI_ACTIVE per XCD over each kernel's duration), or None when the
+    kernel sources changed since it was taken.  The GPU exposes no clock a
+    host thread can sample at this time scale (its metrics table refreshes
+    about once a second), so the clock comes from the counters."""
+    try:
+        with open(CLOCK_FILE) as fh:
+            c = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return {"mean_ghz": c["mean_clock_ghz"], "per_kernel_ghz": {k: v["clock_ghz"] for k, v in c["kernels"].items()},
+            "source": "profiles/clock_c5_mlp.json: " + c["method"]}
+
+
+def pct_at_clock(value):
+    c = sustained_clock()
+    return round(100 * value / (PEAK_BF16_TFLOPS * c["mean_ghz"] / 2.4), 2) if c else None
+
+
+def device_info(torch):
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
+            "sustained_clock": sustained_clock()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, inp, outs, torch, rows_n=None):
     """The fp64 oracle on the host's cores for the same step (all rows of
     the headline workload unless rows_n bounds it), timed; its outputs also
@@ -228,7 +284,7 @@ def cpu_baseline(wl, inp, outs, torch, rows_n=None):
         err["dW2"] = O.max_rel_err(host("dW2"), bw["dW2"])
     what = "the whole step" if rows_n is None else f"{len(rows)} of {wl.M} token rows"
     return ({"value": round(fl / secs / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-             "seconds": round(secs, 3),
+             "seconds": round(secs, 3), "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
              "sample": f"fp64 numpy oracle, shard fwd+bwd on {what} ({fl / 1e9:.0f} GFLOP); "
                        f"its outputs are compared with every GPU output tensor"}, err)
 
@@ -618,7 +674,7 @@ def main():
         print(json.dumps({args.only: extras[args.only](tp, torch, args.steps, args.warmup)}), flush=True)
         return
     wl = tpsynth.WORKLOADS["C5"]
-    ms, wall, per, flops, inp, outs = run_headline(tp, torch, wl, args.steps, args.warmup)
+    ms, wall, per, flops, inp, outs, step_ms = run_headline(tp, torch, wl, args.steps, args.warmup)
     if args.profile:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -649,6 +705,11 @@ def main():
                    "tp_degree": wl.n_shards, "f_local": wl.f_local,
                    "parallelism": "one TP shard on one GPU"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "peak_basis": "headline pct_of_peak is against the 2.5 PFLOP/s spec peak at 2.4 GHz; "
+                      "pct_of_peak_at_measured_clock scales that peak to the products' sustained clock",
+        "pct_of_peak_at_measured_clock": pct_at_clock(value),
+        "step_ms_percentiles": step_percentiles(step_ms),
+        "device": device_info(torch),
         "flop_per_step": flops,
         "wall_s_timed": round(wall, 3),
         "roofline": roofline_for(per, wl.M, wl.d, wl.f_local),
