@@ -27,6 +27,7 @@ __all__ = [
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtpshard.so")
+ABI_VERSION = 8          # TP_ABI_VERSION of include/tp_shard.h these wrappers are written for
 
 TP_DT_F32 = 0
 TP_DT_BF16 = 1
@@ -99,8 +100,14 @@ def lib() -> ctypes.CDLL:
                               "megatron_tensor_transformer_fwd_amd.build.build()")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in EXPORTS.items():
-            fn = getattr(L, name)
+            try:
+                fn = getattr(L, name)
+            except AttributeError:
+                raise ImportError(f"{LIB_PATH} does not export {name}: it is stale, rebuild it") from None
             fn.restype, fn.argtypes = res, args
+        if L.tp_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI version {L.tp_abi_version()}, the binding expects "
+                              f"{ABI_VERSION}: rebuild it")
         _LIB = L
     return _LIB
 

@@ -33,7 +33,9 @@ def test_header_and_binding_agree_and_library_exports_all():
 
 
 def test_version_and_strerror():
-    assert tp.tp_abi_version() == 8
+    hdr = open(HEADER).read()
+    declared = int(re.search(r"#define TP_ABI_VERSION (\d+)", hdr).group(1))
+    assert tp.tp_abi_version() == declared == tp.ABI_VERSION
     L = tp.lib()
     for code in (OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP):
         assert L.tp_strerror(code) and L.tp_strerror(code) != b"unknown status"
