@@ -91,8 +91,11 @@ __device__ __forceinline__ desc_t range_desc(const void* base, int64_t bytes) {
 }  // namespace attnb
 
 // D[bh, t] = sum_c dO[t, h*128 + c] * O[t, h*128 + c]; one thread per (t, h).
+// Also the forward's log-sum-exp in base 2, L2 = L log2(e), which the flash
+// kernels subtract inside exp2 without a multiply per score.
 __global__ void __launch_bounds__(256) attn_bwd_rowdot_kernel(const bf16* __restrict__ dO,
-                                                              const bf16* __restrict__ O, float* __restrict__ Dv,
+                                                              const bf16* __restrict__ O, const float* __restrict__ L,
+                                                              float* __restrict__ Dv, float* __restrict__ L2,
                                                               int64_t rows, int hl, int s, int64_t ld) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= rows * hl) return;
@@ -110,6 +113,7 @@ __global__ void __launch_bounds__(256) attn_bwd_rowdot_kernel(const bf16* __rest
   }
   const int64_t bi = row / s, t = row % s;
   Dv[(bi * hl + h) * s + t] = acc;
+  L2[(bi * hl + h) * s + t] = L[(bi * hl + h) * s + t] * attnb::kLog2e;   // log-sum-exp in base 2
 }
 
 // Key-tile kernel: dK and dV of 128 keys (four waves of 32) of one (batch,
@@ -122,7 +126,7 @@ __global__ void __launch_bounds__(256) attn_bwd_rowdot_kernel(const bf16* __rest
 template <class TO>
 __global__ void __launch_bounds__(256, 1)
 attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                    const bf16* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
+                    const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dv,
                     TO* __restrict__ dK, TO* __restrict__ dV, int nb, int hl, int group, int s, int causal,
                     float scale, int64_t ld_o, int64_t ld_g) {
   using namespace attnb;
@@ -168,7 +172,7 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
     const bf16* dorow = dO + ((int64_t)bi * s + q0) * ld_o + (int64_t)h * D;
     dma_rows<BQ>(range_desc(dorow, (int64_t)(s - q0 - 1) * ld_o * 2 + ROWB), (uint32_t)(ld_o * 2), st + QT, wave,
                  lane);
-    if (wave == 0) dma_vec(range_desc(L + (int64_t)bh * s + q0, (int64_t)(s - q0) * 4), st + 2 * QT, lane * 4u);
+    if (wave == 0) dma_vec(range_desc(L2 + (int64_t)bh * s + q0, (int64_t)(s - q0) * 4), st + 2 * QT, lane * 4u);
     if (wave == 1) dma_vec(range_desc(Dv + (int64_t)bh * s + q0, (int64_t)(s - q0) * 4), st + 2 * QT + VEC, lane * 4u);
   };
 
@@ -188,38 +192,46 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
     const float* Ds = Ls + BQ;
 
     // S[key][q] and dP[key][q] for two 32-query blocks (four independent chains)
-    f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+    f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Qs, qb * 32, kk, lane), kf[kk], sacc[qb], 0, 0, 0);
-        pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(dOs, qb * 32, kk, lane), vf[kk], pacc[qb], 0, 0, 0);
+        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Qs, qb * 32, kk, lane), kf[kk],
+                                                           kk ? sacc[qb] : f32x16{}, 0, 0, 0);
+        pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(dOs, qb * 32, kk, lane), vf[kk],
+                                                           kk ? pacc[qb] : f32x16{}, 0, 0, 0);
       }
-    // register r of block qb: query q0 + qb*32 + 8 (r/4) + 4 g + r%4
+    // register r of block qb: query q0 + qb*32 + 8 (r/4) + 4 g + r%4.  The
+    // mask is evaluated only where some (key, query) pair of the wave can be
+    // out of range: past the sequence, or a key after a query (causal).
     bf16x8 pf[2][2], sf[2][2];
+    auto softmax = [&]<bool MASK>() {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int ql = qb * 32 + 8 * r4 + 4 * g;      // first of four consecutive queries
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int ql = qb * 32 + 8 * r4 + 4 * g;    // first of four consecutive queries
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e, q = q0 + ql + e;
-          const bool ok = q < s && (!causal || key <= q);
-          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], sl2, -l4[e] * kLog2e)) : 0.f;
-          sacc[qb][r] = p;
-          pacc[qb][r] = p * (pacc[qb][r] - d4[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e, q = q0 + ql + e;
+            float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], sl2, -l4[e]));
+            if constexpr (MASK) p = (q < s && (!causal || key <= q)) ? p : 0.f;
+            sacc[qb][r] = p;
+            pacc[qb][r] = p * (pacc[qb][r] - d4[e]);
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          pf[qb][hh] = pack8(sacc[qb], 8 * hh);
+          sf[qb][hh] = pack8(pacc[qb], 8 * hh);
         }
       }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        pf[qb][hh] = pack8(sacc[qb], 8 * hh);
-        sf[qb][hh] = pack8(pacc[qb], 8 * hh);
-      }
-    }
+    };
+    if (q0 + BQ > s || (causal && kw + 31 > q0)) softmax.template operator()<true>();
+    else softmax.template operator()<false>();
     // dV[key][d] += P^T dO, dK[key][d] += dS^T Q (four d blocks each, interleaved)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -258,7 +270,7 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
 // dQ += dS K needs K transposed in the key order of the dS registers.
 __global__ void __launch_bounds__(256, 2)
 attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                   const bf16* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
+                   const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dv,
                    bf16* __restrict__ dQ, int nb, int hl, int group, int s, int causal, float scale,
                    int64_t ld_o, int64_t ld_g) {
   using namespace attnb;
@@ -293,7 +305,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     }
   }
   const bool live = qme < s;
-  const float l2 = live ? L[(int64_t)bh * s + qme] * kLog2e : 0.f;
+  const float l2 = live ? L2[(int64_t)bh * s + qme] : 0.f;
   const float dq = live ? Dv[(int64_t)bh * s + qme] : 0.f;
 
   const int kv_end = causal ? min(s, q0 + BQ) : s;
@@ -318,28 +330,36 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     if (causal && kv0 > qw + 31) continue;
     const char* Ks = smem + (t & 1) * STAGE;
     const char* Vs = Ks + KT;
-    f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+    f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Ks, kb * 32, kk, lane), qf[kk], sacc[kb], 0, 0, 0);
-        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Vs, kb * 32, kk, lane), of[kk], pacc[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Ks, kb * 32, kk, lane), qf[kk],
+                                                           kk ? sacc[kb] : f32x16{}, 0, 0, 0);
+        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Vs, kb * 32, kk, lane), of[kk],
+                                                           kk ? pacc[kb] : f32x16{}, 0, 0, 0);
       }
-    // register r of block kb: key kv0 + kb*32 + 8 (r/4) + 4 g + r%4 of query qme
+    // register r of block kb: key kv0 + kb*32 + 8 (r/4) + 4 g + r%4 of query
+    // qme.  The mask is evaluated only where a key of the chunk can be past
+    // the sequence or (causal) after a query of the wave.
     bf16x8 sf[2][2];
-    const int lim = (causal ? min(qme, s - 1) : s - 1) - (kv0 + 4 * g);
+    auto softmax = [&]<bool MASK>() {
+      const int lim = (causal ? min(qme, s - 1) : s - 1) - (kv0 + 4 * g);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool ok = kb * 32 + 8 * (r >> 2) + (r & 3) <= lim;
-        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -l2)) : 0.f;
-        pacc[kb][r] = p * (pacc[kb][r] - dq);
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -l2));
+          if constexpr (MASK) p = (kb * 32 + 8 * (r >> 2) + (r & 3) <= lim) ? p : 0.f;
+          pacc[kb][r] = p * (pacc[kb][r] - dq);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) sf[kb][hh] = pack8(pacc[kb], 8 * hh);
       }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) sf[kb][hh] = pack8(pacc[kb], 8 * hh);
-    }
+    };
+    if (kv0 + BKV > s || (causal && kv0 + BKV - 1 > qw)) softmax.template operator()<true>();
+    else softmax.template operator()<false>();
     // dQ[q][d] += dS K (four d blocks, interleaved)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -427,7 +447,7 @@ static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 // heads the per-query-head fp32 dK and dV contributions [M x N] each, then
 // the split-K partials of dW_O.
 struct AttnBwdLayout {
-  size_t dO, dQKV, Wcat, Dv, part, split, total;
+  size_t dO, dQKV, Wcat, Dv, L2, part, split, total;
 };
 
 static AttnBwdLayout attn_bwd_layout(int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv,
@@ -439,7 +459,8 @@ static AttnBwdLayout attn_bwd_layout(int64_t b, int64_t s, int64_t d, int64_t h_
   l.dQKV = l.dO + up256((size_t)M * N * 2);
   l.Wcat = l.dQKV + up256((size_t)M * Nt * 2);
   l.Dv = l.Wcat + up256((size_t)d * Nt * 2);
-  l.part = l.Dv + up256((size_t)b * h_local * s * 4);
+  l.L2 = l.Dv + up256((size_t)b * h_local * s * 4);
+  l.part = l.L2 + up256((size_t)b * h_local * s * 4);
   l.split = l.part + (h_kv != h_local ? 2 * up256((size_t)M * N * 4) : 0);
   l.total = l.split + (pwo.split > 1 ? up256((size_t)pwo.split * N * d * 4) : 0);
   return l;
@@ -464,6 +485,7 @@ hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
   bf16* dQKV = reinterpret_cast<bf16*>(w + lay.dQKV);  // [M x Nt]: dQ | dK | dV
   bf16* Wcat = reinterpret_cast<bf16*>(w + lay.Wcat);  // [d x Nt]: W_Q | W_K | W_V
   float* Dv = reinterpret_cast<float*>(w + lay.Dv);
+  float* L2 = reinterpret_cast<float*>(w + lay.L2);
   float* part = reinterpret_cast<float*>(w + lay.part);
   float* split_ws = reinterpret_cast<float*>(w + lay.split);
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d_head);
@@ -481,10 +503,10 @@ hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
                             return launch_gemm<false, false, false>(st, "attn_bwd.ot_dy", p, e, g);
                           }));
   }
-  {  // D = rowsum(dO * O)
+  {  // D = rowsum(dO * O); L in base 2
     const int64_t n = M * h_local;
     TPK_TRY(launch("attn_bwd.rowdot", attn_bwd_rowdot_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st,
-                   (const bf16*)dO, static_cast<const bf16*>(O), Dv, M, (int)h_local, (int)s, N));
+                   (const bf16*)dO, static_cast<const bf16*>(O), L, Dv, L2, M, (int)h_local, (int)s, N));
   }
   const bf16* q = static_cast<const bf16*>(Q);
   const bf16* k = static_cast<const bf16*>(K);
@@ -493,12 +515,12 @@ hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
   const unsigned grid = (unsigned)(((s + 127) / 128) * nbh);
   if (group == 1) {  // dK, dV straight into their columns of [dQ | dK | dV]
     TPK_TRY(launch("attn_bwd.dkv", attn_bwd_dkv_kernel<bf16>, dim3(grid), dim3(256), st, q, k, v, (const bf16*)dO,
-                   L, (const float*)Dv, dQKV + N, dQKV + 2 * N, (int)b, (int)h_local, 1, (int)s, causal, sc, N, Nt));
+                   (const float*)L2, (const float*)Dv, dQKV + N, dQKV + 2 * N, (int)b, (int)h_local, 1, (int)s, causal, sc, N, Nt));
   } else {  // per-query-head contributions, then the ordered sum over each group
     float* pk = part;
     float* pv = reinterpret_cast<float*>(reinterpret_cast<char*>(part) + up256((size_t)M * N * 4));
     TPK_TRY(launch("attn_bwd.dkv", attn_bwd_dkv_kernel<float>, dim3(grid), dim3(256), st, q, k, v, (const bf16*)dO,
-                   L, (const float*)Dv, pk, pv, (int)b, (int)h_local, group, (int)s, causal, sc, N, N));
+                   (const float*)L2, (const float*)Dv, pk, pv, (int)b, (int)h_local, group, (int)s, causal, sc, N, N));
     const int64_t n = M * Nkv / 8;
     const dim3 g2((unsigned)((n + 255) / 256));
     TPK_TRY(launch("attn_bwd.group_sum", attn_bwd_group_sum_kernel, g2, dim3(256), st, (const float*)pk, dQKV + N, M,
@@ -506,7 +528,8 @@ hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
     TPK_TRY(launch("attn_bwd.group_sum", attn_bwd_group_sum_kernel, g2, dim3(256), st, (const float*)pv,
                    dQKV + N + Nkv, M, (int)h_local, group, Nt));
   }
-  TPK_TRY(launch("attn_bwd.dq", attn_bwd_dq_kernel, dim3(grid), dim3(256), st, q, k, v, (const bf16*)dO, L,
+  TPK_TRY(launch("attn_bwd.dq", attn_bwd_dq_kernel, dim3(grid), dim3(256), st, q, k, v, (const bf16*)dO,
+                 (const float*)L2,
                  (const float*)Dv, dQKV, (int)b, (int)h_local, group, (int)s, causal, sc, N, Nt));
   {  // [W_Q | W_K | W_V]
     const int64_t n = d * (Nt / 8);
