@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtpshard.so")
 ARCH = "gfx950"
 
-SOURCES = ["shard_reduce.hip", "mlp.hip", "swiglu.hip", "attention.hip", "attention_bwd.hip", "sp.hip", "vocab.hip", "tp_shard.cpp"]
+SOURCES = ["shard_reduce.hip", "mlp.hip", "swiglu.hip", "attention.hip", "attention_bwd.hip", "attention_bwd_core.hip", "sp.hip", "vocab.hip", "tp_shard.cpp"]
 
 
 def hipcc() -> str:
@@ -38,9 +38,16 @@ def common_flags():
     ]
 
 
+# Per-source code-generation options.  The flash-attention backward kernels
+# keep their MFMA accumulators in architectural VGPRs (the VALU softmax reads
+# them directly); the default accumulation-register form made the compiler
+# copy every score and fragment between the two register files.
+SOURCE_FLAGS = {"attention_bwd_core.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags() + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

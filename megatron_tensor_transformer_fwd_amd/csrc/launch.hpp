@@ -39,6 +39,15 @@ hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
                            int64_t d_head, int causal, float scale,
                            const void* X, const void* Wq, const void* Wk, const void* Wv,
                            const void* Wo, void* Q, void* K, void* V, void* O, void* Z, float* L);
+// Flash-attention backward kernels (attention_bwd_core.hip); bf16 tensors.
+hipError_t launch_attn_bwd_rowdot(hipStream_t st, const void* dO, const void* O, const float* L, float* Dv,
+                                  float* L2, int64_t rows, int hl, int s, int64_t ld);
+hipError_t launch_attn_bwd_flash(hipStream_t st, int b, int hl, int group, int s, int causal, float scale,
+                                 const void* Q, const void* K, const void* V, const void* dO, const float* L2,
+                                 const float* Dv, int64_t ld_o, void* dQKV, int64_t ld_g, int64_t n_q,
+                                 int64_t n_kv, float* part_k, float* part_v);
+hipError_t launch_attn_concat3(hipStream_t st, const void* A, const void* B, const void* C, void* out, int64_t rows,
+                               int64_t n0, int64_t n1);
 size_t attn_bwd_ws_bytes(int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv, int64_t d_head);
 hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv,
                            int64_t d_head, int causal, float scale,
