@@ -29,11 +29,13 @@ struct EpiF32Parts {
 static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace: dO [M x N] bf16, [dQ | dK | dV] [M x (N + 2 Nkv)] bf16,
-// [W_Q | W_K | W_V] [d x (N + 2 Nkv)] bf16, D [b h s] fp32, with grouped K/V
-// heads the per-query-head fp32 dK and dV contributions [M x N] each, then
-// the split-K partials of dW_O.
+// [W_Q | W_K | W_V] [d x (N + 2 Nkv)] bf16, D and L2 [b h s] fp32, with
+// grouped K/V heads the per-query-head fp32 dK and dV contributions [M x N]
+// each, then the split-K partials of dW_O, then the fp32 partial tiles of the
+// weight-gradient product's split last round.
 struct AttnBwdLayout {
-  size_t dO, dQKV, Wcat, Dv, L2, part, split, total;
+  size_t dO, dQKV, Wcat, Dv, L2, part, split, tail, total;
+  GemmPlan wqkv;     // [dW_Q | dW_K | dW_V] = X^T [dQ | dK | dV]
 };
 
 static AttnBwdLayout attn_bwd_layout(int64_t b, int64_t s, int64_t d, int64_t h_local, int64_t h_kv,
@@ -48,7 +50,9 @@ static AttnBwdLayout attn_bwd_layout(int64_t b, int64_t s, int64_t d, int64_t h_
   l.L2 = l.Dv + up256((size_t)b * h_local * s * 4);
   l.part = l.L2 + up256((size_t)b * h_local * s * 4);
   l.split = l.part + (h_kv != h_local ? 2 * up256((size_t)M * N * 4) : 0);
-  l.total = l.split + (pwo.split > 1 ? up256((size_t)pwo.split * N * d * 4) : 0);
+  l.tail = l.split + (pwo.split > 1 ? up256((size_t)pwo.split * N * d * 4) : 0);
+  l.wqkv = plan_gemm(d, Nt, M, false, false, true);
+  l.total = l.tail + up256(gemm_tail_ws_bytes(l.wqkv, d, Nt));
   return l;
 }
 
@@ -106,7 +110,8 @@ hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
   {  // [dW_Q | dW_K | dW_V] = X^T [dQ | dK | dV]
     GemmParams p = make_params(d, Nt, make_seg(X, d, M * d, dQKV, Nt, M * Nt, M));
     EpiF32Parts e{{dWq, dWk, dWv}, N, Nkv};
-    TPK_TRY((launch_gemm<false, false, false>(st, "attn_bwd.xt_dqkv", p, e, plan_gemm(d, Nt, M, false, false))));
+    TPK_TRY((launch_gemm<false, false, false>(st, "attn_bwd.xt_dqkv", p, e, lay.wqkv, 1,
+                                              reinterpret_cast<float*>(w + lay.tail))));
   }
   return hipSuccess;
 }

@@ -56,6 +56,7 @@ struct GemmParams {
   const bf16* Bz[3];   // batched products: per-batch right operand of segment 0 (or NULL)
   int tiles_m, tiles_n;
   int split_k;         // K-tile ranges over blockIdx.y
+  int tile_base;       // the grid covers tiles tile_base .. tile_base + gridDim.x - 1 of the grouped order
 };
 
 template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NSA_ = 2, int NSB_ = 2, int SPA_ = 1,
@@ -183,19 +184,35 @@ __device__ __forceinline__ void dma_lds_barrier() {
 // ----------------------------------------------------------------------------
 // Workgroup -> output tile: XCD-contiguous, then grouped along m.
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n,
-                                            int& tm, int& tn) {
-  constexpr int NXCD = 8, GROUP = 8;
-  const int q = nblocks / NXCD, r = nblocks % NXCD;
-  const int xcd = bid % NXCD, local = bid / NXCD;
-  const int t = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
-  const int per_group = GROUP * tiles_n;
+constexpr int kTileGroup = 8;
+
+// Tile at position t of the grouped order: groups of 8 m-tiles, and inside a
+// group the 8 m-tiles of one n-tile after another.
+__host__ __device__ inline void tile_of(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = kTileGroup * tiles_n;
   const int g = t / per_group;
-  const int first_m = g * GROUP;
-  const int gsize = min(tiles_m - first_m, GROUP);
+  const int first_m = g * kTileGroup;
+  const int gsize = min(tiles_m - first_m, kTileGroup);
   const int w = t % per_group;
   tm = first_m + w % gsize;
   tn = w / gsize;
+}
+
+// Position of tile (tm, tn) in the grouped order (the inverse of tile_of).
+__host__ __device__ inline int position_of(int tm, int tn, int tiles_m, int tiles_n) {
+  const int g = tm / kTileGroup;
+  const int first_m = g * kTileGroup;
+  const int gsize = min(tiles_m - first_m, kTileGroup);
+  return g * kTileGroup * tiles_n + tn * gsize + (tm - first_m);
+}
+
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int base,
+                                            int& tm, int& tn) {
+  constexpr int NXCD = 8;
+  const int q = nblocks / NXCD, r = nblocks % NXCD;
+  const int xcd = bid % NXCD, local = bid / NXCD;
+  const int t = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
+  tile_of(base + t, tiles_m, tiles_n, tm, tn);
 }
 
 template <int N, class F>
@@ -493,7 +510,7 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.tile_base, tm, tn);
   const int64_t m0 = (int64_t)tm * Cfg::BM;
   const int64_t n0 = (int64_t)tn * BNL;
   const int zb = blockIdx.z;

@@ -7,6 +7,12 @@
 #include "launch.hpp"
 #include "profile.hpp"
 
+#define TPK_TRY(expr)                         \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return e_;          \
+  } while (0)
+
 namespace tpk {
 
 // Tile shapes.  L: 256x256, 8 waves of 128x64 (two per SIMD), the shape for
@@ -32,6 +38,7 @@ enum { CFG_L = 0, CFG_M = 1, CFG_S = 2 };
 struct GemmPlan {
   int cfg;
   int split;
+  int tail = 0;   // > 1: the last partial round of 256x256 tiles is split along K this many ways
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -60,7 +67,15 @@ inline int64_t tiles_for(int cfg, int64_t M, int64_t N, bool dual) {
 // 4 TB/s).  Splitting is allowed only where the caller has an fp32 workspace
 // (weight gradients).  Near-ties go to the larger tile and the smaller split.
 // Dual-B products always take the L shape (two 128-column sub-tiles).
-inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow_split) {
+//
+// With allow_tail (the caller has a workspace for it), the 256x256 shape may
+// also run its whole rounds as usual and split the tiles of a last round
+// that fills at most half the CUs along K (tail = 2..8 ways, at least 8
+// k-tiles each): the round then costs a tile's work / tail, plus a pass that
+// writes and reads the fp32 partial tiles and applies the epilogue.
+constexpr int kTailMaxSplit = 8;
+
+inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow_split, bool allow_tail = false) {
   constexpr double CUS = 256.0, CU_FLOPS = 4.4e12, REDUCE_BPS = 4.0e12, LAUNCH_S = 4e-6;
   const double rate[3] = {1.0, TPK_RATE_M, TPK_RATE_S};
   GemmPlan best{CFG_L, 1};
@@ -81,8 +96,68 @@ inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow
         best = GemmPlan{cfg, s};
       }
     }
+    if (cfg == CFG_L && allow_tail && !dual) {
+      const int64_t full = tiles / 256 * 256, rem = tiles - full;
+      const int64_t kt = cdiv(K, 64);
+      int ways = rem > 0 ? (int)std::min<int64_t>(kTailMaxSplit, 256 / rem) : 0;
+      while (ways > 1 && kt / ways < 8) --ways;
+      if (ways > 1) {
+        const double tile_t = 2.0 * (double)(bm * bn * K) / CU_FLOPS;
+        const double fix_bytes = (double)rem * ways * bm * bn * 4.0 * 2.0 + (double)rem * bm * bn * 4.0;
+        const double t = (double)(full / 256) * tile_t + tile_t / ways + fix_bytes / REDUCE_BPS + 2 * LAUNCH_S;
+        if (t < best_t * 0.97) {
+          best_t = t;
+          best = GemmPlan{CFG_L, 1, ways};
+        }
+      }
+    }
   }
   return best;
+}
+
+// fp32 workspace the tail split of `plan` needs (0 without one).
+inline size_t gemm_tail_ws_bytes(const GemmPlan& plan, int64_t M, int64_t N) {
+  if (plan.tail <= 1) return 0;
+  const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
+  return (size_t)(tiles % 256) * plan.tail * 256 * 256 * 4;
+}
+
+// Partial sums of the split tail tiles: the tile at grouped position base + j,
+// split s, is stored densely (BM x BN floats, row-major) at ws + (s * count + j) * BM * BN.
+template <int BM, int BN>
+struct EpiTilePartial {
+  static constexpr int NOUT = 1;
+  template <int O> using OutT = float;
+  float* ws;
+  int count, base, tiles_m, tiles_n;
+  template <int O> __device__ __forceinline__ bool has_out() const { return true; }
+  template <int O> __device__ __forceinline__ float* out_ptr(int64_t m, int64_t n, int split, int) const {
+    const int j = position_of((int)(m / BM), (int)(n / BN), tiles_m, tiles_n) - base;
+    return ws + ((int64_t)split * count + j) * (BM * BN) + (m % BM) * BN + (n % BN);
+  }
+  template <int O> __device__ __forceinline__ f32x4 value(int64_t, int64_t, f32x4 v) const { return v; }
+};
+
+// Sum of the tail tiles' partials in split order, then the product's own
+// epilogue; one thread per four consecutive outputs.
+template <int BM, int BN, class Epi>
+__global__ void __launch_bounds__(256)
+gemm_tail_fixup_kernel(const float* __restrict__ ws, int splits, int count, int base, int tiles_m, int tiles_n,
+                       int M, int N, Epi epi) {
+  constexpr int QPT = BM * BN / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)count * QPT) return;
+  const int j = (int)(i / QPT), q = (int)(i % QPT);
+  int tm, tn;
+  tile_of(base + j, tiles_m, tiles_n, tm, tn);
+  const int r = q / (BN / 4), c = (q % (BN / 4)) * 4;
+  const int64_t m = (int64_t)tm * BM + r, n = (int64_t)tn * BN + c;
+  if (m >= M || n >= N) return;
+  const float* p = ws + (int64_t)j * (BM * BN) + r * BN + c;
+  f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  for (int s = 1; s < splits; ++s)
+    v += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + (int64_t)s * count * (BM * BN)));
+  epi_store_direct(epi, m, n, v, 0, 0);
 }
 
 template <class Cfg, bool A_KM, bool B_KM, bool DUAL, class Epi>
@@ -94,9 +169,44 @@ hipError_t launch_gemm_cfg(hipStream_t st, const char* label, GemmParams p, cons
   return launch(label, gemm_bf16_kernel<Cfg, A_KM, B_KM, DUAL, Epi>, grid, dim3(Cfg::NT), st, p, epi);
 }
 
+// The whole rounds of 256x256 tiles as usual, then the remaining tiles split
+// `plan.tail` ways along K into the fp32 workspace, then the fixup pass.
+template <bool A_KM, bool B_KM, class Epi>
+hipError_t launch_gemm_tail(hipStream_t st, const char* label, GemmParams p, const Epi& epi, GemmPlan plan,
+                            float* tail_ws) {
+  p.tiles_m = (int)cdiv(p.M, CfgL::BM);
+  p.tiles_n = (int)cdiv(p.N, CfgL::BN);
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int full = tiles / 256 * 256, rem = tiles - full;
+  if (full > 0) {
+    GemmParams p1 = p;
+    p1.split_k = 1;
+    p1.tile_base = 0;
+    TPK_TRY(launch(label, gemm_bf16_kernel<CfgL, A_KM, B_KM, false, Epi>, dim3((unsigned)full), dim3(CfgL::NT), st,
+                   p1, epi));
+  }
+  GemmParams p2 = p;
+  p2.split_k = plan.tail;
+  p2.tile_base = full;
+  EpiTilePartial<CfgL::BM, CfgL::BN> e2{tail_ws, rem, full, p.tiles_m, p.tiles_n};
+  TPK_TRY(launch("gemm.tail_split", gemm_bf16_kernel<CfgL, A_KM, B_KM, false, EpiTilePartial<CfgL::BM, CfgL::BN>>,
+                 dim3((unsigned)rem, (unsigned)plan.tail), dim3(CfgL::NT), st, p2, e2));
+  const int64_t quads = (int64_t)rem * (CfgL::BM * CfgL::BN / 4);
+  return launch("gemm.tail_fixup", gemm_tail_fixup_kernel<CfgL::BM, CfgL::BN, Epi>,
+                dim3((unsigned)cdiv(quads, 256)), dim3(256), st, (const float*)tail_ws, plan.tail, rem, full,
+                p.tiles_m, p.tiles_n, p.M, p.N, epi);
+}
+
 template <bool A_KM, bool B_KM, bool DUAL, class Epi>
 hipError_t launch_gemm(hipStream_t st, const char* label, GemmParams p, const Epi& epi, GemmPlan plan,
-                       int nz = 1) {
+                       int nz = 1, float* tail_ws = nullptr) {
+  if constexpr (!DUAL && !epi_row_reduce<Epi>::value) {
+    if (plan.tail > 1) {
+      if (nz != 1 || plan.cfg != CFG_L || plan.split != 1 || !tail_ws) return hipErrorInvalidValue;
+      return launch_gemm_tail<A_KM, B_KM>(st, label, p, epi, plan, tail_ws);
+    }
+  }
+  if (plan.tail > 1) return hipErrorInvalidValue;
   p.split_k = plan.split;
   switch (plan.cfg) {
     case CFG_L: return launch_gemm_cfg<CfgL, A_KM, B_KM, DUAL, Epi>(st, label, p, epi, nz);
@@ -168,12 +278,6 @@ inline GemmParamsF32 make_params_f32(int64_t M, int64_t N, GemmSegF32 s0) {
   p.split_k = 1;
   return p;
 }
-
-#define TPK_TRY(expr)                         \
-  do {                                        \
-    hipError_t e_ = (expr);                   \
-    if (e_ != hipSuccess) return e_;          \
-  } while (0)
 
 // fp32 weight gradient C[Mo x No] = A^T B over K tokens, through the split-K
 // workspace when the plan splits.

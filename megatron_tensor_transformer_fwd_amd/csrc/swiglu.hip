@@ -31,22 +31,29 @@ static hipError_t swiglu_fwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t 
 }
 
 struct SwigluBwdPlan {
-  GemmPlan dW2;
-  size_t dGU_bytes, split_bytes;
+  GemmPlan dH, dW2, dW13;
+  size_t dGU_bytes, split_bytes, tail_bytes;
 };
 
+// Workspace: [dG | dU], then the split-K partials of dW2, then the fp32
+// partial tiles of a split last round (shared by the dH and [dW1 | dW3]
+// products, which run one after the other).
 static SwigluBwdPlan swiglu_bwd_plan(int dt, int64_t M, int64_t d, int64_t f) {
   SwigluBwdPlan pl;
   const size_t es = dt == DT_BF16 ? 2 : 4;
   pl.dGU_bytes = align256((size_t)M * 2 * f * es);
-  pl.dW2 = dt == DT_BF16 ? plan_gemm(f, d, M, false, true) : GemmPlan{CFG_S, 1};
+  const bool bf = dt == DT_BF16;
+  pl.dH = bf ? plan_gemm(M, f, d, false, false, true) : GemmPlan{CFG_S, 1};
+  pl.dW2 = bf ? plan_gemm(f, d, M, false, true) : GemmPlan{CFG_S, 1};
+  pl.dW13 = bf ? plan_gemm(d, 2 * f, M, false, false, true) : GemmPlan{CFG_S, 1};
   pl.split_bytes = pl.dW2.split > 1 ? align256((size_t)pl.dW2.split * f * d * 4) : 0;
+  pl.tail_bytes = align256(std::max(gemm_tail_ws_bytes(pl.dH, M, f), gemm_tail_ws_bytes(pl.dW13, d, 2 * f)));
   return pl;
 }
 
 size_t swiglu_bwd_ws_bytes(int dt, int64_t M, int64_t d, int64_t f) {
   const SwigluBwdPlan pl = swiglu_bwd_plan(dt, M, d, f);
-  return pl.dGU_bytes + pl.split_bytes;
+  return pl.dGU_bytes + pl.split_bytes + pl.tail_bytes;
 }
 
 static hipError_t swiglu_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t f,
@@ -56,10 +63,11 @@ static hipError_t swiglu_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t 
   const SwigluBwdPlan pl = swiglu_bwd_plan(DT_BF16, M, d, f);
   bf16* dGU = static_cast<bf16*>(ws);
   float* split_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.dGU_bytes);
+  float* tail_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.dGU_bytes + pl.split_bytes);
   {  // dH = dY W2^T -> dG, dU
     GemmParams p = make_params(M, f, make_seg(dY, d, M * d, W2, d, f * d, d));
     EpiDSwiGLU<bf16> e{static_cast<const bf16*>(G), static_cast<const bf16*>(U), dGU, f};
-    TPK_TRY((launch_gemm<true, true, false>(st, "swiglu_bwd.dyw2t_dswiglu", p, e, plan_gemm(M, f, d, false, false))));
+    TPK_TRY((launch_gemm<true, true, false>(st, "swiglu_bwd.dyw2t_dswiglu", p, e, pl.dH, 1, tail_ws)));
   }
   {  // dW2 = H^T dY
     GemmParams p = make_params(f, d, make_seg(H, f, M * f, dY, d, M * d, M));
@@ -82,7 +90,7 @@ static hipError_t swiglu_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t 
   {  // [dW1 | dW3] = X^T [dG | dU]
     GemmParams p = make_params(d, 2 * f, make_seg(X, d, M * d, dGU, 2 * f, M * 2 * f, M));
     EpiF32Halves e{dW1, dW3, f};
-    TPK_TRY((launch_gemm<false, false, false>(st, "swiglu_bwd.xtdgu", p, e, plan_gemm(d, 2 * f, M, false, false))));
+    TPK_TRY((launch_gemm<false, false, false>(st, "swiglu_bwd.xtdgu", p, e, pl.dW13, 1, tail_ws)));
   }
   return hipSuccess;
 }
