@@ -646,7 +646,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
-    ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--only", choices=["C2", "C3", "C4", "G1", "S1", "E1"],
                     help="for kernel traces: time only this workload (--steps/--warmup apply) and print "
                          "its JSON object")
@@ -728,7 +728,7 @@ def main():
         wls = {}
         for name, fn in extras.items():
             log(f"timing {name}")
-            wls[name] = fn(tp, torch, args.extra_steps, 2)
+            wls[name] = fn(tp, torch, args.extra_steps, 5)
             torch.cuda.empty_cache()
         result["workloads"] = wls
     print(json.dumps(result), flush=True)
