@@ -6,6 +6,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <vector>
+
 namespace tpk {
 
 struct ProfileState {
@@ -13,8 +15,7 @@ struct ProfileState {
   hipEvent_t const* stop = nullptr;
   int capacity = 0;
   int count = 0;
-  static constexpr int kMaxLabels = 1024;
-  const char* labels[kMaxLabels] = {};
+  std::vector<const char*> labels;   // one per event pair, sized at arming
 };
 
 ProfileState& profile_state();   // thread-local, defined in tp_shard.cpp
@@ -24,7 +25,7 @@ inline hipError_t launch(const char* label, F kernel, dim3 grid, dim3 block, hip
   ProfileState& ps = profile_state();
   if (ps.start && ps.count < ps.capacity) {
     hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ps.start[ps.count], ps.stop[ps.count], 0, args...);
-    if (ps.count < ProfileState::kMaxLabels) ps.labels[ps.count] = label;
+    ps.labels[ps.count] = label;
     ++ps.count;
   } else {
     hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);

@@ -158,6 +158,7 @@ int tp_profile_begin(void* const* start_events, void* const* stop_events, int ca
   tpk::ProfileState& ps = tpk::profile_state();
   ps.start = reinterpret_cast<hipEvent_t const*>(start_events);
   ps.stop = reinterpret_cast<hipEvent_t const*>(stop_events);
+  ps.labels.assign((size_t)capacity, nullptr);
   ps.capacity = capacity;
   ps.count = 0;
   return ok();
@@ -173,7 +174,7 @@ int tp_profile_end(void) {
 
 const char* tp_profile_label(int i) {
   const tpk::ProfileState& ps = tpk::profile_state();
-  if (i < 0 || i >= ps.count || i >= tpk::ProfileState::kMaxLabels || !ps.labels[i]) return "";
+  if (i < 0 || i >= ps.count || i >= (int)ps.labels.size() || !ps.labels[i]) return "";
   return ps.labels[i];
 }
 
