@@ -112,6 +112,32 @@ def timed(tp, torch, step, steps: int, warmup: int, kernels_per_step: int, per_s
     return t0.elapsed_time(t1) / steps, wall, per, step_ms
 
 
+_COPY_GBPS = None
+
+
+def copy_ceiling_gbps(torch) -> float:
+    """Practical HBM ceiling of this GPU: a plain 1 GiB device-to-device
+    copy (torch copy_, reads 1 GiB and writes 1 GiB; 4x the 256 MB Infinity
+    Cache, so it streams from HBM), best of 3, in GB/s of bytes moved."""
+    global _COPY_GBPS
+    if _COPY_GBPS is None:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        best = None
+        for _ in range(4):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            dst.copy_(src)
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b)
+            best = t if best is None else min(best, t)
+        del src, dst
+        _COPY_GBPS = round(2 * (1 << 30) / best / 1e6, 1)
+    return _COPY_GBPS
+
+
 def graph_timed(torch, step, steps: int) -> float:
     """ms per step of the same step captured once as a HIP graph (through
     torch.cuda.CUDAGraph, on a side stream of default priority) and replayed
@@ -348,7 +374,7 @@ def run_c2(tp, torch, steps, warmup):
             "shard_reduce": {"bytes": rbytes, "warm_ms": round(red_ms, 4) if red_ms else None,
                              "warm_GBps": round(rbytes / red_ms / 1e6, 1) if red_ms else None,
                              "cold_ms": round(cold_ms, 4), "cold_GBps": round(rbytes / cold_ms / 1e6, 1),
-                             "peak_GBps": PEAK_HBM_GBS},
+                             "peak_GBps": PEAK_HBM_GBS, "copy_GBps": copy_ceiling_gbps(torch)},
             "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in per.items()}}
 
 
@@ -563,13 +589,16 @@ def run_s1(tp, torch, steps, warmup):
                         "the 8 shards' input gradients on the stripe + all-gather of dy",
             "ms_per_step": round(ms, 4), "graph_ms_per_step": round(gms, 4), "bwd_ms_per_step": round(ms_b, 4),
             "ln_bwd": {"bytes": bwd_bytes, "warm_ms": round(bwd_ms, 4) if bwd_ms else None,
-                       "warm_GBps": gbs(bwd_bytes, bwd_ms), "peak_GBps": PEAK_HBM_GBS},
+                       "warm_GBps": gbs(bwd_bytes, bwd_ms), "peak_GBps": PEAK_HBM_GBS,
+                       "copy_GBps": copy_ceiling_gbps(torch)},
             "rs_ln": {"bytes": rs_bytes, "warm_ms": round(rs_ms, 4) if rs_ms else None,
                       "warm_GBps": gbs(rs_bytes, rs_ms), "cold_ms": round(min(cold_rs), 4),
-                      "cold_GBps": gbs(rs_bytes, min(cold_rs)), "peak_GBps": PEAK_HBM_GBS},
+                      "cold_GBps": gbs(rs_bytes, min(cold_rs)), "peak_GBps": PEAK_HBM_GBS,
+                      "copy_GBps": copy_ceiling_gbps(torch)},
             "all_gather": {"bytes": ag_bytes, "warm_ms": round(ag_ms, 4) if ag_ms else None,
                            "warm_GBps": gbs(ag_bytes, ag_ms), "cold_ms": round(min(cold_ag), 4),
-                           "cold_GBps": gbs(ag_bytes, min(cold_ag)), "peak_GBps": PEAK_HBM_GBS},
+                           "cold_GBps": gbs(ag_bytes, min(cold_ag)), "peak_GBps": PEAK_HBM_GBS,
+                           "copy_GBps": copy_ceiling_gbps(torch)},
             "kernels_ms": {key: round(sum(v) / len(v), 4) for key, v in list(per.items()) +
                            [("bwd." + kk, vv) for kk, vv in per_b.items()]}}
 
@@ -639,6 +668,16 @@ def run_e1(tp, torch, steps, warmup):
             "kernels_ms": {key: round(sum(v) / len(v), 4) for key, v in per.items()}}
 
 
+def calibration_copy(torch):
+    """One plain 1 GiB device copy, the last kernel of a counter run: its
+    FETCH_SIZE / WRITE_SIZE readings calibrate the counters' units."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)            # reads and writes exactly 1 GiB
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -651,8 +690,8 @@ def main():
                     help="for kernel traces: time only this workload (--steps/--warmup apply) and print "
                          "its JSON object")
     ap.add_argument("--profile", action="store_true",
-                    help="for counter runs: headline steps only, then one plain 1 GiB device copy "
-                         "whose FETCH_SIZE/WRITE_SIZE calibrate the counters")
+                    help="for counter runs: headline steps only (or the --only workload), then one plain "
+                         "1 GiB device copy whose FETCH_SIZE/WRITE_SIZE calibrate the counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -672,15 +711,13 @@ def main():
     extras = {"C2": run_c2, "C3": run_c3, "C4": run_c4, "G1": run_g1, "S1": run_s1, "E1": run_e1}
     if args.only:
         print(json.dumps({args.only: extras[args.only](tp, torch, args.steps, args.warmup)}), flush=True)
+        if args.profile:
+            calibration_copy(torch)
         return
     wl = tpsynth.WORKLOADS["C5"]
     ms, wall, per, flops, inp, outs, step_ms = run_headline(tp, torch, wl, args.steps, args.warmup)
     if args.profile:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)            # calibration: reads and writes exactly 1 GiB
-        torch.cuda.synchronize()
+        calibration_copy(torch)
         print(json.dumps({"profile": True, "ms_per_step": round(ms, 4), "calibration_copy_bytes": 1 << 30,
                           "kernel_source_hash": kernel_source_hash(),
                           "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in per.items()}}), flush=True)
