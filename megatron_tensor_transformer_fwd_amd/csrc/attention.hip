@@ -461,14 +461,28 @@ hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
                            const void* X, const void* Wq, const void* Wk, const void* Wv,
                            const void* Wo, void* Q, void* K, void* V, void* O, void* Z, float* L) {
   const int64_t M = b * s, N = h_local * d_head, Nkv = h_kv * d_head;
-  if (h_kv == h_local) {  // Q, K, V = X W{q,k,v}, one batched product scattered to [b, h_local, s, d_head]
+  if (h_kv == h_local) {  // Q, K, V = X W{q,k,v}, scattered to [b, h_local, s, d_head]
+    // One batched product of the three, or Q and K batched and V on its own
+    // (in its own tile shape) when the three leave a partly filled last round
+    // of tiles that the two launches avoid, by the planner's estimates.
+    const GemmPlan p3 = plan_gemm(M, 3 * N, d, false, false);
+    const GemmPlan p2 = plan_gemm(M, 2 * N, d, false, false);
+    const GemmPlan pv = plan_gemm(M, N, d, false, false);
+    const bool split_v = p2.est + pv.est + kGemmLaunchS < 0.97 * p3.est;
     GemmParams p = make_params(M, N, make_seg(X, d, M * d, Wq, N, d * N, d));
     p.Bz[0] = static_cast<const bf16*>(Wq);
     p.Bz[1] = static_cast<const bf16*>(Wk);
     p.Bz[2] = static_cast<const bf16*>(Wv);
     EpiHeadScatter<bf16> e{{static_cast<bf16*>(Q), static_cast<bf16*>(K), static_cast<bf16*>(V)},
                            (int)s, (int)h_local, (int)d_head};
-    TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wqkv_scatter", p, e, plan_gemm(M, 3 * N, d, false, false), 3)));
+    if (split_v) {
+      TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wqk_scatter", p, e, p2, 2)));
+      GemmParams q = make_params(M, N, make_seg(X, d, M * d, Wv, N, d * N, d));
+      EpiHeadScatter<bf16> ev{{static_cast<bf16*>(V), nullptr, nullptr}, (int)s, (int)h_local, (int)d_head};
+      TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wv_scatter", q, ev, pv)));
+    } else {
+      TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wqkv_scatter", p, e, p3, 3)));
+    }
   } else {  // grouped-query: Q over h_local heads, then K and V over h_kv heads
     GemmParams pq = make_params(M, N, make_seg(X, d, M * d, Wq, N, d * N, d));
     EpiHeadScatter<bf16> eq{{static_cast<bf16*>(Q), nullptr, nullptr}, (int)s, (int)h_local, (int)d_head};

@@ -38,7 +38,8 @@ enum { CFG_L = 0, CFG_M = 1, CFG_S = 2 };
 struct GemmPlan {
   int cfg;
   int split;
-  int tail = 0;   // > 1: the last partial round of 256x256 tiles is split along K this many ways
+  int tail = 0;      // > 1: the last partial round of 256x256 tiles is split along K this many ways
+  double est = 0.0;  // the planner's estimated duration in seconds
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -74,9 +75,10 @@ inline int64_t tiles_for(int cfg, int64_t M, int64_t N, bool dual) {
 // k-tiles each): the round then costs a tile's work / tail, plus a pass that
 // writes and reads the fp32 partial tiles and applies the epilogue.
 constexpr int kTailMaxSplit = 8;
+constexpr double kGemmLaunchS = 4e-6;   // per extra launch
 
 inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow_split, bool allow_tail = false) {
-  constexpr double CUS = 256.0, CU_FLOPS = 4.4e12, REDUCE_BPS = 4.0e12, LAUNCH_S = 4e-6;
+  constexpr double CUS = 256.0, CU_FLOPS = 4.4e12, REDUCE_BPS = 4.0e12, LAUNCH_S = kGemmLaunchS;
   const double rate[3] = {1.0, TPK_RATE_M, TPK_RATE_S};
   GemmPlan best{CFG_L, 1};
   double best_t = 1e30;
@@ -112,6 +114,7 @@ inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow
       }
     }
   }
+  best.est = best_t;
   return best;
 }
 
