@@ -74,14 +74,33 @@ class HipEvents:
             self.hip.hipEventDestroy(self.stop[i])
 
 
-def timed(tp, torch, step, steps: int, warmup: int, kernels_per_step: int, per_step: bool = False):
+def timed(tp, torch, step, steps: int, warmup: int, kernels_per_step: int, per_step: bool = False,
+          hook_in_timed: bool = True):
     """Warm up, then time exactly `steps` steps between two synchronisations;
     per-kernel durations come from the library's hipEvent hook on the same
     stream.  With per_step, an event between consecutive steps also gives
-    each step's duration (returned as the fifth value)."""
+    each step's duration (returned as the fifth value).
+
+    The hook launches every kernel with a start/stop event pair, which costs
+    about 3 us per launch (1% of the large MLP step, 25% of the 82-launch
+    all-shards step).  With hook_in_timed (the headline, whose roofline takes
+    its kernel durations from the timed region itself) the timed steps run
+    with the hook armed; otherwise they run without it and the per-kernel
+    durations come from as many hooked steps run after the timed region."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    if not hook_in_timed:
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        wall0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        _, _, per = timed(tp, torch, step, steps, 0, kernels_per_step)
+        return t0.elapsed_time(t1) / steps, wall, per
     ev = HipEvents(steps * kernels_per_step + 8)
     L = tp.lib()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -344,7 +363,7 @@ def run_c2(tp, torch, steps, warmup):
             tp.tp_mlp_bwd(X, W1s[i], W2s[i], A[i], H[i], dY, dXp[i], dW1[i], dW2[i], ws)
         tp.tp_shard_reduce(dXp, dX, n, M * d)
 
-    ms, _, per = timed(tp, torch, step, steps, warmup, 8 * 10 + 2)
+    ms, _, per = timed(tp, torch, step, steps, warmup, 8 * 10 + 2, hook_in_timed=False)
     gms = graph_timed(torch, step, steps)
     flops = n * 6 * gemm_flops(M, f, d)
     red = per.get("shard_reduce.vec8", [])
@@ -397,7 +416,7 @@ def run_c3(tp, torch, steps, warmup):
         tp.tp_swiglu_fwd(X, W1, W3, W2, G, U, H, Z)
         tp.tp_swiglu_bwd(X, W1, W3, W2, G, U, H, dY, dX, dW1, dW3, dW2, ws)
 
-    ms, _, per = timed(tp, torch, step, steps, warmup, 8)
+    ms, _, per = timed(tp, torch, step, steps, warmup, 8, hook_in_timed=False)
     flops = 9 * gemm_flops(M, f, d)
     return {"workload": "C3 SwiGLU MLP shard, b 4 s 2048 d 4096 d_ff 11008, TP 4 (slice 2752), fwd+bwd",
             "ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
@@ -432,8 +451,8 @@ def run_c4(tp, torch, steps, warmup):
         tp.tp_attn_shard_bwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, L, dY, dX, dWq, dWk, dWv, dWo, ws, b, s, hl, dh,
                              causal=True)
 
-    ms_f, _, per_f = timed(tp, torch, fwd, steps, warmup, 4)
-    ms_b, _, per_b = timed(tp, torch, bwd, steps, warmup, 12)
+    ms_f, _, per_f = timed(tp, torch, fwd, steps, warmup, 4, hook_in_timed=False)
+    ms_b, _, per_b = timed(tp, torch, bwd, steps, warmup, 12, hook_in_timed=False)
 
     def both():
         fwd()
@@ -489,8 +508,8 @@ def run_g1(tp, torch, steps, warmup):
         tp.tp_attn_gqa_shard_bwd(X, Wq, Wk, Wv, Wo, Q, K, V, Ob, L, dY, dX, dWq, dWk, dWv, dWo, ws, b, s, hl, hkv,
                                  dh, causal=True)
 
-    ms_f, _, per_f = timed(tp, torch, fwd, steps, warmup, 4)
-    ms_b, _, per_b = timed(tp, torch, bwd, steps, warmup, 12)
+    ms_f, _, per_f = timed(tp, torch, fwd, steps, warmup, 4, hook_in_timed=False)
+    ms_b, _, per_b = timed(tp, torch, bwd, steps, warmup, 12, hook_in_timed=False)
     core = 2 * 2.0 * b * hl * (s * (s + 1) / 2) * dh
     Nt = N + 2 * Nkv
     f_fwd = gemm_flops(M, N, d) + 2 * gemm_flops(M, Nkv, d) + core + gemm_flops(M, d, N)
@@ -535,7 +554,7 @@ def run_s1(tp, torch, steps, warmup):
                                    keep=keep, p_drop=p_drop)
         tp.tp_sp_all_gather(stripes, full)
 
-    ms, _, per = timed(tp, torch, step, steps, warmup, 2)
+    ms, _, per = timed(tp, torch, step, steps, warmup, 2, hook_in_timed=False)
     gms = graph_timed(torch, step, steps)
     # backward: this stripe's LayerNorm/dropout backward of the 8 shards' input gradients, then the
     # all-gather of the 8 stripes' dy (the row-parallel products' output gradient)
@@ -551,7 +570,7 @@ def run_s1(tp, torch, steps, warmup):
                                        keep=keep, p_drop=p_drop, dres=dres, dbias=dbias)
         tp.tp_sp_all_gather(dys, full)
 
-    ms_b, _, per_b = timed(tp, torch, bwd, steps, warmup, 3)
+    ms_b, _, per_b = timed(tp, torch, bwd, steps, warmup, 3, hook_in_timed=False)
     e = k * cols
     rs_bytes = (n + 1) * e * 2 + e + 3 * cols * 2 + 2 * e * 2
     ag_bytes = 2 * n * e * 2
@@ -642,7 +661,7 @@ def run_e1(tp, torch, steps, warmup):
         tp.tp_vocab_ce_bwd(X, E0, tg, logits, lse, dloss, dX, dE, ws, 0)
         tp.tp_vocab_embed_bwd(ids, dEmb, dE_in, 0)
 
-    ms, _, per = timed(tp, torch, step, steps, warmup, 13)
+    ms, _, per = timed(tp, torch, step, steps, warmup, 13, hook_in_timed=False)
     gms = graph_timed(torch, step, steps)
     flops = 3 * gemm_flops(T, vl, d)
     avg = lambda lab: (sum(per[lab]) / len(per[lab])) if per.get(lab) else None
