@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 8
+#define TP_ABI_VERSION 9
 
 typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype_t;
 
@@ -412,8 +412,14 @@ int tp_shard_reduce(void* stream, tp_dtype_t dt_in, tp_dtype_t dt_out,
  * number of kernels that recorded events; tp_profile_label(i) names kernel i
  * (static text such as "mlp_fwd.xw1_gelu"; "" out of range).  Launches past
  * `capacity` run untimed.  Returns TP_E_NULL / TP_E_DIM on bad arguments.
+ * tp_profile_only(label) restricts the armed hook on the calling thread to
+ * launches whose label equals `label` (copied): the others launch without
+ * events and do not count.  NULL lifts the restriction; tp_profile_end also
+ * lifts it.  Each event pair costs the launch a few microseconds, so a
+ * measurement that needs one kernel's duration arms only that kernel.
  * ------------------------------------------------------------------------- */
 int tp_profile_begin(void* const* start_events, void* const* stop_events, int capacity);
+int tp_profile_only(const char* label);
 int tp_profile_end(void);
 const char* tp_profile_label(int i);
 

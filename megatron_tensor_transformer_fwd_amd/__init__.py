@@ -27,7 +27,7 @@ __all__ = [
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtpshard.so")
-ABI_VERSION = 8          # TP_ABI_VERSION of include/tp_shard.h these wrappers are written for
+ABI_VERSION = 9          # TP_ABI_VERSION of include/tp_shard.h these wrappers are written for
 
 TP_DT_F32 = 0
 TP_DT_BF16 = 1
@@ -77,6 +77,7 @@ EXPORTS = {
     "tp_last_error_detail": (ctypes.c_char_p, []),
     "tp_abi_version": (_i32, []),
     "tp_profile_begin": (_i32, [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32]),
+    "tp_profile_only": (_i32, [ctypes.c_char_p]),
     "tp_profile_end": (_i32, []),
     "tp_profile_label": (ctypes.c_char_p, [_i32]),
 }

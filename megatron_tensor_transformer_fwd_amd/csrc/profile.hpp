@@ -6,6 +6,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <string>
 #include <vector>
 
 namespace tpk {
@@ -16,6 +17,7 @@ struct ProfileState {
   int capacity = 0;
   int count = 0;
   std::vector<const char*> labels;   // one per event pair, sized at arming
+  std::string only;                  // if not empty: the one label that records events
 };
 
 ProfileState& profile_state();   // thread-local, defined in tp_shard.cpp
@@ -23,7 +25,7 @@ ProfileState& profile_state();   // thread-local, defined in tp_shard.cpp
 template <class F, class... Args>
 inline hipError_t launch(const char* label, F kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
   ProfileState& ps = profile_state();
-  if (ps.start && ps.count < ps.capacity) {
+  if (ps.start && ps.count < ps.capacity && (ps.only.empty() || ps.only == label)) {
     hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ps.start[ps.count], ps.stop[ps.count], 0, args...);
     ps.labels[ps.count] = label;
     ++ps.count;

@@ -164,8 +164,15 @@ int tp_profile_begin(void* const* start_events, void* const* stop_events, int ca
   return ok();
 }
 
+int tp_profile_only(const char* label) {
+  tpk::ProfileState& ps = tpk::profile_state();
+  ps.only = label ? label : "";
+  return ok();
+}
+
 int tp_profile_end(void) {
   tpk::ProfileState& ps = tpk::profile_state();
+  ps.only.clear();
   const int n = ps.count < ps.capacity ? ps.count : ps.capacity;
   ps.start = ps.stop = nullptr;
   ps.capacity = 0;
