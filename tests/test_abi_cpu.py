@@ -42,6 +42,22 @@ def test_version_and_strerror():
     assert L.tp_strerror(-99) == b"unknown status"
 
 
+def test_profile_hook_arguments():
+    """The timing hook's host-side contract: bad arrays or capacities are
+    refused, a label filter can be set and lifted, and ending an armed hook
+    that launched nothing reports zero kernels and an empty label."""
+    import ctypes
+    L = tp.lib()
+    ev = (ctypes.c_void_p * 4)()
+    assert L.tp_profile_begin(None, ev, 4) == E_NULL
+    assert L.tp_profile_begin(ev, ev, 0) == E_DIM
+    assert L.tp_profile_begin(ev, ev, 4) == OK
+    assert L.tp_profile_only(b"mlp_bwd.dyw2t_dgelu") == OK
+    assert L.tp_profile_only(None) == OK
+    assert L.tp_profile_end() == 0
+    assert L.tp_profile_label(0) == b""
+
+
 def test_shard_range():
     assert tp.tp_shard_range(4096, 8, 3) == (1536, 512)
     assert tp.tp_shard_range(11008, 4, 3) == (8256, 2752)
