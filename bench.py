@@ -698,6 +698,80 @@ def run_e1(tp, torch, steps, warmup):
             "kernels_ms": {key: round(sum(v) / len(v), 4) for key, v in per.items()}}
 
 
+C5_LABELS = ["mlp_fwd.xw1_gelu", "mlp_fwd.hw2", "mlp_bwd.dyw2t_dgelu", "mlp_bwd.htdy", "mlp_bwd.daw1t",
+             "mlp_bwd.xtda"]
+
+
+def write_counter_files(root):
+    """profiles/traffic_c5_mlp.json and profiles/clock_c5_mlp.json from the
+    rocprofv3 counter runs of `bench.py --profile` under `root`: pmc_fetch/
+    (FETCH_SIZE), pmc_write/ (WRITE_SIZE) and c5pmc1/ (GRBM_GUI_ACTIVE,
+    SQ_VALU_MFMA_BUSY_CYCLES, ...), each holding the run's
+    counter_collection.csv and, as <dir>.log, the run's output, whose JSON line
+    names the hash of the kernel sources the run was built from.  The six
+    products are the library's GEMM dispatches in launch order, six per step;
+    every dispatch of a product is averaged.  Counter units are calibrated by
+    the run's last device copy (1 GiB read and written)."""
+    import csv
+    import glob
+
+    def run(d):
+        path = glob.glob(os.path.join(root, d, "**", "*counter_collection.csv"), recursive=True)
+        if not path:
+            raise SystemExit(f"no counter_collection.csv under {os.path.join(root, d)}")
+        disp = {}
+        with open(path[0]) as fh:
+            for r in csv.DictReader(fh):
+                k = int(r["Dispatch_Id"])
+                if k not in disp:
+                    disp[k] = [r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), {}]
+                c = disp[k][2]
+                c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        src_hash = None
+        with open(os.path.join(root, d + ".log")) as fh:
+            for line in fh:
+                if line.startswith("{") and "kernel_source_hash" in line:
+                    src_hash = json.loads(line)["kernel_source_hash"]
+        gemms = [v for _, v in sorted(disp.items()) if "gemm_bf16_kernel" in v[0]]
+        if not gemms or len(gemms) % 6:
+            raise SystemExit(f"{d}: {len(gemms)} GEMM dispatches, not whole steps of six")
+        per = {lab: gemms[i::6] for i, lab in enumerate(C5_LABELS)}
+        copies = [v for _, v in sorted(disp.items()) if "copyBuffer" in v[0]]
+        return per, (copies[-1][2] if copies else None), src_hash
+
+    avg = lambda xs: sum(xs) / len(xs)
+    pf, cf, hf = run("pmc_fetch")
+    pw, cw, hw = run("pmc_write")
+    p1, _, h1 = run("c5pmc1")
+    if not (hf and hf == hw == h1):
+        raise SystemExit(f"counter runs from different or unknown sources: {hf} {hw} {h1}")
+    kib = 1 << 20                                  # the calibration copy moves 1 GiB each way
+    sf, sw = round(kib / cf["FETCH_SIZE"], 4), round(kib / cw["WRITE_SIZE"], 4)
+    work = "C5 large GeLU MLP shard fwd+bwd (M 8192, d 8192, f 4096)"
+    traffic = {"workload": work, "kernel_source_hash": hf, "fetch_size_scale": sf, "write_size_scale": sw,
+               "calibration": f"torch copy_ of 1 GiB (__amd_rocclr_copyBuffer): FETCH_SIZE "
+                              f"{cf['FETCH_SIZE']:.0f} KiB, WRITE_SIZE {cw['WRITE_SIZE']:.0f} KiB",
+               "kernels": {}}
+    clock = {"workload": work, "kernel_source_hash": hf,
+             "method": "GRBM_GUI_ACTIVE / 8 XCDs / kernel duration, per product, from the first counter pass",
+             "kernels": {}}
+    for lab in C5_LABELS:
+        fb = int(avg([v[2]["FETCH_SIZE"] for v in pf[lab]]) * 1024 * sf)
+        wb = int(avg([v[2]["WRITE_SIZE"] for v in pw[lab]]) * 1024 * sw)
+        traffic["kernels"][lab] = {"fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                                   "hbm_bytes_per_launch": fb + wb}
+        gui = avg([v[2]["GRBM_GUI_ACTIVE"] for v in p1[lab]])
+        dur = avg([v[1] for v in p1[lab]])
+        mfma = avg([v[2]["SQ_VALU_MFMA_BUSY_CYCLES"] for v in p1[lab]])
+        clock["kernels"][lab] = {"clock_ghz": round(gui / 8 / dur, 3),
+                                 "mfma_busy": round(mfma / (gui / 8 * 1024), 4), "duration_us": round(dur / 1e3, 1)}
+    clock["mean_clock_ghz"] = round(avg([v["clock_ghz"] for v in clock["kernels"].values()]), 3)
+    for path, obj in ((TRAFFIC_FILE, traffic), (CLOCK_FILE, clock)):
+        with open(path, "w") as fh:
+            json.dump(obj, fh, indent=1)
+        print(f"wrote {path}")
+
+
 def calibration_copy(torch):
     """One plain 1 GiB device copy, the last kernel of a counter run: its
     FETCH_SIZE / WRITE_SIZE readings calibrate the counters' units."""
@@ -719,10 +793,16 @@ def main():
     ap.add_argument("--only", choices=["C2", "C3", "C4", "G1", "S1", "E1"],
                     help="for kernel traces: time only this workload (--steps/--warmup apply) and print "
                          "its JSON object")
+    ap.add_argument("--counters-from", metavar="DIR",
+                    help="write the committed counter files (traffic, sustained clock) from the rocprofv3 "
+                         "counter runs of --profile under DIR; no GPU needed")
     ap.add_argument("--profile", action="store_true",
                     help="for counter runs: headline steps only (or the --only workload), then one plain "
                          "1 GiB device copy whose FETCH_SIZE/WRITE_SIZE calibrate the counters")
     args = ap.parse_args()
+    if args.counters_from:
+        write_counter_files(args.counters_from)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's TP shard on one GPU only; --gpus {args.gpus} "
