@@ -1,6 +1,8 @@
 """The C ABI without a GPU: the library loads, exports every function the
 header declares, and rejects bad arguments with the documented status before
-any HIP call (so none of these calls touches a device)."""
+any HIP call.  The addresses passed are fabricated, so the few calls whose
+arguments pass validation are made only where no device is visible (they
+then fail at the launch); nothing here touches a device."""
 import ctypes
 import os
 import re
@@ -15,6 +17,30 @@ HEADER = os.path.join(ROOT, "include", "tp_shard.h")
 pytestmark = pytest.mark.skipif(not os.path.exists(tp.LIB_PATH), reason="libtpshard.so not built")
 
 OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def _device_count() -> int:
+    """HIP devices visible to this process (0 on a machine without a GPU)."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return 0
+    n = ctypes.c_int(0)
+    return n.value if hip.hipGetDeviceCount(ctypes.byref(n)) == 0 else 0
+
+
+NO_DEVICE = _device_count() == 0
+
+
+def _fails_at_launch(call):
+    """A call whose arguments pass validation, made on this module's
+    fabricated addresses: with no device it fails at the launch with
+    TP_E_HIP.  Where a GPU is visible it would launch kernels on those
+    addresses, so it is not made there."""
+    if NO_DEVICE:
+        assert call() == E_HIP
+
+
 BF16, F32 = tp.TP_DT_BF16, tp.TP_DT_F32
 
 
@@ -270,7 +296,7 @@ def test_sp_reduce_scatter_ln_validation():
     assert rs(h=P + 2 * 64 * 32 * 2) == E_ALIAS           # output inside the partials
     # bias and keep are optional; with keep NULL p_drop is not examined.  Such
     # calls pass validation and fail only at the launch (no device here).
-    assert rs(bias=None, keep=None, p_drop=5.0) == E_HIP
+    _fails_at_launch(lambda: rs(bias=None, keep=None, p_drop=5.0))
 
 
 def test_sp_all_gather_validation():
@@ -294,7 +320,7 @@ def test_sp_all_gather_validation():
     # ... another stripe's place as well
     assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, arr(s0, full, s2, s3), full) == E_ALIAS
     # exactly in place is accepted (it is not copied); the launch then fails without a device
-    assert L.tp_sp_all_gather(None, BF16, 4, 16, 32, arr(s0, full + stripe, s2, s3), full) == E_HIP
+    _fails_at_launch(lambda: L.tp_sp_all_gather(None, BF16, 4, 16, 32, arr(s0, full + stripe, s2, s3), full))
 
 
 def test_vocab_validation():
@@ -308,13 +334,13 @@ def test_vocab_validation():
     assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, -1, ids, E, Y) == E_DIM
     assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, None, E, Y) == E_NULL
     assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, ids + 4, E, Y) == E_ALIGN
-    assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, ids + 8, E, Y) == E_HIP   # 8 bytes suffice
+    _fails_at_launch(lambda: L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, ids + 8, E, Y))   # 8 bytes suffice
     assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, ids, E + 8, Y) == E_ALIGN
     assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, 128, 0, ids, E, E + 64) == E_ALIAS
     assert L.tp_vocab_embed_fwd(None, BF16, 16, 64, (1 << 21) + 8, 0, ids, E, Y) == E_DIM
     assert L.tp_vocab_embed_fwd(None, BF16, (1 << 24) + 1, 64, 128, 0, ids, E, Y) == E_DIM
     # input embedding backward
-    assert L.tp_vocab_embed_bwd(None, BF16, 16, 64, 128, 0, ids, Y, E) == E_HIP
+    _fails_at_launch(lambda: L.tp_vocab_embed_bwd(None, BF16, 16, 64, 128, 0, ids, Y, E))
     assert L.tp_vocab_embed_bwd(None, BF16, 16, 64, 100, 0, ids, Y, E) == E_DIVIS
     assert L.tp_vocab_embed_bwd(None, BF16, 16, 64, 128, 0, None, Y, E) == E_NULL
     assert L.tp_vocab_embed_bwd(None, BF16, 16, 64, 128, 0, ids, Y, Y + 64) == E_ALIAS
@@ -328,12 +354,12 @@ def test_vocab_validation():
     assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, X, st, ws, fws) == E_ALIAS
     assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, lg, st, None, 0) == E_WS
     assert L.tp_vocab_ce_fwd(None, BF16, 16, 64, 128, 0, X, E, tg, lg, st, ws, fws - 1) == E_WS
-    assert L.tp_vocab_ce_fwd(None, F32, 16, 64, 128, 0, X, E, tg, lg, st, None, 0) == E_HIP   # fp32: no workspace
+    _fails_at_launch(lambda: L.tp_vocab_ce_fwd(None, F32, 16, 64, 128, 0, X, E, tg, lg, st, None, 0))   # fp32: no workspace
     assert L.tp_vocab_ce_combine(None, 0, 16, st, 48, loss, lse) == E_DIM
     assert L.tp_vocab_ce_combine(None, 4, 16, st, 40, loss, lse) == E_DIM       # stride < 3 * n_tokens
     assert L.tp_vocab_ce_combine(None, 4, 16, st, 48, loss, loss) == E_ALIAS
     assert L.tp_vocab_ce_combine(None, 4, 16, st + 2, 48, loss, lse) == E_ALIGN
-    assert L.tp_vocab_ce_combine(None, 4, 16, st + 4, 49, loss + 12, lse + 4) == E_HIP
+    _fails_at_launch(lambda: L.tp_vocab_ce_combine(None, 4, 16, st + 4, 49, loss + 12, lse + 4))
     assert L.tp_vocab_ce_combine(None, 4, 16, st, 48, st + 64, lse) == E_ALIAS
     need = L.tp_vocab_ce_bwd_workspace_bytes(BF16, 16, 64, 128)
     assert need >= 16 * 128 * 2
@@ -387,4 +413,4 @@ def test_sp_ln_bwd_validation():
     assert bw(ws=None) == E_WS and bw(wsb=need - 1) == E_WS
     assert bw(dh=h) == E_ALIAS and bw(dy=dh) == E_ALIAS
     assert bw(dg=dg + 2) == E_ALIGN
-    assert bw(dg=dg + 4, dbi=None, dres=None, keep=None, p=3.0) == E_HIP      # 4-byte fp32 arrays; optional inputs
+    _fails_at_launch(lambda: bw(dg=dg + 4, dbi=None, dres=None, keep=None, p=3.0))      # 4-byte fp32 arrays; optional inputs
