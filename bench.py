@@ -708,9 +708,9 @@ def write_counter_files(root):
     (FETCH_SIZE), pmc_write/ (WRITE_SIZE) and c5pmc1/ (GRBM_GUI_ACTIVE,
     SQ_VALU_MFMA_BUSY_CYCLES, ...), each holding the run's
     counter_collection.csv and, as <dir>.log, the run's output, whose JSON line
-    names the hash of the kernel sources the run was built from.  The six
-    products are the library's GEMM dispatches in launch order, six per step;
-    every dispatch of a product is averaged.  Counter units are calibrated by
+    names the hash of the kernel sources the run was built from and lists the
+    six products in launch order.  The GEMM dispatches are taken six per step
+    in that order; every dispatch of a product is averaged.  Counter units are calibrated by
     the run's last device copy (1 GiB read and written)."""
     import csv
     import glob
@@ -727,15 +727,19 @@ def write_counter_files(root):
                     disp[k] = [r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), {}]
                 c = disp[k][2]
                 c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-        src_hash = None
+        src_hash, labels = None, None
         with open(os.path.join(root, d + ".log")) as fh:
             for line in fh:
                 if line.startswith("{") and "kernel_source_hash" in line:
-                    src_hash = json.loads(line)["kernel_source_hash"]
+                    j = json.loads(line)
+                    src_hash, labels = j["kernel_source_hash"], list(j["kernels_ms"])
+        if sorted(labels or []) != sorted(C5_LABELS):
+            raise SystemExit(f"{d}: the run's products {labels} are not the six of the large MLP step")
         gemms = [v for _, v in sorted(disp.items()) if "gemm_bf16_kernel" in v[0]]
         if not gemms or len(gemms) % 6:
             raise SystemExit(f"{d}: {len(gemms)} GEMM dispatches, not whole steps of six")
-        per = {lab: gemms[i::6] for i, lab in enumerate(C5_LABELS)}
+        # the run's own kernels_ms lists the products in launch order
+        per = {lab: gemms[i::6] for i, lab in enumerate(labels)}
         copies = [v for _, v in sorted(disp.items()) if "copyBuffer" in v[0]]
         return per, (copies[-1][2] if copies else None), src_hash
 

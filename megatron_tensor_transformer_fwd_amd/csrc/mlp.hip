@@ -62,16 +62,18 @@ static hipError_t mlp_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t f,
   const MlpBwdPlan pl = mlp_bwd_plan(DT_BF16, M, d, f);
   bf16* dA = static_cast<bf16*>(ws);
   float* split_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.dA_bytes);
-  {  // dA = (dY W2^T) * GeLU'(A);  B(k, n) = W2[n][k]
-    GemmParams p = make_params(M, f, make_seg(dY, d, M * d, W2, d, f * d, d));
-    EpiDGelu<bf16> e{static_cast<const bf16*>(A), dA, f};
-    TPK_TRY((launch_gemm<true, true, false>(st, "mlp_bwd.dyw2t_dgelu", p, e, plan_gemm(M, f, d, false, false))));
-  }
+  // dW2 first: it reads dY, which the dgrad then finds in the Infinity Cache,
+  // and the dgrad's output dA is then fresh for the two products that read it.
   {  // dW2 = H^T dY:  A(m, k) = H[k][m], B(k, n) = dY[k][n]
     GemmParams p = make_params(f, d, make_seg(H, f, M * f, dY, d, M * d, M));
     TPK_TRY(wgrad_f32_out(st, pl.dW2, f, d, dW2, split_ws, [&](const EpiStore<float>& e, GemmPlan g) {
       return launch_gemm<false, false, false>(st, "mlp_bwd.htdy", p, e, g);
     }));
+  }
+  {  // dA = (dY W2^T) * GeLU'(A);  B(k, n) = W2[n][k]
+    GemmParams p = make_params(M, f, make_seg(dY, d, M * d, W2, d, f * d, d));
+    EpiDGelu<bf16> e{static_cast<const bf16*>(A), dA, f};
+    TPK_TRY((launch_gemm<true, true, false>(st, "mlp_bwd.dyw2t_dgelu", p, e, plan_gemm(M, f, d, false, false))));
   }
   {  // dX = dA W1^T;  B(k, n) = W1[n][k]
     GemmParams p = make_params(M, d, make_seg(dA, f, M * f, W1, f, d * f, f));
