@@ -626,4 +626,19 @@ def max_rel_err(y, ref) -> float:
     return num / den
 
 
-__all__.append("max_rel_err")
+def per_element_rel_err(y, ref, floor: float = 1e-3) -> float:
+    """max_e |y_e - ref_e| / max(|ref_e|, floor * ||ref||_inf): the relative
+    error of each element, with entries far below the tensor's largest
+    measured against floor * ||ref||_inf instead of their own size."""
+    y, ref = _f64(y), _f64(ref)
+    if not ref.size:
+        return 0.0
+    big = float(np.max(np.abs(ref)))
+    den = np.maximum(np.abs(ref), floor * big)
+    num = np.abs(y - ref)
+    if big == 0.0:
+        return float(np.max(num))
+    return float(np.max(num / den))
+
+
+__all__ += ["max_rel_err", "per_element_rel_err"]

@@ -1,101 +1,60 @@
-"""The C ABI without a GPU: the library loads, exports every function the
-header declares, and rejects bad arguments with the documented status before
-any HIP call.  The addresses passed are fabricated, so the few calls whose
-arguments pass validation are made only where no device is visible (they
-then fail at the launch); nothing here touches a device."""
+"""The C ABI without a GPU: every entry point rejects bad arguments with the
+documented status before any HIP call.  The addresses passed are fabricated,
+so the module runs only on a machine that provably has no GPU (the few calls
+whose arguments pass validation then fail at the launch); nothing here
+touches a device."""
 import ctypes
 import os
-import re
 
 import pytest
 
 import megatron_tensor_transformer_fwd_amd as tp
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "tp_shard.h")
-
-pytestmark = pytest.mark.skipif(not os.path.exists(tp.LIB_PATH), reason="libtpshard.so not built")
 
 OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
-def _device_count() -> int:
-    """HIP devices visible to this process (0 on a machine without a GPU)."""
-    try:
-        hip = ctypes.CDLL("libamdhip64.so")
-    except OSError:
-        return 0
-    n = ctypes.c_int(0)
-    return n.value if hip.hipGetDeviceCount(ctypes.byref(n)) == 0 else 0
+def _no_device_proven() -> bool:
+    """True only where this process provably sees no GPU: no /dev/kfd and the
+    HIP runtime reports no device.  Anything else (the device node exists, the
+    runtime cannot be loaded, or it answers with another error) counts as a
+    device that may be present."""
+    if os.path.exists("/dev/kfd"):
+        return False
+    for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+        try:
+            hip = ctypes.CDLL(name)
+            break
+        except OSError:
+            continue
+    else:
+        return False
+    n = ctypes.c_int(-1)
+    rc = hip.hipGetDeviceCount(ctypes.byref(n))
+    hip_error_no_device = 100
+    return rc == hip_error_no_device or (rc == 0 and n.value == 0)
 
 
-NO_DEVICE = _device_count() == 0
+NO_DEVICE = _no_device_proven()
+
+# Every call below passes fabricated device addresses: validation must refuse
+# them on the host, and the few that pass validation fail at the launch for
+# want of a device.  On a machine with a GPU such a call would reach a kernel,
+# so the whole module runs only where no device is provably present.
+pytestmark = [pytest.mark.skipif(not os.path.exists(tp.LIB_PATH), reason="libtpshard.so not built"),
+              pytest.mark.skipif(not NO_DEVICE, reason="fabricated device addresses: CPU-only machines")]
 
 
 def _fails_at_launch(call):
     """A call whose arguments pass validation, made on this module's
     fabricated addresses: with no device it fails at the launch with
-    TP_E_HIP.  Where a GPU is visible it would launch kernels on those
-    addresses, so it is not made there."""
-    if NO_DEVICE:
-        assert call() == E_HIP
+    TP_E_HIP (the module runs only where no device is present)."""
+    assert NO_DEVICE
+    assert call() == E_HIP
 
 
 BF16, F32 = tp.TP_DT_BF16, tp.TP_DT_F32
-
-
-def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", text)))
-
-
-def test_header_and_binding_agree_and_library_exports_all():
-    names = _declared_functions()
-    assert set(names) == set(tp.EXPORTS), (names, sorted(tp.EXPORTS))
-    L = tp.lib()
-    for n in names:
-        assert hasattr(L, n), n
-
-
-def test_version_and_strerror():
-    hdr = open(HEADER).read()
-    declared = int(re.search(r"#define TP_ABI_VERSION (\d+)", hdr).group(1))
-    assert tp.tp_abi_version() == declared == tp.ABI_VERSION
-    L = tp.lib()
-    for code in (OK, E_NULL, E_DIM, E_DIVIS, E_DTYPE, E_ALIGN, E_ALIAS, E_WS, E_HIP):
-        assert L.tp_strerror(code) and L.tp_strerror(code) != b"unknown status"
-    assert L.tp_strerror(-99) == b"unknown status"
-
-
-def test_profile_hook_arguments():
-    """The timing hook's host-side contract: bad arrays or capacities are
-    refused, a label filter can be set and lifted, and ending an armed hook
-    that launched nothing reports zero kernels and an empty label."""
-    import ctypes
-    L = tp.lib()
-    ev = (ctypes.c_void_p * 4)()
-    assert L.tp_profile_begin(None, ev, 4) == E_NULL
-    assert L.tp_profile_begin(ev, ev, 0) == E_DIM
-    assert L.tp_profile_begin(ev, ev, 4) == OK
-    assert L.tp_profile_only(b"mlp_bwd.dyw2t_dgelu") == OK
-    assert L.tp_profile_only(None) == OK
-    assert L.tp_profile_end() == 0
-    assert L.tp_profile_label(0) == b""
-
-
-def test_shard_range():
-    assert tp.tp_shard_range(4096, 8, 3) == (1536, 512)
-    assert tp.tp_shard_range(11008, 4, 3) == (8256, 2752)
-    assert tp.tp_shard_range(32, 4, 0) == (0, 8)
-    with pytest.raises(tp.TPError) as e:
-        tp.tp_shard_range(11008, 3, 0)
-    assert e.value.status == E_DIVIS and "divisible" in e.value.detail
-    for args in ((0, 4, 0), (16, 0, 0), (16, 4, 4), (16, 4, -1)):
-        with pytest.raises(tp.TPError) as e:
-            tp.tp_shard_range(*args)
-        assert e.value.status == E_DIM
-    assert tp.lib().tp_shard_range(8, 2, 0, None, None) == E_NULL
 
 
 # Fake, well separated, 16-byte aligned device addresses: validation never

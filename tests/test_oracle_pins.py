@@ -825,3 +825,23 @@ def test_workload_shapes():
     assert (W["C2"].M, W["C2"].f_local) == (8192, 512)
     assert W["C3"].f_local == 2752 and W["C4"].h_local == 8
     assert (W["C5"].M, W["C5"].d, W["C5"].f_local) == (8192, 8192, 4096)
+
+
+# --------------------------------------------------------------- error metrics
+
+def test_error_metrics():
+    ref = np.array([1.0, -2.0, 1e-6, 0.0])
+    # max_rel_err is measured against the tensor's largest entry
+    y = ref.copy()
+    y[2] += 1e-6                     # doubles a tiny entry
+    assert O.max_rel_err(y, ref) == pytest.approx(5e-7)
+    # per-element: that entry's error against the floor 1e-3 * ||ref||_inf = 2e-3
+    assert O.per_element_rel_err(y, ref) == pytest.approx(1e-6 / 2e-3)
+    # an entry above the floor is measured against itself
+    z = ref * np.array([1.0, 1.0 + 3e-3, 1.0, 1.0])
+    assert O.per_element_rel_err(z, ref) == pytest.approx(3e-3)
+    assert O.max_rel_err(z, ref) == pytest.approx(3e-3)
+    # a uniform relative error is the same under both metrics
+    w = ref * (1 + 1e-4)
+    assert O.per_element_rel_err(w, ref) == pytest.approx(1e-4)
+    assert O.max_rel_err(ref, ref) == 0.0 and O.per_element_rel_err(ref, ref) == 0.0
