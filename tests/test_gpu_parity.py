@@ -607,20 +607,41 @@ def test_gqa_bwd_g1_grouping_long_sequence(tp):
         check(k, out[k], ref[k], "bf16")
 
 
-def test_gqa_bwd_g1_full_size_deterministic(tp):
-    """G1 at full size: the backward runs, its outputs are finite and two runs
-    agree bit for bit (every gradient has one owner and a fixed summation
-    order, including the sum over each K/V head's group)."""
-    _say("gqa bwd G1 full size, determinism")
+def test_gqa_bwd_g1_full_size(tp):
+    """G1 at full size (b 2, s 4096, d 16384, 16 query heads on one K/V head)
+    against the oracle, every gradient whole.  Its QKV weight gradient
+    ([16384 x 2304], 576 tiles of 256 x 256) runs two whole rounds of tiles and
+    splits the last 64 tiles (rows 14336..16383, columns 256..2303) along K,
+    finished by the ordered fixup kernel: the launch list must contain that
+    fixup, and the rows it writes are also checked on their own (normalised by
+    their own largest value, so an error there cannot hide behind larger rows
+    elsewhere).  Two runs agree bit for bit."""
+    import bench
+    _say("gqa bwd G1 full size against the oracle (tail-split weight gradient)")
     wl = tpsynth.WORKLOADS["G1"]
     inp = tpsynth.gqa_inputs(wl)
     b, s, h_l, h_kv, dh = wl.b, wl.s, wl.h_local, wl.h_kv_local, wl.d_head
-    dY = torch.from_numpy(np.random.default_rng(95).standard_normal((b * s, wl.d)).astype(np.float32))
-    dY = dY.to(torch.bfloat16).cuda()
+    dYn = tpsynth.normal(np.random.default_rng(95), (b * s, wl.d), 1.0, "bf16")
+    dY = dev(dYn, "bf16")
     fwd = run_gqa(tp, inp, b, s, h_l, h_kv, dh)
+    L = tp.lib()
+    ev = bench.HipEvents(64)
+    assert L.tp_profile_begin(ev.start, ev.stop, ev.n) == 0
     a = run_gqa_bwd(tp, inp, fwd, dY, b, s, h_l, h_kv, dh)
+    n = L.tp_profile_end()
+    labels = [L.tp_profile_label(i).decode() for i in range(n)]
+    ev.close()
+    assert "gemm.tail_split" in labels and "gemm.tail_fixup" in labels, labels
     c = run_gqa_bwd(tp, inp, fwd, dY, b, s, h_l, h_kv, dh)
     for k in a:
-        assert torch.isfinite(a[k]).all(), k
         assert torch.equal(a[k], c[k]), k
+    del c, fwd
+    _say("gqa bwd G1 full size: oracle")
+    ref = O.attn_gqa_shard_bwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], dYn, b, s, h_l, h_kv, dh)
+    for k in ("dX", "dWq", "dWk", "dWv", "dWo"):
+        check(k, a[k], ref[k], "bf16")
+    r0, c0 = 56 * 256, 256          # the tail tiles: m-tiles 56..63, columns 256.. of [dWq | dWk | dWv]
+    check("dWq tail", a["dWq"][r0:, c0:], ref["dWq"][r0:, c0:], "bf16")
+    check("dWk tail", a["dWk"][r0:], ref["dWk"][r0:], "bf16")
+    check("dWv tail", a["dWv"][r0:], ref["dWv"][r0:], "bf16")
 
