@@ -54,7 +54,11 @@ extern "C" {
 
 #define TP_ABI_VERSION 9
 
-typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype_t;
+/* dtype codes; tp_dtype_t is a plain 32-bit int so that any value a caller
+ * passes is well defined on both sides of the ABI, and values other than
+ * these are refused with TP_E_DTYPE */
+typedef int32_t tp_dtype_t;
+enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 };
 
 /* status codes */
 #define TP_OK           0

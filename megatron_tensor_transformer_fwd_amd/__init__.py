@@ -26,7 +26,9 @@ __all__ = [
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtpshard.so")
+# TPSHARD_LIB selects another build of the same library (the host-sanitizer
+# build of the CPU ABI checks); unset, the in-tree library is loaded.
+LIB_PATH = os.environ.get("TPSHARD_LIB") or os.path.join(HERE, "libtpshard.so")
 ABI_VERSION = 9          # TP_ABI_VERSION of include/tp_shard.h these wrappers are written for
 
 TP_DT_F32 = 0
