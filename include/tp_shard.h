@@ -29,8 +29,9 @@
  *    aligned unless an entry point says otherwise.  The
  *    caller owns all memory; the library allocates nothing, never
  *    synchronises and never changes the current device.  The only state it
- *    keeps between calls is thread-local: the last error text and the
- *    optional kernel-timing hook (tp_profile_begin).
+ *    keeps between calls is thread-local (the last error text and the
+ *    optional kernel-timing hook, tp_profile_begin), plus the per-device
+ *    scratch array of tp_mlp_bwd_noalloc and its address on each device.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue work and return; faults raised while a kernel runs surface at
  *    the caller's next synchronisation.
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 9
+#define TP_ABI_VERSION 10
 
 /* dtype codes; tp_dtype_t is a plain 32-bit int so that any value a caller
  * passes is well defined on both sides of the ABI, and values other than
@@ -112,6 +113,29 @@ int tp_mlp_bwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
                const void* A, const void* H, const void* dY,
                void* dX, float* dW1, float* dW2, void* ws, size_t ws_bytes);
 size_t tp_mlp_bwd_workspace_bytes(tp_dtype_t dt, int64_t M, int64_t d, int64_t f);
+
+/* ---------------------------------------------------------------------------
+ * tp_mlp_bwd_noalloc — tp_mlp_bwd for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving or training
+ * loops, harnesses that forbid hipMalloc.  Same arguments, results and
+ * kernels as tp_mlp_bwd (bitwise the same outputs), without ws: its
+ * workspace is a static device array of TP_MLP_BWD_NOALLOC_MAX_WORKSPACE
+ * bytes (64 MiB) inside the library, one per GPU, held from the library's
+ * first use on that GPU until the process ends.  Sizes whose
+ * tp_mlp_bwd_workspace_bytes exceeds it return TP_E_WORKSPACE before any HIP
+ * call (the 8192-token shards of a 8192 x 32768 layer at TP 8 and of a
+ * 1024 x 4096 layer at TP 8 fit).  It calls no allocator.  The first call on
+ * each GPU looks up that GPU's copy of the array (hipGetSymbolAddress, with
+ * that GPU current); make it once outside graph capture.  Every call on a
+ * GPU uses the same array, whatever its stream: calls that overlap in time
+ * on one GPU (two streams, two threads) race on it, and it keeps the last
+ * call's contents (nothing in it needs to start at zero).
+ * ------------------------------------------------------------------------- */
+#define TP_MLP_BWD_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+int tp_mlp_bwd_noalloc(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
+                       const void* X, const void* W1, const void* W2,
+                       const void* A, const void* H, const void* dY,
+                       void* dX, float* dW1, float* dW2);
 
 /* ---------------------------------------------------------------------------
  * tp_swiglu_fwd — SwiGLU MLP shard forward ([JY] FFN, SwiGLU part: W1 and

@@ -14,7 +14,7 @@ from typing import Optional
 
 __all__ = [
     "TPError", "lib", "LIB_PATH", "TP_DT_F32", "TP_DT_BF16",
-    "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_workspace_bytes",
+    "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_workspace_bytes", "tp_mlp_bwd_noalloc", "MLP_BWD_NOALLOC_MAX_WORKSPACE",
     "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes",
     "tp_attn_shard_fwd", "tp_attn_gqa_shard_fwd", "tp_attn_shard_bwd", "tp_attn_shard_bwd_workspace_bytes",
     "tp_attn_gqa_shard_bwd", "tp_attn_gqa_shard_bwd_workspace_bytes",
@@ -29,10 +29,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # TPSHARD_LIB selects another build of the same library (the host-sanitizer
 # build of the CPU ABI checks); unset, the in-tree library is loaded.
 LIB_PATH = os.environ.get("TPSHARD_LIB") or os.path.join(HERE, "libtpshard.so")
-ABI_VERSION = 9          # TP_ABI_VERSION of include/tp_shard.h these wrappers are written for
+ABI_VERSION = 10         # TP_ABI_VERSION of include/tp_shard.h these wrappers are written for
 
 TP_DT_F32 = 0
 TP_DT_BF16 = 1
+MLP_BWD_NOALLOC_MAX_WORKSPACE = 64 << 20    # TP_MLP_BWD_NOALLOC_MAX_WORKSPACE
 
 STATUS = {0: "TP_OK", -1: "TP_E_NULL", -2: "TP_E_DIM", -3: "TP_E_DIVIS", -4: "TP_E_DTYPE",
           -5: "TP_E_ALIGN", -6: "TP_E_ALIAS", -7: "TP_E_WORKSPACE", -8: "TP_E_HIP"}
@@ -48,6 +49,7 @@ EXPORTS = {
     "tp_mlp_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
     "tp_mlp_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz]),
     "tp_mlp_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
+    "tp_mlp_bwd_noalloc": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "tp_swiglu_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p]),
     "tp_swiglu_bwd": (_i32, [_p, _i32, _i64, _i64, _i64] + [_p] * 8 + [_p] * 4 + [_p, _sz]),
     "tp_swiglu_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
@@ -209,6 +211,23 @@ def tp_mlp_bwd(X, W1, W2, A, H, dY, dX, dW1, dW2, ws, stream=None) -> None:
     _check(lib().tp_mlp_bwd(_stream(stream), _dt(X), M, d, f, _ptr(X), _ptr(W1), _ptr(W2), _ptr(A),
                             _ptr(H), _ptr(dY), _ptr(dX), _ptr(dW1), _ptr(dW2), _ptr(ws),
                             ws.numel() * ws.element_size()))
+
+
+def tp_mlp_bwd_noalloc(X, W1, W2, A, H, dY, dX, dW1, dW2, stream=None) -> None:
+    """tp_mlp_bwd with the library's own per-GPU scratch instead of ws."""
+    M, d = X.shape
+    f = W1.shape[1]
+    dt = X.dtype
+    _need("W1", W1, d * f, dt)
+    _need("W2", W2, f * d, dt)
+    for name, t in (("A", A), ("H", H)):
+        _need(name, t, M * f, dt)
+    for name, t in (("dY", dY), ("dX", dX)):
+        _need(name, t, M * d, dt)
+    _need("dW1", dW1, d * f, _f32())
+    _need("dW2", dW2, f * d, _f32())
+    _check(lib().tp_mlp_bwd_noalloc(_stream(stream), _dt(X), M, d, f, _ptr(X), _ptr(W1), _ptr(W2), _ptr(A),
+                                    _ptr(H), _ptr(dY), _ptr(dX), _ptr(dW1), _ptr(dW2)))
 
 
 def tp_swiglu_fwd(X, W1, W3, W2, G, U, H, Z, stream=None) -> None:

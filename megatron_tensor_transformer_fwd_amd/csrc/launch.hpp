@@ -21,6 +21,9 @@ hipError_t launch_mlp_fwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t 
                           const void* X, const void* W1, const void* W2,
                           void* A, void* H, void* Z);
 size_t mlp_bwd_ws_bytes(int dt, int64_t M, int64_t d, int64_t f);
+// The current device's address of the allocation-free MLP backward's scratch
+// array (looked up once per device).
+hipError_t mlp_bwd_scratch(void** ptr);
 hipError_t launch_mlp_bwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t f,
                           const void* X, const void* W1, const void* W2,
                           const void* A, const void* H, const void* dY,

@@ -6,10 +6,41 @@
 //           dW2 = H^T dY                   TN product (fp32, split-K if narrow)
 //           dX = dA W1^T                   NT product (this shard's summand)
 //           dW1 = X^T dA                   TN product (fp32, split-K if narrow)
+#include <mutex>
+
 #include "epilogues.hpp"
 #include "gemm_dispatch.hpp"
+#include "tp_shard.h"
 
 namespace tpk {
+
+// Workspace of the allocation-free MLP backward: a device array in this code
+// object, so every GPU the library runs on holds its own copy from the
+// library's first use there until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device memory: kernels and copies
+// take the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[TP_MLP_BWD_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t mlp_bwd_scratch(void** ptr) {
+  int dev = -1;
+  TPK_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    TPK_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));   // with device `dev` current
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 static inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 

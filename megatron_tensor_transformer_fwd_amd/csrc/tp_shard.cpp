@@ -249,6 +249,29 @@ int tp_mlp_bwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
                     "tp_mlp_bwd");
 }
 
+int tp_mlp_bwd_noalloc(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
+                       const void* X, const void* W1, const void* W2, const void* A, const void* H,
+                       const void* dY, void* dX, float* dW1, float* dW2) {
+  TP_CHECK(mlp_common(dt, M, d, f));
+  const size_t need = tpk::mlp_bwd_ws_bytes(dt, M, d, f);
+  if (need > TP_MLP_BWD_NOALLOC_MAX_WORKSPACE)
+    return fail(TP_E_WORKSPACE, "M=%lld d=%lld f=%lld needs %zu bytes of workspace; the allocation-free entry "
+                "point holds %zu (use tp_mlp_bwd with a caller workspace)", (long long)M, (long long)d,
+                (long long)f, need, (size_t)TP_MLP_BWD_NOALLOC_MAX_WORKSPACE);
+  const size_t e = esize(dt);
+  TP_CHECK(check_buffers(
+      {{"X", X, M * d * e}, {"W1", W1, d * f * e}, {"W2", W2, f * d * e}, {"A", A, M * f * e},
+       {"H", H, M * f * e}, {"dY", dY, M * d * e}},
+      {{"dX", dX, M * d * e}, {"dW1", dW1, d * f * (size_t)4}, {"dW2", dW2, f * d * (size_t)4}},
+      {"X", "W1", "W2", "A", "H", "dY", "dX", "dW1", "dW2"}));
+  void* ws = nullptr;
+  const hipError_t e0 = tpk::mlp_bwd_scratch(&ws);
+  if (e0 != hipSuccess) return hip_status(e0, "tp_mlp_bwd_noalloc: scratch lookup");
+  return hip_status(tpk::launch_mlp_bwd(static_cast<hipStream_t>(stream), dt, M, d, f, X, W1, W2, A, H, dY,
+                                        dX, dW1, dW2, ws),
+                    "tp_mlp_bwd_noalloc");
+}
+
 int tp_swiglu_fwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
                   const void* X, const void* W1, const void* W3, const void* W2,
                   void* G, void* U, void* H, void* Z) {

@@ -113,6 +113,37 @@ def test_mlp_bwd_validation_and_workspace():
     assert _mlp_bwd(f=12) == E_DIVIS
 
 
+def _mlp_bwd_noalloc(**kw):
+    names = ["X", "W1", "W2", "A", "H", "dY", "dX", "dW1", "dW2"]
+    args = dict(stream=None, dt=BF16, M=64, d=64, f=128)
+    args.update(dict(zip(names, _addrs(9))))
+    args.update(kw)
+    rc = tp.lib().tp_mlp_bwd_noalloc(*args.values())
+    return rc, tp.lib().tp_last_error_detail().decode()
+
+
+def test_mlp_bwd_noalloc_validation_and_limit():
+    """The allocation-free backward validates like tp_mlp_bwd and refuses
+    shapes whose workspace exceeds its 64 MiB scratch before any HIP call."""
+    limit = tp.MLP_BWD_NOALLOC_MAX_WORKSPACE
+    assert limit == 64 << 20
+    # the 8192-token shards of the large (f 4096) and GPT-2-medium (f 512) layers fit
+    assert tp.tp_mlp_bwd_workspace_bytes(BF16, 8192, 8192, 4096) <= limit
+    assert tp.tp_mlp_bwd_workspace_bytes(BF16, 8192, 1024, 512) <= limit
+    for M, d, f in ((8192, 8192, 8192), (16384, 8192, 4096), (8192, 4096, 4104)):
+        assert tp.tp_mlp_bwd_workspace_bytes(BF16, M, d, f) > limit
+        rc, msg = _mlp_bwd_noalloc(M=M, d=d, f=f)
+        assert rc == E_WS and "allocation-free" in msg, msg
+    assert _mlp_bwd_noalloc(A=None)[0] == E_NULL
+    assert _mlp_bwd_noalloc(dW2=BASE + 8)[0] == E_ALIGN
+    assert _mlp_bwd_noalloc(dX=BASE + 5 * (1 << 32))[0] == E_ALIAS     # dX on top of dY
+    assert _mlp_bwd_noalloc(f=12)[0] == E_DIVIS
+    assert _mlp_bwd_noalloc(dt=7)[0] == E_DTYPE
+    assert _mlp_bwd_noalloc(M=0)[0] == E_DIM
+    # arguments that pass validation fail only at the scratch lookup or launch
+    _fails_at_launch(lambda: _mlp_bwd_noalloc()[0])
+
+
 def test_mlp_bwd_workspace_grows_with_split_k():
     # narrow weight-gradient outputs take a split-K workspace of fp32 partials
     small = tp.tp_mlp_bwd_workspace_bytes(BF16, 8192, 1024, 512)
