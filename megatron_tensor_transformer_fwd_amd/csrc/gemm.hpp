@@ -83,7 +83,6 @@ struct TileCfg {
   // may spread over the whole k-tile.
   static_assert(SPA >= 1 && SPA <= KK && (NSA > 2 || SPA < KK), "A DMA spread");
   static_assert(SPB >= 1 && SPB <= KK && (NSB > 2 || SPB < KK), "B DMA spread");
-  static_assert(NSA == 2 || NSB == 2, "one of the rings has one tile of look-ahead");
   static_assert(BARQ >= 0 && BARQ < TM * TN, "barrier position");
   static_assert(NSA >= 2 && NSB >= 2 && SMEM_BYTES <= 160 * 1024, "LDS stages");
 };
@@ -484,7 +483,28 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
   // its last instruction (the other ring's) may still be in flight.  In the
   // prologue, whole tiles were issued: the later tiles of each ring.
   constexpr int VM_PRO = (LA - 1) * NA + (LB - 1) * NB;
-  constexpr int VM_LOOP = [=]() {
+  // At k-tile t's barrier the DMAs of tile t+1 must have landed: the own DMAs
+  // allowed in flight are those issued after the last one of tile t+1.  Found
+  // by walking the issue order of a steady-state k-tile and its predecessors.
+  constexpr int VM_SIM = [=]() {
+    constexpr int L = LA > LB ? LA : LB;
+    const int t = L + 1;                         // a steady-state k-tile
+    int count = 0, after = -1;                   // instructions so far; position after tile t+1's last
+    for (int u = t + 1 - L; u <= t; ++u)
+      for (int kk = 0; kk < KK; ++kk)
+        for (int q = 0; q < Q; ++q) {
+          if (u == t && kk == KK - 1 && q == BARQ) return count - after;
+          for (int r = 0; r < 2; ++r) {
+            const bool is_b = (r == 0) == B_FIRST;
+            const int n = is_b ? NB : NA, sp = is_b ? Cfg::SPB : Cfg::SPA, look = is_b ? LB : LA;
+            const int k = upto(n, sp, kk, q) - before(n, sp, kk, q);
+            count += k;
+            if (k > 0 && u + look == t + 1) after = count;
+          }
+        }
+    return -1;
+  }();
+  constexpr int VM_LOOP_OLD = [=]() {
     const int NN = B_FIRST ? NB : NA, SN = B_FIRST ? Cfg::SPB : Cfg::SPA;   // near ring
     const int NF = B_FIRST ? NA : NB, SF = B_FIRST ? Cfg::SPA : Cfg::SPB;   // far ring
     const bool far_deadline = (B_FIRST ? LA : LB) == 1;
@@ -498,7 +518,9 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
     // and before the barrier
     return upto(NF, SF, KK - 1, BARQ - 1) - before(NF, SF, lk, lq);
   }();
-  static_assert(VM_PRO <= 63 && VM_LOOP <= 63, "vmcnt range");
+  static_assert(NSA != 2 && NSB != 2 || VM_SIM == VM_LOOP_OLD, "issue-order walk agrees with the one-ring rule");
+  constexpr int VM_LOOP = VM_SIM;
+  static_assert(VM_PRO <= 63 && VM_LOOP >= 0 && VM_LOOP <= 63, "vmcnt range");
   static_assert(!DUAL || !B_KM, "dual-B products take N-major right operands");
   static_assert(!DUAL || Cfg::BN == 256, "dual-B tiles hold two 128-column sub-tiles");
 
