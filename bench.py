@@ -549,8 +549,8 @@ def run_c2(tp, torch, steps, warmup):
     dev = lambda a: torch.from_numpy(a).to(bf).cuda()
     M, d, f, n = wl.M, wl.d, wl.f_local, wl.n_shards
     X, dY = dev(inp["X"]), dev(inp["dY"])
-    W1s = [dev(w) for w in inp["W1s"]]
-    W2s = [dev(w) for w in inp["W2s"]]
+    W1st, W2st = dev(np.stack(inp["W1s"])), dev(np.stack(inp["W2s"]))     # shard-stacked
+    W1s, W2s = list(W1st), list(W2st)
     A = torch.empty((n, M, f), dtype=bf, device="cuda")
     H = torch.empty_like(A)
     Zp = torch.empty((n, M, d), dtype=bf, device="cuda")
@@ -560,8 +560,18 @@ def run_c2(tp, torch, steps, warmup):
     dW1 = torch.empty((n, d, f), dtype=torch.float32, device="cuda")
     dW2 = torch.empty((n, f, d), dtype=torch.float32, device="cuda")
     ws = torch.empty(tp.tp_mlp_bwd_workspace_bytes(tp.TP_DT_BF16, M, d, f), dtype=torch.uint8, device="cuda")
+    ws_all = torch.empty(tp.tp_mlp_bwd_shards_workspace_bytes(tp.TP_DT_BF16, n, M, d, f), dtype=torch.uint8,
+                         device="cuda")
 
     def step():
+        # all 8 shards per call, one launch per product over the shards
+        tp.tp_mlp_fwd_shards(X, W1st, W2st, A, H, Zp)
+        tp.tp_shard_reduce(Zp, Z, n, M * d)
+        tp.tp_mlp_bwd_shards(X, W1st, W2st, A, H, dY, dXp, dW1, dW2, ws_all)
+        tp.tp_shard_reduce(dXp, dX, n, M * d)
+
+    def step_per_shard():
+        # the same step as 8 calls per direction, one shard each (one GPU's work in an 8-GPU layer)
         for i in range(n):
             tp.tp_mlp_fwd(X, W1s[i], W2s[i], A[i], H[i], Zp[i])
         tp.tp_shard_reduce(Zp, Z, n, M * d)
@@ -569,8 +579,9 @@ def run_c2(tp, torch, steps, warmup):
             tp.tp_mlp_bwd(X, W1s[i], W2s[i], A[i], H[i], dY, dXp[i], dW1[i], dW2[i], ws)
         tp.tp_shard_reduce(dXp, dX, n, M * d)
 
-    ms, _, per = timed(tp, torch, step, steps, warmup, 8 * 10 + 2, hook_in_timed=False)
+    ms, _, per = timed(tp, torch, step, steps, warmup, 16, hook_in_timed=False)
     gms = graph_timed(torch, step, steps)
+    ms_ps, _, per_ps = timed(tp, torch, step_per_shard, steps, warmup, 8 * 10 + 2, hook_in_timed=False)
     pr = mlp_products(M, d, f)
     flops = n * (products_flops(pr["fwd"]) + products_flops(pr["bwd"]))
     red = per.get("shard_reduce.vec8", [])
@@ -596,6 +607,8 @@ def run_c2(tp, torch, steps, warmup):
             "ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
             "pct_of_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
             "graph_ms_per_step": round(gms, 4), "graph_tflops": round(flops / gms / 1e9, 1),
+            "per_shard_calls": {"ms_per_step": round(ms_ps, 4), "tflops": round(flops / ms_ps / 1e9, 1),
+                                "kernels_ms": {k: round(sum(v) / len(v), 4) for k, v in per_ps.items()}},
             "shard_reduce": {"bytes": rbytes, "warm_ms": round(red_ms, 4) if red_ms else None,
                              "warm_GBps": round(rbytes / red_ms / 1e6, 1) if red_ms else None,
                              "cold_ms": round(cold_ms, 4), "cold_GBps": round(rbytes / cold_ms / 1e6, 1),

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 10
+#define TP_ABI_VERSION 11
 
 /* dtype codes; tp_dtype_t is a plain 32-bit int so that any value a caller
  * passes is well defined on both sides of the ABI, and values other than
@@ -113,6 +113,28 @@ int tp_mlp_bwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
                const void* A, const void* H, const void* dY,
                void* dX, float* dW1, float* dW2, void* ws, size_t ws_bytes);
 size_t tp_mlp_bwd_workspace_bytes(tp_dtype_t dt, int64_t M, int64_t d, int64_t f);
+
+/* ---------------------------------------------------------------------------
+ * tp_mlp_fwd_shards / tp_mlp_bwd_shards — every one of n_shards shards of the
+ * GeLU MLP at once, for a layer whose shards are all held on this GPU (the
+ * local stand-in for the TP group of [HC] 3.4: each shard's products depend
+ * only on X forward and dY backward, so shard i computes exactly what
+ * tp_mlp_fwd / tp_mlp_bwd compute for W1_i, W2_i).  Each product runs as one
+ * launch over the shards.  Shard-stacked layouts (shard i's block follows
+ * shard i-1's): W1s [n_shards x d x f] (shard i's column slice W1_i as its own
+ * [d x f] matrix), W2s [n_shards x f x d]; A, H [n_shards x M x f]; Z, dX
+ * [n_shards x M x d] (the partials that tp_shard_reduce sums); dW1s
+ * [n_shards x d x f] and dW2s [n_shards x f x d], fp32.  X and dY [M x d] are
+ * shared.  1 <= n_shards <= 64; other sizes, dtypes and errors as tp_mlp_fwd /
+ * tp_mlp_bwd; ws: tp_mlp_bwd_shards_workspace_bytes(...) bytes.  Results equal
+ * the per-shard calls' within rounding (the tile shapes may differ).
+ * ------------------------------------------------------------------------- */
+int tp_mlp_fwd_shards(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t M, int64_t d, int64_t f,
+                      const void* X, const void* W1s, const void* W2s, void* A, void* H, void* Z);
+int tp_mlp_bwd_shards(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t M, int64_t d, int64_t f,
+                      const void* X, const void* W1s, const void* W2s, const void* A, const void* H,
+                      const void* dY, void* dX, float* dW1s, float* dW2s, void* ws, size_t ws_bytes);
+size_t tp_mlp_bwd_shards_workspace_bytes(tp_dtype_t dt, int64_t n_shards, int64_t M, int64_t d, int64_t f);
 
 /* ---------------------------------------------------------------------------
  * tp_mlp_bwd_noalloc — tp_mlp_bwd for callers that cannot allocate device

@@ -15,6 +15,7 @@ from typing import Optional
 __all__ = [
     "TPError", "lib", "LIB_PATH", "TP_DT_F32", "TP_DT_BF16",
     "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_workspace_bytes", "tp_mlp_bwd_noalloc", "MLP_BWD_NOALLOC_MAX_WORKSPACE",
+    "tp_mlp_fwd_shards", "tp_mlp_bwd_shards", "tp_mlp_bwd_shards_workspace_bytes",
     "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes",
     "tp_attn_shard_fwd", "tp_attn_gqa_shard_fwd", "tp_attn_shard_bwd", "tp_attn_shard_bwd_workspace_bytes",
     "tp_attn_gqa_shard_bwd", "tp_attn_gqa_shard_bwd_workspace_bytes",
@@ -29,7 +30,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # TPSHARD_LIB selects another build of the same library (the host-sanitizer
 # build of the CPU ABI checks); unset, the in-tree library is loaded.
 LIB_PATH = os.environ.get("TPSHARD_LIB") or os.path.join(HERE, "libtpshard.so")
-ABI_VERSION = 10         # TP_ABI_VERSION of include/tp_shard.h these wrappers are written for
+ABI_VERSION = 11         # TP_ABI_VERSION of include/tp_shard.h these wrappers are written for
 
 TP_DT_F32 = 0
 TP_DT_BF16 = 1
@@ -50,6 +51,9 @@ EXPORTS = {
     "tp_mlp_bwd": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz]),
     "tp_mlp_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
     "tp_mlp_bwd_noalloc": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "tp_mlp_fwd_shards": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
+    "tp_mlp_bwd_shards": (_i32, [_p, _i32, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz]),
+    "tp_mlp_bwd_shards_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i64]),
     "tp_swiglu_fwd": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p]),
     "tp_swiglu_bwd": (_i32, [_p, _i32, _i64, _i64, _i64] + [_p] * 8 + [_p] * 4 + [_p, _sz]),
     "tp_swiglu_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
@@ -228,6 +232,44 @@ def tp_mlp_bwd_noalloc(X, W1, W2, A, H, dY, dX, dW1, dW2, stream=None) -> None:
     _need("dW2", dW2, f * d, _f32())
     _check(lib().tp_mlp_bwd_noalloc(_stream(stream), _dt(X), M, d, f, _ptr(X), _ptr(W1), _ptr(W2), _ptr(A),
                                     _ptr(H), _ptr(dY), _ptr(dX), _ptr(dW1), _ptr(dW2)))
+
+
+def tp_mlp_fwd_shards(X, W1s, W2s, A, H, Z, stream=None) -> None:
+    """Every shard at once: W1s [n x d x f], W2s [n x f x d]; A, H [n x M x f];
+    Z [n x M x d] (the partials)."""
+    n, d, f = W1s.shape
+    M = X.shape[0]
+    dt = X.dtype
+    _need("X", X, M * d, dt)
+    _need("W2s", W2s, n * f * d, dt)
+    _need("A", A, n * M * f, dt, optional=True)
+    _need("H", H, n * M * f, dt)
+    _need("Z", Z, n * M * d, dt)
+    _check(lib().tp_mlp_fwd_shards(_stream(stream), _dt(X), n, M, d, f, _ptr(X), _ptr(W1s), _ptr(W2s), _ptr(A),
+                                   _ptr(H), _ptr(Z)))
+
+
+def tp_mlp_bwd_shards_workspace_bytes(dtype: int, n_shards: int, M: int, d: int, f: int) -> int:
+    return lib().tp_mlp_bwd_shards_workspace_bytes(dtype, n_shards, M, d, f)
+
+
+def tp_mlp_bwd_shards(X, W1s, W2s, A, H, dY, dX, dW1s, dW2s, ws, stream=None) -> None:
+    """Every shard's backward at once: dX [n x M x d] (summands), dW1s
+    [n x d x f] and dW2s [n x f x d] fp32."""
+    n, d, f = W1s.shape
+    M = X.shape[0]
+    dt = X.dtype
+    _need("X", X, M * d, dt)
+    _need("W2s", W2s, n * f * d, dt)
+    for name, t in (("A", A), ("H", H)):
+        _need(name, t, n * M * f, dt)
+    _need("dY", dY, M * d, dt)
+    _need("dX", dX, n * M * d, dt)
+    _need("dW1s", dW1s, n * d * f, _f32())
+    _need("dW2s", dW2s, n * f * d, _f32())
+    _check(lib().tp_mlp_bwd_shards(_stream(stream), _dt(X), n, M, d, f, _ptr(X), _ptr(W1s), _ptr(W2s), _ptr(A),
+                                   _ptr(H), _ptr(dY), _ptr(dX), _ptr(dW1s), _ptr(dW2s), _ptr(ws),
+                                   ws.numel() * ws.element_size()))
 
 
 def tp_swiglu_fwd(X, W1, W3, W2, G, U, H, Z, stream=None) -> None:

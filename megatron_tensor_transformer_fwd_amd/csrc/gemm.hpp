@@ -54,6 +54,11 @@ struct GemmParams {
   int nseg;            // 1 or 2 K segments, summed into one accumulator
   GemmSeg seg[2];
   const bf16* Bz[3];   // batched products: per-batch right operand of segment 0 (or NULL)
+  // Strided batches (grid z = batch, e.g. the shards of a TP layer held on one
+  // GPU): batch z reads segment 0's A at A + z*a_zs and B (B2) at B + z*b_zs,
+  // and its outputs are row-stacked: the epilogue sees row m + z*z_rows.
+  int64_t a_zs, b_zs;
+  int z_rows;
   int tiles_m, tiles_n;
   int split_k;         // K-tile ranges over blockIdx.y
   int tile_base;       // the grid covers tiles tile_base .. tile_base + gridDim.x - 1 of the grouped order
@@ -251,6 +256,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
   const int lrow = lane & 31;
   const int g4 = (lane >> 5) * 4;
   const int split = (int)blockIdx.y;
+  const int64_t zrow = (int64_t)zb * p.z_rows;     // row offset of this batch's outputs
   static_for<Epi::NOUT>([&]<int O>() {
     if (!epi.template has_out<O>()) return;
     using TO = typename Epi::template OutT<O>;
@@ -280,7 +286,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
               const int64_t n = n0 + wn * WTN + j * 32 + 8 * b + g4;
-              if (m < p.M && n < p.N) ax[j][b] = epi.template aux_load<O>(m, n);
+              if (m < p.M && n < p.N) ax[j][b] = epi.template aux_load<O>(m + zrow, n);
             }
         }
 #pragma unroll
@@ -294,15 +300,15 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
               if constexpr (epi_aux<Epi>::value) {
                 static_assert(!DUAL, "auxiliary inputs in single-B products only");
                 const f32x4 a = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2], acc[i][j][4 * b + 3]};
-                v = epi.template value_aux<O>(m, n, a, ax[j][b]);
+                v = epi.template value_aux<O>(m + zrow, n, a, ax[j][b]);
               } else if constexpr (DUAL) {
                 const int jj = j + TN / 2;
                 const f32x4 g = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2], acc[i][j][4 * b + 3]};
                 const f32x4 u = {acc[i][jj][4 * b], acc[i][jj][4 * b + 1], acc[i][jj][4 * b + 2], acc[i][jj][4 * b + 3]};
-                v = epi.template value2<O>(m, n, g, u);
+                v = epi.template value2<O>(m + zrow, n, g, u);
               } else {
                 const f32x4 a = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2], acc[i][j][4 * b + 3]};
-                v = epi.template value<O>(m, n, a);
+                v = epi.template value<O>(m + zrow, n, a);
               }
               const int byte = nl * ES;
               const int pc = (byte >> 4) ^ (r & (CPR - 1));
@@ -323,7 +329,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
           const u32x4 w = *reinterpret_cast<const u32x4*>(smem + r * ROWB + ((c ^ (r & (CPR - 1))) * 16));
           // streaming store: the tile is not read again by this product, and
           // its dirty lines would otherwise compete with the operand stream
-          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(epi.template out_ptr<O>(m, n, split, zb)));
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(epi.template out_ptr<O>(m + zrow, n, split, zb)));
         }
       }
     }
@@ -537,9 +543,12 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
   const int64_t n0 = (int64_t)tn * BNL;
   const int zb = blockIdx.z;
 
-  const SegRegs g0 = seg_regs(p.seg[0]);
+  SegRegs g0 = seg_regs(p.seg[0]);
   const SegRegs g1 = seg_regs(p.seg[1]);
-  const bf16* bz = p.Bz[zb];
+  g0.A += zb * p.a_zs;
+  g0.B += zb * p.b_zs;
+  if (g0.B2) g0.B2 += zb * p.b_zs;
+  const bf16* bz = zb < 3 ? p.Bz[zb] : nullptr;
   const int kt_seg0 = (g0.K + BK - 1) / BK;
   const int kt_total = kt_seg0 + (p.nseg > 1 ? (g1.K + BK - 1) / BK : 0);
   const int kt_begin = (int)(((int64_t)kt_total * blockIdx.y) / p.split_k);

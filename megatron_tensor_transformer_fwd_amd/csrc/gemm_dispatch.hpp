@@ -77,7 +77,10 @@ inline int64_t tiles_for(int cfg, int64_t M, int64_t N, bool dual) {
 constexpr int kTailMaxSplit = 8;
 constexpr double kGemmLaunchS = 4e-6;   // per extra launch
 
-inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow_split, bool allow_tail = false) {
+// nbatch: the launch runs that many products of this shape side by side
+// (grid z), so their tiles share the rounds.
+inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow_split, bool allow_tail = false,
+                          int64_t nbatch = 1) {
   constexpr double CUS = 256.0, CU_FLOPS = 4.4e12, REDUCE_BPS = 4.0e12, LAUNCH_S = kGemmLaunchS;
   const double rate[3] = {1.0, TPK_RATE_M, TPK_RATE_S};
   GemmPlan best{CFG_L, 1};
@@ -86,19 +89,19 @@ inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow
     if (dual && cfg != CFG_L) break;
     const int64_t bm = cfg == CFG_S ? 128 : 256;
     const int64_t bn = cfg == CFG_L ? 256 : 128;   // output columns per tile (dual: two halves)
-    const int64_t tiles = cdiv(M, bm) * cdiv(N, dual ? bn / 2 : bn);
+    const int64_t tiles = cdiv(M, bm) * cdiv(N, dual ? bn / 2 : bn) * nbatch;
     for (int s = 1; s <= (allow_split ? 16 : 1); s *= 2) {
       const int64_t kc = cdiv(K, s);
       if (s > 1 && kc < 512) break;
       const double rounds = std::ceil((double)(tiles * s) / CUS);
       double t = rounds * 2.0 * (double)(bm * bn * kc) / (rate[cfg] * CU_FLOPS);
-      if (s > 1) t += (double)(s + 1) * (double)M * (double)N * 4.0 / REDUCE_BPS + LAUNCH_S;
+      if (s > 1) t += (double)(s + 1) * (double)M * (double)N * (double)nbatch * 4.0 / REDUCE_BPS + LAUNCH_S;
       if (t < best_t * 0.97) {
         best_t = t;
         best = GemmPlan{cfg, s};
       }
     }
-    if (cfg == CFG_L && allow_tail && !dual) {
+    if (cfg == CFG_L && allow_tail && !dual && nbatch == 1) {
       const int64_t full = tiles / 256 * 256, rem = tiles - full;
       const int64_t kt = cdiv(K, 64);
       int ways = rem > 0 ? (int)std::min<int64_t>(kTailMaxSplit, 256 / rem) : 0;
@@ -283,14 +286,17 @@ inline GemmParamsF32 make_params_f32(int64_t M, int64_t N, GemmSegF32 s0) {
 }
 
 // fp32 weight gradient C[Mo x No] = A^T B over K tokens, through the split-K
-// workspace when the plan splits.
+// workspace when the plan splits.  With nbatch > 1 the launch computes
+// nbatch such products (grid z, outputs row-stacked: [nbatch x Mo x No]); the
+// split partials are laid out [split][nbatch][Mo x No] and summed in split
+// order by one reduce over all batches.
 template <class Launch>
 inline hipError_t wgrad_f32_out(hipStream_t st, GemmPlan plan, int64_t Mo, int64_t No,
-                                float* out, float* split_ws, Launch&& run) {
+                                float* out, float* split_ws, Launch&& run, int64_t nbatch = 1) {
   if (plan.split > 1) {
-    EpiStore<float> e{split_ws, No, Mo * No};
+    EpiStore<float> e{split_ws, No, nbatch * Mo * No};
     TPK_TRY(run(e, plan));
-    return launch_shard_reduce(st, DT_F32, DT_F32, plan.split, Mo * No, split_ws, Mo * No,
+    return launch_shard_reduce(st, DT_F32, DT_F32, plan.split, nbatch * Mo * No, split_ws, nbatch * Mo * No,
                                nullptr, 0, out);
   }
   EpiStore<float> e{out, No, 0};

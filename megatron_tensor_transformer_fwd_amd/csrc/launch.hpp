@@ -21,6 +21,13 @@ hipError_t launch_mlp_fwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t 
                           const void* X, const void* W1, const void* W2,
                           void* A, void* H, void* Z);
 size_t mlp_bwd_ws_bytes(int dt, int64_t M, int64_t d, int64_t f);
+// All n shards of the GeLU MLP (shard-stacked weights, activations and outputs).
+hipError_t launch_mlp_fwd_shards(hipStream_t st, int dt, int64_t n, int64_t M, int64_t d, int64_t f,
+                                 const void* X, const void* W1s, const void* W2s, void* A, void* H, void* Z);
+hipError_t launch_mlp_bwd_shards(hipStream_t st, int dt, int64_t n, int64_t M, int64_t d, int64_t f,
+                                 const void* X, const void* W1s, const void* W2s, const void* A, const void* H,
+                                 const void* dY, void* dX, float* dW1s, float* dW2s, void* ws);
+size_t mlp_shards_bwd_ws_bytes(int dt, int64_t n, int64_t M, int64_t d, int64_t f);
 // The current device's address of the allocation-free MLP backward's scratch
 // array (looked up once per device).
 hipError_t mlp_bwd_scratch(void** ptr);

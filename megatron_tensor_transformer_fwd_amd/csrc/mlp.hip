@@ -120,6 +120,121 @@ static hipError_t mlp_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t f,
   return hipSuccess;
 }
 
+// ------------------------------------------- all shards of the layer at once
+// Every shard's products are independent given X (forward) or dY (backward)
+// ([HC] 3.4), so with all n shards held on one GPU each product runs as one
+// launch over the n shards (grid z = shard): the n narrow products fill the
+// chip together where one alone would leave most compute units idle.
+// Weights are shard-stacked ([n x d x f] and [n x f x d]), as are the
+// per-shard activations, partials and weight gradients.
+
+struct MlpShardsPlan {
+  GemmPlan xw1, hw2, htdy, dyw2t, daw1t, xtda;
+  size_t dA_bytes, split_bytes;
+};
+
+static MlpShardsPlan mlp_shards_plan(int64_t n, int64_t M, int64_t d, int64_t f) {
+  MlpShardsPlan pl;
+  pl.xw1 = plan_gemm(M, f, d, false, false, false, n);
+  pl.hw2 = plan_gemm(M, d, f, false, false, false, n);
+  pl.htdy = plan_gemm(f, d, M, false, true, false, n);
+  pl.dyw2t = plan_gemm(M, f, d, false, false, false, n);
+  pl.daw1t = plan_gemm(M, d, f, false, false, false, n);
+  pl.xtda = plan_gemm(d, f, M, false, true, false, n);
+  pl.dA_bytes = align256((size_t)n * M * f * 2);
+  const int smax = std::max(pl.htdy.split, pl.xtda.split);
+  pl.split_bytes = smax > 1 ? align256((size_t)smax * n * d * f * 4) : 0;
+  return pl;
+}
+
+size_t mlp_shards_bwd_ws_bytes(int dt, int64_t n, int64_t M, int64_t d, int64_t f) {
+  if (dt != DT_BF16) return mlp_bwd_ws_bytes(dt, M, d, f);   // fp32: shard by shard, one workspace
+  const MlpShardsPlan pl = mlp_shards_plan(n, M, d, f);
+  return pl.dA_bytes + pl.split_bytes;
+}
+
+hipError_t launch_mlp_fwd_shards(hipStream_t st, int dt, int64_t n, int64_t M, int64_t d, int64_t f,
+                                 const void* X, const void* W1s, const void* W2s, void* A, void* H, void* Z) {
+  if (dt != DT_BF16) {
+    const size_t e = 4;
+    for (int64_t i = 0; i < n; ++i) {
+      auto at = [&](const void* b, int64_t elems) { return static_cast<const char*>(b) + i * elems * e; };
+      auto mt = [&](void* b, int64_t elems) { return b ? static_cast<char*>(b) + i * elems * e : nullptr; };
+      TPK_TRY(launch_mlp_fwd(st, dt, M, d, f, X, at(W1s, d * f), at(W2s, f * d), mt(A, M * f), mt(H, M * f),
+                             mt(Z, M * d)));
+    }
+    return hipSuccess;
+  }
+  const MlpShardsPlan pl = mlp_shards_plan(n, M, d, f);
+  {  // A_i = X W1_i, H_i = GeLU(A_i): X shared, W1_i and the outputs per shard
+    GemmParams p = make_params(M, f, make_seg(X, d, M * d, W1s, f, d * f, d));
+    p.b_zs = d * f;
+    p.z_rows = (int)M;
+    EpiGelu<bf16> e{static_cast<bf16*>(A), static_cast<bf16*>(H), f};
+    TPK_TRY((launch_gemm<true, false, false>(st, "mlp_fwd.xw1_gelu", p, e, pl.xw1, (int)n)));
+  }
+  {  // Z_i = H_i W2_i
+    GemmParams p = make_params(M, d, make_seg(H, f, M * f, W2s, d, f * d, f));
+    p.a_zs = M * f;
+    p.b_zs = f * d;
+    p.z_rows = (int)M;
+    EpiStore<bf16> e{static_cast<bf16*>(Z), d, 0};
+    TPK_TRY((launch_gemm<true, false, false>(st, "mlp_fwd.hw2", p, e, pl.hw2, (int)n)));
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_mlp_bwd_shards(hipStream_t st, int dt, int64_t n, int64_t M, int64_t d, int64_t f,
+                                 const void* X, const void* W1s, const void* W2s, const void* A, const void* H,
+                                 const void* dY, void* dX, float* dW1s, float* dW2s, void* ws) {
+  if (dt != DT_BF16) {
+    const size_t e = 4;
+    for (int64_t i = 0; i < n; ++i) {
+      auto at = [&](const void* b, int64_t elems) { return static_cast<const char*>(b) + i * elems * e; };
+      TPK_TRY(launch_mlp_bwd(st, dt, M, d, f, X, at(W1s, d * f), at(W2s, f * d), at(A, M * f), at(H, M * f), dY,
+                             static_cast<char*>(dX) + i * M * d * e, dW1s + i * d * f, dW2s + i * f * d, ws));
+    }
+    return hipSuccess;
+  }
+  const MlpShardsPlan pl = mlp_shards_plan(n, M, d, f);
+  bf16* dA = static_cast<bf16*>(ws);
+  float* split_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.dA_bytes);
+  {  // dW2_i = H_i^T dY
+    GemmParams p = make_params(f, d, make_seg(H, f, M * f, dY, d, M * d, M));
+    p.a_zs = M * f;
+    p.z_rows = (int)f;
+    TPK_TRY(wgrad_f32_out(
+        st, pl.htdy, f, d, dW2s, split_ws,
+        [&](const EpiStore<float>& e, GemmPlan g) { return launch_gemm<false, false, false>(st, "mlp_bwd.htdy", p, e, g, (int)n); },
+        n));
+  }
+  {  // dA_i = (dY W2_i^T) * GeLU'(A_i)
+    GemmParams p = make_params(M, f, make_seg(dY, d, M * d, W2s, d, f * d, d));
+    p.b_zs = f * d;
+    p.z_rows = (int)M;
+    EpiDGelu<bf16> e{static_cast<const bf16*>(A), dA, f};
+    TPK_TRY((launch_gemm<true, true, false>(st, "mlp_bwd.dyw2t_dgelu", p, e, pl.dyw2t, (int)n)));
+  }
+  {  // dX_i = dA_i W1_i^T
+    GemmParams p = make_params(M, d, make_seg(dA, f, M * f, W1s, f, d * f, f));
+    p.a_zs = M * f;
+    p.b_zs = d * f;
+    p.z_rows = (int)M;
+    EpiStore<bf16> e{static_cast<bf16*>(dX), d, 0};
+    TPK_TRY((launch_gemm<true, true, false>(st, "mlp_bwd.daw1t", p, e, pl.daw1t, (int)n)));
+  }
+  {  // dW1_i = X^T dA_i
+    GemmParams p = make_params(d, f, make_seg(X, d, M * d, dA, f, M * f, M));
+    p.b_zs = M * f;
+    p.z_rows = (int)d;
+    TPK_TRY(wgrad_f32_out(
+        st, pl.xtda, d, f, dW1s, split_ws,
+        [&](const EpiStore<float>& e, GemmPlan g) { return launch_gemm<false, false, false>(st, "mlp_bwd.xtda", p, e, g, (int)n); },
+        n));
+  }
+  return hipSuccess;
+}
+
 // ------------------------------------------------------------------ fp32
 static hipError_t mlp_fwd_f32(hipStream_t st, int64_t M, int64_t d, int64_t f,
                               const void* X, const void* W1, const void* W2,

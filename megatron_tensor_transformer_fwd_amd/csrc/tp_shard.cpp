@@ -249,6 +249,51 @@ int tp_mlp_bwd(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
                     "tp_mlp_bwd");
 }
 
+namespace {
+int mlp_shards_common(tp_dtype_t dt, int64_t n, int64_t M, int64_t d, int64_t f) {
+  TP_CHECK(mlp_common(dt, M, d, f));
+  if (n < 1 || n > 64) return fail(TP_E_DIM, "n_shards = %lld is outside [1, 64]", (long long)n);
+  if ((double)n * (double)M * (double)std::max(d, f) * 2 > 9.0e15) return fail(TP_E_DIM, "operands too large");
+  return TP_OK;
+}
+}  // namespace
+
+int tp_mlp_fwd_shards(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t M, int64_t d, int64_t f,
+                      const void* X, const void* W1s, const void* W2s, void* A, void* H, void* Z) {
+  TP_CHECK(mlp_shards_common(dt, n_shards, M, d, f));
+  const size_t e = esize(dt), n = (size_t)n_shards;
+  TP_CHECK(check_buffers({{"X", X, M * d * e}, {"W1s", W1s, n * d * f * e}, {"W2s", W2s, n * f * d * e}},
+                         {{"A", A, n * M * f * e}, {"H", H, n * M * f * e}, {"Z", Z, n * M * d * e}},
+                         {"X", "W1s", "W2s", "H", "Z"}));
+  return hip_status(tpk::launch_mlp_fwd_shards(static_cast<hipStream_t>(stream), dt, n_shards, M, d, f, X, W1s,
+                                               W2s, A, H, Z),
+                    "tp_mlp_fwd_shards");
+}
+
+size_t tp_mlp_bwd_shards_workspace_bytes(tp_dtype_t dt, int64_t n_shards, int64_t M, int64_t d, int64_t f) {
+  if (mlp_shards_common(dt, n_shards, M, d, f) != TP_OK) return 0;
+  return tpk::mlp_shards_bwd_ws_bytes(dt, n_shards, M, d, f);
+}
+
+int tp_mlp_bwd_shards(void* stream, tp_dtype_t dt, int64_t n_shards, int64_t M, int64_t d, int64_t f,
+                      const void* X, const void* W1s, const void* W2s, const void* A, const void* H,
+                      const void* dY, void* dX, float* dW1s, float* dW2s, void* ws, size_t ws_bytes) {
+  TP_CHECK(mlp_shards_common(dt, n_shards, M, d, f));
+  const size_t e = esize(dt), n = (size_t)n_shards;
+  const size_t need = tpk::mlp_shards_bwd_ws_bytes(dt, n_shards, M, d, f);
+  TP_CHECK(check_buffers(
+      {{"X", X, M * d * e}, {"W1s", W1s, n * d * f * e}, {"W2s", W2s, n * f * d * e}, {"A", A, n * M * f * e},
+       {"H", H, n * M * f * e}, {"dY", dY, M * d * e}},
+      {{"dX", dX, n * M * d * e}, {"dW1s", dW1s, n * d * f * (size_t)4}, {"dW2s", dW2s, n * f * d * (size_t)4},
+       {"ws", ws, need}},
+      {"X", "W1s", "W2s", "A", "H", "dY", "dX", "dW1s", "dW2s"}));
+  if (!ws || ws_bytes < need)
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes given, %zu required", ws ? ws_bytes : (size_t)0, need);
+  return hip_status(tpk::launch_mlp_bwd_shards(static_cast<hipStream_t>(stream), dt, n_shards, M, d, f, X, W1s, W2s,
+                                               A, H, dY, dX, dW1s, dW2s, ws),
+                    "tp_mlp_bwd_shards");
+}
+
 int tp_mlp_bwd_noalloc(void* stream, tp_dtype_t dt, int64_t M, int64_t d, int64_t f,
                        const void* X, const void* W1, const void* W2, const void* A, const void* H,
                        const void* dY, void* dX, float* dW1, float* dW2) {

@@ -144,6 +144,32 @@ def test_mlp_bwd_noalloc_validation_and_limit():
     _fails_at_launch(lambda: _mlp_bwd_noalloc()[0])
 
 
+def test_mlp_shards_validation():
+    """The all-shards entry points: n_shards in [1, 64], the shard-stacked
+    extents in the overlap checks, and the workspace."""
+    L = tp.lib()
+    X, W1s, W2s, A, H, Z, dY, dX, dW1s, dW2s, ws = _addrs(11)
+    fwd = lambda **kw: L.tp_mlp_fwd_shards(*dict(dict(stream=None, dt=BF16, n=4, M=64, d=64, f=128, X=X, W1s=W1s,
+                                                      W2s=W2s, A=A, H=H, Z=Z), **kw).values())
+    assert fwd(n=0) == E_DIM and fwd(n=65) == E_DIM
+    assert fwd(W2s=None) == E_NULL and fwd(f=12) == E_DIVIS and fwd(dt=3) == E_DTYPE
+    # H holds 4 shards of [64 x 128] bf16 = 64 KiB: a Z starting inside it overlaps
+    assert fwd(Z=H + 4 * 64 * 128 * 2 - 16) == E_ALIAS
+    _fails_at_launch(lambda: fwd(Z=H + 4 * 64 * 128 * 2))
+    need = L.tp_mlp_bwd_shards_workspace_bytes(BF16, 4, 64, 64, 128)
+    assert need >= 4 * 64 * 128 * 2
+    assert L.tp_mlp_bwd_shards_workspace_bytes(BF16, 0, 64, 64, 128) == 0
+    assert L.tp_mlp_bwd_shards_workspace_bytes(F32, 4, 64, 64, 128) == L.tp_mlp_bwd_workspace_bytes(F32, 64, 64, 128)
+    bwd = lambda **kw: L.tp_mlp_bwd_shards(*dict(dict(stream=None, dt=BF16, n=4, M=64, d=64, f=128, X=X, W1s=W1s,
+                                                      W2s=W2s, A=A, H=H, dY=dY, dX=dX, dW1s=dW1s, dW2s=dW2s, ws=ws,
+                                                      ws_bytes=need), **kw).values())
+    assert bwd(ws_bytes=need - 1) == E_WS
+    assert bwd(dW1s=BASE + 4) == E_ALIGN
+    assert bwd(dX=dY + 16) == E_ALIAS
+    assert bwd(n=100) == E_DIM
+    _fails_at_launch(lambda: bwd())
+
+
 def test_mlp_bwd_workspace_grows_with_split_k():
     # narrow weight-gradient outputs take a split-K workspace of fp32 partials
     small = tp.tp_mlp_bwd_workspace_bytes(BF16, 8192, 1024, 512)

@@ -282,6 +282,74 @@ def test_mlp_c2_all_shards_and_reduces(tp):
     check("dX", dX, O.mlp_unsharded_bwd(inp["X"], inp["W1"], inp["W2"], inp["dY"])["dX"], "bf16")
 
 
+def run_mlp_shards(tp, X, W1s, W2s, dY, dtype):
+    """Every shard in one call per direction (tp_mlp_fwd_shards / _bwd_shards)."""
+    n, d, f = W1s.shape
+    M = X.shape[0]
+    A, H = empty((n, M, f), dtype), empty((n, M, f), dtype)
+    Z, dX = empty((n, M, d), dtype), empty((n, M, d), dtype)
+    dW1 = torch.empty((n, d, f), dtype=torch.float32, device="cuda")
+    dW2 = torch.empty((n, f, d), dtype=torch.float32, device="cuda")
+    dt = tp.TP_DT_BF16 if dtype == "bf16" else tp.TP_DT_F32
+    ws = torch.empty(tp.tp_mlp_bwd_shards_workspace_bytes(dt, n, M, d, f), dtype=torch.uint8, device="cuda")
+    tp.tp_mlp_fwd_shards(X, W1s, W2s, A, H, Z)
+    tp.tp_mlp_bwd_shards(X, W1s, W2s, A, H, dY, dX, dW1, dW2, ws)
+    torch.cuda.synchronize()
+    return dict(A=A, H=H, Z=Z, dX=dX, dW1=dW1, dW2=dW2)
+
+
+def test_mlp_c2_shards_in_one_call(tp):
+    """C2's 8 shards through the all-shards entry points: every tensor of
+    every shard against the oracle, and both shard-reduces against the
+    unsharded layer."""
+    _say("mlp C2 bf16, all 8 shards per call + Z/dX shard-reduce")
+    wl = tpsynth.WORKLOADS["C2"]
+    inp = tpsynth.mlp_inputs(wl)
+    M, d = inp["X"].shape
+    n = wl.n_shards
+    W1s = dev(np.stack(inp["W1s"]), "bf16")
+    W2s = dev(np.stack(inp["W2s"]), "bf16")
+    out = run_mlp_shards(tp, dev(inp["X"], "bf16"), W1s, W2s, dev(inp["dY"], "bf16"), "bf16")
+    for i in range(n):
+        ref = O.mlp_shard_fwd(inp["X"], inp["W1s"][i], inp["W2s"][i])
+        refb = O.mlp_shard_bwd(inp["X"], inp["W1s"][i], inp["W2s"][i], inp["dY"])
+        for k in ("A", "H", "Z"):
+            check(f"{k}_{i}", out[k][i], ref[k], "bf16")
+        for k in ("dX", "dW1", "dW2"):
+            check(f"{k}_{i}", out[k][i], refb[k], "bf16")
+    Z, dX = empty((M, d), "bf16"), empty((M, d), "bf16")
+    tp.tp_shard_reduce(out["Z"], Z, n, M * d)
+    tp.tp_shard_reduce(out["dX"], dX, n, M * d)
+    torch.cuda.synchronize()
+    check("Y", Z, O.mlp_unsharded(inp["X"], inp["W1"], inp["W2"]), "bf16")
+    check("dX", dX, O.mlp_unsharded_bwd(inp["X"], inp["W1"], inp["W2"], inp["dY"])["dX"], "bf16")
+
+
+@pytest.mark.parametrize("dtype,n,M,d,f", [
+    ("bf16", 3, 300, 72, 40),       # ragged in every dimension
+    ("bf16", 5, 1000, 520, 264),    # several tiles, ragged tails
+    ("bf16", 1, 64, 64, 128),
+    ("f32", 2, 32, 64, 128),        # C1's shape
+    ("f32", 3, 100, 40, 24),
+])
+def test_mlp_shards_ragged(tp, dtype, n, M, d, f):
+    _say(f"mlp all shards per call {dtype} n={n} M={M} d={d} f={f}")
+    inp = tpsynth.random_mlp(M, d, n * f, dtype, seed=M + n)
+    W1s = np.stack([inp["W1"][:, i * f:(i + 1) * f] for i in range(n)])
+    W2s = np.stack([inp["W2"][i * f:(i + 1) * f] for i in range(n)])
+    out = run_mlp_shards(tp, dev(inp["X"], dtype), dev(W1s, dtype), dev(W2s, dtype), dev(inp["dY"], dtype), dtype)
+    for i in range(n):
+        ref = O.mlp_shard_fwd(inp["X"], W1s[i], W2s[i])
+        refb = O.mlp_shard_bwd(inp["X"], W1s[i], W2s[i], inp["dY"])
+        for k in ("A", "H", "Z"):
+            check(f"{k}_{i}", out[k][i], ref[k], dtype)
+        for k in ("dX", "dW1", "dW2"):
+            check(f"{k}_{i}", out[k][i], refb[k], dtype)
+    # the shards' Z sum to the unsharded layer's output
+    full = O.mlp_unsharded(inp["X"], inp["W1"], inp["W2"])
+    check("sum Z", host(out["Z"]).sum(axis=0), full, dtype)
+
+
 def test_mlp_bwd_bitwise_deterministic(tp):
     _say("mlp C2-shard backward twice, bitwise")
     wl = tpsynth.WORKLOADS["C2"]
