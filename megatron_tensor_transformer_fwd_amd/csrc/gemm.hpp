@@ -60,7 +60,7 @@ struct GemmParams {
   int64_t a_zs, b_zs;
   int z_rows;
   int tiles_m, tiles_n;
-  int split_k;         // K-tile ranges over blockIdx.y
+  int split_k;         // K-tile ranges (grid y)
   int tile_base;       // the grid covers tiles tile_base .. tile_base + gridDim.x - 1 of the grouped order
 };
 
@@ -210,13 +210,26 @@ __host__ __device__ inline int position_of(int tm, int tn, int tiles_m, int tile
   return g * kTileGroup * tiles_n + tn * gsize + (tm - first_m);
 }
 
-__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int base,
-                                            int& tm, int& tn) {
+// Workgroup -> (tile position lx, K split ly, batch lz) and its XCD.  The
+// hardware hands consecutive workgroup ids (x fastest, then y, then z) to
+// the 8 XCDs in turn; the whole grid is remapped so that each XCD runs one
+// contiguous range of the logical order (split slowest, then batch, then the
+// grouped tile order).  The tiles an XCD runs together then share operand
+// slices in its L2: the same K range of a split product, the same batch.
+// A one-dimensional grid keeps the plain XCD-contiguous tile order.
+__device__ __forceinline__ void grid_coords(int& lx, int& ly, int& lz, int& xcd) {
   constexpr int NXCD = 8;
-  const int q = nblocks / NXCD, r = nblocks % NXCD;
-  const int xcd = bid % NXCD, local = bid / NXCD;
+  const int nx = (int)gridDim.x, ny = (int)gridDim.y, nz = (int)gridDim.z;
+  const int total = nx * ny * nz;
+  const int lin = (int)blockIdx.x + nx * ((int)blockIdx.y + ny * (int)blockIdx.z);
+  const int q = total / NXCD, r = total % NXCD;
+  xcd = lin % NXCD;
+  const int local = lin / NXCD;
   const int t = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
-  tile_of(base + t, tiles_m, tiles_n, tm, tn);
+  lx = t % nx;
+  const int t2 = t / nx;
+  lz = t2 % nz;
+  ly = t2 / nz;
 }
 
 template <int N, class F>
@@ -250,12 +263,11 @@ template <class E> struct epi_aux_type<E, true> { using type = typename E::Aux; 
 template <class Cfg, bool DUAL, class Epi>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN], const GemmParams& p,
                                            const Epi& epi, int64_t m0, int64_t n0, int wm, int wn,
-                                           int lane, int zb, char* smem, int tid) {
+                                           int lane, int zb, int split, char* smem, int tid) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM, WTN = Cfg::WTN, BM = Cfg::BM;
   constexpr int BNL = DUAL ? Cfg::BN / 2 : Cfg::BN;
   const int lrow = lane & 31;
   const int g4 = (lane >> 5) * 4;
-  const int split = (int)blockIdx.y;
   const int64_t zrow = (int64_t)zb * p.z_rows;     // row offset of this batch's outputs
   static_for<Epi::NOUT>([&]<int O>() {
     if (!epi.template has_out<O>()) return;
@@ -537,11 +549,11 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.tile_base, tm, tn);
+  int lx, split, zb, xcd, tm, tn;
+  grid_coords(lx, split, zb, xcd);
+  tile_of(p.tile_base + lx, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * Cfg::BM;
   const int64_t n0 = (int64_t)tn * BNL;
-  const int zb = blockIdx.z;
 
   SegRegs g0 = seg_regs(p.seg[0]);
   const SegRegs g1 = seg_regs(p.seg[1]);
@@ -551,12 +563,12 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
   const bf16* bz = zb < 3 ? p.Bz[zb] : nullptr;
   const int kt_seg0 = (g0.K + BK - 1) / BK;
   const int kt_total = kt_seg0 + (p.nseg > 1 ? (g1.K + BK - 1) / BK : 0);
-  const int kt_begin = (int)(((int64_t)kt_total * blockIdx.y) / p.split_k);
-  const int kt_end = (int)(((int64_t)kt_total * (blockIdx.y + 1)) / p.split_k);
+  const int kt_begin = (int)(((int64_t)kt_total * split) / p.split_k);
+  const int kt_end = (int)(((int64_t)kt_total * (split + 1)) / p.split_k);
   const int T = kt_end - kt_begin;
   const uint32_t lds0 = lds_addr(smem);
   // k-tile processed at step t (t >= T: past the end, loads that are never read)
-  const int rot = (Cfg::ROT && T > 0) ? (int)(((int64_t)(blockIdx.x % 8) * T) / 8) : 0;
+  const int rot = (Cfg::ROT && T > 0) ? (int)(((int64_t)xcd * T) / 8) : 0;
   auto kt_of = [&](int t) {
     const int u = t + rot;
     return kt_begin + (u >= T ? u - T : u);
@@ -644,7 +656,7 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
     });
   }
 
-  store_tile<Cfg, DUAL>(acc, p, epi, m0, n0, wm, wn, lane, zb, smem, tid);
+  store_tile<Cfg, DUAL>(acc, p, epi, m0, n0, wm, wn, lane, zb, split, smem, tid);
 }
 
 }  // namespace tpk
