@@ -121,152 +121,220 @@ __global__ void __launch_bounds__(256) attn_bwd_rowdot_kernel(const bf16* __rest
   L2[(bi * hl + h) * s + t] = L[(bi * hl + h) * s + t] * attnb::kLog2e;   // log-sum-exp in base 2
 }
 
-// Key-tile kernel: dK and dV of 128 keys (four waves of 32) of one (batch,
-// query head), streaming 64-query chunks of Q and dO.  Lanes index keys: the
-// accumulators of S = Q K^T and dP = dO V^T hold, per lane, one key and 16
-// queries, exactly the operand layout of dV += P^T dO and dK += dS^T Q.  With
+// Key-tile kernel: dK and dV of 128 keys of one (batch, query head),
+// streaming 64-query chunks of Q and dO.  Lanes index keys: the accumulators
+// of S = Q K^T and dP = dO V^T hold, per lane, one key and 16 queries,
+// exactly the operand layout of dV += P^T dO and dK += dS^T Q.  With
 // grouped-query attention (group > 1) the keys and values are those of K/V
 // head h / group, and the outputs are this query head's fp32 contributions,
 // summed over the group afterwards.
+//
+// Eight waves in two roles per block of 32 keys (two waves per SIMD):
+//  * P waves (0-3) recompute S for chunk c, form P = exp2(S scale log2e - L2),
+//    hand P (bf16, in their register order) to their partner through LDS and
+//    accumulate dV += P^T dO;
+//  * dS waves (4-7) run one chunk behind: in step c they form
+//    dS = P (dP - D) for chunk c-1 from their partner's P and the dP they
+//    computed in step c-1, accumulate dK += dS^T Q, then compute dP for chunk c.
+// On every SIMD one role's softmax or dS arithmetic overlaps the other's
+// MFMAs.  Chunks rotate through three LDS stages (the dS waves still read
+// chunk c-1 while chunk c+1 is loading) and P through two buffers; one
+// barrier per step orders them.
 template <class TO>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(512, 1)
 attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                     const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dv,
                     TO* __restrict__ dK, TO* __restrict__ dV, int nb, int hl, int group, int s, int causal,
                     float scale, int64_t ld_o, int64_t ld_g) {
   using namespace attnb;
-  constexpr int BKEY = 128, BQ = 64;
+  constexpr int BKEY = 128, BQ = 64, NSTG = 3;
   constexpr int QT = BQ * ROWB, VEC = BQ * 4;
   constexpr int STAGE = 2 * QT + 2 * VEC;            // Q, dO, L, D
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr int PWAVE = 64 * 64;                     // one P wave's chunk of P: 64 lanes x four bf16x8
+  constexpr int PBUF = NW * PWAVE;
+  __shared__ __attribute__((aligned(1024))) char smem[NSTG * STAGE + 2 * PBUF];
 
-  const int nkt = (s + BKEY - 1) / BKEY;
   const int nbh = nb * hl;
   const int kt = (int)(blockIdx.x / nbh);            // key tile 0 (most queries) first
   const int bh = (int)(blockIdx.x % nbh);
   const int bi = bh / hl, h = bh % hl;
-  (void)nkt;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool prole = wave < NW;                       // uniform per wave
+  const int kb = wave & (NW - 1);                     // this wave's block of 32 keys
   const int lk = lane & 31, g = lane >> 5;
-  const int k0 = kt * BKEY, kw = k0 + wave * 32, key = kw + lk;
+  const int k0 = kt * BKEY, kw = k0 + kb * 32, key = kw + lk;
   const int64_t head = (int64_t)bh * s * D;
   const int64_t kvhead = ((int64_t)bi * (hl / group) + h / group) * s * D;
   const uint32_t lds0 = lds_addr(smem);
+  char* pbuf = smem + NSTG * STAGE;
   const float sl2 = scale * kLog2e;
 
-  // This wave's keys and values as row fragments (zero past the sequence).
-  bf16x8 kf[D / 16], vf[D / 16];
+  // P waves hold their keys, dS waves their values, as row fragments (zero
+  // past the sequence).
+  bf16x8 kvf[D / 16];
   {
-    const rsrc_t rk = make_rsrc(K + kvhead, (uint64_t)s * ROWB);
-    const rsrc_t rv = make_rsrc(V + kvhead, (uint64_t)s * ROWB);
+    const rsrc_t r = make_rsrc((prole ? K : V) + kvhead, (uint64_t)s * ROWB);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const uint32_t off = (uint32_t)(((int64_t)key * D + kk * 16 + g * 8) * 2);
-      kf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
-      vf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
-    }
+    for (int kk = 0; kk < D / 16; ++kk)
+      kvf[kk] = __builtin_bit_cast(bf16x8, buf_load16(r, (uint32_t)(((int64_t)key * D + kk * 16 + g * 8) * 2)));
   }
 
   const int nqc = (s + BQ - 1) / BQ;
   const int c_begin = causal ? k0 / BQ : 0;
+  // Q rows by the P waves, dO rows by the dS waves, L and D by one wave each.
   auto issue = [&](int c) {
     const int q0 = c * BQ;
-    const uint32_t st = lds0 + (uint32_t)((c & 1) * STAGE);
-    dma_rows<BQ>(range_desc(Q + head + (int64_t)q0 * D, (int64_t)(s - q0) * ROWB), ROWB, st, wave, lane);
-    const bf16* dorow = dO + ((int64_t)bi * s + q0) * ld_o + (int64_t)h * D;
-    dma_rows<BQ>(range_desc(dorow, (int64_t)(s - q0 - 1) * ld_o * 2 + ROWB), (uint32_t)(ld_o * 2), st + QT, wave,
-                 lane);
-    if (wave == 0) dma_vec(range_desc(L2 + (int64_t)bh * s + q0, (int64_t)(s - q0) * 4), st + 2 * QT, lane * 4u);
-    if (wave == 1) dma_vec(range_desc(Dv + (int64_t)bh * s + q0, (int64_t)(s - q0) * 4), st + 2 * QT + VEC, lane * 4u);
+    const uint32_t st = lds0 + (uint32_t)((c % NSTG) * STAGE);
+    if (prole) {
+      dma_rows<BQ>(range_desc(Q + head + (int64_t)q0 * D, (int64_t)(s - q0) * ROWB), ROWB, st, kb, lane);
+      if (kb == 0) dma_vec(range_desc(L2 + (int64_t)bh * s + q0, (int64_t)(s - q0) * 4), st + 2 * QT, lane * 4u);
+    } else {
+      const bf16* dorow = dO + ((int64_t)bi * s + q0) * ld_o + (int64_t)h * D;
+      dma_rows<BQ>(range_desc(dorow, (int64_t)(s - q0 - 1) * ld_o * 2 + ROWB), (uint32_t)(ld_o * 2), st + QT, kb,
+                   lane);
+      if (kb == 0) dma_vec(range_desc(Dv + (int64_t)bh * s + q0, (int64_t)(s - q0) * 4), st + 2 * QT + VEC, lane * 4u);
+    }
   };
+  // chunk c has a query at or after one of this block's keys
+  auto live = [&](int c) { return c >= c_begin && c < nqc && !(causal && c * BQ + BQ - 1 < kw); };
+  // the mask matters only where a pair can be past the sequence or (causal) a key after a query
+  auto masked = [&](int c) { return c * BQ + BQ > s || (causal && kw + 31 > c * BQ); };
 
-  f32x16 adk[D / 32], adv[D / 32];
+  f32x16 acc[D / 32];                                 // dV (P waves) or dK (dS waves)
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) adk[i] = adv[i] = f32x16{};
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
 
+  // The two roles run separate loops with the same steps and one barrier per
+  // step, so that each role's registers are allocated on their own.
   if (c_begin < nqc) issue(c_begin);
-  for (int c = c_begin; c < nqc; ++c) {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (c + 1 < nqc) issue(c + 1);
-    const int q0 = c * BQ;
-    if (causal && q0 + BQ - 1 < kw) continue;        // every query precedes this wave's keys
-    const char* Qs = smem + (c & 1) * STAGE;
-    const char* dOs = Qs + QT;
-    const float* Ls = reinterpret_cast<const float*>(Qs + 2 * QT);
-    const float* Ds = Ls + BQ;
-
-    // S[key][q] and dP[key][q] for two 32-query blocks (four independent chains)
-    f32x16 sacc[2], pacc[2];
+  if (prole) {
+    for (int c = c_begin; c <= nqc; ++c) {
+      // chunk c landed (own DMAs), every wave done with step c-1: chunk c-2's
+      // stage and the P buffer of chunk c-2 are free again
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (c + 1 < nqc) issue(c + 1);
+      if (!live(c)) continue;
+      const char* st = smem + (c % NSTG) * STAGE;
+      const int q0 = c * BQ;
+      const char* Qs = st;
+      const char* dOs = st + QT;
+      const float* Ls = reinterpret_cast<const float*>(st + 2 * QT);
+      f32x16 sacc[2];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+      for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Qs, qb * 32, kk, lane),
-                                                           kf[kk],
-                                                           kk ? sacc[qb] : f32x16{}, 0, 0, 0);
-        pacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(dOs, qb * 32, kk, lane),
-                                                           vf[kk],
-                                                           kk ? pacc[qb] : f32x16{}, 0, 0, 0);
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Qs, qb * 32, kk, lane), kvf[kk],
+                                                             kk ? sacc[qb] : f32x16{}, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // keep fragment reads next to their MFMAs (register budget)
       }
-    // register r of block qb: query q0 + qb*32 + 8 (r/4) + 4 g + r%4.  The
-    // mask is evaluated only where some (key, query) pair of the wave can be
-    // out of range: past the sequence, or a key after a query (causal).
-    bf16x8 pf[2][2], sf[2][2];
-    auto softmax = [&]<bool MASK>() {
+      // register r of block qb: query q0 + qb*32 + 8 (r/4) + 4 g + r%4
+      bf16x8 pf[2][2];
+      auto softmax = [&]<bool MASK>() {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int ql = qb * 32 + 8 * r4 + 4 * g;    // first of four consecutive queries
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql);
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int ql = qb * 32 + 8 * r4 + 4 * g;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e, q = q0 + ql + e;
-            float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], sl2, -l4[e]));
-            if constexpr (MASK) p = (q < s && (!causal || key <= q)) ? p : 0.f;
-            sacc[qb][r] = p;
-            pacc[qb][r] = p * (pacc[qb][r] - d4[e]);
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * r4 + e, q = q0 + ql + e;
+              float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][r], sl2, -l4[e]));
+              if constexpr (MASK) p = (q < s && (!causal || key <= q)) ? p : 0.f;
+              sacc[qb][r] = p;
+            }
+          }
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) pf[qb][hh] = pack8(sacc[qb], 8 * hh);
+        }
+      };
+      if (masked(c)) softmax.template operator()<true>();
+      else softmax.template operator()<false>();
+      char* pw = pbuf + (c & 1) * PBUF + kb * PWAVE;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) *reinterpret_cast<bf16x8*>(pw + (qb * 2 + hh) * 1024 + lane * 16) = pf[qb][hh];
+      // dV[key][d] += P^T dO (four d blocks)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_col(dOs, db * 32, qb * 32 + hh * 16, lane),
+                                                              pf[qb][hh], acc[db], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  } else {
+    f32x16 dp[2];                                     // dP of the previous chunk
+    dp[0] = dp[1] = f32x16{};
+    for (int c = c_begin; c <= nqc; ++c) {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (c + 1 < nqc) issue(c + 1);
+      if (live(c - 1)) {
+        // dS = P (dP - D) for chunk c-1, then dK[key][d] += dS^T Q
+        const char* sp = smem + ((c - 1) % NSTG) * STAGE;
+        const char* Qp = sp;
+        const float* Dp = reinterpret_cast<const float*>(sp + 2 * QT + VEC);
+        const char* pr = pbuf + ((c - 1) & 1) * PBUF + kb * PWAVE;
+        bf16x8 sf[2][2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const u32x4 pw = *reinterpret_cast<const u32x4*>(pr + (qb * 2 + hh) * 1024 + lane * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * hh + 2 * e;                     // registers r, r+1
+              const int ql = qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+              const float d0 = Dp[ql], d1 = Dp[ql + 1];
+              dp[qb][r] = bf16_lo(pw[e]) * (dp[qb][r] - d0);
+              dp[qb][r + 1] = bf16_hi(pw[e]) * (dp[qb][r + 1] - d1);
+            }
+            sf[qb][hh] = pack8(dp[qb], 8 * hh);
           }
         }
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          pf[qb][hh] = pack8(sacc[qb], 8 * hh);
-          sf[qb][hh] = pack8(pacc[qb], 8 * hh);
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_col(Qp, db * 32, qb * 32 + hh * 16, lane),
+                                                                sf[qb][hh], acc[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+      if (live(c)) {
+        const char* dOs = smem + (c % NSTG) * STAGE + QT;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(dOs, qb * 32, kk, lane), kvf[kk],
+                                                             kk ? dp[qb] : f32x16{}, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-    };
-    if (q0 + BQ > s || (causal && kw + 31 > q0)) softmax.template operator()<true>();
-    else softmax.template operator()<false>();
-    // dV[key][d] += P^T dO, dK[key][d] += dS^T Q (four d blocks each, interleaved)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          adv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_col(dOs, db * 32, qb * 32 + hh * 16, lane),
-                                                            pf[qb][hh], adv[db], 0, 0, 0);
-          adk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_col(Qs, db * 32, qb * 32 + hh * 16, lane),
-                                                            sf[qb][hh], adk[db], 0, 0, 0);
-        }
+    }
   }
 
   // register r of block db: d = db*32 + 8 (r/4) + 4 g + r%4 of key `key`
   if (key < s) {
-    TO* krow = dK + ((int64_t)bi * s + key) * ld_g + (int64_t)h * D;
-    TO* vrow = dV + ((int64_t)bi * s + key) * ld_g + (int64_t)h * D;
+    TO* row = (prole ? dV : dK) + ((int64_t)bi * s + key) * ld_g + (int64_t)h * D;
+    const float f = prole ? 1.0f : scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int b4 = 0; b4 < 4; ++b4) {
         const int c = db * 32 + 8 * b4 + 4 * g;
-        const f32x4 kv = {adk[db][4 * b4] * scale, adk[db][4 * b4 + 1] * scale, adk[db][4 * b4 + 2] * scale,
-                          adk[db][4 * b4 + 3] * scale};
-        const f32x4 vv = {adv[db][4 * b4], adv[db][4 * b4 + 1], adv[db][4 * b4 + 2], adv[db][4 * b4 + 3]};
-        Quad<TO>::store(krow + c, kv);
-        Quad<TO>::store(vrow + c, vv);
+        const f32x4 v = {acc[db][4 * b4] * f, acc[db][4 * b4 + 1] * f, acc[db][4 * b4 + 2] * f,
+                         acc[db][4 * b4 + 3] * f};
+        Quad<TO>::store(row + c, v);
       }
   }
 }
@@ -452,10 +520,10 @@ hipError_t launch_attn_bwd_flash(hipStream_t st, int b, int hl, int group, int s
   const int nbh = b * hl;
   const unsigned grid = (unsigned)(((s + 127) / 128) * nbh);
   if (group == 1) {  // dK, dV straight into their columns of [dQ | dK | dV]
-    TPK_TRY(launch("attn_bwd.dkv", attn_bwd_dkv_kernel<bf16>, dim3(grid), dim3(256), st, Q, K, V, dO, L2, Dv,
+    TPK_TRY(launch("attn_bwd.dkv", attn_bwd_dkv_kernel<bf16>, dim3(grid), dim3(512), st, Q, K, V, dO, L2, Dv,
                    dQKV + n_q, dQKV + n_q + n_kv, b, hl, 1, s, causal, scale, ld_o, ld_g));
   } else {  // per-query-head contributions, then the ordered sum over each group
-    TPK_TRY(launch("attn_bwd.dkv", attn_bwd_dkv_kernel<float>, dim3(grid), dim3(256), st, Q, K, V, dO, L2, Dv,
+    TPK_TRY(launch("attn_bwd.dkv", attn_bwd_dkv_kernel<float>, dim3(grid), dim3(512), st, Q, K, V, dO, L2, Dv,
                    part_k, part_v, b, hl, group, s, causal, scale, ld_o, n_q));
     const int64_t rows = (int64_t)b * s;
     const int64_t n = rows * n_kv / 8;
