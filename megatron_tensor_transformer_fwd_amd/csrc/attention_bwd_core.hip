@@ -19,8 +19,8 @@
 // index keys, so P arrives in the layout the dK/dV products consume), the
 // query-tile kernel owns dQ of 128 queries (lanes index queries, as in the
 // forward).  Tiles stream through LDS by DMA with a 16-byte-chunk swizzle
-// c ^ (row % 16) that serves both the row-wise fragment reads and the
-// transposing ds_read_b64_tr_b16 reads.
+// (swz below) that keeps both the row-wise fragment reads and the
+// transposing ds_read_b64_tr_b16 reads free of bank conflicts.
 //
 // This file holds the flash kernels and their launchers; the products and
 // the workspace layout are in attention_bwd.hip.  It is compiled with the
@@ -36,6 +36,17 @@ constexpr int D = 128, NT = 256, NW = 4;
 constexpr int ROWB = D * 2;                   // bytes per tile row
 constexpr float kLog2e = 1.4426950408889634f;
 
+// 16-byte chunk c of tile row r is stored at chunk c ^ swz(r), swz a
+// permutation of r's low four bits r3 r2 r1 r0 into (r3^r1^r0, r0, r1, r2).
+// The row fragments read 8 (or 16) consecutive rows at one chunk; each
+// 16-lane group of a transposing read reads 4 consecutive rows at 2 (or 4)
+// adjacent aligned chunks.  Both then fall on distinct chunks modulo 8 and
+// modulo 16, so neither pattern has bank conflicts whether the LDS serves
+// 128 or 256 bytes per cycle.
+__device__ __forceinline__ int swz(int row) {
+  return ((row >> 2) & 1) | (row & 2) | ((row & 1) << 2) | ((((row >> 3) ^ (row >> 1) ^ row) & 1) << 3);
+}
+
 // DMA of `rows` rows of 128 bf16 (row pitch `ld_b` bytes in memory) into a
 // swizzled LDS tile: 4 rows per 1 KiB instruction; NI instructions per wave.
 template <int ROWS>
@@ -46,7 +57,7 @@ __device__ __forceinline__ void dma_rows(desc_t r, uint32_t ld_b, uint32_t lds, 
   for (int j = 0; j < NI; ++j) {
     const int ins = wave * NI + j;
     const int row = ins * 4 + (lane >> 4);
-    const int lc = (lane & 15) ^ (row & 15);
+    const int lc = (lane & 15) ^ swz(row);
     dma16(r, lds + ins * 1024, (uint32_t)row * ld_b + (uint32_t)lc * 16u);
   }
 }
@@ -60,7 +71,7 @@ __device__ __forceinline__ void dma_vec(desc_t r, uint32_t lds, uint32_t voff) {
 // Row fragment: lane l holds row row0 + l%32, columns kk*16 + 8 (l/32) .. +8.
 __device__ __forceinline__ bf16x8 frag_row(const char* t, int row0, int kk, int lane) {
   const int row = row0 + (lane & 31);
-  const int pc = (kk * 2 + (lane >> 5)) ^ (row & 15);
+  const int pc = (kk * 2 + (lane >> 5)) ^ swz(row);
   return *reinterpret_cast<const bf16x8*>(t + row * ROWB + pc * 16);
 }
 
@@ -74,8 +85,8 @@ __device__ __forceinline__ bf16x8 frag_col(const char* t, int d0, int r0, int la
   const int G = lane >> 4, i = lane & 15;
   const int col = d0 + 16 * (G & 1) + 4 * (i & 3);
   const int k = r0 + 4 * (G >> 1) + (i >> 2);
-  const char* plo = t + k * ROWB + (((col >> 3) ^ (k & 15)) * 16) + (col & 7) * 2;
-  const char* phi = t + (k + 8) * ROWB + (((col >> 3) ^ ((k + 8) & 15)) * 16) + (col & 7) * 2;
+  const char* plo = t + k * ROWB + (((col >> 3) ^ swz(k)) * 16) + (col & 7) * 2;
+  const char* phi = t + (k + 8) * ROWB + (((col >> 3) ^ swz(k + 8)) * 16) + (col & 7) * 2;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(plo));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(phi));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
