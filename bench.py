@@ -329,6 +329,15 @@ def mlp_product_bytes(M, d, f):
             "mlp_bwd.xtda": M * d * b + M * f * b + d * f * 4}            # X, dA -> dW1
 
 
+def oracle_mlp_step_flops(M, d, f):
+    """(the GPU step's FLOPs, the FLOPs the fp64 oracle executes for the same
+    step).  The oracle's backward recomputes A = X W1 from its inputs, so it
+    runs the step's six products plus that one."""
+    pr = mlp_products(M, d, f)
+    step = products_flops(pr["fwd"]) + products_flops(pr["bwd"])
+    return step, step + gemm_flops(*pr["fwd"][0])
+
+
 # ------------------------------------------------------------ headline (C5)
 def run_headline(tp, torch, wl, steps, warmup):
     import tpsynth
@@ -473,11 +482,7 @@ def cpu_baseline(wl, inp, outs, torch, rows_n=None):
     fw = O.mlp_shard_fwd(X, W1, W2)
     bw = O.mlp_shard_bwd(X, W1, W2, dY)
     secs = time.perf_counter() - t
-    # the oracle's backward recomputes A = X W1 from its inputs, so it runs
-    # the six products of the step plus that one
-    pr = mlp_products(len(rows), wl.d, wl.f_local)
-    step_fl = products_flops(pr["fwd"]) + products_flops(pr["bwd"])
-    fl = step_fl + gemm_flops(*pr["fwd"][0])
+    step_fl, fl = oracle_mlp_step_flops(len(rows), wl.d, wl.f_local)
     host = lambda name: outs[name].float().cpu().numpy()
     pairs = [(k, host(k)[rows], fw[k]) for k in ("A", "H", "Z")] + [("dX", host("dX")[rows], bw["dX"])]
     if rows_n is None:

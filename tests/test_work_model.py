@@ -117,3 +117,30 @@ def test_hbm_kernel_bytes_are_tensor_sizes():
     rows = np.zeros((owned, d), np.float16)
     assert bench.vocab_embed_bytes(T, d, owned) == size(ids, rows, np.zeros((T, d), np.float16))
     assert bench.vocab_embed_bwd_bytes(T, d, vl, owned) == size(ids, rows, np.zeros((vl, d), np.float32))
+
+
+def test_oracle_step_flops_count_the_oracles_products(monkeypatch):
+    """The CPU baseline's FLOP count equals what the oracle's MLP forward and
+    backward actually multiply: every matrix product they perform is recorded
+    (2 m n k each) through an ndarray subclass handed in for their inputs."""
+    import oracle.tp_oracle as T
+    seen = []
+
+    class Counted(np.ndarray):
+        def __matmul__(self, other):
+            a, b = np.asarray(self), np.asarray(other)
+            seen.append(2 * a.shape[0] * a.shape[1] * b.shape[1])
+            return (a @ b).view(Counted)
+
+    monkeypatch.setattr(T, "_f64", lambda a: np.asarray(a, dtype=np.float64).view(Counted))
+    M, d, f = 24, 16, 8
+    r = np.random.default_rng(0)
+    X, W1, W2, dY = r.standard_normal((M, d)), r.standard_normal((d, f)), r.standard_normal((f, d)), \
+        r.standard_normal((M, d))
+    T.mlp_shard_fwd(X, W1, W2)
+    fwd = sum(seen)
+    T.mlp_shard_bwd(X, W1, W2, dY)
+    step, executed = bench.oracle_mlp_step_flops(M, d, f)
+    assert len(seen) == 7
+    assert sum(seen) == executed
+    assert executed - step == fwd / 2         # the one recomputed forward product
