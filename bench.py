@@ -510,7 +510,8 @@ def run_c1(tp, torch, steps, warmup):
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
     M, d, f, n = wl.M, wl.d, wl.f_local, wl.n_shards
     X, dY = dev(inp["X"]), dev(inp["dY"])
-    W1s, W2s = [dev(w) for w in inp["W1s"]], [dev(w) for w in inp["W2s"]]
+    W1st, W2st = dev(np.stack(inp["W1s"])), dev(np.stack(inp["W2s"]))     # shard-stacked
+    W1s, W2s = list(W1st), list(W2st)
     f32 = torch.float32
     A, H = (torch.empty((n, M, f), dtype=f32, device="cuda") for _ in range(2))
     Zp, dXp = (torch.empty((n, M, d), dtype=f32, device="cuda") for _ in range(2))
@@ -518,8 +519,17 @@ def run_c1(tp, torch, steps, warmup):
     dW1 = torch.empty((n, d, f), dtype=f32, device="cuda")
     dW2 = torch.empty((n, f, d), dtype=f32, device="cuda")
     ws = torch.empty(tp.tp_mlp_bwd_workspace_bytes(tp.TP_DT_F32, M, d, f), dtype=torch.uint8, device="cuda")
+    ws_all = torch.empty(tp.tp_mlp_bwd_shards_workspace_bytes(tp.TP_DT_F32, n, M, d, f), dtype=torch.uint8,
+                         device="cuda")
 
     def step():
+        # both shards per call, one launch per product over the shards
+        tp.tp_mlp_fwd_shards(X, W1st, W2st, A, H, Zp)
+        tp.tp_shard_reduce(Zp, Z, n, M * d)
+        tp.tp_mlp_bwd_shards(X, W1st, W2st, A, H, dY, dXp, dW1, dW2, ws_all)
+        tp.tp_shard_reduce(dXp, dX, n, M * d)
+
+    def step_per_shard():
         for i in range(n):
             tp.tp_mlp_fwd(X, W1s[i], W2s[i], A[i], H[i], Zp[i])
         tp.tp_shard_reduce(Zp, Z, n, M * d)
@@ -527,7 +537,9 @@ def run_c1(tp, torch, steps, warmup):
             tp.tp_mlp_bwd(X, W1s[i], W2s[i], A[i], H[i], dY, dXp[i], dW1[i], dW2[i], ws)
         tp.tp_shard_reduce(dXp, dX, n, M * d)
 
-    ms, _, per = timed(tp, torch, step, steps, warmup, 2 * (2 + 4) + 2, hook_in_timed=False)
+    ms_ps, _, _ = timed(tp, torch, step_per_shard, steps, warmup, 2 * (2 + 4) + 2, hook_in_timed=False)
+    gms_ps = graph_timed(torch, step_per_shard, steps)
+    ms, _, per = timed(tp, torch, step, steps, warmup, 2 + 4 + 2, hook_in_timed=False)
     gms = graph_timed(torch, step, steps)
     W1, W2 = np.concatenate(inp["W1s"], axis=1), np.concatenate(inp["W2s"], axis=0)
     ref = O.mlp_unsharded_bwd(inp["X"], W1, W2, inp["dY"])
@@ -540,6 +552,7 @@ def run_c1(tp, torch, steps, warmup):
     return {"workload": "C1 tiny fp32 GeLU MLP, X [32x64], W1 [64x256], W2 [256x64], 2 TP shards of 128: both "
                         "shards fwd+bwd + Z and dX shard-reduce",
             "us_per_step": round(1e3 * ms, 2), "graph_us_per_step": round(1e3 * gms, 2), "flop_per_step": flops,
+            "per_shard_calls": {"us_per_step": round(1e3 * ms_ps, 2), "graph_us_per_step": round(1e3 * gms_ps, 2)},
             "max_rel_err": {k: float(f"{O.max_rel_err(y, r):.3e}") for k, y, r in pairs},
             "per_element_rel_err": {k: float(f"{O.per_element_rel_err(y, r):.3e}") for k, y, r in pairs},
             "tolerance": 1e-5,

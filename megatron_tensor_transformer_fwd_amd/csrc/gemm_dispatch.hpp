@@ -254,9 +254,19 @@ inline GemmParams make_params(int64_t M, int64_t N, GemmSeg s0) {
 }
 
 // fp32 path
+// nbatch > 1: one product per batch (grid z = batch x column tiles), operands
+// advanced by p.a_zs / p.b_zs elements per batch, outputs row-stacked by p.z_rows.
 template <bool A_KM, bool B_KM, bool DUAL, class Epi>
-hipError_t launch_gemm_f32(hipStream_t st, const char* label, GemmParamsF32 p, const Epi& epi) {
-  const dim3 grid((unsigned)cdiv(p.M, 64), (unsigned)p.split_k, (unsigned)cdiv(p.N, 64));
+hipError_t launch_gemm_f32(hipStream_t st, const char* label, GemmParamsF32 p, const Epi& epi, int nbatch = 1) {
+  p.tiles_n = (int)cdiv(p.N, 64);
+  auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  bool vec = (p.a_zs % 4 == 0) && (p.b_zs % 4 == 0);
+  for (int s = 0; s < p.nseg; ++s) {
+    const GemmSegF32& g = p.seg[s];
+    vec = vec && al16(g.A) && al16(g.B) && (!DUAL || al16(g.B2)) && g.lda % 4 == 0 && g.ldb % 4 == 0;
+  }
+  p.vec = vec ? 1 : 0;
+  const dim3 grid((unsigned)cdiv(p.M, 64), (unsigned)p.split_k, (unsigned)(p.tiles_n * nbatch));
   return launch(label, gemm_f32_kernel<A_KM, B_KM, DUAL, Epi>, grid, dim3(256), st, p, epi);
 }
 

@@ -120,6 +120,74 @@ static hipError_t mlp_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t f,
   return hipSuccess;
 }
 
+// ------------------------------------------------------------------ fp32
+// n shards per launch (n = 1: one shard), shard-stacked as in the bf16 path;
+// dA ([n x M x f]) lives in the workspace.
+static hipError_t mlp_fwd_f32(hipStream_t st, int64_t n, int64_t M, int64_t d, int64_t f,
+                              const void* X, const void* W1s, const void* W2s,
+                              void* A, void* H, void* Z) {
+  {  // A_i = X W1_i, H_i = GeLU(A_i)
+    GemmParamsF32 p = make_params_f32(M, f, make_seg_f32(X, d, M, W1s, f, f, d));
+    p.b_zs = d * f;
+    p.z_rows = (int)M;
+    EpiGelu<float> e{static_cast<float*>(A), static_cast<float*>(H), f};
+    TPK_TRY((launch_gemm_f32<true, false, false>(st, "mlp_f32.nn", p, e, (int)n)));
+  }
+  {  // Z_i = H_i W2_i
+    GemmParamsF32 p = make_params_f32(M, d, make_seg_f32(H, f, M, W2s, d, d, f));
+    p.a_zs = M * f;
+    p.b_zs = f * d;
+    p.z_rows = (int)M;
+    EpiStore<float> e{static_cast<float*>(Z), d, 0};
+    TPK_TRY((launch_gemm_f32<true, false, false>(st, "mlp_f32.nn", p, e, (int)n)));
+  }
+  return hipSuccess;
+}
+
+static hipError_t mlp_bwd_f32(hipStream_t st, int64_t n, int64_t M, int64_t d, int64_t f,
+                              const void* X, const void* W1s, const void* W2s,
+                              const void* A, const void* H, const void* dY,
+                              void* dX, float* dW1s, float* dW2s, void* ws) {
+  float* dA = static_cast<float*>(ws);
+  {  // dA_i = (dY W2_i^T) * GeLU'(A_i)
+    GemmParamsF32 p = make_params_f32(M, f, make_seg_f32(dY, d, M, W2s, d, f, d));
+    p.b_zs = f * d;
+    p.z_rows = (int)M;
+    EpiDGelu<float> e{static_cast<const float*>(A), dA, f};
+    TPK_TRY((launch_gemm_f32<true, true, false>(st, "mlp_f32.nt", p, e, (int)n)));
+  }
+  {  // dW2_i = H_i^T dY
+    GemmParamsF32 p = make_params_f32(f, d, make_seg_f32(H, f, f, dY, d, d, M));
+    p.a_zs = M * f;
+    p.z_rows = (int)f;
+    EpiStore<float> e{dW2s, d, 0};
+    TPK_TRY((launch_gemm_f32<false, false, false>(st, "mlp_f32.tn", p, e, (int)n)));
+  }
+  {  // dX_i = dA_i W1_i^T
+    GemmParamsF32 p = make_params_f32(M, d, make_seg_f32(dA, f, M, W1s, f, d, f));
+    p.a_zs = M * f;
+    p.b_zs = d * f;
+    p.z_rows = (int)M;
+    EpiStore<float> e{static_cast<float*>(dX), d, 0};
+    TPK_TRY((launch_gemm_f32<true, true, false>(st, "mlp_f32.nt", p, e, (int)n)));
+  }
+  {  // dW1_i = X^T dA_i
+    GemmParamsF32 p = make_params_f32(d, f, make_seg_f32(X, d, d, dA, f, f, M));
+    p.b_zs = M * f;
+    p.z_rows = (int)d;
+    EpiStore<float> e{dW1s, f, 0};
+    TPK_TRY((launch_gemm_f32<false, false, false>(st, "mlp_f32.tn", p, e, (int)n)));
+  }
+  return hipSuccess;
+}
+
+// Shards per fp32 launch: all of them while the grid's z extent (shards x
+// column tiles of the widest product) stays within the launch limit.
+static int64_t f32_shards_per_launch(int64_t n, int64_t d, int64_t f) {
+  const int64_t tiles = cdiv(std::max(d, f), 64);
+  return std::max<int64_t>(1, std::min<int64_t>(n, 65535 / tiles));
+}
+
 // ------------------------------------------- all shards of the layer at once
 // Every shard's products are independent given X (forward) or dY (backward)
 // ([HC] 3.4), so with all n shards held on one GPU each product runs as one
@@ -148,7 +216,8 @@ static MlpShardsPlan mlp_shards_plan(int64_t n, int64_t M, int64_t d, int64_t f)
 }
 
 size_t mlp_shards_bwd_ws_bytes(int dt, int64_t n, int64_t M, int64_t d, int64_t f) {
-  if (dt != DT_BF16) return mlp_bwd_ws_bytes(dt, M, d, f);   // fp32: shard by shard, one workspace
+  if (dt != DT_BF16)   // fp32: dA of the shards one launch covers
+    return align256((size_t)f32_shards_per_launch(n, d, f) * M * f * 4);
   const MlpShardsPlan pl = mlp_shards_plan(n, M, d, f);
   return pl.dA_bytes + pl.split_bytes;
 }
@@ -156,12 +225,13 @@ size_t mlp_shards_bwd_ws_bytes(int dt, int64_t n, int64_t M, int64_t d, int64_t 
 hipError_t launch_mlp_fwd_shards(hipStream_t st, int dt, int64_t n, int64_t M, int64_t d, int64_t f,
                                  const void* X, const void* W1s, const void* W2s, void* A, void* H, void* Z) {
   if (dt != DT_BF16) {
-    const size_t e = 4;
-    for (int64_t i = 0; i < n; ++i) {
-      auto at = [&](const void* b, int64_t elems) { return static_cast<const char*>(b) + i * elems * e; };
-      auto mt = [&](void* b, int64_t elems) { return b ? static_cast<char*>(b) + i * elems * e : nullptr; };
-      TPK_TRY(launch_mlp_fwd(st, dt, M, d, f, X, at(W1s, d * f), at(W2s, f * d), mt(A, M * f), mt(H, M * f),
-                             mt(Z, M * d)));
+    const int64_t per = f32_shards_per_launch(n, d, f);
+    for (int64_t i = 0; i < n; i += per) {
+      const int64_t k = std::min(per, n - i);
+      auto at = [&](const void* b, int64_t elems) { return static_cast<const float*>(b) + i * elems; };
+      auto mt = [&](void* b, int64_t elems) { return b ? static_cast<float*>(b) + i * elems : nullptr; };
+      TPK_TRY(mlp_fwd_f32(st, k, M, d, f, X, at(W1s, d * f), at(W2s, f * d), mt(A, M * f), mt(H, M * f),
+                          mt(Z, M * d)));
     }
     return hipSuccess;
   }
@@ -188,11 +258,12 @@ hipError_t launch_mlp_bwd_shards(hipStream_t st, int dt, int64_t n, int64_t M, i
                                  const void* X, const void* W1s, const void* W2s, const void* A, const void* H,
                                  const void* dY, void* dX, float* dW1s, float* dW2s, void* ws) {
   if (dt != DT_BF16) {
-    const size_t e = 4;
-    for (int64_t i = 0; i < n; ++i) {
-      auto at = [&](const void* b, int64_t elems) { return static_cast<const char*>(b) + i * elems * e; };
-      TPK_TRY(launch_mlp_bwd(st, dt, M, d, f, X, at(W1s, d * f), at(W2s, f * d), at(A, M * f), at(H, M * f), dY,
-                             static_cast<char*>(dX) + i * M * d * e, dW1s + i * d * f, dW2s + i * f * d, ws));
+    const int64_t per = f32_shards_per_launch(n, d, f);
+    for (int64_t i = 0; i < n; i += per) {
+      const int64_t k = std::min(per, n - i);
+      auto at = [&](const void* b, int64_t elems) { return static_cast<const float*>(b) + i * elems; };
+      TPK_TRY(mlp_bwd_f32(st, k, M, d, f, X, at(W1s, d * f), at(W2s, f * d), at(A, M * f), at(H, M * f), dY,
+                          static_cast<float*>(dX) + i * M * d, dW1s + i * d * f, dW2s + i * f * d, ws));
     }
     return hipSuccess;
   }
@@ -235,56 +306,11 @@ hipError_t launch_mlp_bwd_shards(hipStream_t st, int dt, int64_t n, int64_t M, i
   return hipSuccess;
 }
 
-// ------------------------------------------------------------------ fp32
-static hipError_t mlp_fwd_f32(hipStream_t st, int64_t M, int64_t d, int64_t f,
-                              const void* X, const void* W1, const void* W2,
-                              void* A, void* H, void* Z) {
-  {
-    GemmParamsF32 p = make_params_f32(M, f, make_seg_f32(X, d, M, W1, f, f, d));
-    EpiGelu<float> e{static_cast<float*>(A), static_cast<float*>(H), f};
-    TPK_TRY((launch_gemm_f32<true, false, false>(st, "mlp_f32.nn", p, e)));
-  }
-  {
-    GemmParamsF32 p = make_params_f32(M, d, make_seg_f32(H, f, M, W2, d, d, f));
-    EpiStore<float> e{static_cast<float*>(Z), d, 0};
-    TPK_TRY((launch_gemm_f32<true, false, false>(st, "mlp_f32.nn", p, e)));
-  }
-  return hipSuccess;
-}
-
-static hipError_t mlp_bwd_f32(hipStream_t st, int64_t M, int64_t d, int64_t f,
-                              const void* X, const void* W1, const void* W2,
-                              const void* A, const void* H, const void* dY,
-                              void* dX, float* dW1, float* dW2, void* ws) {
-  float* dA = static_cast<float*>(ws);
-  {
-    GemmParamsF32 p = make_params_f32(M, f, make_seg_f32(dY, d, M, W2, d, f, d));
-    EpiDGelu<float> e{static_cast<const float*>(A), dA, f};
-    TPK_TRY((launch_gemm_f32<true, true, false>(st, "mlp_f32.nt", p, e)));
-  }
-  {
-    GemmParamsF32 p = make_params_f32(f, d, make_seg_f32(H, f, f, dY, d, d, M));
-    EpiStore<float> e{dW2, d, 0};
-    TPK_TRY((launch_gemm_f32<false, false, false>(st, "mlp_f32.tn", p, e)));
-  }
-  {
-    GemmParamsF32 p = make_params_f32(M, d, make_seg_f32(dA, f, M, W1, f, d, f));
-    EpiStore<float> e{static_cast<float*>(dX), d, 0};
-    TPK_TRY((launch_gemm_f32<true, true, false>(st, "mlp_f32.nt", p, e)));
-  }
-  {
-    GemmParamsF32 p = make_params_f32(d, f, make_seg_f32(X, d, d, dA, f, f, M));
-    EpiStore<float> e{dW1, f, 0};
-    TPK_TRY((launch_gemm_f32<false, false, false>(st, "mlp_f32.tn", p, e)));
-  }
-  return hipSuccess;
-}
-
 hipError_t launch_mlp_fwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t f,
                           const void* X, const void* W1, const void* W2,
                           void* A, void* H, void* Z) {
   return dt == DT_BF16 ? mlp_fwd_bf16(st, M, d, f, X, W1, W2, A, H, Z)
-                       : mlp_fwd_f32(st, M, d, f, X, W1, W2, A, H, Z);
+                       : mlp_fwd_f32(st, 1, M, d, f, X, W1, W2, A, H, Z);
 }
 
 hipError_t launch_mlp_bwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t f,
@@ -292,7 +318,7 @@ hipError_t launch_mlp_bwd(hipStream_t st, int dt, int64_t M, int64_t d, int64_t 
                           const void* A, const void* H, const void* dY,
                           void* dX, float* dW1, float* dW2, void* ws) {
   return dt == DT_BF16 ? mlp_bwd_bf16(st, M, d, f, X, W1, W2, A, H, dY, dX, dW1, dW2, ws)
-                       : mlp_bwd_f32(st, M, d, f, X, W1, W2, A, H, dY, dX, dW1, dW2, ws);
+                       : mlp_bwd_f32(st, 1, M, d, f, X, W1, W2, A, H, dY, dX, dW1, dW2, ws);
 }
 
 }  // namespace tpk

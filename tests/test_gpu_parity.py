@@ -350,6 +350,34 @@ def test_mlp_shards_ragged(tp, dtype, n, M, d, f):
     check("sum Z", host(out["Z"]).sum(axis=0), full, dtype)
 
 
+def test_mlp_shards_f32_beyond_one_launch(tp):
+    """fp32 shards whose launch grid would exceed the z limit (64 shards x
+    1024 column tiles of f = 65536) run in groups of shards: every tensor of
+    the first, a middle and the last shard against the oracle.  W1's columns
+    and W2's rows are zero outside 16 positions per shard (the same ones), so
+    the 65536-long sums have at most 16 nonzero terms and the fp32 results
+    stay within the fp32 tolerance; the positions include both ends of f."""
+    n, M, d, f = 64, 8, 8, 65536
+    _say(f"mlp all shards per call f32 n={n} M={M} d={d} f={f} (shard groups)")
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((M, d)).astype(np.float32)
+    dY = rng.standard_normal((M, d)).astype(np.float32)
+    W1s = np.zeros((n, d, f), np.float32)
+    W2s = np.zeros((n, f, d), np.float32)
+    for i in range(n):
+        cols = np.unique(np.concatenate([[0, f - 1], rng.choice(f, 14, replace=False)]))
+        W1s[i][:, cols] = rng.standard_normal((d, cols.size)).astype(np.float32)
+        W2s[i][cols, :] = rng.standard_normal((cols.size, d)).astype(np.float32)
+    out = run_mlp_shards(tp, dev(X, "f32"), dev(W1s, "f32"), dev(W2s, "f32"), dev(dY, "f32"), "f32")
+    for i in (0, 31, 62, 63):
+        ref = O.mlp_shard_fwd(X, W1s[i], W2s[i])
+        refb = O.mlp_shard_bwd(X, W1s[i], W2s[i], dY)
+        for k in ("A", "H", "Z"):
+            check(f"{k}_{i}", out[k][i], ref[k], "f32")
+        for k in ("dX", "dW1", "dW2"):
+            check(f"{k}_{i}", out[k][i], refb[k], "f32")
+
+
 def test_mlp_bwd_bitwise_deterministic(tp):
     _say("mlp C2-shard backward twice, bitwise")
     wl = tpsynth.WORKLOADS["C2"]
