@@ -132,6 +132,30 @@ __global__ void __launch_bounds__(256) attn_bwd_rowdot_kernel(const bf16* __rest
   L2[(bi * hl + h) * s + t] = L[(bi * hl + h) * s + t] * attnb::kLog2e;   // log-sum-exp in base 2
 }
 
+// acc[db] += B^T X over a 64-row chunk: B the four bf16x8 operand quarters
+// (32 rows x 16 per quarter, rows qb*32 + hh*16..) in register order, X the
+// chunk's rows read transposed from LDS tile T (four 32-column blocks).  The
+// fragments of quarter i+1 are read before quarter i's MFMAs issue.
+__device__ __forceinline__ void acc_cols(f32x16 (&acc)[attnb::D / 32], const char* T, const bf16x8 (&B)[2][2],
+                                         int lane) {
+  using namespace attnb;
+  bf16x8 fc[2][D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) fc[0][db] = frag_col(T, db * 32, 0, lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qb = i >> 1, hh = i & 1;
+    if (i + 1 < 4)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        fc[(i + 1) & 1][db] = frag_col(T, db * 32, ((i + 1) >> 1) * 32 + ((i + 1) & 1) * 16, lane);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc[i & 1][db], B[qb][hh], acc[db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Key-tile kernel: dK and dV of 128 keys of one (batch, query head),
 // streaming 64-query chunks of Q and dO.  Lanes index keys: the accumulators
 // of S = Q K^T and dP = dO V^T hold, per lane, one key and 16 queries,
@@ -232,13 +256,21 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
       const char* dOs = st + QT;
       const float* Ls = reinterpret_cast<const float*>(st + 2 * QT);
       f32x16 sacc[2];
+      {  // fragments of step kk+1 are read before step kk's MFMAs issue
+        bf16x8 fr[2][2];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+        for (int qb = 0; qb < 2; ++qb) fr[0][qb] = frag_row(Qs, qb * 32, 0, lane);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(Qs, qb * 32, kk, lane), kvf[kk],
-                                                             kk ? sacc[qb] : f32x16{}, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);   // keep fragment reads next to their MFMAs (register budget)
+        for (int kk = 0; kk < D / 16; ++kk) {
+          if (kk + 1 < D / 16)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) fr[(kk + 1) & 1][qb] = frag_row(Qs, qb * 32, kk + 1, lane);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk & 1][qb], kvf[kk], kk ? sacc[qb] : f32x16{},
+                                                               0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       // register r of block qb: query q0 + qb*32 + 8 (r/4) + 4 g + r%4
       bf16x8 pf[2][2];
@@ -268,17 +300,9 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) *reinterpret_cast<bf16x8*>(pw + (qb * 2 + hh) * 1024 + lane * 16) = pf[qb][hh];
-      // dV[key][d] += P^T dO (four d blocks)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_col(dOs, db * 32, qb * 32 + hh * 16, lane),
-                                                              pf[qb][hh], acc[db], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      // dV[key][d] += P^T dO (four d blocks); each quarter's fragments are
+      // read before the previous quarter's MFMAs issue
+      acc_cols(acc, dOs, pf, lane);
     }
   } else {
     f32x16 dp[2];                                     // dP of the previous chunk
@@ -309,25 +333,22 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
             sf[qb][hh] = pack8(dp[qb], 8 * hh);
           }
         }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_col(Qp, db * 32, qb * 32 + hh * 16, lane),
-                                                                sf[qb][hh], acc[db], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+        acc_cols(acc, Qp, sf, lane);
       }
       if (live(c)) {
         const char* dOs = smem + (c % NSTG) * STAGE + QT;
+        bf16x8 fr[2][2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) fr[0][qb] = frag_row(dOs, qb * 32, 0, lane);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
+          if (kk + 1 < D / 16)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) fr[(kk + 1) & 1][qb] = frag_row(dOs, qb * 32, kk + 1, lane);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
-            dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_row(dOs, qb * 32, kk, lane), kvf[kk],
-                                                             kk ? dp[qb] : f32x16{}, 0, 0, 0);
+            dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk & 1][qb], kvf[kk], kk ? dp[qb] : f32x16{}, 0,
+                                                             0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
