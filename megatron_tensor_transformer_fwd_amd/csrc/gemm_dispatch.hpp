@@ -59,6 +59,16 @@ inline int64_t tiles_for(int cfg, int64_t M, int64_t N, bool dual) {
 #ifndef TPK_RATE_S
 #define TPK_RATE_S 0.60
 #endif
+// Batched split-K weight gradients (all shards of a layer in one launch):
+// the S shape's 64 KiB of LDS lets two of its workgroups share a CU, and on
+// eight 512 x 1024 shard gradients over 8192 tokens two 128 x 128 tiles per
+// CU over K 4096 take as long as one 256 x 256 tile over K 2048, with half
+// the fp32 partials to reduce.  On unbatched products the pairing did not
+// hold (forward products, dgrads and the other workloads' gradients were
+// 3-6% slower), so the paired rate is used for this case only.
+#ifndef TPK_RATE_S2
+#define TPK_RATE_S2 0.95
+#endif
 
 // Tile shape and K split of a product: the choice with the smallest
 // estimated duration, where a launch takes ceil(tiles / 256) rounds of tiles
@@ -93,8 +103,10 @@ inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow
     for (int s = 1; s <= (allow_split ? 16 : 1); s *= 2) {
       const int64_t kc = cdiv(K, s);
       if (s > 1 && kc < 512) break;
-      const double rounds = std::ceil((double)(tiles * s) / CUS);
-      double t = rounds * 2.0 * (double)(bm * bn * kc) / (rate[cfg] * CU_FLOPS);
+      const double tile_flop = 2.0 * (double)(bm * bn * kc);
+      double t = std::ceil((double)(tiles * s) / CUS) * tile_flop / (rate[cfg] * CU_FLOPS);
+      if (cfg == CFG_S && allow_split && nbatch > 1 && tiles * s > 256)   // two S tiles per CU
+        t = std::ceil((double)(tiles * s) / (2.0 * CUS)) * 2.0 * tile_flop / (TPK_RATE_S2 * CU_FLOPS);
       if (s > 1) t += (double)(s + 1) * (double)M * (double)N * (double)nbatch * 4.0 / REDUCE_BPS + LAUNCH_S;
       if (t < best_t * 0.97) {
         best_t = t;
