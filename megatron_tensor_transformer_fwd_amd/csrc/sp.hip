@@ -243,18 +243,44 @@ sp_ln_bwd_kernel(const T* __restrict__ P, int64_t stride, int n, int64_t row0, i
 #pragma unroll
     for (int e = 0; e < 8; ++e) agam[k][e] = abet[k][e] = abias[k][e] = 0.f;
   const float inv_cols = 1.0f / (float)cols;
+  // With two chunks per thread (rows up to 8192 values) gamma is read once
+  // per workgroup and a row's residual gradient and mask loads go out with
+  // its partials', although they are used only after the row's three
+  // reductions.  With four chunks the registers are not there (the fp32
+  // variant would spill), and they are read where they are used.
+  constexpr bool EARLY = CH <= 2;
+  float gam[EARLY ? CH : 1][8];
+  if constexpr (EARLY) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int64_t c = ((int64_t)k * NTH + threadIdx.x) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gam[k][e] = 0.f;
+      if (c < cols) Vec8<T>::load(gamma + c, gam[k]);
+    }
+  }
 
   for (int rr = 0; rr < R; ++rr) {
     const int64_t r = (int64_t)blockIdx.x * R + rr;
     if (r >= k_rows) break;                          // uniform over the workgroup
     const int64_t src = (row0 + r) * cols, dst = r * cols;
-    float dx[CH][8], hv[CH][8];
+    float dx[CH][8], hv[CH][8], dr[EARLY ? CH : 1][8];
+    u32x2 km[EARLY ? CH : 1];
     float hsum = 0.f;
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int64_t c = ((int64_t)k * NTH + threadIdx.x) * 8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dx[k][e] = hv[k][e] = 0.f;
+      if constexpr (EARLY) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dr[k][e] = 0.f;
+        km[k] = u32x2{0x01010101u, 0x01010101u};
+        if (c < cols) {
+          if (dres) Vec8<T>::template load<kNtIn>(dres + dst + c, dr[k]);
+          if (keep) km[k] = ld16<kNtIn>(reinterpret_cast<const u32x2*>(keep + dst + c));
+        }
+      }
       if (c < cols) {
         const T* p = P + src + c;
         constexpr int SB = sizeof(T) == 2 ? 8 : 4;      // shards' loads in flight
@@ -296,7 +322,12 @@ sp_ln_bwd_kernel(const T* __restrict__ P, int64_t stride, int n, int64_t row0, i
       const int64_t c = ((int64_t)k * NTH + threadIdx.x) * 8;
       if (c < cols) {
         float g[8];
-        Vec8<T>::load(gamma + c, g);
+        if constexpr (EARLY) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) g[e] = gam[k][e];
+        } else {
+          Vec8<T>::load(gamma + c, g);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float xh = (hv[k][e] - mean) * rstd;
@@ -312,15 +343,24 @@ sp_ln_bwd_kernel(const T* __restrict__ P, int64_t stride, int n, int64_t row0, i
     for (int k = 0; k < CH; ++k) {
       const int64_t c = ((int64_t)k * NTH + threadIdx.x) * 8;
       if (c < cols) {
-        float g[8], dr[8], dh[8], dy[8];
-        Vec8<T>::load(gamma + c, g);
-        if (dres) Vec8<T>::template load<kNtIn>(dres + dst + c, dr);
+        float g[8], r8[8], dh[8], dy[8];
         u32x2 m = {0x01010101u, 0x01010101u};
-        if (keep) m = ld16<kNtIn>(reinterpret_cast<const u32x2*>(keep + dst + c));
+        if constexpr (EARLY) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            g[e] = gam[k][e];
+            r8[e] = dr[k][e];
+          }
+          m = km[k];
+        } else {
+          Vec8<T>::load(gamma + c, g);
+          if (dres) Vec8<T>::template load<kNtIn>(dres + dst + c, r8);
+          if (keep) m = ld16<kNtIn>(reinterpret_cast<const u32x2*>(keep + dst + c));
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float xh = (hv[k][e] - mean) * rstd;
-          dh[e] = rstd * (dx[k][e] * g[e] - m1 - xh * m2) + (dres ? dr[e] : 0.f);
+          dh[e] = rstd * (dx[k][e] * g[e] - m1 - xh * m2) + (dres ? r8[e] : 0.f);
           const uint32_t byte = (m[e >> 2] >> (8 * (e & 3))) & 0xFFu;
           dy[e] = keep ? (byte ? dh[e] * keep_scale : 0.f) : dh[e];
           agam[k][e] += dx[k][e] * xh;
