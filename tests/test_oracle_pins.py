@@ -845,3 +845,27 @@ def test_error_metrics():
     w = ref * (1 + 1e-4)
     assert O.per_element_rel_err(w, ref) == pytest.approx(1e-4)
     assert O.max_rel_err(ref, ref) == 0.0 and O.per_element_rel_err(ref, ref) == 0.0
+
+
+def test_per_element_error_of_bf16_rounding_alone():
+    """What the per-element figure means for a bf16 path.  Rounding only the
+    stored hidden activation H to bf16 (everything else exact, fp64) already
+    gives Z = H W2 a per-element error near 1 against the fp64 oracle, while
+    its norm-relative error stays far inside the 2e-2 bound: entries of Z
+    that cancel to below 1e-3 of its largest carry the rounding error of the
+    whole sum.  This is the figure the C5 line reports for Z, dX and the
+    weight gradients."""
+    import tpsynth
+    rng = np.random.default_rng(5)
+    M, d, f = 512, 256, 1024
+    X = tpsynth.round_to_bf16(rng.standard_normal((M, d)).astype(np.float32)).astype(np.float64)
+    W1 = tpsynth.round_to_bf16((0.02 * rng.standard_normal((d, f))).astype(np.float32)).astype(np.float64)
+    W2 = tpsynth.round_to_bf16((0.02 * rng.standard_normal((f, d))).astype(np.float32)).astype(np.float64)
+    ref = O.mlp_shard_fwd(X, W1, W2)
+    Hb = tpsynth.round_to_bf16(ref["H"].astype(np.float32)).astype(np.float64)
+    Z = Hb @ W2
+    assert O.max_rel_err(Z, ref["Z"]) < 5e-3
+    assert O.per_element_rel_err(Z, ref["Z"]) > 0.1
+    # the hidden activation itself is one rounding away (2^-9 relative, more
+    # only for entries measured against the floor)
+    assert O.per_element_rel_err(Hb, ref["H"]) < 1e-2
