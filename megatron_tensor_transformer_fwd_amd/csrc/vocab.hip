@@ -89,11 +89,20 @@ vocab_embed_bwd_kernel(const int64_t* __restrict__ ids, int64_t n_tokens, const 
       uint32_t rowbits[PER / 8];                   // 4 bits per token: row, 0xF = no hit
 #pragma unroll
       for (int j = 0; j < PER / 8; ++j) rowbits[j] = 0xFFFFFFFFu;
+      // the thread's PER ids: all loads in flight before the first compare
+      // (unconditional where the whole run is inside the tokens)
+      int64_t idv[PER];
+      if (t0 + PER <= n_tokens) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) idv[j] = ids[t0 + j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) idv[j] = t0 + j < n_tokens ? ids[t0 + j] : v0 - 1;
+      }
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
-        const int64_t t = t0 + j;
-        if (t < n_tokens) {
-          const int64_t r = ids[t] - v0;
+        {
+          const int64_t r = idv[j] - v0;
           if (r >= 0 && r < rows) {
             rowbits[j >> 3] = (rowbits[j >> 3] & ~(0xFu << (4 * (j & 7)))) | ((uint32_t)r << (4 * (j & 7)));
             ++cnt;
