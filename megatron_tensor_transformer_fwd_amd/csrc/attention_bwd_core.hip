@@ -49,10 +49,10 @@ __device__ __forceinline__ int swz(int row) {
 
 // DMA of `rows` rows of 128 bf16 (row pitch `ld_b` bytes in memory) into a
 // swizzled LDS tile: 4 rows per 1 KiB instruction; NI instructions per wave.
-template <int ROWS>
+template <int ROWS, int NWV = NW>
 __device__ __forceinline__ void dma_rows(desc_t r, uint32_t ld_b, uint32_t lds, int wave, int lane) {
-  constexpr int NI = ROWS / 4 / NW;
-  static_assert(NI * 4 * NW == ROWS, "tile rows");
+  constexpr int NI = ROWS / 4 / NWV;
+  static_assert(NI * 4 * NWV == ROWS, "tile rows");
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int ins = wave * NI + j;
@@ -375,25 +375,33 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
 // head), streaming 64-key chunks of K and V.  Lanes index queries, as in the
 // forward: S^T = K Q^T and dP^T = V dO^T need row fragments of K and V, and
 // dQ += dS K needs K transposed in the key order of the dS registers.
-__global__ void __launch_bounds__(256, 2)
+//
+// HPW = 2 (grouped-query attention, an even group): one workgroup of eight
+// waves takes the same query tile of two query heads of one group, which read
+// the same K/V head, so each K/V chunk goes into LDS once for both (half the
+// DMA bytes per FLOP; both heads have the same causal extent, so the waves
+// stay in step).
+template <int HPW>
+__global__ void __launch_bounds__(256 * HPW, 2 / HPW)
 attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                    const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dv,
                    bf16* __restrict__ dQ, int nb, int hl, int group, int s, int causal, float scale,
                    int64_t ld_o, int64_t ld_g) {
   using namespace attnb;
-  constexpr int BQ = 128, BKV = 64;
+  constexpr int BQ = 128, BKV = 64, NWV = NW * HPW;
   constexpr int KT = BKV * ROWB, STAGE = 2 * KT;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int nqt = (s + BQ - 1) / BQ;
-  const int nbh = nb * hl;
-  const int qt = nqt - 1 - (int)(blockIdx.x / nbh);   // heaviest tiles first
-  const int bh = (int)(blockIdx.x % nbh);
-  const int bi = bh / hl, h = bh % hl;
+  const int ngrp = nb * hl / HPW;                     // (batch, head set) pairs
+  const int qt = nqt - 1 - (int)(blockIdx.x / ngrp);   // heaviest tiles first
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave % NW;                           // wave within its head
+  const int bh = (int)(blockIdx.x % ngrp) * HPW + wave / NW;
+  const int bi = bh / hl, h = bh % hl;
   const int lq = lane & 31, g = lane >> 5;
-  const int q0 = qt * BQ, qw = q0 + wave * 32, qme = qw + lq;
+  const int q0 = qt * BQ, qw = q0 + wq * 32, qme = qw + lq;
   const int64_t head = (int64_t)bh * s * D;
   const int64_t kvhead = ((int64_t)bi * (hl / group) + h / group) * s * D;
   const uint32_t lds0 = lds_addr(smem);
@@ -421,8 +429,8 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     const int kv0 = t * BKV;
     const uint32_t st = lds0 + (uint32_t)((t & 1) * STAGE);
     const int64_t rem = (int64_t)(s - kv0) * ROWB;
-    dma_rows<BKV>(range_desc(K + kvhead + (int64_t)kv0 * D, rem), ROWB, st, wave, lane);
-    dma_rows<BKV>(range_desc(V + kvhead + (int64_t)kv0 * D, rem), ROWB, st + KT, wave, lane);
+    dma_rows<BKV, NWV>(range_desc(K + kvhead + (int64_t)kv0 * D, rem), ROWB, st, wave, lane);
+    dma_rows<BKV, NWV>(range_desc(V + kvhead + (int64_t)kv0 * D, rem), ROWB, st + KT, wave, lane);
   };
 
   f32x16 adq[D / 32];
@@ -565,7 +573,10 @@ hipError_t launch_attn_bwd_flash(hipStream_t st, int b, int hl, int group, int s
     TPK_TRY(launch("attn_bwd.group_sum", attn_bwd_group_sum_kernel, g2, dim3(256), st, (const float*)part_v,
                    dQKV + n_q + n_kv, rows, hl, group, ld_g));
   }
-  return launch("attn_bwd.dq", attn_bwd_dq_kernel, dim3(grid), dim3(256), st, Q, K, V, dO, L2, Dv, dQKV, b, hl,
+  if (group % 2 == 0 && hl % 2 == 0)   // two query heads of a group per workgroup, K/V chunks shared
+    return launch("attn_bwd.dq", attn_bwd_dq_kernel<2>, dim3(grid / 2), dim3(512), st, Q, K, V, dO, L2, Dv, dQKV,
+                  b, hl, group, s, causal, scale, ld_o, ld_g);
+  return launch("attn_bwd.dq", attn_bwd_dq_kernel<1>, dim3(grid), dim3(256), st, Q, K, V, dO, L2, Dv, dQKV, b, hl,
                 group, s, causal, scale, ld_o, ld_g);
 }
 
