@@ -31,6 +31,12 @@
 
 namespace tpk {
 
+// K/V stages of the two-head query-tile kernel (one workgroup per CU, so the
+// LDS has room): G1 225 us with two, 208 with three, 230 with four.
+#ifndef TPK_DQ2_STAGES
+#define TPK_DQ2_STAGES 3
+#endif
+
 namespace attnb {
 constexpr int D = 128, NT = 256, NW = 4;
 constexpr int ROWB = D * 2;                   // bytes per tile row
@@ -380,7 +386,9 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
 // waves takes the same query tile of two query heads of one group, which read
 // the same K/V head, so each K/V chunk goes into LDS once for both (half the
 // DMA bytes per FLOP; both heads have the same causal extent, so the waves
-// stay in step).
+// stay in step).  Alone on its CU, it loads the chunks two steps ahead
+// through three LDS stages; with one step of look-ahead its waits for the
+// DMA cost about 8%.
 template <int HPW>
 __global__ void __launch_bounds__(256 * HPW, 2 / HPW)
 attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -390,7 +398,10 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   using namespace attnb;
   constexpr int BQ = 128, BKV = 64, NWV = NW * HPW;
   constexpr int KT = BKV * ROWB, STAGE = 2 * KT;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // one workgroup per CU with two heads: the LDS holds a deeper ring
+  constexpr int NSTG = HPW == 2 ? TPK_DQ2_STAGES : 2;
+  constexpr int DMA_PER_CHUNK = 2 * (BKV / 4 / NWV);    // K and V instructions per wave
+  __shared__ __attribute__((aligned(1024))) char smem[NSTG * STAGE];
 
   const int nqt = (s + BQ - 1) / BQ;
   const int ngrp = nb * hl / HPW;                     // (batch, head set) pairs
@@ -427,7 +438,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   const int ntiles = (kv_end + BKV - 1) / BKV;
   auto issue = [&](int t) {
     const int kv0 = t * BKV;
-    const uint32_t st = lds0 + (uint32_t)((t & 1) * STAGE);
+    const uint32_t st = lds0 + (uint32_t)((t % NSTG) * STAGE);
     const int64_t rem = (int64_t)(s - kv0) * ROWB;
     dma_rows<BKV, NWV>(range_desc(K + kvhead + (int64_t)kv0 * D, rem), ROWB, st, wave, lane);
     dma_rows<BKV, NWV>(range_desc(V + kvhead + (int64_t)kv0 * D, rem), ROWB, st + KT, wave, lane);
@@ -437,13 +448,33 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) adq[i] = f32x16{};
 
-  if (ntiles > 0) issue(0);
+#pragma unroll
+  for (int t = 0; t < NSTG - 1; ++t)
+    if (t < ntiles) issue(t);
+  if constexpr (NSTG > 2) {   // the fragment loads above are retired here, so no wait inside the loop drains the ring
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      settle(qf[kk]);
+      settle(of[kk]);
+    }
+    settle(l2);
+    settle(dq);
+  }
   for (int t = 0; t < ntiles; ++t) {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (t + 1 < ntiles) issue(t + 1);
+    // chunk t landed; the DMAs of up to NSTG - 2 later chunks may still be in flight
+    if constexpr (NSTG > 2) {
+      const int ahead = min(NSTG - 2, ntiles - 1 - t);
+      static_assert(NSTG <= 4 && DMA_PER_CHUNK == 4, "the barrier's vmcnt immediates");
+      if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (t + NSTG - 1 < ntiles) issue(t + NSTG - 1);   // into the stage step t-1 read
     const int kv0 = t * BKV;
     if (causal && kv0 > qw + 31) continue;
-    const char* Ks = smem + (t & 1) * STAGE;
+    const char* Ks = smem + (t % NSTG) * STAGE;
     const char* Vs = Ks + KT;
     f32x16 sacc[2], pacc[2];
 #pragma unroll

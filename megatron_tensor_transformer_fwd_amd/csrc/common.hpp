@@ -28,6 +28,17 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
+// Retire loads issued before a loop whose waits are inline asm (the flash
+// kernels' "s_waitcnt ... s_barrier"): the compiler's wait-count tracking
+// cannot see an asm s_waitcnt, so it would keep such loads pending through
+// the loop, and its waits for them (vmcnt counts in issue order) would also
+// wait for the loop's own DMAs in flight.  An asm use makes the compiler
+// wait for them here, once.
+template <class T>
+__device__ __forceinline__ void settle(const T& v) {
+  asm volatile("" ::"v"(v));
+}
+
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
