@@ -209,20 +209,24 @@ constexpr int NK = K_BYTES / 1024 / NW, NV = V_BYTES / 1024 / NW;   // DMA instr
 
 // K tile: row r (key) of 256 bytes, logical 16-byte chunk c at c ^ (r % 16).
 // V tile: row r (key) of 256 bytes (128 d values), chunk c at c ^ 4 (r & 3).
+template <int NWV = NW>
 __device__ __forceinline__ void dma_k(desc_t rk, uint32_t lds, int wave, int lane) {
+  constexpr int NKW = K_BYTES / 1024 / NWV;
 #pragma unroll
-  for (int j = 0; j < NK; ++j) {
-    const int ins = wave * NK + j;
+  for (int j = 0; j < NKW; ++j) {
+    const int ins = wave * NKW + j;
     const int row = ins * 4 + (lane >> 4);
     const int lc = (lane & 15) ^ (row & 15);
     dma16(rk, lds + ins * 1024, (uint32_t)row * (D * 2) + (uint32_t)lc * 16u);
   }
 }
 
+template <int NWV = NW>
 __device__ __forceinline__ void dma_v(desc_t rv, uint32_t lds, int wave, int lane) {
+  constexpr int NVW = V_BYTES / 1024 / NWV;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int ins = wave * NV + j;
+  for (int j = 0; j < NVW; ++j) {
+    const int ins = wave * NVW + j;
     const int row = ins * 4 + (lane >> 4);
     const int lc = (lane & 15) ^ (4 * (row & 3));
     dma16(rv, lds + ins * 1024, (uint32_t)row * (D * 2) + (uint32_t)lc * 16u);
@@ -263,34 +267,52 @@ __device__ __forceinline__ bf16x8 frag_v(const char* vt, int d0, int kvb, int la
 // two-stage rings: at the top of iteration t (one barrier) K_{t+1} and V_t
 // have landed, and the DMAs of K_{t+2} and V_{t+1} go into the stages that
 // held K_t (consumed at iteration t-1) and V_{t-1}.
-__global__ void __launch_bounds__(256, 2)
+//
+// HPW = 1: four waves (128 queries of one head), two workgroups per CU,
+// causal tiles in heavy/light pairs over the CU's two slots.
+// HPW = 2 (grouped-query attention, an even group): eight waves take the same
+// query tile of two query heads of one group, which read the same K/V head,
+// so each K/V tile goes into LDS once for both (G1 185 -> 163 us); one
+// workgroup per CU, heaviest tiles first.  Deeper rings, which its LDS would
+// allow, were slower here (four stages: 170 us).
+template <int HPW>
+__global__ void __launch_bounds__(256 * HPW, 2 / HPW)
 flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                               const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ L,
                               int nb, int hl, int group, int s, int causal, float scale_log2) {
   using namespace attn128;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * K_BYTES + 2 * V_BYTES];
+  constexpr int NWV = NW * HPW, NS = 2;
+  constexpr int NKW = K_BYTES / 1024 / NWV, NVW = V_BYTES / 1024 / NWV;   // DMA instructions per wave
+  __shared__ __attribute__((aligned(1024))) char smem[NS * K_BYTES + NS * V_BYTES];
 
   const int nqt = (s + BQ - 1) / BQ;
-  const int nbh = nb * hl;
-  const int half = (int)(gridDim.x / 2);
+  const int ngrp = nb * hl / HPW;
   const int bid = (int)blockIdx.x;
-  const bool light = (nqt % 2 == 0) && bid >= half;
-  const int rank = light ? bid - half : bid;
-  const int qt = light ? rank / nbh : nqt - 1 - rank / nbh;
-  const int bh = rank % nbh;
-  const int bi = bh / hl, h = bh % hl;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int qt, bh;
+  if (HPW == 1) {
+    const int half = (int)(gridDim.x / 2);
+    const bool light = (nqt % 2 == 0) && bid >= half;
+    const int rank = light ? bid - half : bid;
+    qt = light ? rank / ngrp : nqt - 1 - rank / ngrp;
+    bh = rank % ngrp;
+  } else {
+    qt = nqt - 1 - bid / ngrp;                      // heaviest tiles first
+    bh = (bid % ngrp) * HPW + wave / NW;
+  }
+  const int bi = bh / hl, h = bh % hl;
+  const int wq = wave % NW;                         // wave within its head
   const int lq = lane & 31, g = lane >> 5;
   const int64_t head = (int64_t)bh * s * D;
   const int64_t kvhead = ((int64_t)bi * (hl / group) + h / group) * s * D;
   const bf16* Kh = K + kvhead;
   const bf16* Vh = V + kvhead;
   const int q0 = qt * BQ;
-  const int qw = q0 + wave * 32;
+  const int qw = q0 + wq * 32;
   const int qme = qw + lq;
   const uint32_t lds0 = lds_addr(smem);
-  const uint32_t kring = lds0, vring = lds0 + 2 * K_BYTES;
+  const uint32_t kring = lds0, vring = lds0 + NS * K_BYTES;
 
   const int kv_end = causal ? min(s, q0 + BQ) : s;
   const int ntiles = (kv_end + BKV - 1) / BKV;
@@ -301,8 +323,8 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
     const int64_t rb = (int64_t)(s - kv0) * D * 2;
     return make_desc(base + kv0 * D, rb < 0x7FFFFFFF ? (uint32_t)rb : 0x7FFFFFFFu);
   };
-  auto issue_k = [&](int t) { dma_k(desc_of(Kh, t), kring + (t & 1) * K_BYTES, wave, lane); };
-  auto issue_v = [&](int t) { dma_v(desc_of(Vh, t), vring + (t & 1) * V_BYTES, wave, lane); };
+  auto issue_k = [&](int t) { dma_k<NWV>(desc_of(Kh, t), kring + (t % NS) * K_BYTES, wave, lane); };
+  auto issue_v = [&](int t) { dma_v<NWV>(desc_of(Vh, t), vring + (t % NS) * V_BYTES, wave, lane); };
 
   bf16x8 qf[D / 16];
   {
@@ -311,12 +333,15 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
     for (int kk = 0; kk < D / 16; ++kk)
       qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(((int64_t)qme * D + kk * 16 + g * 8) * 2)));
   }
-  issue_k(0);
-  issue_v(0);
-  if (ntiles > 1) issue_k(1);
+  // the tiles before the loop's first issues: K_0 .. K_{NS-1}, V_0 .. V_{NS-2}
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    if (j < ntiles) issue_k(j);
+    if (j + 1 < NS && j < ntiles) issue_v(j);
+  }
 
   auto scores = [&](int t, f32x16 (&sc)[2]) {
-    const char* Ks = smem + (t & 1) * K_BYTES;
+    const char* Ks = smem + (t % NS) * K_BYTES;
     sc[0] = f32x16{};
     sc[1] = f32x16{};
 #pragma unroll
@@ -338,8 +363,8 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   for (int t = 0; t < ntiles; ++t) {
     // K_{t+1} and V_t have landed for every wave; every wave is done with K_t and V_{t-1}.
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (t + 1 < ntiles) issue_v(t + 1);
-    if (t + 2 < ntiles) issue_k(t + 2);
+    if (t + NS - 1 < ntiles) issue_v(t + NS - 1);
+    if (t + NS < ntiles) issue_k(t + NS);
     if (t > wlast) continue;                        // uniform per wave
     f32x16 sn[2];
     if (t + 1 <= wlast) scores(t + 1, sn);          // next tile's scores, independent of this softmax
@@ -387,7 +412,7 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
     rs += __shfl_xor(rs, 32);
     l_run += rs;
 
-    const char* Vs = smem + 2 * K_BYTES + (t & 1) * V_BYTES;
+    const char* Vs = smem + NS * K_BYTES + (t % NS) * V_BYTES;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -522,8 +547,11 @@ hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
     const bf16* k = static_cast<const bf16*>(K);
     const bf16* v = static_cast<const bf16*>(V);
     bf16* o = static_cast<bf16*>(O);
-    if (d_head == 128)
-      TPK_TRY(launch("attn.core_d128", flash_attn_fwd_d128_kernel, grid, dim3(256), st, q, k, v, o, L, (int)b,
+    if (d_head == 128 && group % 2 == 0 && h_local % 2 == 0)   // two query heads per workgroup
+      TPK_TRY(launch("attn.core_d128", flash_attn_fwd_d128_kernel<2>, dim3(grid.x / 2), dim3(512), st, q, k, v, o,
+                     L, (int)b, (int)h_local, group, (int)s, causal, sl2));
+    else if (d_head == 128)
+      TPK_TRY(launch("attn.core_d128", flash_attn_fwd_d128_kernel<1>, grid, dim3(256), st, q, k, v, o, L, (int)b,
                      (int)h_local, group, (int)s, causal, sl2));
     else
       TPK_TRY(launch("attn.core_d64", flash_attn_fwd_kernel<64>, grid, dim3(256), st, q, k, v, o, L, (int)b,
