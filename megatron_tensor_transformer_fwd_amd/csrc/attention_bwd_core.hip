@@ -460,8 +460,9 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     settle(l2);
     settle(dq);
   }
-  for (int t = 0; t < ntiles; ++t) {
-    // chunk t landed; the DMAs of up to NSTG - 2 later chunks may still be in flight
+  // chunk t landed; the DMAs of up to NSTG - 2 later chunks may still be in
+  // flight; then the DMA of chunk t + NSTG - 1 into the stage step t-1 read
+  auto step_sync = [&](int t) {
     if constexpr (NSTG > 2) {
       const int ahead = min(NSTG - 2, ntiles - 1 - t);
       static_assert(NSTG <= 4 && DMA_PER_CHUNK == 4, "the barrier's vmcnt immediates");
@@ -471,9 +472,16 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     } else {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    if (t + NSTG - 1 < ntiles) issue(t + NSTG - 1);   // into the stage step t-1 read
+    if (t + NSTG - 1 < ntiles) issue(t + NSTG - 1);
+  };
+  // The chunks this wave computes on come first (causal: up to its last
+  // query's diagonal); the rest of the workgroup's chunks only pass through
+  // the barriers.  Keeping the skip out of the computing loop keeps a single
+  // path through the dQ accumulation, whose registers then stay in place.
+  const int wend = causal ? min(ntiles, (qw + 31) / BKV + 1) : ntiles;
+  for (int t = 0; t < wend; ++t) {
+    step_sync(t);
     const int kv0 = t * BKV;
-    if (causal && kv0 > qw + 31) continue;
     const char* Ks = smem + (t % NSTG) * STAGE;
     const char* Vs = Ks + KT;
     f32x16 sacc[2], pacc[2];
@@ -516,6 +524,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
           adq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_col(Ks, db * 32, kb * 32 + hh * 16, lane),
                                                             sf[kb][hh], adq[db], 0, 0, 0);
   }
+  for (int t = wend; t < ntiles; ++t) step_sync(t);
 
   if (live) {
     bf16* qrow = dQ + ((int64_t)bi * s + qme) * ld_g + (int64_t)h * D;

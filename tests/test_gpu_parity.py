@@ -494,6 +494,8 @@ def run_attn(tp, inp, b, s, h_l, dh, causal=True, dY=None):
     (2, 130, 64, 1, 128, False),
     (1, 1, 32, 2, 128, True),        # one token: o = v
     (3, 257, 96, 2, 64, True),
+    (1, 900, 64, 1, 128, False),     # 15 key tiles, split 8 + 7 over a workgroup's two halves
+    (1, 1000, 64, 2, 128, True),     # 8 query tiles: key ranges of 2 to 16 tiles split in halves
 ])
 def test_attention_small_shapes(tp, b, s, d, h_l, dh, causal):
     _say(f"attention b={b} s={s} d={d} h_l={h_l} dh={dh} causal={causal}")
@@ -625,6 +627,7 @@ def run_gqa(tp, inp, b, s, h_l, h_kv, dh, causal=True):
     (1, 257, 96, 4, 1, 128, True),
     (2, 130, 64, 6, 3, 64, False),
     (1, 64, 72, 16, 1, 128, True),    # the G1 grouping, 16 query heads on one K/V head
+    (1, 300, 64, 3, 1, 128, True),    # an odd group: one query head per workgroup, key tiles split
     (1, 256, 2048, 4, 1, 128, True),  # long d: the K/V projection splits K (2 ways) through Z's memory
     (2, 128, 4096, 4, 2, 128, True),  # 4-way split, two K/V heads scattered
 ])
