@@ -27,8 +27,10 @@
 // wave's softmax overlaps another's matrix products.  Within a wave the
 // loop is software-pipelined: the next key tile's score MFMAs are issued
 // before this tile's softmax, so both kinds of work are in flight (K and V
-// have separate two-stage LDS rings for that).  The O^T rescale is skipped
-// when no running max of the wave changed.  d_head 64 uses the
+// have separate two-stage LDS rings for that).  The subtracted running max
+// may lag a row's true max by up to 2^8, so O^T and the sum are rescaled only
+// when a row of the wave moves past that (not each time a max moves, which
+// with random scores is nearly every tile).  d_head 64 uses the
 // register-staged variant.
 #include "epilogues.hpp"
 #include "gemm_dispatch.hpp"
@@ -206,6 +208,9 @@ namespace attn128 {
 constexpr int D = 128, BQ = 128, BKV = 64, NT = 256, NW = 4;
 constexpr int K_BYTES = BKV * D * 2, V_BYTES = BKV * D * 2;
 constexpr int NK = K_BYTES / 1024 / NW, NV = V_BYTES / 1024 / NW;   // DMA instructions per wave
+constexpr float kLazyMax = 8.0f;                  // lag allowed to the subtracted running max, log2 units
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kBf16One2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // K tile: row r (key) of 256 bytes, logical 16-byte chunk c at c ^ (r % 16).
 // V tile: row r (key) of 256 bytes (128 d values), chunk c at c ^ 4 (r & 3).
@@ -357,16 +362,16 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   float m_run = -1e30f, l_run = 0.f;
 
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  f32x16 sc[2];
-  scores(0, sc);
-
-  for (int t = 0; t < ntiles; ++t) {
-    // K_{t+1} and V_t have landed for every wave; every wave is done with K_t and V_{t-1}.
+  // Top of iteration t: K_{t+1} and V_t have landed for every wave; every
+  // wave is done with K_t and V_{t-1}, whose stages take the next DMAs.
+  auto sync = [&](int t) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (t + NS - 1 < ntiles) issue_v(t + NS - 1);
     if (t + NS < ntiles) issue_k(t + NS);
-    if (t > wlast) continue;                        // uniform per wave
-    f32x16 sn[2];
+  };
+  // One key tile: sc holds its scores; the next tile's go into sn.
+  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    sync(t);
     if (t + 1 <= wlast) scores(t + 1, sn);          // next tile's scores, independent of this softmax
 
     const int kv0 = t * BKV;
@@ -385,14 +390,19 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx * scale_log2);
-    // rescale O^T and the sum only when a running max of the wave moved
-    if (__builtin_amdgcn_read_exec() & __ballot(m_new > m_run)) {
+    // The subtracted max m_run may lag the row's true running max by up to
+    // kLazyMax (log2 units), so P <= 2^kLazyMax: any m_run gives the same O and
+    // L, and the lag only bounds P's range.  O^T and the sum are rescaled when
+    // a row of the wave moves past it (with random scores, after the first few
+    // tiles almost never), not each time a running max moves.
+    if (__builtin_amdgcn_read_exec() & __ballot(m_new > m_run + kLazyMax)) {
       const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= corr;
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc_o[i] *= corr;
+      for (int j = 0; j < D / 32; ++j) acc_o[j] *= corr;
       m_run = m_new;
     }
+    // the row sum is taken over the bf16 probabilities the P V product uses
     float rs = 0.f;
     bf16x8 pf[2][2];
 #pragma unroll
@@ -404,8 +414,9 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
         for (int e = 0; e < 4; ++e) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hh + 2 * e], scale_log2, -m_run));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hh + 2 * e + 1], scale_log2, -m_run));
-          rs += p0 + p1;
-          wv[e] = pack_bf16x2(p0, p1);
+          const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
+          wv[e] = __builtin_bit_cast(uint32_t, pk);
+          rs = __builtin_amdgcn_fdot2_f32_bf16(pk, kBf16One2, rs, false);
         }
         pf[kb][hh] = __builtin_bit_cast(bf16x8, wv);
       }
@@ -421,11 +432,19 @@ flash_attn_fwd_d128_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
         for (int db = 0; db < D / 32; ++db)
           acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_v(Vs, db * 32, kb * 32 + hh * 16, lane),
                                                               pf[kb][hh], acc_o[db], 0, 0, 0);
-    if (t + 1 <= wlast) {
-      sc[0] = sn[0];
-      sc[1] = sn[1];
-    }
+  };
+  // The tiles this wave computes on (causal: up to its last query's
+  // diagonal), two per iteration so the score registers alternate without
+  // copies; then the workgroup's remaining tiles only pass the barriers.
+  f32x16 sa[2], sb[2];
+  scores(0, sa);
+  int t = 0;
+  for (; t + 1 <= wlast; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
   }
+  if (t <= wlast) step(t++, sa, sb);
+  for (; t < ntiles; ++t) sync(t);
 
   if (qme < s) {
     const float inv = 1.0f / l_run;

@@ -494,8 +494,8 @@ def run_attn(tp, inp, b, s, h_l, dh, causal=True, dY=None):
     (2, 130, 64, 1, 128, False),
     (1, 1, 32, 2, 128, True),        # one token: o = v
     (3, 257, 96, 2, 64, True),
-    (1, 900, 64, 1, 128, False),     # 15 key tiles, split 8 + 7 over a workgroup's two halves
-    (1, 1000, 64, 2, 128, True),     # 8 query tiles: key ranges of 2 to 16 tiles split in halves
+    (1, 900, 64, 1, 128, False),     # 15 key tiles (an odd count), non-causal
+    (1, 1000, 64, 2, 128, True),     # 8 query tiles with 2 to 16 key tiles each
 ])
 def test_attention_small_shapes(tp, b, s, d, h_l, dh, causal):
     _say(f"attention b={b} s={s} d={d} h_l={h_l} dh={dh} causal={causal}")
@@ -595,6 +595,56 @@ def test_attention_bwd_c4_full_size_sampled(tp):
 
 # ------------------------------------------------------- grouped-query attention
 
+def _growing_rows(X, b, s, rate):
+    """X with token t's row scaled by 1 + t / rate (then rounded to bf16):
+    queries and keys grow along the sequence, so a row's running max of the
+    scaled scores keeps rising from one key tile to the next."""
+    f = 1.0 + np.arange(s, dtype=np.float64) / rate
+    return tpsynth.round_to_bf16((X.reshape(b, s, -1) * f[None, :, None]).reshape(b * s, -1).astype(np.float32))
+
+
+def _max_rise_after_first_tile(Q, K, dh):
+    """Over every (batch, head, query), the largest rise of the running max of
+    the scaled scores in log2 units (the forward's units) after the query's
+    first 64-key tile (causal)."""
+    sl2 = dh ** -0.5 * math.log2(math.e)
+    worst = 0.0
+    for bi in range(Q.shape[0]):
+        for j in range(Q.shape[1]):
+            S = (Q[bi, j] @ K[bi, j].T) * sl2
+            S[np.triu_indices(S.shape[0], 1)] = -np.inf
+            first = S[:, :64].max(axis=1)
+            worst = max(worst, float((S.max(axis=1) - first).max()))
+    return worst
+
+
+@pytest.mark.parametrize("h_l,h_kv", [(2, 2), (4, 2)])
+def test_attention_growing_scores(tp, h_l, h_kv):
+    """Scores that keep growing along the sequence: the forward subtracts a
+    running max that may lag the true one by up to 2^8, and rescales O and
+    the sum when a row's max moves past that, mid-stream.  One head per
+    workgroup (MHA) and two query heads of a group per workgroup."""
+    b, s, d, dh = 1, 512, 64, 128
+    _say(f"attention growing scores h_l={h_l} h_kv={h_kv}")
+    inp = tpsynth.random_gqa(b, s, d, h_l, h_kv, dh, "bf16", seed=91 + h_l, w_std=0.1)
+    # grow by 1 + t/384: a row's max rises up to 14-16 log2 units past its
+    # first tile, while the scores stay well enough conditioned for bf16 Q and
+    # K (a steeper ramp makes the softmax so peaked that bf16 rounding alone
+    # moves O past the tolerance)
+    inp["X"] = _growing_rows(inp["X"], b, s, 384.0)
+    ref = O.attn_gqa_shard_fwd(inp["X"], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], b, s, h_l, h_kv, dh, True)
+    group = h_l // h_kv
+    Kq = np.repeat(ref["K"], group, axis=1)
+    assert _max_rise_after_first_tile(ref["Q"], Kq, dh) > 8.0   # past the lag: rescales happen mid-stream
+    if h_kv == h_l:
+        out = run_attn(tp, inp, b, s, h_l, dh, True)
+    else:
+        out = run_gqa(tp, inp, b, s, h_l, h_kv, dh, True)
+    for k in ("O", "Z"):
+        check(k, out[k], ref[k], "bf16")
+    assert np.abs(host(out["L"]) - ref["L"]).max() < 2e-2 * max(1.0, np.abs(ref["L"]).max())
+
+
 def test_attention_sequence_limit(tp):
     """s at the ABI's sequence limit (2^22 tokens, one head of 128: 1 GiB per
     head of K or V, the most the core's 32-bit key/value offsets address),
@@ -627,7 +677,7 @@ def run_gqa(tp, inp, b, s, h_l, h_kv, dh, causal=True):
     (1, 257, 96, 4, 1, 128, True),
     (2, 130, 64, 6, 3, 64, False),
     (1, 64, 72, 16, 1, 128, True),    # the G1 grouping, 16 query heads on one K/V head
-    (1, 300, 64, 3, 1, 128, True),    # an odd group: one query head per workgroup, key tiles split
+    (1, 300, 64, 3, 1, 128, True),    # an odd group: one query head per workgroup
     (1, 256, 2048, 4, 1, 128, True),  # long d: the K/V projection splits K (2 ways) through Z's memory
     (2, 128, 4096, 4, 2, 128, True),  # 4-way split, two K/V heads scattered
 ])
