@@ -112,9 +112,11 @@ __device__ __forceinline__ desc_t range_desc(const void* base, int64_t bytes) {
 }
 }  // namespace attnb
 
-// D[bh, t] = sum_c dO[t, h*128 + c] * O[t, h*128 + c]; one thread per (t, h).
-// Also the forward's log-sum-exp in base 2, L2 = L log2(e), which the flash
-// kernels subtract inside exp2 without a multiply per score.
+// D[bh, t] = sum_c dO[t, h*128 + c] * O[t, h*128 + c], stored negated (the
+// flash kernels form dP - D, and the key-tile kernel starts its dP
+// accumulators from -D); one thread per (t, h).  Also the forward's
+// log-sum-exp in base 2, L2 = L log2(e), which the flash kernels subtract
+// inside exp2 without a multiply per score.
 __global__ void __launch_bounds__(256) attn_bwd_rowdot_kernel(const bf16* __restrict__ dO,
                                                               const bf16* __restrict__ O, const float* __restrict__ L,
                                                               float* __restrict__ Dv, float* __restrict__ L2,
@@ -134,7 +136,7 @@ __global__ void __launch_bounds__(256) attn_bwd_rowdot_kernel(const bf16* __rest
     for (int e = 0; e < 4; ++e) acc += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
   }
   const int64_t bi = row / s, t = row % s;
-  Dv[(bi * hl + h) * s + t] = acc;
+  Dv[(bi * hl + h) * s + t] = -acc;
   L2[(bi * hl + h) * s + t] = L[(bi * hl + h) * s + t] * attnb::kLog2e;   // log-sum-exp in base 2
 }
 
@@ -317,10 +319,10 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (c + 1 < nqc) issue(c + 1);
       if (live(c - 1)) {
-        // dS = P (dP - D) for chunk c-1, then dK[key][d] += dS^T Q
+        // dS = P (dP - D) for chunk c-1 (dp already holds dP - D), then
+        // dK[key][d] += dS^T Q
         const char* sp = smem + ((c - 1) % NSTG) * STAGE;
         const char* Qp = sp;
-        const float* Dp = reinterpret_cast<const float*>(sp + 2 * QT + VEC);
         const char* pr = pbuf + ((c - 1) & 1) * PBUF + kb * PWAVE;
         bf16x8 sf[2][2];
 #pragma unroll
@@ -331,10 +333,8 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 8 * hh + 2 * e;                     // registers r, r+1
-              const int ql = qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-              const float d0 = Dp[ql], d1 = Dp[ql + 1];
-              dp[qb][r] = bf16_lo(pw[e]) * (dp[qb][r] - d0);
-              dp[qb][r + 1] = bf16_hi(pw[e]) * (dp[qb][r + 1] - d1);
+              dp[qb][r] = bf16_lo(pw[e]) * dp[qb][r];
+              dp[qb][r + 1] = bf16_hi(pw[e]) * dp[qb][r + 1];
             }
             sf[qb][hh] = pack8(dp[qb], 8 * hh);
           }
@@ -342,7 +342,19 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
         acc_cols(acc, Qp, sf, lane);
       }
       if (live(c)) {
+        // dP - D for chunk c: the accumulators start from -D of the
+        // chunk's queries (register r of block qb: query qb*32 + 8 (r/4) + 4 g + r%4)
         const char* dOs = smem + (c % NSTG) * STAGE + QT;
+        const float* nDs = reinterpret_cast<const float*>(smem + (c % NSTG) * STAGE + 2 * QT + VEC);
+        f32x16 nd[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(nDs + qb * 32 + 8 * r4 + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nd[qb][4 * r4 + e] = v[e];
+          }
         bf16x8 fr[2][2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) fr[0][qb] = frag_row(dOs, qb * 32, 0, lane);
@@ -353,7 +365,7 @@ attn_bwd_dkv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, cons
             for (int qb = 0; qb < 2; ++qb) fr[(kk + 1) & 1][qb] = frag_row(dOs, qb * 32, kk + 1, lane);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
-            dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk & 1][qb], kvf[kk], kk ? dp[qb] : f32x16{}, 0,
+            dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk & 1][qb], kvf[kk], kk ? dp[qb] : nd[qb], 0,
                                                              0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -432,7 +444,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   }
   const bool live = qme < s;
   const float l2 = live ? L2[(int64_t)bh * s + qme] : 0.f;
-  const float dq = live ? Dv[(int64_t)bh * s + qme] : 0.f;
+  const float ndq = live ? Dv[(int64_t)bh * s + qme] : 0.f;   // -D
 
   const int kv_end = causal ? min(s, q0 + BQ) : s;
   const int ntiles = (kv_end + BKV - 1) / BKV;
@@ -458,7 +470,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
       settle(of[kk]);
     }
     settle(l2);
-    settle(dq);
+    settle(ndq);
   }
   // chunk t landed; the DMAs of up to NSTG - 2 later chunks may still be in
   // flight; then the DMA of chunk t + NSTG - 1 into the stage step t-1 read
@@ -506,7 +518,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
         for (int r = 0; r < 16; ++r) {
           float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -l2));
           if constexpr (MASK) p = (kb * 32 + 8 * (r >> 2) + (r & 3) <= lim) ? p : 0.f;
-          pacc[kb][r] = p * (pacc[kb][r] - dq);
+          pacc[kb][r] = p * (pacc[kb][r] + ndq);
         }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) sf[kb][hh] = pack8(pacc[kb], 8 * hh);
