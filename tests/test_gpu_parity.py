@@ -678,6 +678,7 @@ def run_gqa(tp, inp, b, s, h_l, h_kv, dh, causal=True):
     (2, 130, 64, 6, 3, 64, False),
     (1, 64, 72, 16, 1, 128, True),    # the G1 grouping, 16 query heads on one K/V head
     (1, 300, 64, 3, 1, 128, True),    # an odd group: one query head per workgroup
+    (1, 200, 64, 4, 2, 128, False),   # two query heads per workgroup, non-causal (every wave on every tile)
     (1, 256, 2048, 4, 1, 128, True),  # long d: the K/V projection splits K (2 ways) through Z's memory
     (2, 128, 4096, 4, 2, 128, True),  # 4-way split, two K/V heads scattered
 ])
