@@ -53,8 +53,8 @@ vocab_embed_kernel(const int64_t* __restrict__ ids, int64_t n_tokens, int64_t ro
 // block-wide prefix sum of per-thread hit counts).  Threads own 8 columns
 // each; when a row has fewer 8-column chunks than the workgroup has
 // threads, HL groups of threads ("hit lanes") take every HL-th hit, each
-// keeping per-row register accumulators and issuing four hits' loads at a
-// time.  The lanes' sums are added in lane order at the end, so the
+// keeping per-row register accumulators and issuing eight (then four) hits'
+// loads at a time.  The lanes' sums are added in lane order at the end, so the
 // summation order is fixed (bitwise deterministic).  Rows wider than the
 // workgroup's columns take several column passes over the same windows.
 constexpr int EB_R = 8, EB_NT = 256, EB_W = 4096;
@@ -132,6 +132,24 @@ vocab_embed_bwd_kernel(const int64_t* __restrict__ ids, int64_t n_tokens, const 
       __syncthreads();
       if (mine) {
         int k = hl;
+        for (; k + 7 * HL < nh; k += 8 * HL) {      // eight hits' loads in flight
+          float v[8][8];
+          int rr8[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int e = hits[k + u * HL];
+            rr8[u] = e % EB_R;
+            Vec8<T>::template load<kNtIn>(dY + (w0 + e / EB_R) * d + c, v[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int rr = 0; rr < EB_R; ++rr)
+              if (rr == rr8[u]) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[rr][q] += v[u][q];
+              }
+        }
         for (; k + 3 * HL < nh; k += 4 * HL) {      // four hits' loads in flight
           float v[4][8];
           int rr4[4];
