@@ -164,6 +164,37 @@ def test_mlp_ragged_shapes(tp, dtype, M, d, f):
         check(k, out[k], refb[k], dtype)
 
 
+def _slice_rel_err(got, ref, axis):
+    """The worst slice's ||got - ref||_inf / ||ref||_inf, slices taken along
+    `axis` (axis 0: each column over its rows; axis 1: each row)."""
+    g = host(got).astype(np.float64)
+    return float((np.abs(g - ref).max(axis=axis) / np.abs(ref).max(axis=axis)).max())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mlp_slices_of_unequal_scale(tp, dtype):
+    """W1's columns and W2's rows scaled over three decades (log-spaced 1e-3 .. 1
+    along d_ff): A, H and dW1 then have columns, and dW2 rows, from about 1e-3
+    to 1 of the tensor's largest.  Each such slice depends only on its own
+    weight slice, and each is compared with the oracle against its own largest
+    value, so a small slice cannot pass on the tensor's norm alone."""
+    M, d, f = 512, 256, 384
+    _say(f"mlp slices of unequal scale {dtype} M={M} d={d} f={f}")
+    inp = tpsynth.random_mlp(M, d, f, dtype, seed=17, w_std=0.05)
+    sc = np.logspace(-3.0, 0.0, f)
+    rnd = tpsynth.round_to_bf16 if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    W1 = rnd((inp["W1"] * sc[None, :]).astype(np.float32))
+    W2 = rnd((inp["W2"] * sc[:, None]).astype(np.float32))
+    out = run_mlp_shard(tp, dev(inp["X"], dtype), dev(W1, dtype), dev(W2, dtype), dev(inp["dY"], dtype), dtype)
+    ref = O.mlp_shard_fwd(inp["X"], W1, W2)
+    refb = O.mlp_shard_bwd(inp["X"], W1, W2, inp["dY"])
+    for k, r, axis in (("A", ref["A"], 0), ("H", ref["H"], 0), ("dW1", refb["dW1"], 0), ("dW2", refb["dW2"], 1)):
+        err = _slice_rel_err(out[k], r, axis)
+        assert err <= TOL[dtype], f"{k}: worst slice max_rel_err {err:.3e} > {TOL[dtype]}"
+    for k in ("Z", "dX"):
+        check(k, out[k], (ref if k == "Z" else refb)[k], dtype)
+
+
 def test_mlp_row_pitch_limit(tp):
     """d at the ABI's row-pitch limit (2^21 elements): every operand tile spans
     256 rows of 4 MiB, the widest the kernels address with 32-bit offsets
@@ -444,6 +475,31 @@ def test_swiglu_ragged_shapes(tp, dtype, M, d, f):
         check(k, out[k], ref[k], dtype)
     for k in ("dX", "dW1", "dW3", "dW2"):
         check(k, out[k], refb[k], dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_swiglu_slices_of_unequal_scale(tp, dtype):
+    """W3's columns and W2's rows scaled over three decades along d_ff: U, H,
+    dW3 (and dW1, through dG = dH U Swish'(G), over six) have columns, dW2
+    rows, of very different size; each slice is compared with the oracle
+    against its own largest value."""
+    M, d, f = 512, 256, 384
+    _say(f"swiglu slices of unequal scale {dtype} M={M} d={d} f={f}")
+    inp = tpsynth.random_swiglu(M, d, f, dtype, seed=23, w_std=0.05)
+    sc = np.logspace(-3.0, 0.0, f)
+    rnd = tpsynth.round_to_bf16 if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    inp["W3"] = rnd((inp["W3"] * sc[None, :]).astype(np.float32))
+    inp["W2"] = rnd((inp["W2"] * sc[:, None]).astype(np.float32))
+    out = run_swiglu(tp, inp, dtype)
+    ref = O.swiglu_shard_fwd(inp["X"], inp["W1"], inp["W3"], inp["W2"])
+    refb = O.swiglu_shard_bwd(inp["X"], inp["W1"], inp["W3"], inp["W2"], inp["dY"])
+    for k, r, axis in (("U", ref["U"], 0), ("H", ref["H"], 0), ("dW1", refb["dW1"], 0), ("dW3", refb["dW3"], 0),
+                       ("dW2", refb["dW2"], 1)):
+        err = _slice_rel_err(out[k], r, axis)
+        assert err <= TOL[dtype], f"{k}: worst slice max_rel_err {err:.3e} > {TOL[dtype]}"
+    for k in ("G", "Z"):
+        check(k, out[k], ref[k], dtype)
+    check("dX", out["dX"], refb["dX"], dtype)
 
 
 def test_swiglu_c3_full_size_sampled(tp):
