@@ -23,9 +23,10 @@
 // natural row-major layout (K rows of 256 bytes with an XOR chunk swizzle, V
 // as [keys][d] rows read back transposed with ds_read_b64_tr_b16 in the key
 // order the P registers hold), no staging registers or register transposes;
-// at most 256 registers per wave, so two workgroups share a CU and one
-// wave's softmax overlaps another's matrix products.  Within a wave the
-// loop is software-pipelined: the next key tile's score MFMAs are issued
+// at most 256 registers per wave, so two waves share each SIMD (two 4-wave
+// workgroups per CU, or one 8-wave workgroup holding two query heads of a
+// group) and one wave's softmax overlaps another's matrix products.  Within a
+// wave the loop is software-pipelined: the next key tile's score MFMAs are issued
 // before this tile's softmax, so both kinds of work are in flight (K and V
 // have separate two-stage LDS rings for that).  The subtracted running max
 // may lag a row's true max by up to 2^8, so O^T and the sum are rescaled only
