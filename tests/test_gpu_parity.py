@@ -552,6 +552,7 @@ def run_attn(tp, inp, b, s, h_l, dh, causal=True, dY=None):
     (3, 257, 96, 2, 64, True),
     (1, 900, 64, 1, 128, False),     # 15 key tiles (an odd count), non-causal
     (1, 1000, 64, 2, 128, True),     # 8 query tiles with 2 to 16 key tiles each
+    (1, 3000, 64, 2, 128, True),     # long and ragged: up to 47 key tiles, the last one partial
 ])
 def test_attention_small_shapes(tp, b, s, d, h_l, dh, causal):
     _say(f"attention b={b} s={s} d={d} h_l={h_l} dh={dh} causal={causal}")
@@ -735,6 +736,7 @@ def run_gqa(tp, inp, b, s, h_l, h_kv, dh, causal=True):
     (1, 64, 72, 16, 1, 128, True),    # the G1 grouping, 16 query heads on one K/V head
     (1, 300, 64, 3, 1, 128, True),    # an odd group: one query head per workgroup
     (1, 200, 64, 4, 2, 128, False),   # two query heads per workgroup, non-causal (every wave on every tile)
+    (1, 3000, 64, 4, 2, 128, True),   # two query heads per workgroup, long and ragged
     (1, 256, 2048, 4, 1, 128, True),  # long d: the K/V projection splits K (2 ways) through Z's memory
     (2, 128, 4096, 4, 2, 128, True),  # 4-way split, two K/V heads scattered
 ])
