@@ -535,17 +535,19 @@ hipError_t launch_attn_fwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
     GemmParams pk = make_params(M, Nkv, make_seg(X, d, M * d, Wk, Nkv, d * Nkv, d));
     pk.Bz[0] = static_cast<const bf16*>(Wk);
     pk.Bz[1] = static_cast<const bf16*>(Wv);
-    // K and V are narrow (h_kv * d_head columns) and K = d is long: split K when
-    // that fills the CUs, with fp32 partials in Z's memory (Z is written only by
-    // the output projection at the end, and holds M * d bf16).
-    const int64_t tiles = cdiv(M, 256) * cdiv(Nkv, 128) * 2;
+    // K and V are narrow (h_kv * d_head columns) and K = d is long: split K
+    // until the 128x128 tiles fill the CUs' 512 slots (two per CU), with fp32
+    // partials in Z's memory (Z is written only by the output projection at
+    // the end, and holds M * d bf16).  G1: 4 ways, 512 workgroups, 99 us;
+    // 256x128 tiles (one per CU, 4 ways) took 123 us.
+    const int64_t tiles = cdiv(M, 128) * cdiv(Nkv, 128) * 2;
     int split = 1;
-    while (split < 16 && tiles * split * 2 <= 256 && d / (split * 2) >= 1024) split *= 2;
+    while (split < 16 && tiles * split * 2 <= 512 && d / (split * 2) >= 1024) split *= 2;
     if ((int64_t)split * 2 * M * Nkv * 4 > M * d * 2) split = 1;
     if (split > 1) {
       float* part = static_cast<float*>(Z);
       EpiSplitZ e{part, Nkv, 2 * M * Nkv, M * Nkv};
-      TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wkv_split", pk, e, GemmPlan{CFG_M, split}, 2)));
+      TPK_TRY((launch_gemm<true, false, false>(st, "attn.x_wkv_split", pk, e, GemmPlan{CFG_S, split}, 2)));
       const int64_t n = 2 * M * Nkv / 8;
       TPK_TRY(launch("attn.kv_split_sum", attn_kv_split_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st,
                      (const float*)part, split, M, Nkv, (int)s, (int)h_kv, (int)d_head, static_cast<bf16*>(K),
