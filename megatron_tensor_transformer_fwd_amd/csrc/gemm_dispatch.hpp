@@ -107,6 +107,14 @@ inline GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool dual, bool allow
       double t = std::ceil((double)(tiles * s) / CUS) * tile_flop / (rate[cfg] * CU_FLOPS);
       if (cfg == CFG_S && allow_split && nbatch > 1 && tiles * s > 256)   // two S tiles per CU
         t = std::ceil((double)(tiles * s) / (2.0 * CUS)) * 2.0 * tile_flop / (TPK_RATE_S2 * CU_FLOPS);
+      // An unbatched product without a K split whose 256x256 tiles would leave
+      // one partly filled round (a narrow output: C4's V projection and dO,
+      // E1's dZ E) fills all of it with 128x128 tiles, two per CU, at the
+      // paired rate: 78.8 -> 70.1 and 94.8 -> 77.2 us at C4 against 256x128
+      // tiles one per CU.
+      if (cfg == CFG_S && !allow_split && nbatch == 1 && s == 1 && tiles > 256 && tiles <= 512 &&
+          cdiv(M, 256) * cdiv(N, 256) < 256)
+        t = 2.0 * tile_flop / (TPK_RATE_S2 * CU_FLOPS);
       if (s > 1) t += (double)(s + 1) * (double)M * (double)N * (double)nbatch * 4.0 / REDUCE_BPS + LAUNCH_S;
       if (t < best_t * 0.97) {
         best_t = t;
