@@ -71,7 +71,7 @@ struct EpiGelu {
     if constexpr (O == 0) return v;
     f32x4 h;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) h[q] = gelu_f(v[q]);
+    for (int q = 0; q < 4; ++q) h[q] = std::is_same_v<T, bf16> ? gelu_bf16(v[q]) : gelu_f(v[q]);
     return h;
   }
 };
@@ -97,7 +97,7 @@ struct EpiDGelu {
     const f32x4 a = Quad<T>::unpack(x.a);
     f32x4 r;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = v[q] * gelu_prime_f(a[q]);
+    for (int q = 0; q < 4; ++q) r[q] = v[q] * (std::is_same_v<T, bf16> ? gelu_prime_bf16(a[q]) : gelu_prime_f(a[q]));
     return r;
   }
   template <int O> __device__ __forceinline__ f32x4 value(int64_t m, int64_t n, f32x4 v) const {
