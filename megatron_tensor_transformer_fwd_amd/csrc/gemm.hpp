@@ -269,83 +269,93 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
   const int lrow = lane & 31;
   const int g4 = (lane >> 5) * 4;
   const int64_t zrow = (int64_t)zb * p.z_rows;     // row offset of this batch's outputs
-  static_for<Epi::NOUT>([&]<int O>() {
-    if (!epi.template has_out<O>()) return;
-    using TO = typename Epi::template OutT<O>;
-    constexpr int ES = sizeof(TO);
-    constexpr int ROWB = BNL * ES;                 // staged row bytes
-    constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
-    constexpr int FIT = Cfg::SMEM_BYTES / ROWB;
-    constexpr int PASS = FIT >= BM ? BM : (FIT >= 128 ? 128 : (FIT >= 64 ? 64 : 32));
-    static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "staged row width");
-    static_assert(PASS * ROWB <= Cfg::SMEM_BYTES && BM % PASS == 0, "staging pass fits the LDS");
+  // A tile wholly inside the output (every tile but the ragged last ones)
+  // takes a copy of the staging without bounds checks: each check is a branch
+  // that cuts the staging loop into one block per quad, so the activation
+  // math of different quads could not be interleaved.
+  const bool inside = m0 + BM <= p.M && n0 + BNL <= p.N;
+  auto stage_all = [&](auto guard) {
+    constexpr bool G = decltype(guard)::value;
+    static_for<Epi::NOUT>([&]<int O>() {
+      if (!epi.template has_out<O>()) return;
+      using TO = typename Epi::template OutT<O>;
+      constexpr int ES = sizeof(TO);
+      constexpr int ROWB = BNL * ES;                 // staged row bytes
+      constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
+      constexpr int FIT = Cfg::SMEM_BYTES / ROWB;
+      constexpr int PASS = FIT >= BM ? BM : (FIT >= 128 ? 128 : (FIT >= 64 ? 64 : 32));
+      static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "staged row width");
+      static_assert(PASS * ROWB <= Cfg::SMEM_BYTES && BM % PASS == 0, "staging pass fits the LDS");
 #pragma unroll
-    for (int pass = 0; pass < BM / PASS; ++pass) {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // LDS free
+      for (int pass = 0; pass < BM / PASS; ++pass) {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // LDS free
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int rl = wm * WTM + i * 32;           // first tile row of block i (uniform)
-        if (rl < pass * PASS || rl >= (pass + 1) * PASS) continue;
-        const int r = rl + lrow - pass * PASS;
-        const int64_t m = m0 + rl + lrow;
-        char* rowp = smem + r * ROWB;
-        constexpr int JN = DUAL ? TN / 2 : TN;
-        using AuxT = typename epi_aux_type<Epi>::type;
-        [[maybe_unused]] AuxT ax[JN][4];
-        if constexpr (epi_aux<Epi>::value) {
+        for (int i = 0; i < TM; ++i) {
+          const int rl = wm * WTM + i * 32;           // first tile row of block i (uniform)
+          if (rl < pass * PASS || rl >= (pass + 1) * PASS) continue;
+          const int r = rl + lrow - pass * PASS;
+          const int64_t m = m0 + rl + lrow;
+          char* rowp = smem + r * ROWB;
+          constexpr int JN = DUAL ? TN / 2 : TN;
+          using AuxT = typename epi_aux_type<Epi>::type;
+          [[maybe_unused]] AuxT ax[JN][4];
+          if constexpr (epi_aux<Epi>::value) {
+#pragma unroll
+            for (int j = 0; j < JN; ++j)
+#pragma unroll
+              for (int b = 0; b < 4; ++b) {
+                const int64_t n = n0 + wn * WTN + j * 32 + 8 * b + g4;
+                if (!G || (m < p.M && n < p.N)) ax[j][b] = epi.template aux_load<O>(m + zrow, n);
+              }
+          }
 #pragma unroll
           for (int j = 0; j < JN; ++j)
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-              const int64_t n = n0 + wn * WTN + j * 32 + 8 * b + g4;
-              if (m < p.M && n < p.N) ax[j][b] = epi.template aux_load<O>(m + zrow, n);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < JN; ++j)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int nl = (DUAL ? wn * (WTN / 2) : wn * WTN) + j * 32 + 8 * b + g4;
-            const int64_t n = n0 + nl;
-            if (m < p.M && n < p.N) {
-              f32x4 v;
-              if constexpr (epi_aux<Epi>::value) {
-                static_assert(!DUAL, "auxiliary inputs in single-B products only");
-                const f32x4 a = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2], acc[i][j][4 * b + 3]};
-                v = epi.template value_aux<O>(m + zrow, n, a, ax[j][b]);
-              } else if constexpr (DUAL) {
-                const int jj = j + TN / 2;
-                const f32x4 g = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2], acc[i][j][4 * b + 3]};
-                const f32x4 u = {acc[i][jj][4 * b], acc[i][jj][4 * b + 1], acc[i][jj][4 * b + 2], acc[i][jj][4 * b + 3]};
-                v = epi.template value2<O>(m + zrow, n, g, u);
-              } else {
-                const f32x4 a = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2], acc[i][j][4 * b + 3]};
-                v = epi.template value<O>(m + zrow, n, a);
+              const int nl = (DUAL ? wn * (WTN / 2) : wn * WTN) + j * 32 + 8 * b + g4;
+              const int64_t n = n0 + nl;
+              if (!G || (m < p.M && n < p.N)) {
+                f32x4 v;
+                if constexpr (epi_aux<Epi>::value) {
+                  static_assert(!DUAL, "auxiliary inputs in single-B products only");
+                  const f32x4 a = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2], acc[i][j][4 * b + 3]};
+                  v = epi.template value_aux<O>(m + zrow, n, a, ax[j][b]);
+                } else if constexpr (DUAL) {
+                  const int jj = j + TN / 2;
+                  const f32x4 g = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2], acc[i][j][4 * b + 3]};
+                  const f32x4 u = {acc[i][jj][4 * b], acc[i][jj][4 * b + 1], acc[i][jj][4 * b + 2], acc[i][jj][4 * b + 3]};
+                  v = epi.template value2<O>(m + zrow, n, g, u);
+                } else {
+                  const f32x4 a = {acc[i][j][4 * b], acc[i][j][4 * b + 1], acc[i][j][4 * b + 2], acc[i][j][4 * b + 3]};
+                  v = epi.template value<O>(m + zrow, n, a);
+                }
+                const int byte = nl * ES;
+                const int pc = (byte >> 4) ^ (r & (CPR - 1));
+                Quad<TO>::store(reinterpret_cast<TO*>(rowp + pc * 16 + (byte & 15)), v);
               }
-              const int byte = nl * ES;
-              const int pc = (byte >> 4) ^ (r & (CPR - 1));
-              Quad<TO>::store(reinterpret_cast<TO*>(rowp + pc * 16 + (byte & 15)), v);
             }
-          }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // staged tile complete
-      if constexpr (epi_row_reduce<Epi>::value)     // per-row statistics of the staged (stored) values
-        epi.template row_reduce<O, Cfg::NT, PASS, CPR, BNL>(smem, pass * PASS, m0, n0, p, tid);
-      constexpr int TOTAL = PASS * CPR;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // staged tile complete
+        if constexpr (epi_row_reduce<Epi>::value)     // per-row statistics of the staged (stored) values
+          epi.template row_reduce<O, Cfg::NT, PASS, CPR, BNL>(smem, pass * PASS, m0, n0, p, tid);
+        constexpr int TOTAL = PASS * CPR;
 #pragma unroll 4
-      for (int idx = tid; idx < TOTAL; idx += Cfg::NT) {
-        const int r = idx / CPR, c = idx % CPR;
-        const int64_t m = m0 + pass * PASS + r;
-        const int64_t n = n0 + c * (16 / ES);
-        if (m < p.M && n < p.N) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(smem + r * ROWB + ((c ^ (r & (CPR - 1))) * 16));
-          // streaming store: the tile is not read again by this product, and
-          // its dirty lines would otherwise compete with the operand stream
-          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(epi.template out_ptr<O>(m + zrow, n, split, zb)));
+        for (int idx = tid; idx < TOTAL; idx += Cfg::NT) {
+          const int r = idx / CPR, c = idx % CPR;
+          const int64_t m = m0 + pass * PASS + r;
+          const int64_t n = n0 + c * (16 / ES);
+          if (!G || (m < p.M && n < p.N)) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(smem + r * ROWB + ((c ^ (r & (CPR - 1))) * 16));
+            // streaming store: the tile is not read again by this product, and
+            // its dirty lines would otherwise compete with the operand stream
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(epi.template out_ptr<O>(m + zrow, n, split, zb)));
+          }
         }
       }
-    }
-  });
+    });
+  };
+  if (inside) stage_all(std::false_type{});
+  else stage_all(std::true_type{});
 }
 
 // Operand description kept in registers for the whole kernel (the kernel
