@@ -274,6 +274,11 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
   // that cuts the staging loop into one block per quad, so the activation
   // math of different quads could not be interleaved.
   const bool inside = m0 + BM <= p.M && n0 + BNL <= p.N;
+  // The main loop's trailing DMAs (issued past the last k-tile into slots no
+  // one reads) must land before the LDS is reused; after that, each pass
+  // waits only for the LDS reads of the one before, so its activation math
+  // runs while the previous pass's stores drain.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   auto stage_all = [&](auto guard) {
     constexpr bool G = decltype(guard)::value;
     static_for<Epi::NOUT>([&]<int O>() {
@@ -288,7 +293,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
       static_assert(PASS * ROWB <= Cfg::SMEM_BYTES && BM % PASS == 0, "staging pass fits the LDS");
 #pragma unroll
       for (int pass = 0; pass < BM / PASS; ++pass) {
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // LDS free
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // LDS free
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const int rl = wm * WTM + i * 32;           // first tile row of block i (uniform)
