@@ -240,15 +240,17 @@ def _elementwise(name, got, ref, scale, rtol):
 _ACT_RTOL = {"bf16": 2.0 ** -8, "f32": 1e-5}
 
 
+@pytest.mark.parametrize("n", [64, 512])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_gelu_elementwise_tails(tp, dtype):
+def test_gelu_elementwise_tails(tp, dtype, n):
     """GeLU and GeLU' value by value over [-10, 10]: with X = W2 = I the forward
     gives A = W1 and H = GeLU(W1), and the backward's dW1 = X^T dA is
     dA = dY * GeLU'(W1) itself, each rounded once to the output type.  The
     bound is relative to each value (to |dY| (Phi + |x| phi) for GeLU', which
-    crosses zero), so the lower tail, where GeLU is tiny, is checked too."""
-    _say(f"gelu elementwise tails {dtype}")
-    n = 64
+    crosses zero), so the lower tail, where GeLU is tiny, is checked too.
+    n = 64 leaves every output tile ragged (the bounds-checked epilogue);
+    n = 512 fills whole tiles (the unchecked one)."""
+    _say(f"gelu elementwise tails {dtype} n {n}")
     I = np.eye(n)
     W1 = _as_dtype(_act_grid(n, seed=1), dtype)
     dY = _as_dtype(np.random.default_rng(2).standard_normal((n, n)), dtype)
@@ -263,13 +265,13 @@ def test_gelu_elementwise_tails(tp, dtype):
     _elementwise("dA (dW1)", out["dW1"], dY * O.gelu_prime(W1), np.abs(dY) * (cdf + np.abs(W1) * phi), rtol)
 
 
+@pytest.mark.parametrize("n", [64, 512])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_swiglu_elementwise_tails(tp, dtype):
+def test_swiglu_elementwise_tails(tp, dtype, n):
     """Swish and Swish' value by value: with X = W2 = I, G = W1 and U = W3, so
     H = Swish(W1) * W3, and the weight gradients are dW1 = dG = dY * U * Swish'(G)
-    and dW3 = dU = dY * Swish(G) themselves."""
-    _say(f"swiglu elementwise tails {dtype}")
-    n = 64
+    and dW3 = dU = dY * Swish(G) themselves (n as in the GeLU test)."""
+    _say(f"swiglu elementwise tails {dtype} n {n}")
     I = np.eye(n)
     W1 = _as_dtype(_act_grid(n, seed=3), dtype)
     W3 = _as_dtype(np.random.default_rng(4).standard_normal((n, n)), dtype)
