@@ -102,17 +102,23 @@ hipError_t launch_attn_bwd(hipStream_t st, int64_t b, int64_t s, int64_t d, int6
                                   dQKV, Nt, N, Nkv, pk, pv));
   }
   TPK_TRY(launch_attn_concat3(st, Wq, Wk, Wv, Wcat, d, N, Nkv));   // [W_Q | W_K | W_V]
-  {  // dX = [dQ | dK | dV] [W_Q | W_K | W_V]^T
-    GemmParams p = make_params(M, d, make_seg(dQKV, Nt, M * Nt, Wcat, Nt, d * Nt, Nt));
-    EpiStore<bf16> e{static_cast<bf16*>(dX), d, 0};
-    TPK_TRY((launch_gemm<true, true, false>(st, "attn_bwd.dqkv_wt", p, e, plan_gemm(M, d, Nt, false, false))));
-  }
-  {  // [dW_Q | dW_K | dW_V] = X^T [dQ | dK | dV]
-    GemmParams p = make_params(d, Nt, make_seg(X, d, M * d, dQKV, Nt, M * Nt, M));
-    EpiF32Parts e{{dWq, dWk, dWv}, N, Nkv};
-    TPK_TRY((launch_gemm<false, false, false>(st, "attn_bwd.xt_dqkv", p, e, lay.wqkv, 1,
-                                              reinterpret_cast<float*>(w + lay.tail))));
-  }
+  // dX = [dQ | dK | dV] [W_Q | W_K | W_V]^T and [dW_Q | dW_K | dW_V] = X^T [dQ | dK | dV]
+  GemmParams px = make_params(M, d, make_seg(dQKV, Nt, M * Nt, Wcat, Nt, d * Nt, Nt));
+  EpiStore<bf16> ex{static_cast<bf16*>(dX), d, 0};
+  const GemmPlan plx = plan_gemm(M, d, Nt, false, false);
+  GemmParams pw = make_params(d, Nt, make_seg(X, d, M * d, dQKV, Nt, M * Nt, M));
+  EpiF32Parts ew{{dWq, dWk, dWv}, N, Nkv};
+  // The two are independent: one launch where the weight gradient's tiles
+  // (K = M, the longer) would leave a partial round (C4: 192 tiles), the
+  // dX tiles filling it.
+  const GemmPlan plw = plan_gemm(d, Nt, M, false, false);
+  if (gemm_pair_est(plw, tiles_for(CFG_L, d, Nt, false), plx, tiles_for(CFG_L, M, d, false)) <
+      0.97 * (lay.wqkv.est + plx.est))
+    return launch_gemm_pair<false, false, EpiF32Parts, true, true, EpiStore<bf16>>(st, "attn_bwd.wgrad_dx_pair",
+                                                                                    pw, ew, px, ex);
+  TPK_TRY((launch_gemm<true, true, false>(st, "attn_bwd.dqkv_wt", px, ex, plx)));
+  TPK_TRY((launch_gemm<false, false, false>(st, "attn_bwd.xt_dqkv", pw, ew, lay.wqkv, 1,
+                                            reinterpret_cast<float*>(w + lay.tail))));
   return hipSuccess;
 }
 

@@ -232,6 +232,15 @@ __device__ __forceinline__ void grid_coords(int& lx, int& ly, int& lz, int& xcd)
   ly = t2 / nz;
 }
 
+// The same remap for workgroup lin of a one-dimensional range of `total`.
+__device__ __forceinline__ void coords_1d(int lin, int total, int& lx, int& xcd) {
+  constexpr int NXCD = 8;
+  const int q = total / NXCD, r = total % NXCD;
+  xcd = lin % NXCD;
+  const int local = lin / NXCD;
+  lx = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
+}
+
 template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   [&]<int... I>(std::integer_sequence<int, I...>) { (f.template operator()<I>(), ...); }(
@@ -487,8 +496,8 @@ __device__ __forceinline__ int bcol_of(int wn, int j) {
 // (deterministic: each tile always sums in the same order).
 // ----------------------------------------------------------------------------
 template <class Cfg, bool A_KM, bool B_KM, bool DUAL, class Epi>
-__global__ void __launch_bounds__(Cfg::NT)
-gemm_bf16_kernel(const GemmParams p, const Epi epi) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const Epi& epi, int lx, int split, int zb, int xcd,
+                                          char* smem) {
   constexpr int BK = Cfg::BK;
   constexpr int TM = Cfg::TM, TN = Cfg::TN, WTM = Cfg::WTM;
   constexpr int BNL = DUAL ? Cfg::BN / 2 : Cfg::BN;   // output columns per tile
@@ -557,15 +566,12 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
   static_assert(!DUAL || !B_KM, "dual-B products take N-major right operands");
   static_assert(!DUAL || Cfg::BN == 256, "dual-B tiles hold two 128-column sub-tiles");
 
-  __shared__ __attribute__((aligned(1024))) char smem[Cfg::SMEM_BYTES];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
-  int lx, split, zb, xcd, tm, tn;
-  grid_coords(lx, split, zb, xcd);
+  int tm, tn;
   tile_of(p.tile_base + lx, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * Cfg::BM;
   const int64_t n0 = (int64_t)tn * BNL;
@@ -672,6 +678,32 @@ gemm_bf16_kernel(const GemmParams p, const Epi epi) {
   }
 
   store_tile<Cfg, DUAL>(acc, p, epi, m0, n0, wm, wn, lane, zb, split, smem, tid);
+}
+
+template <class Cfg, bool A_KM, bool B_KM, bool DUAL, class Epi>
+__global__ void __launch_bounds__(Cfg::NT)
+gemm_bf16_kernel(const GemmParams p, const Epi epi) {
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::SMEM_BYTES];
+  int lx, split, zb, xcd;
+  grid_coords(lx, split, zb, xcd);
+  gemm_tile<Cfg, A_KM, B_KM, DUAL, Epi>(p, epi, lx, split, zb, xcd, smem);
+}
+
+// Two independent products in one launch (one tile shape, no K split, no
+// batches), so that the tiles of one fill the compute units the other's last
+// round leaves idle.  Workgroups 0 .. n1-1 take the first product's tiles
+// (the one with the longer K, dispatched first), the rest the second's; each
+// range is remapped XCD-contiguous like a launch of its own.
+template <class Cfg, bool A1, bool B1, class E1, bool A2, bool B2, class E2>
+__global__ void __launch_bounds__(Cfg::NT)
+gemm_pair_kernel(const GemmParams p1, const E1 e1, const GemmParams p2, const E2 e2, int n1) {
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::SMEM_BYTES];
+  const int b = (int)blockIdx.x;
+  const bool first = b < n1;
+  int lx, xcd;
+  coords_1d(first ? b : b - n1, first ? n1 : (int)gridDim.x - n1, lx, xcd);
+  if (first) gemm_tile<Cfg, A1, B1, false, E1>(p1, e1, lx, 0, 0, xcd, smem);
+  else gemm_tile<Cfg, A2, B2, false, E2>(p2, e2, lx, 0, 0, xcd, smem);
 }
 
 }  // namespace tpk

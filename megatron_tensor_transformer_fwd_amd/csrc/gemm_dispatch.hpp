@@ -245,6 +245,35 @@ hipError_t launch_gemm(hipStream_t st, const char* label, GemmParams p, const Ep
   }
 }
 
+// Two independent products of the 256x256 shape without K splits in one
+// launch (gemm_pair_kernel), the first product's tiles dispatched first.
+// Estimated duration: with tile times t1, t2 (the plans' estimates over their
+// rounds), about (n1 t1 + n2 t2) / 256 plus half the shorter tile for the
+// uneven end, against ceil(n1 / 256) t1 + ceil(n2 / 256) t2 for two launches:
+// it pays where one of them leaves a partial last round.  A huge value where
+// the plans do not fit the pair kernel.
+inline double gemm_pair_est(const GemmPlan& a, int64_t n1, const GemmPlan& b, int64_t n2) {
+  if (a.cfg != CFG_L || b.cfg != CFG_L || a.split != 1 || b.split != 1 || a.tail > 1 || b.tail > 1 || n1 <= 0 ||
+      n2 <= 0)
+    return 1e30;
+  const double t1 = a.est / std::ceil(n1 / 256.0), t2 = b.est / std::ceil(n2 / 256.0);
+  return ((double)n1 * t1 + (double)n2 * t2) / 256.0 + 0.5 * std::min(t1, t2);
+}
+
+template <bool A1, bool B1, class E1, bool A2, bool B2, class E2>
+hipError_t launch_gemm_pair(hipStream_t st, const char* label, GemmParams p1, const E1& e1, GemmParams p2,
+                            const E2& e2) {
+  for (GemmParams* p : {&p1, &p2}) {
+    p->tiles_m = (int)cdiv(p->M, CfgL::BM);
+    p->tiles_n = (int)cdiv(p->N, CfgL::BN);
+    p->split_k = 1;
+    p->tile_base = 0;
+  }
+  const int n1 = p1.tiles_m * p1.tiles_n, n2 = p2.tiles_m * p2.tiles_n;
+  return launch(label, gemm_pair_kernel<CfgL, A1, B1, E1, A2, B2, E2>, dim3((unsigned)(n1 + n2)), dim3(CfgL::NT),
+                st, p1, e1, p2, e2, n1);
+}
+
 // One K segment of a bf16 product.  a_rows_or_k / b: the extent of each
 // operand's slow dimension, used for the readable range.
 inline GemmSeg make_seg(const void* A, int64_t lda, int64_t a_elems,

@@ -64,13 +64,23 @@ static hipError_t swiglu_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t 
   bf16* dGU = static_cast<bf16*>(ws);
   float* split_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.dGU_bytes);
   float* tail_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.dGU_bytes + pl.split_bytes);
-  {  // dH = dY W2^T -> dG, dU
-    GemmParams p = make_params(M, f, make_seg(dY, d, M * d, W2, d, f * d, d));
-    EpiDSwiGLU<bf16> e{static_cast<const bf16*>(G), static_cast<const bf16*>(U), dGU, f};
-    TPK_TRY((launch_gemm<true, true, false>(st, "swiglu_bwd.dyw2t_dswiglu", p, e, pl.dH, 1, tail_ws)));
-  }
-  {  // dW2 = H^T dY
-    GemmParams p = make_params(f, d, make_seg(H, f, M * f, dY, d, M * d, M));
+  // dH = dY W2^T -> dG, dU and dW2 = H^T dY are independent, as are dX and
+  // [dW1 | dW3] below: each pair runs as one launch where that beats two
+  // (partial last rounds; gemm_pair_est), the weight gradient (K = M, the
+  // longer) first.
+  GemmParams ph = make_params(M, f, make_seg(dY, d, M * d, W2, d, f * d, d));
+  EpiDSwiGLU<bf16> eh{static_cast<const bf16*>(G), static_cast<const bf16*>(U), dGU, f};
+  GemmParams p2 = make_params(f, d, make_seg(H, f, M * f, dY, d, M * d, M));
+  EpiStore<float> e2{dW2, d, 0};
+  const GemmPlan ph_plain = plan_gemm(M, f, d, false, false);
+  if (pl.dW2.split == 1 &&
+      gemm_pair_est(pl.dW2, tiles_for(CFG_L, f, d, false), ph_plain, tiles_for(CFG_L, M, f, false)) <
+          0.97 * (pl.dW2.est + pl.dH.est)) {
+    TPK_TRY((launch_gemm_pair<false, false, EpiStore<float>, true, true, EpiDSwiGLU<bf16>>(
+        st, "swiglu_bwd.htdy_dswiglu_pair", p2, e2, ph, eh)));
+  } else {
+    TPK_TRY((launch_gemm<true, true, false>(st, "swiglu_bwd.dyw2t_dswiglu", ph, eh, pl.dH, 1, tail_ws)));
+    GemmParams p = p2;
     if (pl.dW2.split > 1) {
       EpiStore<float> e{split_ws, d, f * d};
       TPK_TRY((launch_gemm<false, false, false>(st, "swiglu_bwd.htdy", p, e, pl.dW2)));
@@ -80,18 +90,21 @@ static hipError_t swiglu_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t 
       TPK_TRY((launch_gemm<false, false, false>(st, "swiglu_bwd.htdy", p, e, pl.dW2)));
     }
   }
-  {  // dX = dG W1^T + dU W3^T
-    GemmParams p = make_params(M, d, make_seg(dGU, 2 * f, M * 2 * f, W1, f, d * f, f));
-    p.nseg = 2;
-    p.seg[1] = make_seg(dGU + f, 2 * f, M * 2 * f - f, W3, f, d * f, f);
-    EpiStore<bf16> e{static_cast<bf16*>(dX), d, 0};
-    TPK_TRY((launch_gemm<true, true, false>(st, "swiglu_bwd.dgu_w13t", p, e, plan_gemm(M, d, 2 * f, false, false))));
-  }
-  {  // [dW1 | dW3] = X^T [dG | dU]
-    GemmParams p = make_params(d, 2 * f, make_seg(X, d, M * d, dGU, 2 * f, M * 2 * f, M));
-    EpiF32Halves e{dW1, dW3, f};
-    TPK_TRY((launch_gemm<false, false, false>(st, "swiglu_bwd.xtdgu", p, e, pl.dW13, 1, tail_ws)));
-  }
+  // dX = dG W1^T + dU W3^T and [dW1 | dW3] = X^T [dG | dU]
+  GemmParams px = make_params(M, d, make_seg(dGU, 2 * f, M * 2 * f, W1, f, d * f, f));
+  px.nseg = 2;
+  px.seg[1] = make_seg(dGU + f, 2 * f, M * 2 * f - f, W3, f, d * f, f);
+  EpiStore<bf16> ex{static_cast<bf16*>(dX), d, 0};
+  const GemmPlan plx = plan_gemm(M, d, 2 * f, false, false);
+  GemmParams pw = make_params(d, 2 * f, make_seg(X, d, M * d, dGU, 2 * f, M * 2 * f, M));
+  EpiF32Halves ew{dW1, dW3, f};
+  const GemmPlan pw_plain = plan_gemm(d, 2 * f, M, false, false);
+  if (gemm_pair_est(pw_plain, tiles_for(CFG_L, d, 2 * f, false), plx, tiles_for(CFG_L, M, d, false)) <
+      0.97 * (pl.dW13.est + plx.est))
+    return launch_gemm_pair<false, false, EpiF32Halves, true, true, EpiStore<bf16>>(st, "swiglu_bwd.xtdgu_dx_pair",
+                                                                                    pw, ew, px, ex);
+  TPK_TRY((launch_gemm<true, true, false>(st, "swiglu_bwd.dgu_w13t", px, ex, plx)));
+  TPK_TRY((launch_gemm<false, false, false>(st, "swiglu_bwd.xtdgu", pw, ew, pl.dW13, 1, tail_ws)));
   return hipSuccess;
 }
 
