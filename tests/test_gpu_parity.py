@@ -215,6 +215,22 @@ def test_mlp_row_pitch_limit(tp):
         check(k, out[k], refb[k], "bf16")
 
 
+def _launch_labels(tp, fn):
+    """Run fn() with the library's launch hook armed; the labels of its launches."""
+    import bench
+    L = tp.lib()
+    ev = bench.HipEvents(128)
+    assert L.tp_profile_begin(ev.start, ev.stop, ev.n) == 0
+    try:
+        r = fn()
+        torch.cuda.synchronize()
+    finally:
+        n = L.tp_profile_end()
+    labels = [L.tp_profile_label(i).decode() for i in range(n)]
+    ev.close()
+    return r, labels
+
+
 def _act_grid(n, lo=-10.0, hi=10.0, seed=0):
     """n x n values spread over [lo, hi] in shuffled order (the activations' tails included)."""
     v = np.linspace(lo, hi, n * n)
@@ -505,10 +521,14 @@ def test_swiglu_slices_of_unequal_scale(tp, dtype):
 
 
 def test_swiglu_c3_full_size_sampled(tp):
+    """At C3 size dW2 and the SwiGLU' dgrad run as one launch (176 and 352
+    tiles of 256 x 256, the dgrad's last column tile ragged): the launch list
+    must show it, and both products' outputs are checked."""
     _say("swiglu C3 bf16 full size, sampled rows/cols")
     wl = tpsynth.WORKLOADS["C3"]
     inp = tpsynth.swiglu_inputs(wl)
-    out = run_swiglu(tp, inp, "bf16")
+    out, labels = _launch_labels(tp, lambda: run_swiglu(tp, inp, "bf16"))
+    assert "swiglu_bwd.htdy_dswiglu_pair" in labels, labels
     X, W1, W3, W2, dY = (inp[k] for k in ("X", "W1", "W3", "W2", "dY"))
     rows = _sample(wl.M, 48, 21)
     cols = np.unique(np.concatenate([_sample(wl.f_local, 14, 22), [2687, 2688, 2751]]))  # ragged last tile
@@ -638,7 +658,9 @@ def test_attention_bwd_c4_full_size_sampled(tp):
     inp = tpsynth.attn_inputs(wl)
     b, s, h_l, dh = wl.b, wl.s, wl.h_local, wl.d_head
     dY = tpsynth.round_to_bf16(np.random.default_rng(44).standard_normal((b * s, wl.d)).astype(np.float32))
-    out = run_attn(tp, inp, b, s, h_l, dh, True, dY=dY)
+    # dX and [dW_Q | dW_K | dW_V] run as one launch at this size
+    out, labels = _launch_labels(tp, lambda: run_attn(tp, inp, b, s, h_l, dh, True, dY=dY))
+    assert "attn_bwd.wgrad_dx_pair" in labels, labels
     bi = 1
     rows = slice(bi * s, (bi + 1) * s)
     ref = O.attn_shard_bwd(inp["X"][rows], inp["Wq"], inp["Wk"], inp["Wv"], inp["Wo"], dY[rows], 1, s, h_l, dh)
