@@ -252,6 +252,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <class E, class = void> struct epi_row_reduce : std::false_type {};
 template <class E> struct epi_row_reduce<E, std::void_t<decltype(E::ROW_REDUCE)>> : std::true_type {};
 
+// An epilogue whose output O the next product reads at once defines
+// keep<O>() true: that output is stored without the streaming hint.
+template <class E, int O> constexpr bool epi_keep() {
+  if constexpr (requires { E::template keep<O>(); }) return E::template keep<O>();
+  else return false;
+}
+
 // An epilogue that reads other tensors at the output positions (a saved
 // activation) defines Aux, aux_load<O>(m, n) and value_aux<O>(m, n, v, aux):
 // the staging loop then issues one 32-row block's loads together before
@@ -362,7 +369,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg::TM][Cfg::TN]
             const u32x4 w = *reinterpret_cast<const u32x4*>(smem + r * ROWB + ((c ^ (r & (CPR - 1))) * 16));
             // streaming store: the tile is not read again by this product, and
             // its dirty lines would otherwise compete with the operand stream
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(epi.template out_ptr<O>(m + zrow, n, split, zb)));
+            // (plain stores for an output the epilogue keeps for its next reader)
+            u32x4* dst = reinterpret_cast<u32x4*>(epi.template out_ptr<O>(m + zrow, n, split, zb));
+            if constexpr (epi_keep<Epi, O>()) *dst = w;
+            else __builtin_nontemporal_store(w, dst);
           }
         }
       }

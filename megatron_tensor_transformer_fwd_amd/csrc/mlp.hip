@@ -7,6 +7,7 @@
 //           dX = dA W1^T                   NT product (this shard's summand)
 //           dW1 = X^T dA                   TN product (fp32, split-K if narrow)
 #include <mutex>
+#include <type_traits>
 
 #include "epilogues.hpp"
 #include "gemm_dispatch.hpp"
@@ -45,13 +46,28 @@ hipError_t mlp_bwd_scratch(void** ptr) {
 static inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // ------------------------------------------------------------------ bf16
+// H and dA are the left operand of the next products, over K = f.  With a
+// short K those products' tiles are mostly operand fetch and epilogue, and
+// H and dA stored without the streaming hint are still in the caches when
+// they start: at C2 (f 512, all shards) the Z and dX products took 79-81
+// instead of 87-88 us.  At f 4096 (C5) the same made the GeLU product 1.5% slower and its
+// readers no faster, so only narrow shards keep them.
+constexpr int64_t kKeepOperandMaxK = 1024;
+
+template <class F>
+static hipError_t with_keep(int64_t f, F&& run) {
+  return f <= kKeepOperandMaxK ? run(std::true_type{}) : run(std::false_type{});
+}
+
 static hipError_t mlp_fwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t f,
                                const void* X, const void* W1, const void* W2,
                                void* A, void* H, void* Z) {
   {  // A = X W1, H = GeLU(A)
     GemmParams p = make_params(M, f, make_seg(X, d, M * d, W1, f, d * f, d));
-    EpiGelu<bf16> e{static_cast<bf16*>(A), static_cast<bf16*>(H), f};
-    TPK_TRY((launch_gemm<true, false, false>(st, "mlp_fwd.xw1_gelu", p, e, plan_gemm(M, f, d, false, false))));
+    TPK_TRY(with_keep(f, [&](auto keep) {
+      EpiGelu<bf16, decltype(keep)::value> e{static_cast<bf16*>(A), static_cast<bf16*>(H), f};
+      return launch_gemm<true, false, false>(st, "mlp_fwd.xw1_gelu", p, e, plan_gemm(M, f, d, false, false));
+    }));
   }
   {  // Z = H W2
     GemmParams p = make_params(M, d, make_seg(H, f, M * f, W2, d, f * d, f));
@@ -103,8 +119,10 @@ static hipError_t mlp_bwd_bf16(hipStream_t st, int64_t M, int64_t d, int64_t f,
   }
   {  // dA = (dY W2^T) * GeLU'(A);  B(k, n) = W2[n][k]
     GemmParams p = make_params(M, f, make_seg(dY, d, M * d, W2, d, f * d, d));
-    EpiDGelu<bf16> e{static_cast<const bf16*>(A), dA, f};
-    TPK_TRY((launch_gemm<true, true, false>(st, "mlp_bwd.dyw2t_dgelu", p, e, plan_gemm(M, f, d, false, false))));
+    TPK_TRY(with_keep(f, [&](auto keep) {
+      EpiDGelu<bf16, decltype(keep)::value> e{static_cast<const bf16*>(A), dA, f};
+      return launch_gemm<true, true, false>(st, "mlp_bwd.dyw2t_dgelu", p, e, plan_gemm(M, f, d, false, false));
+    }));
   }
   {  // dX = dA W1^T;  B(k, n) = W1[n][k]
     GemmParams p = make_params(M, d, make_seg(dA, f, M * f, W1, f, d * f, f));
@@ -240,8 +258,10 @@ hipError_t launch_mlp_fwd_shards(hipStream_t st, int dt, int64_t n, int64_t M, i
     GemmParams p = make_params(M, f, make_seg(X, d, M * d, W1s, f, d * f, d));
     p.b_zs = d * f;
     p.z_rows = (int)M;
-    EpiGelu<bf16> e{static_cast<bf16*>(A), static_cast<bf16*>(H), f};
-    TPK_TRY((launch_gemm<true, false, false>(st, "mlp_fwd.xw1_gelu", p, e, pl.xw1, (int)n)));
+    TPK_TRY(with_keep(f, [&](auto keep) {
+      EpiGelu<bf16, decltype(keep)::value> e{static_cast<bf16*>(A), static_cast<bf16*>(H), f};
+      return launch_gemm<true, false, false>(st, "mlp_fwd.xw1_gelu", p, e, pl.xw1, (int)n);
+    }));
   }
   {  // Z_i = H_i W2_i
     GemmParams p = make_params(M, d, make_seg(H, f, M * f, W2s, d, f * d, f));
@@ -283,8 +303,10 @@ hipError_t launch_mlp_bwd_shards(hipStream_t st, int dt, int64_t n, int64_t M, i
     GemmParams p = make_params(M, f, make_seg(dY, d, M * d, W2s, d, f * d, d));
     p.b_zs = f * d;
     p.z_rows = (int)M;
-    EpiDGelu<bf16> e{static_cast<const bf16*>(A), dA, f};
-    TPK_TRY((launch_gemm<true, true, false>(st, "mlp_bwd.dyw2t_dgelu", p, e, pl.dyw2t, (int)n)));
+    TPK_TRY(with_keep(f, [&](auto keep) {
+      EpiDGelu<bf16, decltype(keep)::value> e{static_cast<const bf16*>(A), dA, f};
+      return launch_gemm<true, true, false>(st, "mlp_bwd.dyw2t_dgelu", p, e, pl.dyw2t, (int)n);
+    }));
   }
   {  // dX_i = dA_i W1_i^T
     GemmParams p = make_params(M, d, make_seg(dA, f, M * f, W1s, f, d * f, f));
