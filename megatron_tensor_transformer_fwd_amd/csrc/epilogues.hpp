@@ -56,16 +56,16 @@ struct EpiStore {
 
 // Column-parallel product with GeLU ([JY] FFN, [HC] Figure 3.4): output 0 is
 // the pre-activation A (optional), output 1 is H = GeLU(A) from the fp32 sum.
-// KEEP_H: H is stored without the streaming hint (keep<O>()), for a next
-// product that reads it at once.
-template <class T, bool KEEP_H = false>
+// KEEP: A and H are stored without the streaming hint (keep<O>()), for the
+// products that read them next (H at once, A in the backward's GeLU' dgrad).
+template <class T, bool KEEP = false>
 struct EpiGelu {
   static constexpr int NOUT = 2;
   template <int O> using OutT = T;
   T* A;   // may be null
   T* H;
   int64_t ld;
-  template <int O> static constexpr bool keep() { return KEEP_H && O == 1; }
+  template <int O> static constexpr bool keep() { return KEEP; }
   template <int O> __device__ __forceinline__ bool has_out() const { return O == 1 || A != nullptr; }
   template <int O> __device__ __forceinline__ T* out_ptr(int64_t m, int64_t n, int, int) const {
     return (O == 0 ? A : H) + m * ld + n;
@@ -81,7 +81,7 @@ struct EpiGelu {
 
 // Backward dgrad of the row-parallel product with GeLU' fused:
 // dA = (dY W2^T) * GeLU'(A), A read back from the forward's saved copy.
-// KEEP: dA is stored without the streaming hint, as H above.
+// KEEP: dA is stored without the streaming hint, as A and H above.
 template <class T, bool KEEP = false>
 struct EpiDGelu {
   static constexpr int NOUT = 1;

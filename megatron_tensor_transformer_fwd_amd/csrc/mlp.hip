@@ -50,8 +50,9 @@ static inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // short K those products' tiles are mostly operand fetch and epilogue, and
 // H and dA stored without the streaming hint are still in the caches when
 // they start: at C2 (f 512, all shards) the Z and dX products took 79-81
-// instead of 87-88 us.  At f 4096 (C5) the same made the GeLU product 1.5% slower and its
-// readers no faster, so only narrow shards keep them.
+// instead of 87-88 us (A, kept as well, saves the GeLU' dgrad another 1 us).
+// At f 4096 (C5) the same made the GeLU product 1.5% slower and its readers
+// no faster, so only narrow shards keep them.
 constexpr int64_t kKeepOperandMaxK = 1024;
 
 template <class F>
