@@ -417,11 +417,19 @@ attn_bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
 
   const int nqt = (s + BQ - 1) / BQ;
   const int ngrp = nb * hl / HPW;                     // (batch, head set) pairs
-  const int qt = nqt - 1 - (int)(blockIdx.x / ngrp);   // heaviest tiles first
+  // Several rounds of workgroups: heaviest tiles first.  One round (at most
+  // two workgroups per CU on 256 CUs, causal, an even tile count): the first
+  // half of the grid takes the heavy tiles in falling order and the second
+  // half the light ones in rising order, so the two workgroups that share a
+  // CU carry nqt + 1 chunks between them.
+  const int bid = (int)blockIdx.x, half = (int)(gridDim.x / 2);
+  const bool light = HPW == 1 && causal && nqt % 2 == 0 && gridDim.x <= 2 * 256 && bid >= half;
+  const int rank = light ? bid - half : bid;
+  const int qt = light ? rank / ngrp : nqt - 1 - rank / ngrp;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = wave % NW;                           // wave within its head
-  const int bh = (int)(blockIdx.x % ngrp) * HPW + wave / NW;
+  const int bh = (rank % ngrp) * HPW + wave / NW;
   const int bi = bh / hl, h = bh % hl;
   const int lq = lane & 31, g = lane >> 5;
   const int q0 = qt * BQ, qw = q0 + wq * 32, qme = qw + lq;
